@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark one rank's ZeRO shard step on one MI355X.
+
+A step is one pass of the whole hot path over resident synthetic inputs:
+for the default workload (Psi = 7.5e9 flat buffer, N_d = 64, rank 0's
+117,187,500-element partition) that is zero_reduce_grad_shard over the 64
+fp16 gradient slices followed by zero_adam_step (fp32 master, m, v in place,
+fresh fp16 params), with the reduce's non-finite flag as the step's skip
+input.  Other workloads (--workload) run the Adam step alone (N_d = 1 or a
+single rank's shard).
+
+Prints one JSON line: params updated per second (value), the per-kernel
+HIP-event durations measured inside the timed region on the launch stream,
+the dominant kernel's roofline against MI355X's 8 TB/s HBM peak, and the CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "params updated/sec and achieved HBM GB/s (% of roofline) per Adam shard step"
+KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", "zs_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def kernel_src_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    pat = re.compile(r"^traffic:\s+(.*)$")
+    for line in open(TRAFFIC_FILE):
+        m = pat.match(line.strip())
+        if not m:
+            continue
+        kv = dict(x.split("=", 1) for x in m.group(1).split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload:
+            if kv.get("src_sha256") != kernel_src_sha():
+                return None
+            return float(kv["hbm_bytes_per_launch"])
+    return None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flat_7p5b_nd64",
+                    choices=["flat_7p5b_nd64", "flat_7p5b_nd8", "gpt2_xl", "llama_7b", "tiny_flat"])
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
+                    help="elements of the shard the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Step:
+    """Device state and the launches of one step for a workload."""
+
+    def __init__(self, zs, W, name):
+        import torch
+        self.zs, self.W, self.torch = zs, W, torch
+        wl = W.WORKLOADS[name]
+        self.wl = wl
+        self.hp = zs.AdamHParams(**W.ADAM_HP)
+        self.flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.rows = None
+        if len(wl.tensors) == 1:
+            lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+            self.layout = lay
+            self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total)
+            self.tensors = [sh]
+            if wl.reduce_slices:
+                self.slice_buf, self.rows = W.device_slices(wl, lay.real_len)
+            else:
+                W.device_fill_grads(wl, self.tensors, 1)
+        else:
+            self.layout = None
+            self.tensors = W.device_list_state(wl)
+            W.device_fill_grads(wl, self.tensors, 1)
+        self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors])
+        self.n_params = self.plan.stats()["n_params"]
+        self.t = 0
+
+    def reduce(self):
+        self.zs.zero_reduce_grad_shard(self.rows, self.tensors[0].g, self.rflag)
+
+    def adam(self):
+        self.t += 1
+        skip = self.rflag if self.rows is not None else None
+        self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip)
+
+    def kernels(self):
+        ks = []
+        if self.rows is not None:
+            ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
+        ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
+        return ks
+
+
+def cpu_baseline(step, sample_n: int):
+    """The oracle as it stands, on contiguous partitions of the first
+    sample_n elements of the shard, one host thread per partition."""
+    import concurrent.futures as cf
+    import numpy as np
+    import torch
+    import oracle
+
+    T = max(1, min(16, len(os.sched_getaffinity(0))))
+    sh = step.tensors[0]
+    n = min(sample_n, sh.n)
+    hp = dict(step.W.ADAM_HP)
+    w = sh.w[:n].cpu().numpy().copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = np.zeros(n, np.uint16)
+    if step.rows is not None:
+        sl = [r[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for r in step.rows]
+        g = np.empty(n, np.uint16)
+    else:
+        g = sh.g[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        sl = None
+    bounds = [(n * i // T, n * (i + 1) // T) for i in range(T)]
+
+    def part(b):
+        lo, hi = b
+        if sl is not None:
+            oracle.reduce_grad([s[lo:hi] for s in sl], g[lo:hi])
+        oracle.adam_step(g[lo:hi], p[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], t=1, **hp)
+
+    oracle.lib()
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(T) as ex:
+        list(ex.map(part, bounds))
+    dt = time.perf_counter() - t0
+    what = ("reduce of %d fp16 slices + Adam step" % step.wl.nd) if sl is not None else "Adam step"
+    return {"value": n / dt, "unit": "params/s", "cores": T, "kind": "oracle",
+            "sample": f"first {n} elements of the shard: {what}, {T} host threads, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the shard step "
+              "has no cross-GPU exchange to time here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from zero_partitioned_mixed_layout_amd import workloads as W
+    from zero_partitioned_mixed_layout_amd import zero_shard as zs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
+    step = Step(zs, W, args.workload)
+    ks = step.kernels()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for _, launch, _ in ks:
+            launch()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
+          flush=True)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ks] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for (a, b), (_, launch, _) in zip(ev[k], ks):
+            a.record(stream)
+            launch()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kstats = {}
+    for j, (name, _, alg_bytes) in enumerate(ks):
+        ms = [ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(args.steps)]
+        avg_s = sum(ms) / len(ms) / 1e3
+        gbps = alg_bytes / avg_s / 1e9
+        kstats[name] = {"avg_us": avg_s * 1e6, "min_us": min(ms) * 1e3,
+                        "alg_bytes_per_launch": alg_bytes, "gbps": gbps,
+                        "frac": gbps / HBM_PEAK_GBPS, "total_s": sum(ms) / 1e3}
+    dom = max(kstats, key=lambda k: kstats[k]["total_s"])
+    d = kstats[dom]
+    traffic = measured_traffic(dom, args.workload)
+    value = step.n_params * args.steps / wall
+    bytes_per_step = sum(b for _, _, b in ks)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(step, args.cpu_sample)
+    cfg = {"workload": args.workload, "psi": step.wl.psi, "nd": step.wl.nd,
+           "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
+           "tensors": len(step.wl.tensors),
+           "kernels_per_step": [k for k, _, _ in ks],
+           "alg_bytes_per_step": bytes_per_step,
+           "step_hbm_gbps": bytes_per_step * args.steps / wall / 1e9}
+    out = {
+        "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": cfg,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["gbps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["frac"],
+                     "traffic": traffic},
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                        for kk, vv in s.items() if kk != "total_s"} for k, s in kstats.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    step.plan.destroy()
+
+
+if __name__ == "__main__":
+    main()

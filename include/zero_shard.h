@@ -1,0 +1,215 @@
+/*
+ * zero_shard.h -- C ABI of libzeroshard.so: one data-parallel rank's ZeRO
+ * partition step for mixed-precision Adam on an AMD MI355X (gfx950).
+ *
+ * Sources (three web pages; cited by title and section):
+ *   [16B]  "Your 7.5B model's weights fit in 15 GB ... the 16-byte parameter
+ *          and ZeRO's three-stage split" (blog.teqners.com)
+ *   [ER10] "ZeRO and the Memory Tricks", The Engine Room ch. 10
+ *          (hoshank.vercel.app)
+ *   [DSZ]  "DeepSpeed ZeRO: account for every training state"
+ *          (chenhuiyu.github.io)
+ *
+ * Conventions for every function:
+ *  - Returns a status: ZERO_OK (0) or a negative ZERO_E* code; outputs are
+ *    written only on ZERO_OK.  No C++ exception crosses this boundary.
+ *  - "Device pointer" means memory of the current HIP device (hipMalloc'd,
+ *    e.g. by PyTorch).  "Host pointer" means ordinary process memory.
+ *  - fp16 arrays hold IEEE binary16 values (2 bytes each), fp32 arrays IEEE
+ *    binary32 values, all contiguous, element i at byte offset i * size.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  Device work is
+ *    enqueued on it and the call returns without synchronising; results are
+ *    ready once the stream reaches that point.
+ *  - The library keeps no global mutable state; the step and reduce entry
+ *    points allocate nothing.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1)    /* bad argument (null, range, alignment, aliasing) */
+#define ZERO_EOVERFLOW (-2) /* a byte or element count exceeds 64 bits */
+#define ZERO_EHIP (-3)      /* HIP runtime or launch error (captured, cleared) */
+#define ZERO_ENOMEM (-4)    /* device allocation failed (plan creation only) */
+
+/* Largest N_d zero_reduce_grad_shard accepts (slice pointers travel as
+ * kernel arguments). */
+#define ZERO_MAX_SLICES 256
+
+/* Shard of a flat buffer of psi elements split over nd ranks. */
+typedef struct zero_layout {
+    uint64_t padded_total; /* psi rounded up to a multiple of nd * align */
+    uint64_t shard_len;    /* padded_total / nd, a multiple of align */
+    uint64_t offset;       /* rank * shard_len: first element of this shard */
+    uint64_t real_len;     /* elements of this shard below psi (rest: pad) */
+} zero_layout;
+
+/* One tensor of this rank's shard: five device arrays of n elements.
+ * param_f16 is written, grad_f16 read, master/m/v read and written in
+ * place.  The five ranges must not overlap.  The memory is borrowed: the
+ * caller owns it and keeps it alive while a plan refers to it. */
+typedef struct zero_tensor {
+    void *param_f16;      /* fp16 parameter (written fresh each step) */
+    const void *grad_f16; /* fp16 gradient of this rank's shard */
+    float *master;        /* fp32 master copy of the parameter */
+    float *m;             /* fp32 Adam first moment */
+    float *v;             /* fp32 Adam second moment */
+    uint64_t n;           /* elements; 0 is allowed (pointers then ignored) */
+} zero_tensor;
+
+/* Adam hyperparameters, as doubles; see zero_adam_scalars for how they
+ * become the fp32 constants of the step. */
+typedef struct zero_adam_hparams {
+    double lr, beta1, beta2, eps;
+    double weight_decay; /* must be 0: the pages define no weight decay */
+} zero_adam_hparams;
+
+/* Opaque multi-tensor plan (device-resident chunk table). */
+typedef struct zero_plan zero_plan;
+
+/* What a plan (or a would-be plan) contains. */
+typedef struct zero_plan_stats {
+    uint64_t n_tensors;
+    uint64_t n_params;      /* sum of n over the tensors */
+    uint64_t n_chunks;      /* work items; one workgroup handles one at a time */
+    uint64_t chunk_elems;   /* elements per chunk (the last of a tensor: fewer) */
+    uint64_t vec8_elems;    /* elements on the 16-byte-vector path */
+    uint64_t vec4_elems;    /* elements on the 8-byte fp16 / 16-byte fp32 path */
+    uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
+                               tensors whose arrays disagree in alignment) */
+    uint64_t table_bytes;   /* device bytes of the chunk table */
+} zero_plan_stats;
+
+/*
+ * zero_shard_layout -- flat-buffer padding and this rank's shard.
+ * Ranks own contiguous slices of the flattened state ([16B] "The part that
+ * sounds too good: communication"; [DSZ] "ZeRO removes replicated state in
+ * stages").  The buffer of psi elements is padded at its tail to
+ * padded_total = ceil(psi / (nd * align)) * nd * align elements; every rank
+ * gets shard_len = padded_total / nd elements starting at rank * shard_len,
+ * of which real_len lie below psi (the padding sits in the last shards).
+ * align is in elements.  psi = 0 is allowed (all zero).
+ * Pure host function.  Errors: EINVAL if out is NULL, nd = 0, align = 0 or
+ * rank >= nd; EOVERFLOW if padded_total exceeds 2^64 - 1.
+ */
+int zero_shard_layout(uint64_t psi, uint32_t nd, uint32_t rank, uint32_t align,
+                      zero_layout *out);
+
+/*
+ * zero_state_bytes -- model-state bytes resident on one rank.
+ * [ER10] "The Mathematics", eq. M_states = (2 + 2 + K) Psi with K = 12 and
+ * eq. M_states(p, N_d); [16B] "The replication nobody questioned", stage
+ * table.  With S the padded shard length of zero_shard_layout:
+ *   stage 0: 16 psi   1: 4 psi + 12 S   2: 2 psi + 14 S   3: 16 S
+ * Activations, communication buffers and allocator effects are excluded
+ * ([DSZ] "ZeRO removes replicated state in stages").
+ * Pure host function.  Errors: EINVAL (out NULL, stage > 3, nd = 0,
+ * align = 0); EOVERFLOW.
+ */
+int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
+                     uint64_t *out_bytes);
+
+/*
+ * zero_plan_create -- chunk table for a list of tensors of mixed sizes.
+ * tensors: host array of n_tensors descriptors (copied; the table does not
+ * keep the host array).  Each tensor is cut into chunks of at most
+ * chunk_elems elements; per tensor the library picks the widest access path
+ * that all five arrays' alignments allow (16-byte vectors, 8-byte fp16 /
+ * 16-byte fp32 vectors, or single elements) after peeling at most 7 leading
+ * elements.  The table is allocated on the current device (hipMalloc) and
+ * filled with a synchronous copy; nothing else is allocated later.
+ * Ownership: *out belongs to the caller until zero_plan_destroy.  The
+ * tensors' memory stays the caller's and must outlive the plan.
+ * Errors: EINVAL (NULL out or tensors with n_tensors > 0, a NULL array of
+ * a non-empty tensor, fp16 arrays not 2-byte or fp32 arrays not 4-byte
+ * aligned, overlapping arrays within a tensor); EOVERFLOW; ENOMEM; EHIP.
+ */
+int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
+                     zero_plan **out);
+
+/* zero_plan_stats_of -- fill *out for an existing plan.  Host only. */
+int zero_plan_stats_of(const zero_plan *plan, zero_plan_stats *out);
+
+/*
+ * zero_plan_describe -- the same classification zero_plan_create would do,
+ * without touching any device: pointers are only inspected as numbers.
+ * Host only.  Errors as zero_plan_create minus ENOMEM and EHIP.
+ */
+int zero_plan_describe(const zero_tensor *tensors, uint32_t n_tensors,
+                       zero_plan_stats *out);
+
+/* zero_plan_destroy -- free the table.  No step using the plan may still be
+ * in flight.  NULL is accepted.  Errors: EHIP. */
+int zero_plan_destroy(zero_plan *plan);
+
+/*
+ * zero_adam_scalars -- the fp32 constants of step t (t >= 1).
+ * out = {lr, b1, 1-b1, b2, 1-b2, 1-b1^t, 1-b2^t, eps}; each is computed in
+ * double from the double hyperparameters and rounded to fp32 once.
+ * Host only.  Errors: EINVAL (NULL, t = 0, weight_decay != 0, lr or eps not
+ * finite, eps < 0, betas outside [0, 1)).
+ */
+int zero_adam_scalars(const zero_adam_hparams *hp, uint64_t t, float out[8]);
+
+/*
+ * zero_adam_step -- one fused mixed-precision Adam step over every tensor of
+ * the plan: this rank updates only its slice ([16B] "The part that sounds
+ * too good: communication"), keeping fp32 master, momentum and variance and
+ * writing fresh fp16 parameters ([16B] "Where 16 bytes per parameter comes
+ * from", state table; "Why you can't just delete the fp32 copies").  Per
+ * element, each an IEEE binary32 operation, in this order, without fused
+ * multiply-add (Kingma and Ba, Algorithm 1; the pages print no equations):
+ *   g = fp32(grad16);  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *   u = (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps);  master = master - lr*u
+ *   param16 = fp16(master), rounded to nearest even
+ * Non-finite values propagate per IEEE.
+ * nonfinite_flag: NULL or a device int32; if any gradient of the plan is
+ *   infinite or NaN, 1 is OR-ed into it (the library never clears it).
+ * skip_if_nonzero: NULL or a device int32 read when the step starts; if
+ *   it is nonzero the step reads and writes nothing (e.g. chain it to the
+ *   flag of zero_reduce_grad_shard).  It must not be nonfinite_flag.
+ * Asynchronous on `stream`; allocates nothing.  A plan must not be stepped
+ * on two streams at once.  Errors: EINVAL (NULL plan or hp, bad
+ * hyperparameters as zero_adam_scalars, flag == skip, plan made on another
+ * device); EHIP.
+ */
+int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp,
+                   uint64_t t, int32_t *nonfinite_flag,
+                   const int32_t *skip_if_nonzero, void *stream);
+
+/*
+ * zero_reduce_grad_shard -- this rank's final gradient for its partition
+ * from the nd ranks' fp16 slices of it: after a reduce-scatter each rank
+ * owns the final gradients of its partition ([16B] "The part that sounds
+ * too good: communication"; [ER10] "The Mathematics", communication
+ * paragraph).  Here the nd slices are given in local device memory.
+ *   out[i] = fp16( (s_0[i] + s_1[i] + ... + s_{nd-1}[i]) / nd )
+ * summed in fp32 in rank order starting from s_0, one IEEE division by nd,
+ * rounded to nearest even fp16.
+ * slices_f16: host array of nd device pointers to n fp16 each (read only;
+ *   copied into the launch, so the host array may be reused at once).
+ * out_f16: device pointer to n fp16 (written); must not overlap a slice.
+ * nonfinite_flag: NULL or a device int32; 1 is OR-ed into it if any output
+ *   is infinite or NaN.
+ * Asynchronous; allocates nothing.  n = 0 launches nothing.
+ * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not
+ * 2-byte aligned, out overlapping a slice); EHIP.
+ */
+int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd,
+                           uint64_t n, void *out_f16, int32_t *nonfinite_flag,
+                           void *stream);
+
+/* zero_status_str -- static description of a status code. */
+const char *zero_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

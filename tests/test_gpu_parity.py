@@ -1,0 +1,371 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on
+small and ragged inputs: every element compared.  Each case prints its name
+and sizes before it touches the GPU."""
+import numpy as np
+import pytest
+
+import oracle
+from parity import check16, check32, host16, host32, to_dev16, to_dev32
+from zero_partitioned_mixed_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(W.ADAM_HP)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_partitioned_mixed_layout_amd import zero_shard
+    torch.cuda.set_device(0)
+    return zero_shard
+
+
+@pytest.fixture(scope="module")
+def torch_mod(zs):
+    import torch
+    return torch
+
+
+def _hp(zs):
+    return zs.AdamHParams(**HP)
+
+
+class HostShard:
+    """Host copies of one tensor's five arrays for the oracle."""
+
+    def __init__(self, g16, p16, w, m, v):
+        self.g, self.p, self.w, self.m, self.v = g16, p16, w, m, v
+
+    def step(self, t, skip=False):
+        return oracle.adam_step(self.g, self.p, self.w, self.m, self.v, t=t, skip=skip, **HP)
+
+
+def _compare(dev_arrays, host: HostShard, what):
+    p, g, w, m, v = dev_arrays
+    r = [check16(host16(p), host.p, f"{what} param"), check32(host32(w), host.w, f"{what} master"),
+         check32(host32(m), host.m, f"{what} m"), check32(host32(v), host.v, f"{what} v")]
+    return sum(x["not_bit_exact"] for x in r)
+
+
+def test_tiny_flat_ten_steps(zs, torch_mod):
+    """2^20 parameters over 4 ranks: rank 0's 262,144-element shard, 10 steps,
+    all elements compared after every step (underflow and swamping sets
+    included)."""
+    torch = torch_mod
+    wl = W.WORKLOADS["tiny_flat"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+    assert lay._asdict() == oracle.shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+    n = lay.real_len
+    say(f"tiny_flat n={n} steps={wl.steps}")
+    master, m, v, p16 = W.tiny_initial_state(wl)
+    host = HostShard(None, p16.view(np.uint16).copy(), master.copy(), m.copy(), v.copy())
+    full = torch.zeros(lay.padded_total, dtype=torch.float16, device="cuda")
+    dp = full[lay.offset:lay.offset + n]
+    dp.copy_(to_dev16(p16.view(np.uint16)))
+    dg = torch.empty(n, dtype=torch.float16, device="cuda")
+    dw, dm, dv = to_dev32(master), to_dev32(m), to_dev32(v)
+    plan = zs.zero_plan_create([(dp, dg, dw, dm, dv)])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    inexact = 0
+    for t in range(1, wl.steps + 1):
+        g = W.tiny_grad16(wl, t)
+        dg.copy_(to_dev16(g.view(np.uint16)))
+        zs.zero_adam_step(plan, _hp(zs), t, flag)
+        host.g = g.view(np.uint16)
+        assert host.step(t) == 0
+        torch.cuda.synchronize()
+        inexact += _compare((dp, dg, dw, dm, dv), host, f"tiny t={t}")
+    assert int(flag.item()) == 0
+    # the rest of the full fp16 buffer (other ranks' shards) is untouched
+    assert int(torch.count_nonzero(full[n:]).item()) == 0
+    assert inexact == 0, f"{inexact} elements within tolerance but not bit-exact"
+    plan.destroy()
+
+
+def _ragged_plan(zs, torch, sizes_offsets, seed, warm=False):
+    """Tensors of the given sizes, each array a view at its own element
+    offset into a larger buffer (so the five arrays of a tensor can disagree
+    in alignment).  Returns device arrays, host mirrors."""
+    rng = np.random.default_rng(seed)
+    dev, host = [], []
+    for k, (n, offs) in enumerate(sizes_offsets):
+        bufs = []
+        for j, (o, dt) in enumerate(zip(offs, (torch.float16, torch.float16, torch.float32,
+                                               torch.float32, torch.float32))):
+            bufs.append(torch.zeros(n + o + 8, dtype=dt, device="cuda")[o:o + n])
+        p, g, w, m, v = bufs
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32) if warm else np.zeros(n, np.float32)
+        v0 = (rng.random(n) * 1e-6).astype(np.float32) if warm else np.zeros(n, np.float32)
+        w.copy_(to_dev32(w0))
+        m.copy_(to_dev32(m0))
+        v.copy_(to_dev32(v0))
+        dev.append((p, g, w, m, v))
+        host.append(HostShard(None, np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy()))
+    return dev, host
+
+
+SIZES = [1, 7, 8, 9, 31, 4095, 4096, 4097, 2048 * 3 + 5, 70001, 0]
+# element offsets of (param, grad, master, m, v) inside their buffers
+OFFSETS = [(0, 0, 0, 0, 0),      # all aligned: 16-byte path
+           (4, 0, 0, 0, 0),      # param 8 mod 16 bytes, grad 0: 8-byte fp16 path
+           (3, 3, 3, 3, 3),      # common phase: peel 5, then 16-byte path
+           (4, 4, 0, 0, 0),      # fp16 8 mod 16 bytes: peel 4, then 16-byte path
+           (1, 0, 0, 0, 0),      # param odd: single elements
+           (0, 0, 1, 0, 0)]      # master 4 mod 16 bytes: single elements
+
+
+@pytest.mark.parametrize("warm", [False, True])
+def test_ragged_sizes_and_alignments(zs, torch_mod, warm):
+    """One plan over tensors of sizes 0..70001 whose arrays sit at every
+    alignment class; three steps; every element compared."""
+    torch = torch_mod
+    so = [(n, OFFSETS[i % len(OFFSETS)]) for i, n in enumerate(SIZES)]
+    so += [(n, OFFSETS[(i + 2) % len(OFFSETS)]) for i, n in enumerate(SIZES)]
+    say(f"ragged warm={warm} tensors={len(so)}")
+    dev, host = _ragged_plan(zs, torch, so, seed=42 + warm, warm=warm)
+    plan = zs.zero_plan_create(dev)
+    st = plan.stats()
+    assert st["vec8_elems"] and st["vec4_elems"] and st["scalar_elems"]
+    assert st["vec8_elems"] + st["vec4_elems"] + st["scalar_elems"] == st["n_params"]
+    rng = np.random.default_rng(7)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t0 = 6 if warm else 1
+    inexact = 0
+    for t in range(t0, t0 + 3):
+        for (p, g, w, m, v), h in zip(dev, host):
+            gh = (rng.standard_normal(w.numel()) * 1e-3).astype(np.float16).view(np.uint16)
+            if w.numel():
+                g.copy_(to_dev16(gh))
+            h.g = gh
+        zs.zero_adam_step(plan, _hp(zs), t, flag)
+        for h in host:
+            h.step(t)
+        torch.cuda.synchronize()
+        for k, (d, h) in enumerate(zip(dev, host)):
+            if d[2].numel():
+                inexact += _compare(d, h, f"ragged tensor {k} n={d[2].numel()} t={t}")
+    assert int(flag.item()) == 0
+    assert inexact == 0
+    plan.destroy()
+
+
+def test_every_fp16_gradient_pattern(zs, torch_mod):
+    """All 65,536 fp16 bit patterns as gradients (subnormals, +-0, +-inf,
+    NaNs) in one step from a warm state; non-finite ones must give the
+    oracle's IEEE classes and raise the flag."""
+    torch = torch_mod
+    n = 1 << 16
+    say("every fp16 gradient pattern")
+    rng = np.random.default_rng(5)
+    g = np.arange(n, dtype=np.uint32).astype(np.uint16)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = (rng.random(n) * 1e-6).astype(np.float32)
+    host = HostShard(g, np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy())
+    dp = torch.zeros(n, dtype=torch.float16, device="cuda")
+    dg, dw, dm, dv = to_dev16(g), to_dev32(w0), to_dev32(m0), to_dev32(v0)
+    plan = zs.zero_plan_create([(dp, dg, dw, dm, dv)])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, _hp(zs), 3, flag)
+    assert host.step(3) == 1
+    torch.cuda.synchronize()
+    assert _compare((dp, dg, dw, dm, dv), host, "all patterns") == 0
+    assert int(flag.item()) == 1
+    plan.destroy()
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00, 0xFD55])
+@pytest.mark.parametrize("where", ["head", "body", "tail"])
+def test_flag_per_class_and_position(zs, torch_mod, bad, where):
+    """One non-finite gradient, in a peeled head element, a vector body or
+    a ragged tail, raises the flag; finite gradients leave it at 0."""
+    torch = torch_mod
+    n = 4096 + 3
+    say(f"flag bad={bad:#x} where={where}")
+    buf16 = [torch.zeros(n + 8, dtype=torch.float16, device="cuda")[3:3 + n] for _ in range(2)]
+    buf32 = [torch.zeros(n + 8, dtype=torch.float32, device="cuda")[3:3 + n] for _ in range(3)]
+    g = np.full(n, 0x1400, np.uint16)
+    pos = {"head": 1, "body": 2000, "tail": n - 1}[where]
+    buf16[1].copy_(to_dev16(g))
+    plan = zs.zero_plan_create([(buf16[0], buf16[1], *buf32)])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, _hp(zs), 1, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    g[pos] = bad
+    buf16[1].copy_(to_dev16(g))
+    zs.zero_adam_step(plan, _hp(zs), 2, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    plan.destroy()
+
+
+def test_skip_writes_nothing(zs, torch_mod):
+    torch = torch_mod
+    n = 10000
+    say("skip")
+    rng = np.random.default_rng(9)
+    arrays = [to_dev16(rng.integers(0, 0x7000, n, dtype=np.uint16)),
+              to_dev16((rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16)),
+              to_dev32(rng.standard_normal(n)), to_dev32(rng.standard_normal(n)),
+              to_dev32(rng.random(n))]
+    before = [a.clone() for a in arrays]
+    plan = zs.zero_plan_create([arrays])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    skip = torch.ones(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, _hp(zs), 4, flag, skip)
+    torch.cuda.synchronize()
+    for a, b in zip(arrays, before):
+        assert torch.equal(a.view(torch.int16 if a.dtype == torch.float16 else torch.int32),
+                           b.view(torch.int16 if b.dtype == torch.float16 else torch.int32))
+    assert int(flag.item()) == 0
+    skip.zero_()
+    zs.zero_adam_step(plan, _hp(zs), 4, flag, skip)
+    torch.cuda.synchronize()
+    assert not torch.equal(arrays[2], before[2])
+    with pytest.raises(zs.ZeroError):
+        zs.zero_adam_step(plan, _hp(zs), 4, flag, flag)       # flag == skip
+    plan.destroy()
+
+
+def test_resume_is_bit_exact(zs, torch_mod):
+    """10 steps == 5 steps, a copy of all five arrays into fresh tensors, a
+    new plan, and 5 more steps continuing t."""
+    torch = torch_mod
+    n = 50000
+    say("resume 5+5")
+    rng = np.random.default_rng(11)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    grads = [to_dev16((rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16))
+             for _ in range(10)]
+
+    def fresh():
+        return [torch.zeros(n, dtype=torch.float16, device="cuda"),
+                torch.zeros(n, dtype=torch.float16, device="cuda"),
+                to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")]
+
+    a = fresh()
+    pa = zs.zero_plan_create([a])
+    for t in range(1, 11):
+        a[1].copy_(grads[t - 1])
+        zs.zero_adam_step(pa, _hp(zs), t, None)
+    b = fresh()
+    pb = zs.zero_plan_create([b])
+    for t in range(1, 6):
+        b[1].copy_(grads[t - 1])
+        zs.zero_adam_step(pb, _hp(zs), t, None)
+    c = [x.clone() for x in b]
+    pc = zs.zero_plan_create([c])
+    for t in range(6, 11):
+        c[1].copy_(grads[t - 1])
+        zs.zero_adam_step(pc, _hp(zs), t, None)
+    torch.cuda.synchronize()
+    for x, y in zip(a, c):
+        assert torch.equal(x.view(torch.int16 if x.dtype == torch.float16 else torch.int32),
+                           y.view(torch.int16 if y.dtype == torch.float16 else torch.int32))
+    for p in (pa, pb, pc):
+        p.destroy()
+
+
+# --------------------------------------------------------------------------
+# Gradient reduction.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 9, 16, 17, 64, 256])
+@pytest.mark.parametrize("layout", ["aligned", "phase3", "mixed4", "odd"])
+def test_reduce_matches_oracle(zs, torch_mod, nd, layout):
+    """Every output element of the N_d-slice average, for N_d from 1 to
+    256, sizes with ragged tails, and slice alignments that select each
+    access path (16-byte, peeled head, 8-byte, single element)."""
+    torch = torch_mod
+    rng = np.random.default_rng(1000 + nd)
+    for n in (1, 7, 9, 4097, 65537):
+        say(f"reduce nd={nd} layout={layout} n={n}")
+        hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
+        offs = {"aligned": [0] * (nd + 1), "phase3": [3] * (nd + 1),
+                "mixed4": [4 * (r % 2) for r in range(nd + 1)],
+                "odd": [r % 3 for r in range(nd + 1)]}[layout]
+        ds = []
+        for r in range(nd):
+            b = torch.zeros(n + 8, dtype=torch.float16, device="cuda")[offs[r]:offs[r] + n]
+            b.copy_(to_dev16(hs[r]))
+            ds.append(b)
+        out = torch.zeros(n + 8, dtype=torch.float16, device="cuda")[offs[nd]:offs[nd] + n]
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        zs.zero_reduce_grad_shard(ds, out, flag)
+        ref, rflag = oracle.reduce_grad(hs)
+        torch.cuda.synchronize()
+        r = check16(host16(out), ref, f"reduce nd={nd} n={n} {layout}")
+        assert r["not_bit_exact"] == 0
+        assert int(flag.item()) == rflag == 0
+
+
+def test_reduce_special_values(zs, torch_mod):
+    """N_d = 1 copies all 65,536 patterns; +inf with -inf gives NaN and the
+    flag; the fp32 sum does not overflow where the fp16 mean fits."""
+    torch = torch_mod
+    say("reduce special values")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    out = torch.zeros(1 << 16, dtype=torch.float16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard([to_dev16(bits)], out, flag)
+    ref, rflag = oracle.reduce_grad([bits])
+    torch.cuda.synchronize()
+    check16(host16(out), ref, "nd=1 copy")
+    assert int(flag.item()) == rflag == 1
+    a = np.array([0x7C00, 0x7BFF, 0x3C00, 0x0001] * 3, np.uint16)
+    b = np.array([0xFC00, 0x7BFF, 0x3C00, 0x8001] * 3, np.uint16)
+    out = torch.zeros(a.size, dtype=torch.float16, device="cuda")
+    flag.zero_()
+    zs.zero_reduce_grad_shard([to_dev16(a), to_dev16(b)], out, flag)
+    ref, rflag = oracle.reduce_grad([a, b])
+    torch.cuda.synchronize()
+    check16(host16(out), ref, "inf mix")
+    assert int(flag.item()) == rflag == 1
+
+
+def test_reduce_then_step_skips_on_nonfinite(zs, torch_mod):
+    """The reduce's flag chained as the step's skip input: an infinite
+    gradient slice leaves every state array untouched."""
+    torch = torch_mod
+    say("reduce -> skip chain")
+    n = 3000
+    rng = np.random.default_rng(3)
+    hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(4)]
+    hs[2][1234] = 0x7C00
+    ds = [to_dev16(h) for h in hs]
+    grad = torch.zeros(n, dtype=torch.float16, device="cuda")
+    st = [torch.zeros(n, dtype=torch.float16, device="cuda"), grad,
+          to_dev32(rng.standard_normal(n)), to_dev32(rng.standard_normal(n) * 1e-3),
+          to_dev32(rng.random(n) * 1e-6)]
+    before = [x.clone() for x in st]
+    reduce_flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    step_flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = zs.zero_plan_create([st])
+    zs.zero_reduce_grad_shard(ds, grad, reduce_flag)
+    zs.zero_adam_step(plan, _hp(zs), 2, step_flag, reduce_flag)
+    torch.cuda.synchronize()
+    assert int(reduce_flag.item()) == 1 and int(step_flag.item()) == 0
+    assert torch.equal(st[0].view(torch.int16), before[0].view(torch.int16))
+    for k in (2, 3, 4):
+        assert torch.equal(st[k].view(torch.int32), before[k].view(torch.int32))
+    plan.destroy()
+
+
+def test_rejects_through_binding(zs, torch_mod):
+    torch = torch_mod
+    a = torch.zeros(16, dtype=torch.float16, device="cuda")
+    with pytest.raises(zs.ZeroError):
+        zs.zero_reduce_grad_shard([a, a[4:12]], a[2:10])      # out overlaps a slice
+    w = torch.zeros(16, device="cuda")
+    with pytest.raises(zs.ZeroError):                          # m aliases master
+        zs.zero_plan_create([(a, a.clone(), w, w, torch.zeros(16, device="cuda"))])
+    with pytest.raises(TypeError):
+        zs.zero_plan_create([(a, a.clone(), w.half(), w.clone(), w.clone())])

@@ -1,0 +1,199 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same entry points, same plans).  The oracle recomputes
+sampled elements one by one from the same seeded inputs -- the initial
+master and every step's gradients gathered at the sampled indices, never a
+value the HIP path produced -- through all warm-up steps; sampled indices
+include both ends of every tensor and, for the infinity workload, every
+injected position.  Properties that hold at any size (untouched padding and
+other ranks' parameters, the non-finite positions, the ZeRO-2 ledger) are
+checked on the whole arrays."""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import check16, check32, host16, host32
+from zero_partitioned_mixed_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+HP = dict(W.ADAM_HP)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_partitioned_mixed_layout_amd import zero_shard
+    torch.cuda.set_device(0)
+    return zero_shard
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    import torch
+    gc.collect()
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def _gather16(t, idx_dev):
+    return host16(t.index_select(0, idx_dev))
+
+
+def _gather32(t, idx_dev):
+    return host32(t.index_select(0, idx_dev))
+
+
+def _oracle_steps(w0, grads_by_step, t0=1):
+    n = w0.size
+    w, m, v = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p = np.zeros(n, np.uint16)
+    flag = 0
+    for k, g in enumerate(grads_by_step):
+        flag |= oracle.adam_step(g, p, w, m, v, t=t0 + k, **HP)
+    return p, w, m, v, flag
+
+
+def _check_all(got, ref, what):
+    p, w, m, v = got
+    rp, rw, rm, rv = ref
+    res = [check16(p, rp, f"{what} param"), check32(w, rw, f"{what} master"),
+           check32(m, rm, f"{what} m"), check32(v, rv, f"{what} v")]
+    inexact = sum(r["not_bit_exact"] for r in res)
+    say(f"{what}: {res[0]['n']} sampled elements, max rel "
+        f"{max(r.get('max_rel', 0) for r in res):.2g}, not bit-exact {inexact}")
+    return inexact
+
+
+@pytest.mark.parametrize("name", ["gpt2_xl", "llama_7b"])
+def test_tensor_list_workload(zs, name):
+    """GPT-2-XL (580 tensors, 1.56e9 params) and Llama-7B (291 tensors,
+    6.74e9 params, 108 GB of state in HBM): 5 warm-up steps, then step 6,
+    one plan over the whole list, N_d = 1."""
+    import torch
+    wl = W.WORKLOADS[name]
+    say(f"{name}: {len(wl.tensors)} tensors, {wl.n_params} params")
+    assert zs.zero_state_bytes(0, wl.n_params, 1) == 16 * wl.n_params
+    tensors = W.device_list_state(wl)
+    plan = zs.zero_plan_create([t.arrays() for t in tensors])
+    st = plan.stats()
+    assert st["n_params"] == wl.n_params and st["vec8_elems"] == wl.n_params
+    idx = [W.sample_indices(t.n, 96, seed=wl.seed + 13 * k) for k, t in enumerate(tensors)]
+    idx_dev = [torch.from_numpy(i).cuda() for i in idx]
+    w0 = np.concatenate([_gather32(t.w, d) for t, d in zip(tensors, idx_dev)])
+    grads = []
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp = zs.AdamHParams(**HP)
+    for t in range(1, wl.warm_steps + 2):
+        W.device_fill_grads(wl, tensors, t)
+        grads.append(np.concatenate([_gather16(x.g, d) for x, d in zip(tensors, idx_dev)]))
+        say(f"{name}: step t={t}")
+        zs.zero_adam_step(plan, hp, t, flag)
+    torch.cuda.synchronize()
+    got = [np.concatenate([f(getattr(x, a), d) for x, d in zip(tensors, idx_dev)])
+           for a, f in (("p", _gather16), ("w", _gather32), ("m", _gather32), ("v", _gather32))]
+    rp, rw, rm, rv, rflag = _oracle_steps(w0, grads)
+    assert int(flag.item()) == rflag == 0
+    assert _check_all(got, (rp, rw, rm, rv), name) == 0
+    plan.destroy()
+
+
+@pytest.mark.parametrize("rank", [0, 1, 63])
+def test_flat_7p5b_nd64_reduce_then_step(zs, rank):
+    """Psi = 7.5e9 over 64 ranks: this rank's 117,187,500-element partition.
+    64 fp16 gradient slices are averaged, then Adam runs at t = 1 with the
+    reduce's flag as its skip input.  Odd ranks' fp16 parameter views start
+    8 bytes off a 16-byte boundary (the 4-wide path).  The whole other-rank
+    part of the fp16 parameter buffer stays untouched, and the allocated
+    ZeRO-2 state equals the ledger's 16,640,625,000 bytes."""
+    import torch
+    wl = W.WORKLOADS["flat_7p5b_nd64"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, rank, wl.align)
+    assert lay._asdict() == oracle.shard_layout(wl.psi, wl.nd, rank, wl.align)
+    n = lay.real_len
+    say(f"flat_7p5b_nd64 rank={rank} n={n} offset={lay.offset}")
+    full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total)
+    buf, rows = W.device_slices(wl, n)
+    ledger = full.numel() * 2 + sh.g.numel() * 2 + 3 * 4 * sh.w.numel()
+    assert ledger == zs.zero_state_bytes(2, wl.psi, wl.nd, wl.align) == 16_640_625_000
+    plan = zs.zero_plan_create([sh.arrays()])
+    st = plan.stats()
+    assert st[("vec8_elems" if rank % 2 == 0 else "vec4_elems")] >= n - 8
+    idx = W.sample_indices(n, 200_000, seed=wl.seed + rank)
+    d = torch.from_numpy(idx).cuda()
+    w0 = _gather32(sh.w, d)
+    slices = [_gather16(r, d) for r in rows]
+    rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    aflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard(rows, sh.g, rflag)
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, aflag, rflag)
+    torch.cuda.synchronize()
+    g_ref, f_ref = oracle.reduce_grad(slices)
+    r = check16(_gather16(sh.g, d), g_ref, "reduced gradient")
+    assert r["not_bit_exact"] == 0 and int(rflag.item()) == f_ref == 0
+    rp, rw, rm, rv, fl = _oracle_steps(w0, [g_ref])
+    got = [_gather16(sh.p, d), _gather32(sh.w, d), _gather32(sh.m, d), _gather32(sh.v, d)]
+    assert _check_all(got, (rp, rw, rm, rv), f"nd64 rank {rank}") == 0
+    assert int(aflag.item()) == 0
+    before = int(torch.count_nonzero(full[:lay.offset]).item())
+    after = int(torch.count_nonzero(full[lay.offset + n:]).item())
+    assert before == after == 0
+    plan.destroy()
+
+
+def test_flat_7p5b_nd8_rank3_with_infinities(zs):
+    """Psi = 7.5e9 over 8 ranks in 512-element units: rank 3's 937,500,160
+    elements at 2,812,500,480.  Five warm-up steps with finite gradients,
+    then step 6 with 93,750 (0.01%) gradients set to +-inf: the flag is 1,
+    and master, m, v and fp16 param are non-finite exactly there."""
+    import torch
+    wl = W.WORKLOADS["flat_7p5b_nd8"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+    assert lay._asdict() == oracle.shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+    assert (lay.shard_len, lay.offset, lay.real_len) == (937_500_160, 2_812_500_480, 937_500_160)
+    n = lay.real_len
+    say(f"flat_7p5b_nd8 rank 3 n={n}")
+    full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total)
+    plan = zs.zero_plan_create([sh.arrays()])
+    pos, sign = W.inf_positions(n, wl.inf_frac, wl.seed)
+    assert pos.size == 93_750
+    idx = W.sample_indices(n, 200_000, seed=wl.seed, must=pos)
+    d = torch.from_numpy(idx).cuda()
+    w0 = _gather32(sh.w, d)
+    grads = []
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp = zs.AdamHParams(**HP)
+    T = wl.warm_steps + 1
+    for t in range(1, T + 1):
+        W.device_fill_grads(wl, [sh], t)
+        if t == T:
+            W.device_inject_inf(sh.g, pos, sign)
+            torch.cuda.synchronize()
+            assert int(flag.item()) == 0          # warm-up steps were finite
+        grads.append(_gather16(sh.g, d))
+        say(f"flat_7p5b_nd8: step t={t}")
+        zs.zero_adam_step(plan, hp, t, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    rp, rw, rm, rv, rflag = _oracle_steps(w0, grads)
+    assert rflag == 1
+    got = [_gather16(sh.p, d), _gather32(sh.w, d), _gather32(sh.m, d), _gather32(sh.v, d)]
+    assert _check_all(got, (rp, rw, rm, rv), "nd8 rank 3") == 0
+    # whole arrays: non-finite exactly at the injected positions
+    pos_dev = torch.from_numpy(pos).cuda()
+    for a in (sh.w, sh.p):
+        bad = torch.nonzero(~torch.isfinite(a)).flatten()
+        assert torch.equal(bad, pos_dev)
+    bad_m = torch.nonzero(~torch.isfinite(sh.m)).flatten()
+    assert torch.equal(bad_m, pos_dev)
+    assert int(torch.count_nonzero(full[:lay.offset]).item()) == 0
+    assert int(torch.count_nonzero(full[lay.offset + n:]).item()) == 0
+    plan.destroy()

@@ -1,0 +1,245 @@
+// zs_host.cpp -- host-only logic of libzeroshard.so: shard layout, model-state
+// ledger, Adam step constants, status strings and the multi-tensor plan
+// builder.  Nothing here touches a device.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "zero_shard.h"
+#include "zs_internal.h"
+
+namespace {
+
+// a * b + c with overflow detection, in 64-bit unsigned arithmetic.
+bool mul_ok(uint64_t a, uint64_t b, uint64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(uint64_t a, uint64_t b, uint64_t *r) { return !__builtin_add_overflow(a, b, r); }
+
+} // namespace
+
+extern "C" int zero_shard_layout(uint64_t psi, uint32_t nd, uint32_t rank, uint32_t align,
+                                 zero_layout *out) {
+    if (!out || nd == 0 || align == 0 || rank >= nd)
+        return ZERO_EINVAL;
+    // Tail padding: round psi up to whole units of nd * align elements
+    // ([16B] "The part that sounds too good: communication": each rank owns
+    // one contiguous slice; the padding rule is this library's).
+    const uint64_t unit = (uint64_t)nd * (uint64_t)align; // < 2^64: both < 2^32
+    const uint64_t units = psi / unit + (psi % unit != 0);
+    uint64_t padded;
+    if (!mul_ok(units, unit, &padded))
+        return ZERO_EOVERFLOW;
+    const uint64_t shard = padded / nd;
+    const uint64_t offset = (uint64_t)rank * shard; // <= padded
+    out->padded_total = padded;
+    out->shard_len = shard;
+    out->offset = offset;
+    out->real_len = offset >= psi ? 0 : std::min(shard, psi - offset);
+    return ZERO_OK;
+}
+
+extern "C" int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
+                                uint64_t *out_bytes) {
+    if (!out_bytes || stage > 3)
+        return ZERO_EINVAL;
+    zero_layout lay;
+    int rc = zero_shard_layout(psi, nd, 0, align, &lay);
+    if (rc != ZERO_OK)
+        return rc;
+    // [ER10] "The Mathematics", eq. M_states(p, N_d): bytes per parameter of
+    // the replicated classes times psi, plus the sharded classes times S.
+    static const uint64_t replicated[4] = {16, 4, 2, 0};
+    static const uint64_t sharded[4] = {0, 12, 14, 16};
+    uint64_t a, b, total;
+    if (!mul_ok(replicated[stage], psi, &a) || !mul_ok(sharded[stage], lay.shard_len, &b) ||
+        !add_ok(a, b, &total))
+        return ZERO_EOVERFLOW;
+    *out_bytes = total;
+    return ZERO_OK;
+}
+
+extern "C" int zero_adam_scalars(const zero_adam_hparams *hp, uint64_t t, float out[8]) {
+    if (!hp || !out || t == 0)
+        return ZERO_EINVAL;
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps;
+    if (!isfinite(lr) || !isfinite(eps) || eps < 0.0 || hp->weight_decay != 0.0)
+        return ZERO_EINVAL;
+    if (!(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0))
+        return ZERO_EINVAL;
+    // Each constant is formed in double and rounded to fp32 once.
+    const double td = (double)t;
+    out[0] = (float)lr;
+    out[1] = (float)b1;
+    out[2] = (float)(1.0 - b1);
+    out[3] = (float)b2;
+    out[4] = (float)(1.0 - b2);
+    out[5] = (float)(1.0 - pow(b1, td));
+    out[6] = (float)(1.0 - pow(b2, td));
+    out[7] = (float)eps;
+    return ZERO_OK;
+}
+
+extern "C" const char *zero_status_str(int status) {
+    switch (status) {
+    case ZERO_OK: return "ok";
+    case ZERO_EINVAL: return "invalid argument";
+    case ZERO_EOVERFLOW: return "size overflows 64 bits";
+    case ZERO_EHIP: return "HIP runtime or launch error";
+    case ZERO_ENOMEM: return "device allocation failed";
+    default: return "unknown status";
+    }
+}
+
+namespace zs {
+
+uint64_t chunk_elems_for(uint64_t n_params) {
+    // Enough chunks to spread a plan over all 256 compute units several
+    // times, but at least 2048 elements (one 16-byte vector per lane of a
+    // 256-lane workgroup) and at most 16384 per chunk.
+    uint64_t c = 2048;
+    while (c < 16384 && n_params / c > 8192)
+        c *= 2;
+    return c;
+}
+
+void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n32,
+                      uint32_t *vec, uint32_t *head) {
+    for (uint32_t w : {8u, 4u}) {
+        const uintptr_t a16 = 2u * w; // bytes one fp16 vector spans
+        for (uint32_t h = 0; h < w; h++) {
+            bool ok = true;
+            for (int i = 0; i < n16 && ok; i++)
+                ok = (f16[i] + 2u * h) % a16 == 0;
+            for (int i = 0; i < n32 && ok; i++)
+                ok = (f32[i] + 4u * h) % 16u == 0;
+            if (ok) {
+                *vec = w;
+                *head = h;
+                return;
+            }
+        }
+    }
+    *vec = 1;
+    *head = 0;
+}
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi; // [lo, hi)
+    bool written;
+};
+
+// True if two ranges overlap where at least one of them is written.
+bool writes_overlap(std::vector<Range> &r) {
+    std::sort(r.begin(), r.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    // Sweep keeping the furthest end seen among written and among all ranges.
+    uintptr_t end_any = 0, end_written = 0;
+    for (const Range &x : r) {
+        if (x.lo < end_written)
+            return true;
+        if (x.written && x.lo < end_any)
+            return true;
+        end_any = std::max(end_any, x.hi);
+        if (x.written)
+            end_written = std::max(end_written, x.hi);
+    }
+    return false;
+}
+
+} // namespace
+
+int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *out) {
+    if (!out || (n_tensors > 0 && !tensors))
+        return ZERO_EINVAL;
+    HostPlan plan;
+    memset(&plan.stats, 0, sizeof(plan.stats));
+    std::vector<Range> ranges;
+    uint64_t n_params = 0;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        const zero_tensor &t = tensors[k];
+        if (t.n == 0)
+            continue;
+        const uintptr_t p = (uintptr_t)t.param_f16, g = (uintptr_t)t.grad_f16,
+                        w = (uintptr_t)t.master, m = (uintptr_t)t.m, v = (uintptr_t)t.v;
+        if (!p || !g || !w || !m || !v)
+            return ZERO_EINVAL;
+        if ((p | g) % 2 || (w | m | v) % 4)
+            return ZERO_EINVAL;
+        uint64_t b2, b4;
+        if (!mul_ok(t.n, 2, &b2) || !mul_ok(t.n, 4, &b4))
+            return ZERO_EOVERFLOW;
+        for (uintptr_t a : {p, g})
+            if (a + b2 < a)
+                return ZERO_EOVERFLOW;
+        for (uintptr_t a : {w, m, v})
+            if (a + b4 < a)
+                return ZERO_EOVERFLOW;
+        ranges.push_back({p, p + b2, true});
+        ranges.push_back({g, g + b2, false});
+        ranges.push_back({w, w + b4, true});
+        ranges.push_back({m, m + b4, true});
+        ranges.push_back({v, v + b4, true});
+        if (!add_ok(n_params, t.n, &n_params))
+            return ZERO_EOVERFLOW;
+        TensorDesc d;
+        d.unused = 0;
+        d.p = (uint16_t *)t.param_f16;
+        d.g = (const uint16_t *)t.grad_f16;
+        d.w = t.master;
+        d.m = t.m;
+        d.v = t.v;
+        d.n = t.n;
+        const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
+        pick_vector_path(a16, 2, a32, 3, &d.vec, &d.head);
+        plan.tensors.push_back(d);
+    }
+    if (writes_overlap(ranges))
+        return ZERO_EINVAL;
+
+    const uint64_t C = chunk_elems_for(n_params);
+    zero_plan_stats &s = plan.stats;
+    s.n_tensors = n_tensors;
+    s.n_params = n_params;
+    s.chunk_elems = C;
+    for (uint32_t k = 0; k < (uint32_t)plan.tensors.size(); k++) {
+        const TensorDesc &d = plan.tensors[k];
+        const uint64_t head = std::min<uint64_t>(d.head, d.n);
+        // first chunk: the peeled head plus up to C elements; then C each
+        uint64_t start = 0;
+        uint64_t first = std::min<uint64_t>(d.n, head + C);
+        plan.chunks.push_back({k, (uint32_t)first, 0});
+        start = first;
+        while (start < d.n) {
+            const uint64_t cnt = std::min<uint64_t>(C, d.n - start);
+            plan.chunks.push_back({k, (uint32_t)cnt, start});
+            start += cnt;
+        }
+        if (d.vec == 1) {
+            s.scalar_elems += d.n;
+        } else {
+            const uint64_t body = (d.n - head) / d.vec * d.vec;
+            (d.vec == 8 ? s.vec8_elems : s.vec4_elems) += body;
+            s.scalar_elems += d.n - body;
+        }
+    }
+    s.n_chunks = plan.chunks.size();
+    s.table_bytes = plan.tensors.size() * sizeof(TensorDesc) + plan.chunks.size() * sizeof(Chunk);
+    *out = std::move(plan);
+    return ZERO_OK;
+}
+
+} // namespace zs
+
+extern "C" int zero_plan_describe(const zero_tensor *tensors, uint32_t n_tensors,
+                                  zero_plan_stats *out) {
+    if (!out)
+        return ZERO_EINVAL;
+    zs::HostPlan plan;
+    int rc = zs::build_host_plan(tensors, n_tensors, &plan);
+    if (rc == ZERO_OK)
+        *out = plan.stats;
+    return rc;
+}

@@ -226,3 +226,74 @@ def sample_indices(n: int, k: int, seed: int, must: Optional[np.ndarray] = None,
     if must is not None:
         parts.append(np.asarray(must, dtype=np.int64))
     return np.unique(np.concatenate(parts))
+
+
+# ---------------------------------------------------------------------------
+# Device state for the large workloads.  Sizes and offsets come from the
+# caller (the shard layout is not computed here).
+# ---------------------------------------------------------------------------
+class DeviceTensor:
+    """The five arrays of one tensor of the shard, on the device."""
+
+    def __init__(self, n: int, device, param=None):
+        import torch
+        self.n = n
+        self.p = param if param is not None else torch.zeros(n, dtype=torch.float16, device=device)
+        self.g = torch.zeros(n, dtype=torch.float16, device=device)
+        self.w = torch.empty(n, dtype=torch.float32, device=device)
+        self.m = torch.zeros(n, dtype=torch.float32, device=device)
+        self.v = torch.zeros(n, dtype=torch.float32, device=device)
+
+    def arrays(self):
+        return (self.p, self.g, self.w, self.m, self.v)
+
+
+def device_list_state(wl: Workload, device="cuda") -> List[DeviceTensor]:
+    """One DeviceTensor per tensor of a list workload; master ~ N(0, 0.02)."""
+    out = []
+    for k, (_, n) in enumerate(wl.tensors):
+        t = DeviceTensor(n, device)
+        device_normal(n, MASTER_STD, master_seed(wl.seed, k), None, device, out=t.w)
+        out.append(t)
+    return out
+
+
+def device_flat_state(wl: Workload, offset: int, length: int, padded_total: int,
+                      device="cuda"):
+    """The flat workloads: the full fp16 parameter buffer of padded_total
+    elements (every rank holds all fp16 parameters under stages 1-2) and this
+    rank's shard of `length` elements at `offset` in it.  Returns
+    (param_full, DeviceTensor)."""
+    import torch
+    full = torch.zeros(padded_total, dtype=torch.float16, device=device)
+    t = DeviceTensor(length, device, param=full[offset:offset + length])
+    device_normal(length, MASTER_STD, master_seed(wl.seed), None, device, out=t.w)
+    return full, t
+
+
+def device_fill_grads(wl: Workload, tensors: Sequence[DeviceTensor], t: int) -> None:
+    """Step-t fp16 gradients ~ N(0, 1e-3) for every tensor, in place."""
+    for k, dt in enumerate(tensors):
+        device_normal(dt.n, GRAD_STD, grad_seed(wl.seed, t, k), None, dt.g.device, out=dt.g)
+
+
+def device_inject_inf(grad, positions: np.ndarray, signs: np.ndarray) -> None:
+    """Set grad[positions] to +inf or -inf (fp16)."""
+    import torch
+    pos = torch.from_numpy(positions).to(grad.device)
+    val = torch.from_numpy(signs.astype(np.float32) * np.float32(np.inf)).to(grad.device)
+    grad.index_copy_(0, pos, val.to(torch.float16))
+
+
+def device_slices(wl: Workload, length: int, device="cuda"):
+    """N_d fp16 gradient slices of this rank's partition, ~ N(0, 1e-3), as
+    rows of one buffer whose row pitch is rounded up to 64 elements (so every
+    row starts 128-byte aligned, as separately allocated receive buffers
+    would).  Returns (buffer, [row views])."""
+    import torch
+    pitch = (length + 63) // 64 * 64
+    buf = torch.zeros(wl.nd, pitch, dtype=torch.float16, device=device)
+    rows = [buf[r, :length] for r in range(wl.nd)]
+    for r in range(wl.nd):
+        device_normal(length, GRAD_STD, slice_seed(wl.seed, r), None, device, out=rows[r])
+    return buf, rows

@@ -1,0 +1,292 @@
+"""Python binding of libzeroshard.so (include/zero_shard.h), via ctypes.
+
+Argument marshalling only: tensors are checked for dtype, device and
+contiguity and passed as raw device pointers together with torch's current
+HIP stream; every step of the shard update runs in the library's kernels.
+Importing this module loads the library and fails loudly if it is missing or
+was not built for this tree; there is no fallback path.
+
+torch is imported first so that the library binds to the HIP runtime torch
+already loaded (both name the same soname, libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import NamedTuple, Optional, Sequence, Tuple
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EOVERFLOW = -2
+ZERO_EHIP = -3
+ZERO_ENOMEM = -4
+ZERO_MAX_SLICES = 256
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({zero_status_str(status)})")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("padded_total", ctypes.c_uint64), ("shard_len", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64), ("real_len", ctypes.c_uint64)]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("param_f16", ctypes.c_void_p), ("grad_f16", ctypes.c_void_p),
+                ("master", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_uint64) for k in (
+        "n_tensors", "n_params", "n_chunks", "chunk_elems", "vec8_elems",
+        "vec4_elems", "scalar_elems", "table_bytes")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, u32, u64, vp = ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p
+    sig = {
+        "zero_shard_layout": [u64, u32, u32, u32, ctypes.POINTER(_Layout)],
+        "zero_state_bytes": [u32, u64, u32, u32, ctypes.POINTER(ctypes.c_uint64)],
+        "zero_plan_create": [ctypes.POINTER(_Tensor), u32, ctypes.POINTER(vp)],
+        "zero_plan_stats_of": [vp, ctypes.POINTER(_Stats)],
+        "zero_plan_describe": [ctypes.POINTER(_Tensor), u32, ctypes.POINTER(_Stats)],
+        "zero_plan_destroy": [vp],
+        "zero_adam_scalars": [ctypes.POINTER(_HParams), u64, ctypes.POINTER(ctypes.c_float)],
+        "zero_adam_step": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp],
+        "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = i32
+    L.zero_status_str.argtypes = [i32]
+    L.zero_status_str.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+# Every symbol include/zero_shard.h declares.
+EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_plan_create",
+           "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
+           "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
+           "zero_status_str")
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def zero_status_str(status: int) -> str:
+    return _lib.zero_status_str(int(status)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != ZERO_OK:
+        raise ZeroError(fn, rc)
+
+
+class Layout(NamedTuple):
+    padded_total: int
+    shard_len: int
+    offset: int
+    real_len: int
+
+
+def zero_shard_layout(psi: int, nd: int, rank: int, align: int = 1) -> Layout:
+    out = _Layout()
+    _check("zero_shard_layout", _lib.zero_shard_layout(psi, nd, rank, align, ctypes.byref(out)))
+    return Layout(out.padded_total, out.shard_len, out.offset, out.real_len)
+
+
+def zero_state_bytes(stage: int, psi: int, nd: int, align: int = 1) -> int:
+    out = ctypes.c_uint64()
+    _check("zero_state_bytes", _lib.zero_state_bytes(stage, psi, nd, align, ctypes.byref(out)))
+    return out.value
+
+
+@dataclass(frozen=True)
+class AdamHParams:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+    def _c(self) -> _HParams:
+        return _HParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay)
+
+
+def _hp(hp) -> _HParams:
+    if isinstance(hp, dict):
+        hp = AdamHParams(**hp)
+    return hp._c()
+
+
+def zero_adam_scalars(hp, t: int) -> Tuple[float, ...]:
+    """{lr, b1, 1-b1, b2, 1-b2, 1-b1^t, 1-b2^t, eps} as the kernel uses them."""
+    out = (ctypes.c_float * 8)()
+    h = _hp(hp)
+    _check("zero_adam_scalars", _lib.zero_adam_scalars(ctypes.byref(h), t, out))
+    return tuple(out)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, dtype, what: str, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: expected a device (cuda/HIP) tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+
+
+def _flag_ptr(flag: Optional[torch.Tensor], what: str, device) -> Optional[int]:
+    if flag is None:
+        return None
+    _need(flag, torch.int32, what, device)
+    if flag.numel() < 1:
+        raise ValueError(f"{what}: needs one int32")
+    return flag.data_ptr()
+
+
+def _tensor_entries(tensors: Sequence[Sequence[torch.Tensor]]):
+    arr = (_Tensor * max(1, len(tensors)))()
+    device = None
+    for k, group in enumerate(tensors):
+        if len(group) != 5:
+            raise ValueError("each tensor is (param_f16, grad_f16, master, m, v)")
+        p, g, w, m, v = group
+        device = device or w.device
+        for x, dt, nm in ((p, torch.float16, "param"), (g, torch.float16, "grad"),
+                          (w, torch.float32, "master"), (m, torch.float32, "m"),
+                          (v, torch.float32, "v")):
+            _need(x, dt, f"tensor {k} {nm}", device)
+        n = w.numel()
+        if not (p.numel() == g.numel() == m.numel() == v.numel() == n):
+            raise ValueError(f"tensor {k}: the five arrays differ in size")
+        arr[k] = _Tensor(p.data_ptr(), g.data_ptr(), w.data_ptr(), m.data_ptr(),
+                         v.data_ptr(), n)
+    return arr, device
+
+
+class Plan:
+    """A zero_plan: the device chunk table over a list of tensors.  Holds
+    references to the tensors so their memory outlives the plan."""
+
+    def __init__(self, handle: int, tensors, device):
+        self._h = handle
+        self._keep = [tuple(g) for g in tensors]
+        self.device = device
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("plan was destroyed")
+        return self._h
+
+    def stats(self) -> dict:
+        s = _Stats()
+        _check("zero_plan_stats_of", _lib.zero_plan_stats_of(self.handle, ctypes.byref(s)))
+        return {k: getattr(s, k) for k, _ in _Stats._fields_}
+
+    def destroy(self) -> None:
+        if self._h:
+            h, self._h = self._h, None
+            _check("zero_plan_destroy", _lib.zero_plan_destroy(h))
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def zero_plan_create(tensors: Sequence[Sequence[torch.Tensor]]) -> Plan:
+    """tensors: sequence of (param_f16, grad_f16, master_f32, m_f32, v_f32)."""
+    arr, device = _tensor_entries(tensors)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check("zero_plan_create", _lib.zero_plan_create(arr, len(tensors), ctypes.byref(h)))
+    return Plan(h.value, tensors, device)
+
+
+def zero_plan_describe(tensors) -> dict:
+    """Classification of a would-be plan, computed on the host only.
+    tensors: sequence of (param, grad, master, m, v, n) with integer
+    addresses, or of torch tensors as for zero_plan_create."""
+    arr = (_Tensor * max(1, len(tensors)))()
+    for k, e in enumerate(tensors):
+        if len(e) == 6:
+            arr[k] = _Tensor(*e)
+        else:
+            a, _ = _tensor_entries([e])
+            arr[k] = a[0]
+    s = _Stats()
+    _check("zero_plan_describe", _lib.zero_plan_describe(arr, len(tensors), ctypes.byref(s)))
+    return {k: getattr(s, k) for k, _ in _Stats._fields_}
+
+
+def zero_plan_destroy(plan: Plan) -> None:
+    plan.destroy()
+
+
+def zero_adam_step(plan: Plan, hp, t: int, nonfinite_flag: Optional[torch.Tensor] = None,
+                   skip_if_nonzero: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue one Adam step over the plan on `stream` (torch's current stream
+    by default)."""
+    h = _hp(hp)
+    f = _flag_ptr(nonfinite_flag, "nonfinite_flag", plan.device)
+    s = _flag_ptr(skip_if_nonzero, "skip_if_nonzero", plan.device)
+    _check("zero_adam_step", _lib.zero_adam_step(plan.handle, ctypes.byref(h), int(t), f, s,
+                                                 _stream_handle(stream)))
+
+
+def zero_reduce_grad_shard(slices: Sequence[torch.Tensor], out: torch.Tensor,
+                           nonfinite_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out = fp16(mean over ranks of the fp16 slices), fp32 sum in rank order."""
+    _need(out, torch.float16, "out")
+    n = out.numel()
+    nd = len(slices)
+    if nd == 0 or nd > ZERO_MAX_SLICES:
+        raise ValueError(f"need 1..{ZERO_MAX_SLICES} slices, got {nd}")
+    ptrs = (ctypes.c_void_p * nd)()
+    for r, s in enumerate(slices):
+        _need(s, torch.float16, f"slice {r}", out.device)
+        if s.numel() != n:
+            raise ValueError(f"slice {r} has {s.numel()} elements, out has {n}")
+        ptrs[r] = s.data_ptr()
+    f = _flag_ptr(nonfinite_flag, "nonfinite_flag", out.device)
+    _check("zero_reduce_grad_shard",
+           _lib.zero_reduce_grad_shard(ptrs, nd, n, out.data_ptr(), f, _stream_handle(stream)))
