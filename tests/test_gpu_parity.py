@@ -363,7 +363,7 @@ def test_rejects_through_binding(zs, torch_mod):
     torch = torch_mod
     a = torch.zeros(16, dtype=torch.float16, device="cuda")
     with pytest.raises(zs.ZeroError):
-        zs.zero_reduce_grad_shard([a, a[4:12]], a[2:10])      # out overlaps a slice
+        zs.zero_reduce_grad_shard([a[:8], a[8:16]], a[2:10])      # out overlaps a slice
     w = torch.zeros(16, device="cuda")
     with pytest.raises(zs.ZeroError):                          # m aliases master
         zs.zero_plan_create([(a, a.clone(), w, w, torch.zeros(16, device="cuda"))])
