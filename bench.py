@@ -63,8 +63,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="flat_7p5b_nd64",
                     choices=["flat_7p5b_nd64", "flat_7p5b_nd8", "gpt2_xl", "llama_7b", "tiny_flat"])
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
+    ap.add_argument("--chunk-elems", type=int, default=0,
+                    help="elements per chunk of the Adam plan (0: library default)")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements of the shard the CPU oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="keep stepping the CPU oracle over its sample until this much "
+                         "wall time has passed (at most 8 steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -72,7 +77,7 @@ def parse():
 class Step:
     """Device state and the launches of one step for a workload."""
 
-    def __init__(self, zs, W, name):
+    def __init__(self, zs, W, name, chunk_elems=0):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         wl = W.WORKLOADS[name]
@@ -94,7 +99,7 @@ class Step:
             self.layout = None
             self.tensors = W.device_list_state(wl)
             W.device_fill_grads(wl, self.tensors, 1)
-        self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors])
+        self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors], chunk_elems)
         self.n_params = self.plan.stats()["n_params"]
         self.t = 0
 
@@ -114,9 +119,12 @@ class Step:
         return ks
 
 
-def cpu_baseline(step, sample_n: int):
+def cpu_baseline(step, sample_n: int, min_seconds: float):
     """The oracle as it stands, on contiguous partitions of the first
-    sample_n elements of the shard, one host thread per partition."""
+    sample_n elements of the shard (first tensor of a list), one host thread
+    per partition: whole steps (the reduce of the N_d slices where the
+    workload has one, then Adam at t = 1, 2, ...) until min_seconds of wall
+    time have passed."""
     import concurrent.futures as cf
     import numpy as np
     import torch
@@ -138,20 +146,25 @@ def cpu_baseline(step, sample_n: int):
         sl = None
     bounds = [(n * i // T, n * (i + 1) // T) for i in range(T)]
 
-    def part(b):
+    def part(b, t):
         lo, hi = b
         if sl is not None:
             oracle.reduce_grad([s[lo:hi] for s in sl], g[lo:hi])
-        oracle.adam_step(g[lo:hi], p[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], t=1, **hp)
+        oracle.adam_step(g[lo:hi], p[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], t=t, **hp)
 
     oracle.lib()
+    steps = 0
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(T) as ex:
-        list(ex.map(part, bounds))
-    dt = time.perf_counter() - t0
+        while True:
+            steps += 1
+            list(ex.map(part, bounds, [steps] * T))
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or steps >= 8:
+                break
     what = ("reduce of %d fp16 slices + Adam step" % step.wl.nd) if sl is not None else "Adam step"
-    return {"value": n / dt, "unit": "params/s", "cores": T, "kind": "oracle",
-            "sample": f"first {n} elements of the shard: {what}, {T} host threads, "
+    return {"value": n * steps / dt, "unit": "params/s", "cores": T, "kind": "oracle",
+            "sample": f"first {n} elements of the shard: {steps} x ({what}), {T} host threads, "
                       f"{dt:.2f} s wall"}
 
 
@@ -170,7 +183,7 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    step = Step(zs, W, args.workload)
+    step = Step(zs, W, args.workload, args.chunk_elems)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -203,10 +216,12 @@ def main():
     traffic = measured_traffic(dom, args.workload)
     value = step.n_params * args.steps / wall
     bytes_per_step = sum(b for _, _, b in ks)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(step, args.cpu_sample)
+    cpu = (None if args.no_cpu_baseline
+           else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
     cfg = {"workload": args.workload, "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
+           "chunk_elems": step.plan.stats()["chunk_elems"],
            "kernels_per_step": [k for k, _, _ in ks],
            "alg_bytes_per_step": bytes_per_step,
            "step_hbm_gbps": bytes_per_step * args.steps / wall / 1e9}

@@ -78,9 +78,10 @@ typedef struct zero_plan_stats {
     uint64_t n_tensors;
     uint64_t n_params;      /* sum of n over the tensors */
     uint64_t n_chunks;      /* work items; one workgroup handles one at a time */
-    uint64_t chunk_elems;   /* elements per chunk (the last of a tensor: fewer) */
-    uint64_t vec8_elems;    /* elements on the 16-byte-vector path */
-    uint64_t vec4_elems;    /* elements on the 8-byte fp16 / 16-byte fp32 path */
+    uint64_t chunk_elems;   /* elements per chunk (a tensor's first chunk also
+                               holds its peeled head; its last may be short) */
+    uint64_t vector_elems;  /* elements moved four at a time (8-byte fp16 and
+                               16-byte fp32 vectors) */
     uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
                                tensors whose arrays disagree in alignment) */
     uint64_t table_bytes;   /* device bytes of the chunk table */
@@ -118,20 +119,25 @@ int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
 /*
  * zero_plan_create -- chunk table for a list of tensors of mixed sizes.
  * tensors: host array of n_tensors descriptors (copied; the table does not
- * keep the host array).  Each tensor is cut into chunks of at most
- * chunk_elems elements; per tensor the library picks the widest access path
- * that all five arrays' alignments allow (16-byte vectors, 8-byte fp16 /
- * 16-byte fp32 vectors, or single elements) after peeling at most 7 leading
- * elements.  The table is allocated on the current device (hipMalloc) and
- * filled with a synchronous copy; nothing else is allocated later.
+ * keep the host array).  Each tensor is cut into chunks of chunk_elems
+ * elements (its last chunk may be shorter); the step runs one 64-lane wave
+ * per 512 consecutive elements of a chunk.
+ * chunk_elems: 0 selects the library default (16384); otherwise a multiple
+ * of 512 between 512 and 2^24.  Per tensor the library takes the vector
+ * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree
+ * in alignment after peeling at most 3 leading elements, else it moves
+ * single elements.  The table is allocated on the current device
+ * (hipMalloc) and filled with a synchronous copy; nothing else is
+ * allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The
  * tensors' memory stays the caller's and must outlive the plan.
  * Errors: EINVAL (NULL out or tensors with n_tensors > 0, a NULL array of
  * a non-empty tensor, fp16 arrays not 2-byte or fp32 arrays not 4-byte
- * aligned, overlapping arrays within a tensor); EOVERFLOW; ENOMEM; EHIP.
+ * aligned, overlapping arrays within or across tensors where one is
+ * written, a bad chunk_elems); EOVERFLOW; ENOMEM; EHIP.
  */
 int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
-                     zero_plan **out);
+                     uint32_t chunk_elems, zero_plan **out);
 
 /* zero_plan_stats_of -- fill *out for an existing plan.  Host only. */
 int zero_plan_stats_of(const zero_plan *plan, zero_plan_stats *out);
@@ -142,7 +148,7 @@ int zero_plan_stats_of(const zero_plan *plan, zero_plan_stats *out);
  * Host only.  Errors as zero_plan_create minus ENOMEM and EHIP.
  */
 int zero_plan_describe(const zero_tensor *tensors, uint32_t n_tensors,
-                       zero_plan_stats *out);
+                       uint32_t chunk_elems, zero_plan_stats *out);
 
 /* zero_plan_destroy -- free the table.  No step using the plan may still be
  * in flight.  NULL is accepted.  Errors: EHIP. */

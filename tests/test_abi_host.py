@@ -109,20 +109,44 @@ def _fake(n, p=0x100000, g=0x200000, w=0x300000, m=0x400000, v=0x500000):
 
 
 def test_plan_describe_paths(zs):
+    # all five arrays aligned: everything on the four-element vector path
     d = zs.zero_plan_describe([_fake(100)])
-    assert (d["vec8_elems"], d["vec4_elems"], d["scalar_elems"]) == (96, 0, 4)
-    # all five arrays share a 4-element phase: peel 4, then 16-byte vectors
-    d = zs.zero_plan_describe([_fake(100, 0x100008, 0x200008, 0x300010, 0x400010, 0x500010)])
-    assert (d["vec8_elems"], d["scalar_elems"]) == (96, 4)
-    # fp16 arrays disagree mod 16 but agree mod 8: the 4-wide path
-    d = zs.zero_plan_describe([_fake(100, 0x100008)])
-    assert (d["vec8_elems"], d["vec4_elems"], d["scalar_elems"]) == (0, 100, 0)
-    # fp16 param 2-byte aligned only: single elements
+    assert (d["vector_elems"], d["scalar_elems"]) == (100, 0)
+    d = zs.zero_plan_describe([_fake(103)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (100, 3)
+    # all five arrays two elements past an aligned boundary: peel 2 singly,
+    # then vectors, then the last 2 singly
+    d = zs.zero_plan_describe([_fake(100, 0x100004, 0x200004, 0x300008, 0x400008, 0x500008)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (96, 4)
+    # fp16 arrays 8-byte aligned but not 16: still the vector path
+    d = zs.zero_plan_describe([_fake(100, 0x100008, 0x200008)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (100, 0)
+    # fp16 param one element off the grad's phase: single elements
     d = zs.zero_plan_describe([_fake(100, 0x100002)])
-    assert d["scalar_elems"] == 100
-    # fp32 master 4-byte aligned only
+    assert (d["vector_elems"], d["scalar_elems"]) == (0, 100)
+    # fp32 master one element off: single elements
     d = zs.zero_plan_describe([_fake(100, w=0x300004)])
-    assert d["vec8_elems"] == 0 and d["vec4_elems"] == 0 and d["scalar_elems"] == 100
+    assert (d["vector_elems"], d["scalar_elems"]) == (0, 100)
+
+
+def test_plan_chunking(zs):
+    """Chunk counts: a tensor's first chunk holds its peeled head plus up to
+    chunk_elems elements, then chunk_elems each; the default is 16384."""
+    d = zs.zero_plan_describe([_fake(40000)])
+    assert d["chunk_elems"] == 16384 and d["n_chunks"] == 3
+    for C in (512, 1024, 4096, 1 << 24):
+        for n in (1, 511, 512, 513, 5000, 100003):
+            d = zs.zero_plan_describe([_fake(n)], C)
+            assert d["chunk_elems"] == C and d["n_chunks"] == -(-n // C), (C, n)
+    # head of 2 rides in the first chunk
+    d = zs.zero_plan_describe([_fake(514, 0x100004, 0x200004, 0x300008, 0x400008, 0x500008)], 512)
+    assert d["n_chunks"] == 1
+    d = zs.zero_plan_describe([_fake(515, 0x100004, 0x200004, 0x300008, 0x400008, 0x500008)], 512)
+    assert d["n_chunks"] == 2
+    for C in (1, 100, 511, 513, 1000, (1 << 24) + 512, 2 ** 31):
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_plan_describe([_fake(10)], C)
+        assert e.value.status == -1
 
 
 def test_plan_describe_workload_lists(zs):
@@ -138,7 +162,8 @@ def test_plan_describe_workload_lists(zs):
             base += 5 * step
         d = zs.zero_plan_describe(ents)
         assert d["n_params"] == wl.n_params and d["n_tensors"] == len(wl.tensors)
-        assert d["vec8_elems"] + d["vec4_elems"] + d["scalar_elems"] == wl.n_params
+        assert d["vector_elems"] + d["scalar_elems"] == wl.n_params
+        assert d["scalar_elems"] == sum(n % 4 for _, n in wl.tensors)
         C = d["chunk_elems"]
         assert d["n_chunks"] == sum((n + C - 1) // C for _, n in wl.tensors)
         assert d["table_bytes"] == 64 * len(wl.tensors) + 16 * d["n_chunks"]

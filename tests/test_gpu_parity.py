@@ -114,27 +114,30 @@ def _ragged_plan(zs, torch, sizes_offsets, seed, warm=False):
 
 SIZES = [1, 7, 8, 9, 31, 4095, 4096, 4097, 2048 * 3 + 5, 70001, 0]
 # element offsets of (param, grad, master, m, v) inside their buffers
-OFFSETS = [(0, 0, 0, 0, 0),      # all aligned: 16-byte path
-           (4, 0, 0, 0, 0),      # param 8 mod 16 bytes, grad 0: 8-byte fp16 path
-           (3, 3, 3, 3, 3),      # common phase: peel 5, then 16-byte path
-           (4, 4, 0, 0, 0),      # fp16 8 mod 16 bytes: peel 4, then 16-byte path
-           (1, 0, 0, 0, 0),      # param odd: single elements
+OFFSETS = [(0, 0, 0, 0, 0),      # all aligned: vector path, no head
+           (4, 0, 0, 0, 0),      # param 8 mod 16 bytes, grad 0: vector path, no head
+           (3, 3, 3, 3, 3),      # common phase: peel 1, then vectors
+           (2, 6, 2, 2, 6),      # phases agree mod a vector: peel 2, then vectors
+           (1, 0, 0, 0, 0),      # param one element off: single elements
            (0, 0, 1, 0, 0)]      # master 4 mod 16 bytes: single elements
 
 
+@pytest.mark.parametrize("chunk", [0, 512, 1536])
 @pytest.mark.parametrize("warm", [False, True])
-def test_ragged_sizes_and_alignments(zs, torch_mod, warm):
+def test_ragged_sizes_and_alignments(zs, torch_mod, warm, chunk):
     """One plan over tensors of sizes 0..70001 whose arrays sit at every
-    alignment class; three steps; every element compared."""
+    alignment class, with the default chunk size and with chunks of one and
+    three wave tiles (many chunk boundaries inside small tensors); three
+    steps; every element compared."""
     torch = torch_mod
     so = [(n, OFFSETS[i % len(OFFSETS)]) for i, n in enumerate(SIZES)]
     so += [(n, OFFSETS[(i + 2) % len(OFFSETS)]) for i, n in enumerate(SIZES)]
-    say(f"ragged warm={warm} tensors={len(so)}")
+    say(f"ragged warm={warm} chunk={chunk} tensors={len(so)}")
     dev, host = _ragged_plan(zs, torch, so, seed=42 + warm, warm=warm)
-    plan = zs.zero_plan_create(dev)
+    plan = zs.zero_plan_create(dev, chunk)
     st = plan.stats()
-    assert st["vec8_elems"] and st["vec4_elems"] and st["scalar_elems"]
-    assert st["vec8_elems"] + st["vec4_elems"] + st["scalar_elems"] == st["n_params"]
+    assert st["vector_elems"] and st["scalar_elems"]
+    assert st["vector_elems"] + st["scalar_elems"] == st["n_params"]
     rng = np.random.default_rng(7)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     t0 = 6 if warm else 1

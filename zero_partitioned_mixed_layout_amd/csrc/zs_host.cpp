@@ -94,19 +94,11 @@ extern "C" const char *zero_status_str(int status) {
 
 namespace zs {
 
-uint64_t chunk_elems_for(uint64_t n_params) {
-    // Enough chunks to spread a plan over all 256 compute units several
-    // times, but at least 2048 elements (one 16-byte vector per lane of a
-    // 256-lane workgroup) and at most 16384 per chunk.
-    uint64_t c = 2048;
-    while (c < 16384 && n_params / c > 8192)
-        c *= 2;
-    return c;
-}
-
 void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n32,
-                      uint32_t *vec, uint32_t *head) {
+                      uint32_t max_width, uint32_t *vec, uint32_t *head) {
     for (uint32_t w : {8u, 4u}) {
+        if (w > max_width)
+            continue;
         const uintptr_t a16 = 2u * w; // bytes one fp16 vector spans
         for (uint32_t h = 0; h < w; h++) {
             bool ok = true;
@@ -151,8 +143,13 @@ bool writes_overlap(std::vector<Range> &r) {
 
 } // namespace
 
-int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *out) {
+int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
+                    HostPlan *out) {
     if (!out || (n_tensors > 0 && !tensors))
+        return ZERO_EINVAL;
+    if (chunk_elems == 0)
+        chunk_elems = kDefaultChunk;
+    if (chunk_elems % kTile != 0 || chunk_elems < kMinChunk || chunk_elems > kMaxChunk)
         return ZERO_EINVAL;
     HostPlan plan;
     memset(&plan.stats, 0, sizeof(plan.stats));
@@ -193,13 +190,13 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *ou
         d.v = t.v;
         d.n = t.n;
         const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
-        pick_vector_path(a16, 2, a32, 3, &d.vec, &d.head);
+        pick_vector_path(a16, 2, a32, 3, 4, &d.vec, &d.head);
         plan.tensors.push_back(d);
     }
     if (writes_overlap(ranges))
         return ZERO_EINVAL;
 
-    const uint64_t C = chunk_elems_for(n_params);
+    const uint64_t C = chunk_elems;
     zero_plan_stats &s = plan.stats;
     s.n_tensors = n_tensors;
     s.n_params = n_params;
@@ -220,9 +217,12 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *ou
         if (d.vec == 1) {
             s.scalar_elems += d.n;
         } else {
-            const uint64_t body = (d.n - head) / d.vec * d.vec;
-            (d.vec == 8 ? s.vec8_elems : s.vec4_elems) += body;
-            s.scalar_elems += d.n - body;
+            // every chunk body but the tensor's last is a whole number of
+            // tiles, so only the tensor's last fewer-than-four elements (and
+            // its head) go singly
+            const uint64_t vec = (d.n - head) / 4 * 4;
+            s.vector_elems += vec;
+            s.scalar_elems += d.n - vec;
         }
     }
     s.n_chunks = plan.chunks.size();
@@ -234,11 +234,11 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *ou
 } // namespace zs
 
 extern "C" int zero_plan_describe(const zero_tensor *tensors, uint32_t n_tensors,
-                                  zero_plan_stats *out) {
+                                  uint32_t chunk_elems, zero_plan_stats *out) {
     if (!out)
         return ZERO_EINVAL;
     zs::HostPlan plan;
-    int rc = zs::build_host_plan(tensors, n_tensors, &plan);
+    int rc = zs::build_host_plan(tensors, n_tensors, chunk_elems, &plan);
     if (rc == ZERO_OK)
         *out = plan.stats;
     return rc;

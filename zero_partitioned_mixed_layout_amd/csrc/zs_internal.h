@@ -19,15 +19,16 @@ struct TensorDesc {
     float *m;          // fp32 first moment
     float *v;          // fp32 second moment
     uint64_t n;
-    uint32_t vec;      // access width in elements: 8, 4 or 1
+    uint32_t vec;      // 4: four-element vector path; 1: single elements
     uint32_t head;     // leading elements done singly so the rest is aligned
     uint64_t unused;   // pads the descriptor to 64 bytes
 };
 static_assert(sizeof(TensorDesc) == 64, "TensorDesc is 64 bytes");
 
-// One work item: `count` elements of tensor `tensor` from element `start`
-// (16 bytes).  Chunk starts other than a tensor's first are aligned for the
-// tensor's vector width.
+// One work item of a workgroup: `count` elements of tensor `tensor` from
+// element `start` (16 bytes).  Chunk starts other than a tensor's first are
+// vector-aligned, and every chunk but a tensor's last holds a whole number
+// of wave tiles (plus the peeled head in a tensor's first chunk).
 struct Chunk {
     uint32_t tensor;
     uint32_t count;
@@ -35,8 +36,36 @@ struct Chunk {
 };
 static_assert(sizeof(Chunk) == 16, "Chunk is 16 bytes");
 
-// Threads per workgroup of both kernels (four 64-wide waves).
-constexpr int kBlock = 256;
+// Lanes of a wave, and threads of every workgroup of both kernels: one wave
+// per workgroup.
+constexpr uint32_t kWave = 64;
+
+// Elements of one Adam wave tile: 64 lanes x two groups of four.
+constexpr uint32_t kTile = 512;
+
+// Chunk sizes a plan accepts (multiples of kTile) and the default.  One
+// workgroup updates one tile; the chunk size only sets how many tiles share
+// a table entry (a tensor's short last chunk leaves some workgroups idle).
+constexpr uint32_t kMinChunk = kTile;
+constexpr uint32_t kMaxChunk = 1u << 24;
+constexpr uint32_t kDefaultChunk = 16384;
+
+// Largest grid of either kernel (64 * 2^24 lanes stays below 2^32); larger
+// work strides over it.
+constexpr uint64_t kMaxGrid = 1u << 24;
+
+// Resident one-wave workgroups per CU for the Adam step (each keeps eight
+// 8- or 16-byte loads per lane in flight).
+constexpr uint32_t kAdamPerCU = 6;
+
+// Resident one-wave workgroups per CU for the reduction over nd slices:
+// about 48 fp16 vectors per lane in flight per CU (3 workgroups at 16
+// slices in flight), between 3 and 8 workgroups.
+inline uint32_t reduce_per_cu(uint32_t nd) {
+    const uint32_t in_flight = nd >= 16 ? 16 : (nd >= 4 ? nd / 4 * 4 : nd);
+    const uint32_t k = (48 + in_flight - 1) / in_flight;
+    return k < 3 ? 3 : (k > 8 ? 8 : k);
+}
 
 struct HostPlan {
     std::vector<TensorDesc> tensors;
@@ -44,17 +73,16 @@ struct HostPlan {
     zero_plan_stats stats;
 };
 
-// Validate and classify; fills `out`.  Pure host code.
-int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, HostPlan *out);
+// Validate and classify; fills `out`.  chunk_elems: 0 for kDefaultChunk,
+// else a multiple of kTile in [kMinChunk, kMaxChunk].  Pure host code.
+int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
+                    HostPlan *out);
 
-// Elements per chunk for a plan of n_params elements.
-uint64_t chunk_elems_for(uint64_t n_params);
-
-// Pick the widest vector width (8, 4, else 1) and the leading-element peel
-// (< width) for which every address is aligned.  fp16 arrays need 2*width
-// bytes, fp32 arrays 16 bytes for widths 8 and 4.
+// Pick the widest vector width, at most max_width (8 or 4; else 1), and the
+// leading-element peel (< width) for which every address is aligned: fp16
+// arrays need 2*width bytes, fp32 arrays 16 bytes.
 void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n32,
-                      uint32_t *vec, uint32_t *head);
+                      uint32_t max_width, uint32_t *vec, uint32_t *head);
 
 } // namespace zs
 

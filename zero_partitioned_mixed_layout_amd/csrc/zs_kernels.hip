@@ -3,10 +3,21 @@
 // the plan upload and the launches behind the C ABI.
 //
 // Both kernels are elementwise HBM streams (Adam: 28 bytes per parameter;
-// reduce: 2 N_d + 2 bytes), so they use no matrix cores.  Each lane moves
-// 16-byte vectors (8 fp16 or 4 fp32), a 64-lane wave covers contiguous
-// 1-2 KiB per instruction, and streamed data is loaded and stored with the
-// nontemporal hint so it does not displace anything in the caches.
+// reduce: 2 N_d + 2 bytes), so they use no matrix cores.  Every load and
+// store instruction of a 64-lane wave covers one contiguous, line-aligned
+// range (Adam: 512 bytes of fp16 or 1 KiB of fp32; reduce: 1 KiB of fp16),
+// and streamed data moves with the nontemporal hint.  On gfx950 nontemporal
+// stores only stream at full rate when each instruction writes whole lines,
+// which is why the Adam wave tile interleaves its two four-element groups
+// across the wave instead of giving each lane eight neighbours.
+//
+// Occupancy is capped on purpose.  Both kernels run one 64-lane wave per
+// workgroup, and each launch reserves dynamic LDS that the kernel never
+// touches, so that only a few workgroups are resident per CU (Adam 6; reduce
+// 3 when 16 slices are in flight per lane).  Measured on MI355X, HBM3E
+// streams these many-array patterns fastest with just enough bytes in
+// flight to cover latency (about 45 KB per CU); with the 20-30 waves per CU
+// that registers alone would allow, the same streams run 10-15% slower.
 //
 // Exactness: every arithmetic step is one IEEE binary32 operation in a fixed
 // order; the library is built with -ffp-contract=off (no fused multiply-add),
@@ -25,7 +36,8 @@
 namespace {
 
 using zs::Chunk;
-using zs::kBlock;
+using zs::kTile;
+using zs::kWave;
 using zs::TensorDesc;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -61,6 +73,23 @@ __device__ __forceinline__ void st_nt(T v, T *p) {
 __device__ __forceinline__ bool f16_bits_nonfinite(uint16_t b) {
     return (b & 0x7C00u) == 0x7C00u;
 }
+
+// Raise the non-finite flag once for this wave if any lane saw a non-finite
+// value.  The flag only ever goes from 0 to 1, so a wave that reads 1 (an
+// agent-coherent load) skips its atomic: with many waves seeing infinities
+// only the first few reach the flag's address.
+__device__ __forceinline__ void raise_flag(int32_t *flag, int bad) {
+    if (flag == nullptr)
+        return;
+    if (__ballot(bad) != 0 && threadIdx.x % 64u == 0) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+            __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Adam step.
+// ---------------------------------------------------------------------------
 
 // One element of the Adam step (Kingma and Ba, Algorithm 1, with bias
 // correction and eps outside the root).  Returns the new fp16 parameter.
@@ -98,127 +127,122 @@ __device__ __forceinline__ void adam_single(const TensorDesc &T, uint64_t i,
     as_global(T.p)[i] = pb;
 }
 
-// 8 consecutive elements from a 16-byte-aligned group start i.
-__device__ __forceinline__ void adam_vec8(const TensorDesc &T, uint64_t i,
-                                          const AdamConsts &c, int &bad) {
-    const f16x8 g = ld_nt(reinterpret_cast<const f16x8 *>(T.g + i));
-    f32x4 w0 = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i));
-    f32x4 w1 = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i + 4));
-    f32x4 m0 = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i));
-    f32x4 m1 = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i + 4));
-    f32x4 v0 = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
-    f32x4 v1 = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i + 4));
-    // keep all seven 16-byte loads in flight before any arithmetic
-    __builtin_amdgcn_sched_barrier(0);
-    f16x8 p;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        uint16_t gb;
-        _Float16 gj = g[j];
-        memcpy(&gb, &gj, 2);
-        bad |= f16_bits_nonfinite(gb);
-        float w = w0[j], m = m0[j], v = v0[j];
-        p[j] = adam_elem((float)gj, w, m, v, c);
-        w0[j] = w;
-        m0[j] = m;
-        v0[j] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        uint16_t gb;
-        _Float16 gj = g[j + 4];
-        memcpy(&gb, &gj, 2);
-        bad |= f16_bits_nonfinite(gb);
-        float w = w1[j], m = m1[j], v = v1[j];
-        p[j + 4] = adam_elem((float)gj, w, m, v, c);
-        w1[j] = w;
-        m1[j] = m;
-        v1[j] = v;
-    }
-    st_nt(w0, reinterpret_cast<f32x4 *>(T.w + i));
-    st_nt(w1, reinterpret_cast<f32x4 *>(T.w + i + 4));
-    st_nt(m0, reinterpret_cast<f32x4 *>(T.m + i));
-    st_nt(m1, reinterpret_cast<f32x4 *>(T.m + i + 4));
-    st_nt(v0, reinterpret_cast<f32x4 *>(T.v + i));
-    st_nt(v1, reinterpret_cast<f32x4 *>(T.v + i + 4));
-    st_nt(p, reinterpret_cast<f16x8 *>(T.p + i));
+// Four consecutive elements held in registers: fp16 gradient (8 bytes) and
+// fp32 master, m, v (16 bytes each).
+struct Quad {
+    f16x4 g;
+    f32x4 w, m, v;
+};
+
+__device__ __forceinline__ void quad_load(const TensorDesc &T, uint64_t i, Quad &q) {
+    q.g = ld_nt(reinterpret_cast<const f16x4 *>(T.g + i));
+    q.w = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i));
+    q.m = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i));
+    q.v = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
 }
 
-// 4 consecutive elements: fp16 arrays 8-byte aligned, fp32 16-byte aligned.
-__device__ __forceinline__ void adam_vec4(const TensorDesc &T, uint64_t i,
-                                          const AdamConsts &c, int &bad) {
-    const f16x4 g = ld_nt(reinterpret_cast<const f16x4 *>(T.g + i));
-    f32x4 w0 = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i));
-    f32x4 m0 = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i));
-    f32x4 v0 = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
-    __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t i, Quad &q,
+                                                  const AdamConsts &c, int &bad) {
     f16x4 p;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+        const _Float16 gj = q.g[j];
         uint16_t gb;
-        _Float16 gj = g[j];
         memcpy(&gb, &gj, 2);
         bad |= f16_bits_nonfinite(gb);
-        float w = w0[j], m = m0[j], v = v0[j];
+        float w = q.w[j], m = q.m[j], v = q.v[j];
         p[j] = adam_elem((float)gj, w, m, v, c);
-        w0[j] = w;
-        m0[j] = m;
-        v0[j] = v;
+        q.w[j] = w;
+        q.m[j] = m;
+        q.v[j] = v;
     }
-    st_nt(w0, reinterpret_cast<f32x4 *>(T.w + i));
-    st_nt(m0, reinterpret_cast<f32x4 *>(T.m + i));
-    st_nt(v0, reinterpret_cast<f32x4 *>(T.v + i));
+    st_nt(q.w, reinterpret_cast<f32x4 *>(T.w + i));
+    st_nt(q.m, reinterpret_cast<f32x4 *>(T.m + i));
+    st_nt(q.v, reinterpret_cast<f32x4 *>(T.v + i));
     st_nt(p, reinterpret_cast<f16x4 *>(T.p + i));
 }
 
-template <int VEC>
-__device__ __forceinline__ void adam_chunk(const TensorDesc &T, const Chunk &ch,
-                                           const AdamConsts &c, int &bad) {
-    const uint32_t tid = threadIdx.x;
-    // the tensor's unaligned head belongs to its first chunk
-    const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
-    if (tid < head)
-        adam_single(T, ch.start + tid, c, bad);
-    const uint64_t base = ch.start + head;
-    const uint32_t nvec = (ch.count - head) / VEC;
-    for (uint32_t k = tid; k < nvec; k += kBlock) {
-        if (VEC == 8)
-            adam_vec8(T, base + (uint64_t)k * 8, c, bad);
-        else
-            adam_vec4(T, base + (uint64_t)k * 4, c, bad);
-    }
-    const uint64_t tail0 = base + (uint64_t)nvec * VEC;
-    const uint32_t tail = ch.count - head - nvec * VEC;
-    if (tid < tail)
-        adam_single(T, tail0 + tid, c, bad);
+// A full wave tile: kTile consecutive elements from `base` (vector-aligned).
+// Lane L takes elements 4L..4L+3 and kTile/2+4L..kTile/2+4L+3, so each of the
+// wave's load and store instructions covers one contiguous 512-byte (fp16)
+// or 1-KiB (fp32) range.  All eight loads are issued before any arithmetic.
+__device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, uint32_t lane,
+                                          const AdamConsts &c, int &bad) {
+    const uint64_t i0 = base + 4u * lane, i1 = i0 + kTile / 2;
+    Quad a, b;
+    quad_load(T, i0, a);
+    quad_load(T, i1, b);
+    __builtin_amdgcn_sched_barrier(0);
+    quad_update_store(T, i0, a, c, bad);
+    quad_update_store(T, i1, b, c, bad);
 }
 
-__global__ __launch_bounds__(kBlock) void zs_adam_kernel(
+// Tile j of a chunk on the vector path.  The tensor's peeled head (fewer
+// than four elements, so that the rest is vector-aligned) rides in its first
+// chunk and is done by tile 0; every other chunk starts vector-aligned.  The
+// chunk's last, partial tile goes four elements per lane, then the final
+// fewer-than-four singly.
+__device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
+                                                   uint32_t j, const AdamConsts &c, int &bad) {
+    const uint32_t lane = threadIdx.x;
+    const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
+    if (j == 0 && lane < head)
+        adam_single(T, lane, c, bad);
+    const uint64_t base = ch.start + head;
+    const uint32_t body = ch.count - head;
+    const uint32_t nfull = body / kTile;
+    if (j < nfull) {
+        adam_tile(T, base + (uint64_t)j * kTile, lane, c, bad);
+        return;
+    }
+    if (j > nfull)
+        return; // past the end of a short chunk
+    const uint64_t rbase = base + (uint64_t)nfull * kTile;
+    const uint32_t rem = body - nfull * kTile; // < kTile
+    const uint32_t nquads = rem / 4u;
+    for (uint32_t q = lane; q < nquads; q += kWave) {
+        Quad x;
+        quad_load(T, rbase + 4u * q, x);
+        quad_update_store(T, rbase + 4u * q, x, c, bad);
+    }
+    const uint32_t tail = rem - 4u * nquads;
+    if (lane < tail)
+        adam_single(T, rbase + 4u * nquads + lane, c, bad);
+}
+
+// Tile j of a chunk of a tensor whose arrays disagree in alignment: the
+// tile's elements one at a time, lane-strided so each access instruction of
+// the wave stays contiguous.
+__device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chunk &ch,
+                                                 uint32_t j, const AdamConsts &c, int &bad) {
+    const uint32_t lo = j * kTile;
+    const uint32_t hi = min(ch.count, lo + kTile);
+    for (uint32_t k = lo + threadIdx.x; k < hi; k += kWave)
+        adam_single(T, ch.start + k, c, bad);
+}
+
+// The fused step over a plan.  Each workgroup is one wave and takes one wave
+// tile: virtual workgroup b is tile b % tiles_per_chunk of chunk
+// b / tiles_per_chunk.  Launches with fewer workgroups than virtual ones
+// stride over them.
+__global__ __launch_bounds__(kWave) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
-    uint64_t n_chunks, AdamConsts c, int32_t *__restrict__ flag,
+    uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
     const int32_t *__restrict__ skip) {
     if (skip != nullptr && *skip != 0)
         return; // the same value for every wave: the whole step is skipped
     int bad = 0;
-    for (uint64_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
+    for (uint64_t vb = blockIdx.x; vb < n_virtual; vb += gridDim.x) {
+        const uint64_t ci = vb / tiles_per_chunk;
+        const uint32_t j = (uint32_t)(vb - ci * tiles_per_chunk);
         const Chunk ch = chunks[ci];
         const TensorDesc T = tensors[ch.tensor];
-        if (T.vec == 8) {
-            adam_chunk<8>(T, ch, c, bad);
-        } else if (T.vec == 4) {
-            adam_chunk<4>(T, ch, c, bad);
-        } else {
-            for (uint32_t k = threadIdx.x; k < ch.count; k += kBlock)
-                adam_single(T, ch.start + k, c, bad);
-        }
+        if (T.vec == 4)
+            adam_tile_of_chunk(T, ch, j, c, bad);
+        else
+            adam_tile_single(T, ch, j, c, bad);
     }
-    // one atomic per wave at most, and only from a wave that saw a
-    // non-finite gradient anywhere in its share of the grid-stride loop
-    if (flag != nullptr) {
-        const uint64_t any = __ballot(bad);
-        if (any != 0 && (threadIdx.x & 63) == 0)
-            atomicOr(flag, 1);
-    }
+    raise_flag(flag, bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -227,13 +251,6 @@ __global__ __launch_bounds__(kBlock) void zs_adam_kernel(
 struct SliceArgs {
     const _Float16 *p[ZERO_MAX_SLICES];
 };
-
-__device__ __forceinline__ float reduce_single(const SliceArgs &s, uint32_t nd, uint64_t i) {
-    float acc = (float)as_global(s.p[0])[i];
-    for (uint32_t r = 1; r < nd; r++)
-        acc = acc + (float)as_global(s.p[r])[i];
-    return acc;
-}
 
 template <int VEC>
 struct HVec;
@@ -246,55 +263,46 @@ struct HVec<4> {
     typedef f16x4 T;
 };
 
+__device__ __forceinline__ float reduce_single(const SliceArgs &s, uint32_t nd, uint64_t i) {
+    float acc = (float)as_global(s.p[0])[i];
+    for (uint32_t r = 1; r < nd; r++)
+        acc = acc + (float)as_global(s.p[r])[i];
+    return acc;
+}
+
+// Adds slices r0 .. r0+B-1, in rank order, at group start i into acc; the B
+// loads are all issued before the first add.  With `first`, slice r0
+// initialises the sum instead of being added to it.
+template <int VEC, int B>
+__device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, uint64_t i,
+                                             bool first, float (&acc)[VEC]) {
+    typedef typename HVec<VEC>::T hv;
+    hv x[B];
+#pragma unroll
+    for (int q = 0; q < B; q++)
+        x[q] = ld_nt(reinterpret_cast<const hv *>(s.p[r0 + q] + i));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < B; q++)
+#pragma unroll
+        for (int j = 0; j < VEC; j++)
+            acc[j] = (first && q == 0) ? (float)x[0][j] : acc[j] + (float)x[q][j];
+}
+
+// One vector group of VEC outputs at element i: the sum over the nd slices
+// in rank order, up to 16 slices in flight per lane, then one division by nd.
 template <int VEC>
 __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, uint64_t i,
                                              float count, _Float16 *out, int &bad) {
     typedef typename HVec<VEC>::T hv;
-    constexpr int B = 8; // slices in flight per lane
     float acc[VEC];
-    uint32_t r;
-    if (nd >= B) {
-        hv x[B];
-#pragma unroll
-        for (int q = 0; q < B; q++)
-            x[q] = ld_nt(reinterpret_cast<const hv *>(s.p[q] + i));
-        // all loads in flight before the first add
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < VEC; j++)
-            acc[j] = (float)x[0][j];
-#pragma unroll
-        for (int q = 1; q < B; q++)
-#pragma unroll
-            for (int j = 0; j < VEC; j++)
-                acc[j] = acc[j] + (float)x[q][j];
-        r = B;
-    } else {
-        const hv x = ld_nt(reinterpret_cast<const hv *>(s.p[0] + i));
-#pragma unroll
-        for (int j = 0; j < VEC; j++)
-            acc[j] = (float)x[j];
-        r = 1;
-    }
-    // the sums stay in rank order: slice r is added after slices 0..r-1
-    for (; r + B <= nd; r += B) {
-        hv x[B];
-#pragma unroll
-        for (int q = 0; q < B; q++)
-            x[q] = ld_nt(reinterpret_cast<const hv *>(s.p[r + q] + i));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < B; q++)
-#pragma unroll
-            for (int j = 0; j < VEC; j++)
-                acc[j] = acc[j] + (float)x[q][j];
-    }
-    for (; r < nd; r++) {
-        const hv x = ld_nt(reinterpret_cast<const hv *>(s.p[r] + i));
-#pragma unroll
-        for (int j = 0; j < VEC; j++)
-            acc[j] = acc[j] + (float)x[j];
-    }
+    uint32_t r = 0;
+    for (; r + 16 <= nd; r += 16)
+        reduce_batch<VEC, 16>(s, r, i, r == 0, acc);
+    for (; r + 4 <= nd; r += 4)
+        reduce_batch<VEC, 4>(s, r, i, r == 0, acc);
+    for (; r < nd; r++)
+        reduce_batch<VEC, 1>(s, r, i, r == 0, acc);
     hv o;
 #pragma unroll
     for (int j = 0; j < VEC; j++) {
@@ -307,47 +315,64 @@ __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, ui
     st_nt(o, reinterpret_cast<hv *>(out + i));
 }
 
+__device__ __forceinline__ void reduce_one(const SliceArgs &s, uint32_t nd, uint64_t i,
+                                           float count, _Float16 *out, int &bad) {
+    const _Float16 o = (_Float16)(reduce_single(s, nd, i) / count);
+    as_global(out)[i] = o;
+    uint16_t b;
+    memcpy(&b, &o, 2);
+    bad |= f16_bits_nonfinite(b);
+}
+
+// Each lane reduces one vector group of VEC elements (grid-striding when the
+// launch is smaller than the work); the unaligned head (fewer than VEC
+// leading elements) and the tail past the last whole group go one element
+// per lane.  VEC = 1: every element singly.
 template <int VEC>
-__global__ __launch_bounds__(kBlock) void zs_reduce_kernel(SliceArgs s, uint32_t nd, uint64_t n,
-                                                           uint32_t head, _Float16 *__restrict__ out,
-                                                           int32_t *__restrict__ flag) {
+__global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t nd, uint64_t n,
+                                                          uint32_t head, _Float16 *__restrict__ out,
+                                                          int32_t *__restrict__ flag) {
     const float count = (float)nd;
-    const uint64_t gtid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint64_t gstride = (uint64_t)gridDim.x * kBlock;
+    const uint64_t gtid = (uint64_t)blockIdx.x * kWave + threadIdx.x;
+    const uint64_t gstride = (uint64_t)gridDim.x * kWave;
     int bad = 0;
     const uint64_t h = head < n ? head : n;
     const uint64_t ngroups = VEC > 1 ? (n - h) / VEC : 0;
     const uint64_t body_end = h + ngroups * VEC;
-    // unaligned head and tail, one element per thread
-    if (gtid < h) {
-        const _Float16 o = (_Float16)(reduce_single(s, nd, gtid) / count);
-        as_global(out)[gtid] = o;
-        uint16_t b;
-        memcpy(&b, &o, 2);
-        bad |= f16_bits_nonfinite(b);
-    }
-    for (uint64_t i = body_end + gtid; i < n; i += gstride) {
-        const _Float16 o = (_Float16)(reduce_single(s, nd, i) / count);
-        as_global(out)[i] = o;
-        uint16_t b;
-        memcpy(&b, &o, 2);
-        bad |= f16_bits_nonfinite(b);
-    }
+    if (gtid < h)
+        reduce_one(s, nd, gtid, count, out, bad);
+    for (uint64_t i = body_end + gtid; i < n; i += gstride)
+        reduce_one(s, nd, i, count, out, bad);
     if (VEC > 1)
         for (uint64_t k = gtid; k < ngroups; k += gstride)
             reduce_group<VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
-    if (flag != nullptr) {
-        const uint64_t any = __ballot(bad);
-        if (any != 0 && (threadIdx.x & 63) == 0)
-            atomicOr(flag, 1);
-    }
+    raise_flag(flag, bad);
 }
 
-// Workgroups of a grid-stride launch: enough to give each of the 256 CUs
-// several resident workgroups, never more than the work needs.
-uint32_t grid_for(uint64_t items_per_thread_units, uint32_t cap) {
-    const uint64_t want = (items_per_thread_units + kBlock - 1) / kBlock;
-    return (uint32_t)(want < 1 ? 1 : (want > cap ? cap : want));
+// ---------------------------------------------------------------------------
+// Launch shapes.
+// ---------------------------------------------------------------------------
+
+// Dynamic LDS to reserve per one-wave workgroup so that at most `per_cu`
+// workgroups fit on a CU: the largest multiple of 256 bytes below
+// lds_per_cu / (per_cu + 1/2), so per_cu of them fit with room to spare and
+// one more does not.  Returns 0 (no cap) if the device does not say.
+size_t lds_cap_bytes(int device, uint32_t per_cu) {
+    int lds_cu = 0, lds_block = 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              device) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, device) !=
+            hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (lds_cu <= 0 || per_cu == 0)
+        return 0;
+    size_t b = (size_t)(2 * (uint64_t)lds_cu / (2 * (uint64_t)per_cu + 1));
+    b = b / 256 * 256;
+    if (lds_block > 0 && b > (size_t)lds_block)
+        b = (size_t)lds_block;
+    return b;
 }
 
 } // namespace
@@ -358,13 +383,15 @@ struct zero_plan {
     void *d_table;
     zero_plan_stats stats;
     int device;
+    size_t lds_cap; // dynamic LDS per Adam workgroup (the occupancy cap)
 };
 
-extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors, zero_plan **out) {
+extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
+                                uint32_t chunk_elems, zero_plan **out) {
     if (!out)
         return ZERO_EINVAL;
     zs::HostPlan hp;
-    int rc = zs::build_host_plan(tensors, n_tensors, &hp);
+    int rc = zs::build_host_plan(tensors, n_tensors, chunk_elems, &hp);
     if (rc != ZERO_OK)
         return rc;
     int dev = 0;
@@ -380,6 +407,7 @@ extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors, 
     plan->d_chunks = nullptr;
     plan->stats = hp.stats;
     plan->device = dev;
+    plan->lds_cap = lds_cap_bytes(dev, zs::kAdamPerCU);
     const size_t tb = hp.tensors.size() * sizeof(zs::TensorDesc);
     const size_t cb = hp.chunks.size() * sizeof(zs::Chunk);
     if (tb + cb > 0) {
@@ -442,12 +470,14 @@ extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp
     if (dev != plan->device)
         return ZERO_EINVAL;
     const AdamConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
-    // one workgroup per chunk, up to 16 resident per CU on 256 CUs; larger
-    // plans grid-stride
-    const uint64_t nch = plan->stats.n_chunks;
-    const uint32_t grid = (uint32_t)(nch < 256u * 16u ? nch : 256u * 16u);
-    hipLaunchKernelGGL(zs_adam_kernel, dim3(grid), dim3(kBlock), 0, (hipStream_t)stream,
-                       plan->d_tensors, plan->d_chunks, nch, c, nonfinite_flag, skip_if_nonzero);
+    // one one-wave workgroup per wave tile, dispatched in order and balanced
+    // over the CUs by the hardware; only plans beyond kMaxGrid tiles stride
+    const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / kTile);
+    const uint64_t n_virtual = plan->stats.n_chunks * tpc;
+    const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
+    hipLaunchKernelGGL(zs_adam_kernel, dim3(grid), dim3(kWave), plan->lds_cap,
+                       (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c,
+                       nonfinite_flag, skip_if_nonzero);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -479,20 +509,28 @@ extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd
         args.p[r] = nullptr;
     if (n == 0)
         return ZERO_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ZERO_EHIP;
+    }
     addr[nd] = o;
     uint32_t vec, head;
-    zs::pick_vector_path(addr, (int)nd + 1, nullptr, 0, &vec, &head);
-    const uint64_t groups = vec > 1 ? (n - (head < n ? head : n)) / vec + 1 : n;
-    const uint32_t grid = grid_for(groups, 256u * 32u);
+    zs::pick_vector_path(addr, (int)nd + 1, nullptr, 0, 8, &vec, &head);
+    // one vector group per lane, one wave per workgroup
+    const uint64_t items = vec > 1 ? (n - (head < n ? head : n)) / vec + 1 : n;
+    const uint64_t want = (items + kWave - 1) / kWave;
+    const uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
+    const size_t lds = lds_cap_bytes(dev, zs::reduce_per_cu(nd));
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
-        hipLaunchKernelGGL(zs_reduce_kernel<8>, dim3(grid), dim3(kBlock), 0, st, args, nd, n,
+        hipLaunchKernelGGL(zs_reduce_kernel<8>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
                            head, (_Float16 *)out_f16, nonfinite_flag);
     else if (vec == 4)
-        hipLaunchKernelGGL(zs_reduce_kernel<4>, dim3(grid), dim3(kBlock), 0, st, args, nd, n,
+        hipLaunchKernelGGL(zs_reduce_kernel<4>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
                            head, (_Float16 *)out_f16, nonfinite_flag);
     else
-        hipLaunchKernelGGL(zs_reduce_kernel<1>, dim3(grid), dim3(kBlock), 0, st, args, nd, n,
+        hipLaunchKernelGGL(zs_reduce_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
                            0u, (_Float16 *)out_f16, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;

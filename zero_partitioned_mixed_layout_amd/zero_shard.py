@@ -54,8 +54,8 @@ class _HParams(ctypes.Structure):
 
 class _Stats(ctypes.Structure):
     _fields_ = [(k, ctypes.c_uint64) for k in (
-        "n_tensors", "n_params", "n_chunks", "chunk_elems", "vec8_elems",
-        "vec4_elems", "scalar_elems", "table_bytes")]
+        "n_tensors", "n_params", "n_chunks", "chunk_elems", "vector_elems",
+        "scalar_elems", "table_bytes")]
 
 
 def _load() -> ctypes.CDLL:
@@ -68,9 +68,9 @@ def _load() -> ctypes.CDLL:
     sig = {
         "zero_shard_layout": [u64, u32, u32, u32, ctypes.POINTER(_Layout)],
         "zero_state_bytes": [u32, u64, u32, u32, ctypes.POINTER(ctypes.c_uint64)],
-        "zero_plan_create": [ctypes.POINTER(_Tensor), u32, ctypes.POINTER(vp)],
+        "zero_plan_create": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(vp)],
         "zero_plan_stats_of": [vp, ctypes.POINTER(_Stats)],
-        "zero_plan_describe": [ctypes.POINTER(_Tensor), u32, ctypes.POINTER(_Stats)],
+        "zero_plan_describe": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(_Stats)],
         "zero_plan_destroy": [vp],
         "zero_adam_scalars": [ctypes.POINTER(_HParams), u64, ctypes.POINTER(ctypes.c_float)],
         "zero_adam_step": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp],
@@ -233,16 +233,18 @@ class Plan:
             pass
 
 
-def zero_plan_create(tensors: Sequence[Sequence[torch.Tensor]]) -> Plan:
-    """tensors: sequence of (param_f16, grad_f16, master_f32, m_f32, v_f32)."""
+def zero_plan_create(tensors: Sequence[Sequence[torch.Tensor]], chunk_elems: int = 0) -> Plan:
+    """tensors: sequence of (param_f16, grad_f16, master_f32, m_f32, v_f32).
+    chunk_elems: 0 for the library default, else a multiple of 512."""
     arr, device = _tensor_entries(tensors)
     h = ctypes.c_void_p()
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        _check("zero_plan_create", _lib.zero_plan_create(arr, len(tensors), ctypes.byref(h)))
+        _check("zero_plan_create", _lib.zero_plan_create(arr, len(tensors), int(chunk_elems),
+                                                         ctypes.byref(h)))
     return Plan(h.value, tensors, device)
 
 
-def zero_plan_describe(tensors) -> dict:
+def zero_plan_describe(tensors, chunk_elems: int = 0) -> dict:
     """Classification of a would-be plan, computed on the host only.
     tensors: sequence of (param, grad, master, m, v, n) with integer
     addresses, or of torch tensors as for zero_plan_create."""
@@ -254,7 +256,8 @@ def zero_plan_describe(tensors) -> dict:
             a, _ = _tensor_entries([e])
             arr[k] = a[0]
     s = _Stats()
-    _check("zero_plan_describe", _lib.zero_plan_describe(arr, len(tensors), ctypes.byref(s)))
+    _check("zero_plan_describe", _lib.zero_plan_describe(arr, len(tensors), int(chunk_elems),
+                                                         ctypes.byref(s)))
     return {k: getattr(s, k) for k, _ in _Stats._fields_}
 
 
