@@ -71,7 +71,29 @@ def parse():
                     help="keep stepping the CPU oracle over its sample until this much "
                          "wall time has passed (at most 8 steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the step: copy a BYTES-byte device buffer into another "
+                         "with torch, --steps times (the plain copy kernel that scales the "
+                         "HBM byte counters), print one JSON line and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device-to-device copy of known size, for scaling rocprofv3's
+    FETCH_SIZE / WRITE_SIZE counters: each launch reads and writes nbytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n,
+                      "launches": reps, "avg_ms": dt * 1e3, "gbps_rw": 8 * n / dt / 1e9}),
+          flush=True)
 
 
 class Step:
@@ -182,6 +204,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems)
     ks = step.kernels()
