@@ -29,18 +29,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "params updated/sec and achieved HBM GB/s (% of roofline) per Adam shard step"
-KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", "zs_kernels.hip")
+# the sources that decide what the kernels do and how they are launched
+KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", f)
+               for f in ("zs_kernels.hip", "zs_internal.h", "zs_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def kernel_src_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel sources (kernels, launch constants,
+    plan builder); else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     pat = re.compile(r"^traffic:\s+(.*)$")

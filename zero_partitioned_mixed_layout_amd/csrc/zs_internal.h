@@ -55,16 +55,18 @@ constexpr uint32_t kDefaultChunk = 16384;
 constexpr uint64_t kMaxGrid = 1u << 24;
 
 // Resident one-wave workgroups per CU for the Adam step (each keeps eight
-// 8- or 16-byte loads per lane in flight).
-constexpr uint32_t kAdamPerCU = 6;
+// 8- or 16-byte loads per lane in flight).  Measured on MI355X over 5..8:
+// 7 is fastest on flat shards from 117M to 6.7G elements and on a 291-tensor
+// list of 118M; the 6.7G-element Llama-7B list alone prefers 6 (by 2%).
+constexpr uint32_t kAdamPerCU = 7;
 
 // Resident one-wave workgroups per CU for the reduction over nd slices:
-// about 48 fp16 vectors per lane in flight per CU (3 workgroups at 16
-// slices in flight), between 3 and 8 workgroups.
+// about 64 fp16 vectors per lane in flight per CU (4 workgroups at 16
+// slices in flight), between 2 and 8 workgroups.
 inline uint32_t reduce_per_cu(uint32_t nd) {
     const uint32_t in_flight = nd >= 16 ? 16 : (nd >= 4 ? nd / 4 * 4 : nd);
-    const uint32_t k = (48 + in_flight - 1) / in_flight;
-    return k < 3 ? 3 : (k > 8 ? 8 : k);
+    const uint32_t k = (64 + in_flight - 1) / in_flight;
+    return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 
 struct HostPlan {

@@ -13,8 +13,8 @@
 //
 // Occupancy is capped on purpose.  Both kernels run one 64-lane wave per
 // workgroup, and each launch reserves dynamic LDS that the kernel never
-// touches, so that only a few workgroups are resident per CU (Adam 6; reduce
-// 3 when 16 slices are in flight per lane).  Measured on MI355X, HBM3E
+// touches, so that only a few workgroups are resident per CU (Adam 7; reduce
+// 4 when 16 slices are in flight per lane).  Measured on MI355X, HBM3E
 // streams these many-array patterns fastest with just enough bytes in
 // flight to cover latency (about 45 KB per CU); with the 20-30 waves per CU
 // that registers alone would allow, the same streams run 10-15% slower.
