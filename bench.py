@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="flat_7p5b_nd64",
                     choices=["flat_7p5b_nd64", "flat_7p5b_nd8", "gpt2_xl", "llama_7b", "tiny_flat"])
+    ap.add_argument("--fused", action="store_true",
+                    help="workloads with gradient slices: one zero_reduce_adam_step launch per "
+                         "step instead of zero_reduce_grad_shard + zero_adam_step")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="elements per chunk of the Adam plan (0: library default)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
@@ -105,7 +108,7 @@ def copy_calibration(nbytes: int, reps: int) -> None:
 class Step:
     """Device state and the launches of one step for a workload."""
 
-    def __init__(self, zs, W, name, chunk_elems=0):
+    def __init__(self, zs, W, name, chunk_elems=0, fused=False):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         wl = W.WORKLOADS[name]
@@ -130,6 +133,7 @@ class Step:
         self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors], chunk_elems)
         self.n_params = self.plan.stats()["n_params"]
         self.t = 0
+        self.fused = fused and self.rows is not None
 
     def reduce(self):
         self.zs.zero_reduce_grad_shard(self.rows, self.tensors[0].g, self.rflag)
@@ -139,7 +143,15 @@ class Step:
         skip = self.rflag if self.rows is not None else None
         self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip)
 
+    def reduce_adam(self):
+        self.t += 1
+        sh = self.tensors[0]
+        self.zs.zero_reduce_adam_step(self.rows, sh.p, sh.w, sh.m, sh.v, self.hp, self.t,
+                                      nonfinite_flag=self.flag)
+
     def kernels(self):
+        if self.fused:
+            return [("zs_fused_kernel", self.reduce_adam, (2 * self.wl.nd + 26) * self.n_params)]
         ks = []
         if self.rows is not None:
             ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
@@ -214,7 +226,7 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    step = Step(zs, W, args.workload, args.chunk_elems)
+    step = Step(zs, W, args.workload, args.chunk_elems, args.fused)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -249,7 +261,7 @@ def main():
     bytes_per_step = sum(b for _, _, b in ks)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
-    cfg = {"workload": args.workload, "psi": step.wl.psi, "nd": step.wl.nd,
+    cfg = {"workload": args.workload + ("+fused" if step.fused else ""), "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
            "chunk_elems": step.plan.stats()["chunk_elems"],

@@ -211,6 +211,35 @@ int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd,
                            uint64_t n, void *out_f16, int32_t *nonfinite_flag,
                            void *stream);
 
+/*
+ * zero_reduce_adam_step -- the stage-2 step of one rank over a flat shard
+ * in one pass: the reduction of zero_reduce_grad_shard followed by the
+ * update of zero_adam_step, without storing and re-reading the fp16
+ * gradient ([16B] "The part that sounds too good: communication": each
+ * rank owns the final gradients of its partition and updates only its
+ * slice).  Per element i:
+ *   g16 = fp16((s_0[i] + ... + s_{nd-1}[i]) / nd)   as zero_reduce_grad_shard
+ *   then the Adam element of zero_adam_step with g = fp32(g16)
+ * so the results are bit-identical to the two calls in sequence (without
+ * a skip input).
+ * slices_f16: host array of nd device pointers to n fp16 each (read only).
+ * param_f16: n fp16, written.  master, m, v: n fp32 each, updated in place.
+ * grad_out_f16: NULL, or n fp16 that receive g16.
+ * nonfinite_flag: NULL or a device int32; 1 is OR-ed into it if any g16 is
+ *   infinite or NaN.  There is no skip input: a single pass cannot know
+ *   before writing that a later element is non-finite; such elements
+ *   propagate per IEEE (use the two separate calls to skip a whole step).
+ * Asynchronous on `stream`; allocates nothing.  n = 0 launches nothing.
+ * Errors: EINVAL (NULL slices or hp, nd = 0 or > ZERO_MAX_SLICES, a NULL
+ * or misaligned array (fp16: 2 bytes, fp32: 4 bytes), a written array
+ * overlapping another array, bad hyperparameters as zero_adam_scalars);
+ * EOVERFLOW; EHIP.
+ */
+int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n,
+                          void *param_f16, float *master, float *m, float *v,
+                          void *grad_out_f16, const zero_adam_hparams *hp,
+                          uint64_t t, int32_t *nonfinite_flag, void *stream);
+
 /* zero_status_str -- static description of a status code. */
 const char *zero_status_str(int status);
 

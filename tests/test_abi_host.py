@@ -212,3 +212,38 @@ def test_step_and_reduce_reject_before_any_device_call(zs):
     assert L.zero_reduce_grad_shard(q, 2, 8, 0x3000, None, None) == -1     # null slice
     # n = 0 with valid pointers returns before launching
     assert L.zero_reduce_grad_shard(p, 2, 0, 0x3000, None, None) == 0
+
+
+def test_fused_rejects_before_any_device_call(zs):
+    """zero_reduce_adam_step validates everything on the host first."""
+    import ctypes
+    L = zs.lib()
+    hp = zs.AdamHParams()._c()
+    bad_hp = zs.AdamHParams(weight_decay=0.1)._c()
+    P = ctypes.c_void_p
+    s2 = (P * 2)(0x100000, 0x200000)
+    args = dict(param=0x300000, w=0x400000, m=0x500000, v=0x600000)
+
+    def call(sl=s2, nd=2, n=64, param=args["param"], w=args["w"], m=args["m"], v=args["v"],
+             gout=None, h=hp, t=1):
+        return L.zero_reduce_adam_step(sl, nd, n, param, w, m, v, gout,
+                                       ctypes.byref(h) if h is not None else None, t, None, None)
+
+    assert call(sl=None) == -1
+    assert call(nd=0) == -1
+    assert call(nd=257) == -1
+    assert call(h=None) == -1
+    assert call(h=bad_hp) == -1
+    assert call(t=0) == -1
+    assert call(param=None) == -1
+    assert call(w=0x400002) == -1                    # fp32 not 4-byte aligned
+    assert call(param=0x300001) == -1                # fp16 not 2-byte aligned
+    assert call(param=0x100000) == -1                # param is a slice
+    assert call(m=0x400000 + 16) == -1               # m overlaps master
+    assert call(gout=0x300000 + 8) == -1             # grad_out overlaps param
+    assert call(sl=(P * 2)(0x100000, 0)) == -1       # null slice
+    assert call(n=2 ** 62) == -2                     # byte counts overflow
+    assert call(n=0) == 0                            # nothing to do, no launch
+    # two ranks' slices may be the same read-only memory: passes validation
+    # (n = 0 stops before any device call)
+    assert call(sl=(P * 2)(0x100000, 0x100000), n=0) == 0

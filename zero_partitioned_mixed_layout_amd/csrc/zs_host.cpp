@@ -117,14 +117,6 @@ void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n
     *head = 0;
 }
 
-namespace {
-
-struct Range {
-    uintptr_t lo, hi; // [lo, hi)
-    bool written;
-};
-
-// True if two ranges overlap where at least one of them is written.
 bool writes_overlap(std::vector<Range> &r) {
     std::sort(r.begin(), r.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
     // Sweep keeping the furthest end seen among written and among all ranges.
@@ -140,8 +132,6 @@ bool writes_overlap(std::vector<Range> &r) {
     }
     return false;
 }
-
-} // namespace
 
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out) {

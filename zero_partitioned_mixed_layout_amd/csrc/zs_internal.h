@@ -60,12 +60,28 @@ constexpr uint64_t kMaxGrid = 1u << 24;
 // list of 118M; the 6.7G-element Llama-7B list alone prefers 6 (by 2%).
 constexpr uint32_t kAdamPerCU = 7;
 
+// Slices whose fp16 vectors one lane keeps in flight at once when reducing
+// nd slices (the kernels load batches of 16, 8, 4, then 1).
+inline uint32_t slices_in_flight(uint32_t nd) {
+    return nd >= 16 ? 16 : (nd >= 8 ? 8 : (nd >= 4 ? 4 : 1));
+}
+
 // Resident one-wave workgroups per CU for the reduction over nd slices:
-// about 64 fp16 vectors per lane in flight per CU (4 workgroups at 16
-// slices in flight), between 2 and 8 workgroups.
+// about 64 16-byte vectors per lane in flight per CU (4 workgroups at 16
+// slices in flight, 8 at 8: the measured optima at N_d = 64 and 8), between
+// 2 and 8 workgroups.
 inline uint32_t reduce_per_cu(uint32_t nd) {
-    const uint32_t in_flight = nd >= 16 ? 16 : (nd >= 4 ? nd / 4 * 4 : nd);
-    const uint32_t k = (64 + in_flight - 1) / in_flight;
+    const uint32_t k = (64 + slices_in_flight(nd) - 1) / slices_in_flight(nd);
+    return k < 2 ? 2 : (k > 8 ? 8 : k);
+}
+
+// Resident one-wave workgroups per CU for the fused reduce + Adam step:
+// about 70 16-byte vectors per lane in flight per CU, counting the six fp32
+// state vectors issued with the first slice batch (4 workgroups at N_d >= 16,
+// 5 at N_d = 8: the measured optima), between 2 and 8 workgroups.
+inline uint32_t fused_per_cu(uint32_t nd) {
+    const uint32_t per_wave = 6 + slices_in_flight(nd);
+    const uint32_t k = (70 + per_wave - 1) / per_wave;
     return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 
@@ -79,6 +95,16 @@ struct HostPlan {
 // else a multiple of kTile in [kMinChunk, kMaxChunk].  Pure host code.
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out);
+
+// A byte range [lo, hi) of one array, and whether the call writes it.
+struct Range {
+    uintptr_t lo, hi;
+    bool written;
+};
+
+// True if two of the ranges overlap where at least one of them is written
+// (read-only ranges may overlap each other).  Sorts r.
+bool writes_overlap(std::vector<Range> &r);
 
 // Pick the widest vector width, at most max_width (8 or 4; else 1), and the
 // leading-element peel (< width) for which every address is aligned: fp16

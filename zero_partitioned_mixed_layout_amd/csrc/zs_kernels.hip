@@ -29,6 +29,7 @@
 #include <string.h>
 
 #include <new>
+#include <vector>
 
 #include "zero_shard.h"
 #include "zs_internal.h"
@@ -290,7 +291,8 @@ __device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, ui
 }
 
 // One vector group of VEC outputs at element i: the sum over the nd slices
-// in rank order, up to 16 slices in flight per lane, then one division by nd.
+// in rank order, in batches of 16, 8, 4 and 1 slices in flight per lane,
+// then one division by nd.
 template <int VEC>
 __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, uint64_t i,
                                              float count, _Float16 *out, int &bad) {
@@ -299,6 +301,8 @@ __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, ui
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
         reduce_batch<VEC, 16>(s, r, i, r == 0, acc);
+    for (; r + 8 <= nd; r += 8)
+        reduce_batch<VEC, 8>(s, r, i, r == 0, acc);
     for (; r + 4 <= nd; r += 4)
         reduce_batch<VEC, 4>(s, r, i, r == 0, acc);
     for (; r < nd; r++)
@@ -346,6 +350,222 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
     if (VEC > 1)
         for (uint64_t k = gtid; k < ngroups; k += gstride)
             reduce_group<VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
+    raise_flag(flag, bad);
+}
+
+// ---------------------------------------------------------------------------
+// Fused stage-2 step over a flat shard: the reduce and the Adam step in one
+// pass.  Element i's gradient is exactly what zs_reduce_kernel would store
+// (fp32 sum of the slices in rank order, one division by nd, rounded to
+// fp16), widened again and fed to the same Adam element, so results are
+// bit-identical to the two kernels run in sequence; the fp16 gradient is
+// stored only if the caller asks for it.
+// ---------------------------------------------------------------------------
+struct FlatState {
+    uint16_t *p;    // fp16 parameter (written)
+    float *w, *m, *v;
+    uint16_t *gout; // fp16 reduced gradient (written), or null
+};
+
+__device__ __forceinline__ void fused_single(const SliceArgs &s, uint32_t nd, uint64_t i,
+                                             float count, const FlatState &F,
+                                             const AdamConsts &c, int &bad) {
+    const _Float16 gh = (_Float16)(reduce_single(s, nd, i) / count);
+    uint16_t gb;
+    memcpy(&gb, &gh, 2);
+    bad |= f16_bits_nonfinite(gb);
+    if (F.gout != nullptr)
+        as_global(F.gout)[i] = gb;
+    float w = as_global(F.w)[i], m = as_global(F.m)[i], v = as_global(F.v)[i];
+    const _Float16 p = adam_elem((float)gh, w, m, v, c);
+    as_global(F.w)[i] = w;
+    as_global(F.m)[i] = m;
+    as_global(F.v)[i] = v;
+    uint16_t pb;
+    memcpy(&pb, &p, 2);
+    as_global(F.p)[i] = pb;
+}
+
+// Adds slices r0 .. r0+B-1 (rank order) at the Q four-element groups
+// starting at i[0..Q-1] into acc; all B*Q loads are issued before the first
+// add.  With `first`, slice r0 initialises the sums.
+template <int B, int Q>
+__device__ __forceinline__ void fused_batch(const SliceArgs &s, uint32_t r0, const uint64_t (&i)[Q],
+                                            bool first, f32x4 (&acc)[Q]) {
+    f16x4 x[B][Q];
+#pragma unroll
+    for (int q = 0; q < B; q++)
+#pragma unroll
+        for (int k = 0; k < Q; k++)
+            x[q][k] = ld_nt(reinterpret_cast<const f16x4 *>(s.p[r0 + q] + i[k]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < B; q++)
+#pragma unroll
+        for (int k = 0; k < Q; k++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[k][j] = (first && q == 0) ? (float)x[0][k][j] : acc[k][j] + (float)x[q][k][j];
+}
+
+// Q four-element groups at i[0..Q-1] (vector-aligned): the fp32 state is
+// loaded first, then the slices in batches of 16, 8, 4 and 1; then the
+// reduced gradient,
+// the update and the stores.
+template <int Q>
+__device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
+                                             const uint64_t (&i)[Q], float count,
+                                             const FlatState &F, const AdamConsts &c, int &bad) {
+    f32x4 w[Q], m[Q], v[Q];
+#pragma unroll
+    for (int k = 0; k < Q; k++) {
+        w[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.w + i[k]));
+        m[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.m + i[k]));
+        v[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.v + i[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[Q];
+    uint32_t r = 0;
+    for (; r + 16 <= nd; r += 16)
+        fused_batch<16, Q>(s, r, i, r == 0, acc);
+    for (; r + 8 <= nd; r += 8)
+        fused_batch<8, Q>(s, r, i, r == 0, acc);
+    for (; r + 4 <= nd; r += 4)
+        fused_batch<4, Q>(s, r, i, r == 0, acc);
+    for (; r < nd; r++)
+        fused_batch<1, Q>(s, r, i, r == 0, acc);
+#pragma unroll
+    for (int k = 0; k < Q; k++) {
+        f16x4 g, p;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            g[j] = (_Float16)(acc[k][j] / count);
+            const _Float16 gj = g[j];
+            uint16_t gb;
+            memcpy(&gb, &gj, 2);
+            bad |= f16_bits_nonfinite(gb);
+            float ww = w[k][j], mm = m[k][j], vv = v[k][j];
+            p[j] = adam_elem((float)gj, ww, mm, vv, c);
+            w[k][j] = ww;
+            m[k][j] = mm;
+            v[k][j] = vv;
+        }
+        if (F.gout != nullptr)
+            st_nt(g, reinterpret_cast<f16x4 *>(F.gout + i[k]));
+        st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
+        st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
+        st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
+        st_nt(p, reinterpret_cast<f16x4 *>(F.p + i[k]));
+    }
+}
+
+// Dynamic LDS of the launch: the part of the occupancy reservation that the
+// fused kernel uses (1 KiB per one-wave workgroup).
+extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
+
+// A full tile with the slices 16-byte aligned: lane L reduces the 8
+// consecutive elements 8L..8L+7 (16-byte loads, 1 KiB per wave
+// instruction, as zs_reduce_kernel), the fp16 gradients go through LDS to
+// the Adam tile's mapping (lane L: 4L..4L+3 and kTile/2+4L..), and the
+// update runs there.  The fp32 state loads are issued first.
+__device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uint64_t lo,
+                                            uint32_t lane, float count, const FlatState &F,
+                                            const AdamConsts &c, int &bad) {
+    const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
+    f32x4 w[2], m[2], v[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        w[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.w + i[k]));
+        m[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.m + i[k]));
+        v[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.v + i[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t j = lo + 8u * lane;
+    float acc[8];
+    uint32_t r = 0;
+    for (; r + 16 <= nd; r += 16)
+        reduce_batch<8, 16>(s, r, j, r == 0, acc);
+    for (; r + 8 <= nd; r += 8)
+        reduce_batch<8, 8>(s, r, j, r == 0, acc);
+    for (; r + 4 <= nd; r += 4)
+        reduce_batch<8, 4>(s, r, j, r == 0, acc);
+    for (; r < nd; r++)
+        reduce_batch<8, 1>(s, r, j, r == 0, acc);
+    f16x8 g8;
+#pragma unroll
+    for (int q = 0; q < 8; q++)
+        g8[q] = (_Float16)(acc[q] / count);
+    reinterpret_cast<f16x8 *>(zs_lds)[lane] = g8;
+    __syncthreads(); // one wave per workgroup: orders the LDS write and reads
+    f16x4 g[2];
+    g[0] = reinterpret_cast<const f16x4 *>(zs_lds)[lane];
+    g[1] = reinterpret_cast<const f16x4 *>(zs_lds)[kWave + lane];
+    __syncthreads(); // the next tile of this workgroup rewrites the buffer
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        f16x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const _Float16 gj = g[k][q];
+            uint16_t gb;
+            memcpy(&gb, &gj, 2);
+            bad |= f16_bits_nonfinite(gb);
+            float ww = w[k][q], mm = m[k][q], vv = v[k][q];
+            p[q] = adam_elem((float)gj, ww, mm, vv, c);
+            w[k][q] = ww;
+            m[k][q] = mm;
+            v[k][q] = vv;
+        }
+        if (F.gout != nullptr)
+            st_nt(g[k], reinterpret_cast<f16x4 *>(F.gout + i[k]));
+        st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
+        st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
+        st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
+        st_nt(p, reinterpret_cast<f16x4 *>(F.p + i[k]));
+    }
+}
+
+// One wave per tile of kTile elements after the peeled head (tile 0 also
+// does the head).  VEC = 8: full tiles by fused_tile8 (slices 16-byte
+// aligned).  VEC = 4: full tiles with each lane reducing its own two groups
+// of four (slices 8-byte aligned).  Both: the last partial tile four per
+// lane, then singly.  VEC = 1: the tile's elements one at a time.  Tiles
+// beyond the grid stride.
+template <int VEC>
+__global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t nd, uint64_t n,
+                                                         uint32_t head, uint64_t ntiles,
+                                                         FlatState F, AdamConsts c,
+                                                         int32_t *__restrict__ flag) {
+    const float count = (float)nd;
+    const uint32_t lane = threadIdx.x;
+    const uint64_t h = head < n ? head : n;
+    int bad = 0;
+    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        if (b == 0 && lane < h)
+            fused_single(s, nd, lane, count, F, c, bad);
+        const uint64_t lo = h + b * kTile;
+        const uint64_t hi = min(n, lo + kTile);
+        if (VEC > 1) {
+            if (hi - lo == kTile && VEC == 8) {
+                fused_tile8(s, nd, lo, lane, count, F, c, bad);
+            } else if (hi - lo == kTile) {
+                const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
+                fused_groups<2>(s, nd, i, count, F, c, bad);
+            } else {
+                const uint32_t nquads = (uint32_t)(hi - lo) / 4u;
+                for (uint32_t q = lane; q < nquads; q += kWave) {
+                    const uint64_t i[1] = {lo + 4u * q};
+                    fused_groups<1>(s, nd, i, count, F, c, bad);
+                }
+                const uint64_t t0 = lo + 4u * (uint64_t)nquads;
+                if (t0 + lane < hi)
+                    fused_single(s, nd, t0 + lane, count, F, c, bad);
+            }
+        } else {
+            for (uint64_t k = lo + lane; k < hi; k += kWave)
+                fused_single(s, nd, k, count, F, c, bad);
+        }
+    }
     raise_flag(flag, bad);
 }
 
@@ -532,6 +752,101 @@ extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd
     else
         hipLaunchKernelGGL(zs_reduce_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
                            0u, (_Float16 *)out_f16, nonfinite_flag);
+    if (hipGetLastError() != hipSuccess)
+        return ZERO_EHIP;
+    return ZERO_OK;
+}
+
+extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n,
+                                     void *param_f16, float *master, float *m, float *v,
+                                     void *grad_out_f16, const zero_adam_hparams *hp,
+                                     uint64_t t, int32_t *nonfinite_flag, void *stream) {
+    if (!slices_f16 || nd == 0 || nd > ZERO_MAX_SLICES || !hp)
+        return ZERO_EINVAL;
+    float sc[8];
+    int rc = zero_adam_scalars(hp, t, sc);
+    if (rc != ZERO_OK)
+        return rc;
+    uint64_t b2, b4;
+    if (__builtin_mul_overflow(n, (uint64_t)2, &b2) || __builtin_mul_overflow(n, (uint64_t)4, &b4))
+        return ZERO_EOVERFLOW;
+    if (n == 0)
+        return ZERO_OK;
+    const uintptr_t p = (uintptr_t)param_f16, go = (uintptr_t)grad_out_f16;
+    const uintptr_t w = (uintptr_t)master, mm = (uintptr_t)m, vv = (uintptr_t)v;
+    if (!p || !w || !mm || !vv || p % 2 || go % 2 || (w | mm | vv) % 4)
+        return ZERO_EINVAL;
+    std::vector<zs::Range> ranges;
+    ranges.reserve(nd + 5);
+    SliceArgs args;
+    uintptr_t a16[ZERO_MAX_SLICES + 2];
+    for (uint32_t r = 0; r < nd; r++) {
+        const uintptr_t a = (uintptr_t)slices_f16[r];
+        if (!a || a % 2)
+            return ZERO_EINVAL;
+        args.p[r] = (const _Float16 *)slices_f16[r];
+        a16[r] = a;
+        ranges.push_back({a, a + b2, false});
+    }
+    for (uint32_t r = nd; r < ZERO_MAX_SLICES; r++)
+        args.p[r] = nullptr;
+    int n16 = (int)nd;
+    a16[n16++] = p;
+    ranges.push_back({p, p + b2, true});
+    if (go) {
+        a16[n16++] = go;
+        ranges.push_back({go, go + b2, true});
+    }
+    for (uintptr_t a : {w, mm, vv})
+        ranges.push_back({a, a + b4, true});
+    for (const zs::Range &x : ranges)
+        if (x.hi < x.lo)
+            return ZERO_EOVERFLOW;
+    if (zs::writes_overlap(ranges))
+        return ZERO_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ZERO_EHIP;
+    }
+    // Access path: a common phase h (elements peeled singly) after which the
+    // slices are 16-byte aligned (VEC 8) or 8-byte aligned (VEC 4), the fp16
+    // outputs 8-byte and the fp32 state 16-byte aligned; else single elements.
+    uint32_t vec = 1, head = 0;
+    for (uint32_t want : {8u, 4u}) {
+        for (uint32_t h = 0; h < want && vec == 1; h++) {
+            bool ok = (w + 4u * h) % 16 == 0 && (mm + 4u * h) % 16 == 0 &&
+                      (vv + 4u * h) % 16 == 0;
+            for (uint32_t r = 0; r < nd && ok; r++)
+                ok = (a16[r] + 2u * h) % (2u * want) == 0;
+            for (int k = (int)nd; k < n16 && ok; k++)
+                ok = (a16[k] + 2u * h) % 8 == 0;
+            if (ok) {
+                vec = want;
+                head = h;
+            }
+        }
+        if (vec != 1)
+            break;
+    }
+    const uint64_t h = head < n ? head : n;
+    const uint64_t ntiles = (n - h + kTile - 1) / kTile + (n == h ? 1 : 0);
+    const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
+    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd));
+    if (lds < 2u * kTile)
+        lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
+    const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
+    const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]};
+    hipStream_t st = (hipStream_t)stream;
+    if (vec == 8)
+        hipLaunchKernelGGL(zs_fused_kernel<8>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
+                           head, ntiles, F, c, nonfinite_flag);
+    else if (vec == 4)
+        hipLaunchKernelGGL(zs_fused_kernel<4>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
+                           head, ntiles, F, c, nonfinite_flag);
+    else
+        hipLaunchKernelGGL(zs_fused_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
+                           0u, ntiles, F, c, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;

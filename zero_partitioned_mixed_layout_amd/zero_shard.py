@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "zero_adam_scalars": [ctypes.POINTER(_HParams), u64, ctypes.POINTER(ctypes.c_float)],
         "zero_adam_step": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp],
         "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
+        "zero_reduce_adam_step": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
+                                  ctypes.POINTER(_HParams), u64, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -91,7 +93,7 @@ _lib = _load()
 EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_plan_create",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
-           "zero_status_str")
+           "zero_reduce_adam_step", "zero_status_str")
 
 
 def lib() -> ctypes.CDLL:
@@ -293,3 +295,40 @@ def zero_reduce_grad_shard(slices: Sequence[torch.Tensor], out: torch.Tensor,
     f = _flag_ptr(nonfinite_flag, "nonfinite_flag", out.device)
     _check("zero_reduce_grad_shard",
            _lib.zero_reduce_grad_shard(ptrs, nd, n, out.data_ptr(), f, _stream_handle(stream)))
+
+
+def zero_reduce_adam_step(slices: Sequence[torch.Tensor], param: torch.Tensor,
+                          master: torch.Tensor, m: torch.Tensor, v: torch.Tensor, hp, t: int,
+                          grad_out: Optional[torch.Tensor] = None,
+                          nonfinite_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Reduce the fp16 slices and apply the Adam step in one pass over a flat
+    shard (bit-identical to zero_reduce_grad_shard then zero_adam_step)."""
+    _need(master, torch.float32, "master")
+    dev = master.device
+    n = master.numel()
+    for x, dt, nm in ((param, torch.float16, "param"), (m, torch.float32, "m"),
+                      (v, torch.float32, "v")):
+        _need(x, dt, nm, dev)
+        if x.numel() != n:
+            raise ValueError(f"{nm} has {x.numel()} elements, master has {n}")
+    nd = len(slices)
+    if nd == 0 or nd > ZERO_MAX_SLICES:
+        raise ValueError(f"need 1..{ZERO_MAX_SLICES} slices, got {nd}")
+    ptrs = (ctypes.c_void_p * nd)()
+    for r, s in enumerate(slices):
+        _need(s, torch.float16, f"slice {r}", dev)
+        if s.numel() != n:
+            raise ValueError(f"slice {r} has {s.numel()} elements, master has {n}")
+        ptrs[r] = s.data_ptr()
+    go = None
+    if grad_out is not None:
+        _need(grad_out, torch.float16, "grad_out", dev)
+        if grad_out.numel() != n:
+            raise ValueError(f"grad_out has {grad_out.numel()} elements, master has {n}")
+        go = grad_out.data_ptr()
+    h = _hp(hp)
+    f = _flag_ptr(nonfinite_flag, "nonfinite_flag", dev)
+    _check("zero_reduce_adam_step",
+           _lib.zero_reduce_adam_step(ptrs, nd, n, param.data_ptr(), master.data_ptr(),
+                                      m.data_ptr(), v.data_ptr(), go, ctypes.byref(h), int(t), f,
+                                      _stream_handle(stream)))
