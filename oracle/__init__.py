@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.orc_adam_step.restype = i32
         L.orc_reduce.argtypes = [u32, vp, u64, vp]
         L.orc_reduce.restype = i32
+        L.orc_comm_volume.argtypes = [u32, u64, u32, u32, vp]
+        L.orc_comm_volume.restype = i32
+        L.orc_gather.argtypes = [u32, vp, u64, vp]
+        L.orc_gather.restype = i32
         _lib = L
     return _lib
 
@@ -159,3 +163,27 @@ def reduce_grad(slices, out=None):
     if rc < 0:
         raise OracleError(f"orc_reduce rc={rc}")
     return out, rc
+
+
+def comm_volume(stage: int, psi: int, nd: int, align: int = 1) -> dict:
+    """Per-rank communication of one step: {passes, volume, ring_send}, in
+    elements (fp16: 2 bytes each)."""
+    out = np.zeros(3, dtype=np.uint64)
+    rc = lib().orc_comm_volume(stage, psi, nd, align, _ptr(out))
+    if rc != 0:
+        raise OracleError(f"orc_comm_volume rc={rc}")
+    return dict(zip(("passes", "volume", "ring_send"), (int(v) for v in out)))
+
+
+def gather(shards) -> np.ndarray:
+    """Concatenate N_d fp16 shards of equal length into the full buffer."""
+    arrs = [np.ascontiguousarray(s).view(np.uint16) for s in shards]
+    nd = len(arrs)
+    n = arrs[0].size if nd else 0
+    assert all(a.size == n for a in arrs)
+    out = np.empty(nd * n, dtype=np.uint16)
+    ptrs = (ctypes.c_void_p * max(nd, 1))(*[_ptr(a) for a in arrs])
+    rc = lib().orc_gather(nd, ctypes.cast(ptrs, ctypes.c_void_p), n, _ptr(out))
+    if rc != 0:
+        raise OracleError(f"orc_gather rc={rc}")
+    return out

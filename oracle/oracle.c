@@ -295,3 +295,55 @@ int orc_reduce(uint32_t nd, const uint16_t *const *slices, uint64_t n,
     }
     return flag;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Communication volume of one training step, per rank.                      */
+/* [16B] "The part that sounds too good: communication"; [ER10] "The         */
+/* Mathematics", communication paragraph, and "What It Enabled", stage      */
+/* table.  A ring all-reduce is a reduce-scatter followed by an all-gather,  */
+/* each moving Psi, so plain data parallelism (stage 0) moves 2 Psi per      */
+/* step.  Stages 1 and 2 reduce-scatter the gradients (Psi) and all-gather   */
+/* the updated fp16 parameters (Psi): 2 Psi.  Stage 3 also all-gathers the   */
+/* parameters on demand in the forward and in the backward pass, besides the */
+/* gradient reduce-scatter: 3 Psi, 1.5x.  Volumes count elements (the pages' */
+/* multiples of Psi); with fp16 gradients and parameters each is 2 bytes.   */
+/* out = {passes, volume = passes * Psi, ring_send = passes * (nd - 1) * S}  */
+/* where one ring pass over the padded layout has every rank send nd - 1     */
+/* shards of S elements to its neighbour.                                    */
+/* ------------------------------------------------------------------------ */
+int orc_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
+                    uint64_t out[3])
+{
+    if (stage > 3)
+        return ORC_EINVAL;
+    uint64_t lay[4];
+    int rc = orc_shard_layout(psi, nd, 0, align, lay);
+    if (rc != ORC_OK)
+        return rc;
+    uint64_t passes = stage == 3 ? 3 : 2;
+    unsigned __int128 volume = (unsigned __int128)passes * psi;
+    unsigned __int128 ring = (unsigned __int128)passes * (nd - 1) * lay[1];
+    if (volume > UINT64_MAX || ring > UINT64_MAX)
+        return ORC_EOVERFLOW;
+    out[0] = passes;
+    out[1] = (uint64_t)volume;
+    out[2] = (uint64_t)ring;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Receive side of the parameter all-gather: after it, every rank holds the */
+/* whole fp16 parameter buffer, rank r's updated shard at r * S ([16B] "The  */
+/* part that sounds too good: communication").  Here the N_d shards are     */
+/* given as N_d arrays of S elements: full[r * S + i] = shards[r][i].        */
+/* ------------------------------------------------------------------------ */
+int orc_gather(uint32_t nd, const uint16_t *const *shards, uint64_t shard_len,
+               uint16_t *full)
+{
+    if (nd == 0)
+        return ORC_EINVAL;
+    for (uint32_t r = 0; r < nd; r++)
+        for (uint64_t i = 0; i < shard_len; i++)
+            full[(uint64_t)r * shard_len + i] = shards[r][i];
+    return ORC_OK;
+}

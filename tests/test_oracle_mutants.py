@@ -48,6 +48,11 @@ MUTANTS = {
                          "if (((grad16[i] >> 10) & 0x1f) == 31 && (grad16[i] & 0x3ff) == 0)"),
     "reduce_flag_ignores_nan": ("if (!orc_f16_is_finite(out[i]))",
                                 "if (((out[i] >> 10) & 0x1f) == 31 && (out[i] & 0x3ff) == 0)"),
+    "comm_stage3_two_passes": ("uint64_t passes = stage == 3 ? 3 : 2;", "uint64_t passes = 2;"),
+    "comm_ring_nd_shards": ("ring = (unsigned __int128)passes * (nd - 1) * lay[1];",
+                            "ring = (unsigned __int128)passes * nd * lay[1];"),
+    "gather_reversed": ("full[(uint64_t)r * shard_len + i] = shards[r][i];",
+                        "full[(uint64_t)r * shard_len + i] = shards[nd - 1 - r][i];"),
 }
 
 
@@ -70,7 +75,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
     env = dict(os.environ, ZERO_ORACLE_LIB=str(so))
     files = [os.path.join(HERE, f) for f in (
         "test_oracle_fp16.py", "test_oracle_ledger_layout.py",
-        "test_oracle_adam.py", "test_oracle_reduce.py")]
+        "test_oracle_adam.py", "test_oracle_reduce.py", "test_oracle_comm.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-k", "not every_fp32_pattern", *files],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
