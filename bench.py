@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="workloads with gradient slices: one zero_reduce_adam_step launch per "
                          "step instead of zero_reduce_grad_shard + zero_adam_step")
+    ap.add_argument("--gather", action="store_true",
+                    help="workloads with gradient slices: end the step with zero_gather_shards "
+                         "of the N_d fp16 shards into the full parameter buffer (this rank's "
+                         "shard in place; the other ranks' shards stood in for by the slices)")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="elements per chunk of the Adam plan (0: library default)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
@@ -108,7 +112,7 @@ def copy_calibration(nbytes: int, reps: int) -> None:
 class Step:
     """Device state and the launches of one step for a workload."""
 
-    def __init__(self, zs, W, name, chunk_elems=0, fused=False):
+    def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         wl = W.WORKLOADS[name]
@@ -134,6 +138,13 @@ class Step:
         self.n_params = self.plan.stats()["n_params"]
         self.t = 0
         self.fused = fused and self.rows is not None
+        self.gather = gather and self.rows is not None
+        if self.gather:
+            # this rank's fp16 shard is the view of the full buffer at its
+            # offset; the other ranks' updated shards are stood in for by
+            # the gradient slices of the same length
+            r0 = self.wl.rank
+            self.shards = [self.tensors[0].p if r == r0 else self.rows[r] for r in range(self.wl.nd)]
 
     def reduce(self):
         self.zs.zero_reduce_grad_shard(self.rows, self.tensors[0].g, self.rflag)
@@ -149,13 +160,20 @@ class Step:
         self.zs.zero_reduce_adam_step(self.rows, sh.p, sh.w, sh.m, sh.v, self.hp, self.t,
                                       nonfinite_flag=self.flag)
 
+    def gather_full(self):
+        self.zs.zero_gather_shards(self.shards, self.full)
+
     def kernels(self):
         if self.fused:
-            return [("zs_fused_kernel", self.reduce_adam, (2 * self.wl.nd + 26) * self.n_params)]
-        ks = []
-        if self.rows is not None:
-            ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
-        ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
+            ks = [("zs_fused_kernel", self.reduce_adam, (2 * self.wl.nd + 26) * self.n_params)]
+        else:
+            ks = []
+            if self.rows is not None:
+                ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
+            ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
+        if self.gather:
+            ks.append(("zs_gather_kernel", self.gather_full,
+                       4 * self.layout.shard_len * (self.wl.nd - 1)))
         return ks
 
 
@@ -226,7 +244,7 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    step = Step(zs, W, args.workload, args.chunk_elems, args.fused)
+    step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -261,7 +279,8 @@ def main():
     bytes_per_step = sum(b for _, _, b in ks)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
-    cfg = {"workload": args.workload + ("+fused" if step.fused else ""), "psi": step.wl.psi, "nd": step.wl.nd,
+    cfg = {"workload": args.workload + ("+fused" if step.fused else "") +
+           ("+gather" if step.gather else ""), "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
            "chunk_elems": step.plan.stats()["chunk_elems"],

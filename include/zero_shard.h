@@ -50,6 +50,15 @@ typedef struct zero_layout {
     uint64_t real_len;     /* elements of this shard below psi (rest: pad) */
 } zero_layout;
 
+/* Per-rank communication of one training step (see zero_comm_volume). */
+typedef struct zero_comm {
+    uint64_t passes;          /* reduce-scatter / all-gather passes: 2 or 3 */
+    uint64_t volume_elems;    /* passes * psi: the pages' per-step volume */
+    uint64_t ring_send_elems; /* passes * (nd - 1) * shard_len: what one rank
+                                 sends in ring collectives over the padded
+                                 layout (fp16: 2 bytes per element) */
+} zero_comm;
+
 /* One tensor of this rank's shard: five device arrays of n elements.
  * param_f16 is written, grad_f16 read, master/m/v read and written in
  * place.  The five ranges must not overlap.  The memory is borrowed: the
@@ -115,6 +124,23 @@ int zero_shard_layout(uint64_t psi, uint32_t nd, uint32_t rank, uint32_t align,
  */
 int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
                      uint64_t *out_bytes);
+
+/*
+ * zero_comm_volume -- elements one rank moves per training step.
+ * [16B] "The part that sounds too good: communication"; [ER10] "The
+ * Mathematics", communication paragraph, and "What It Enabled", stage
+ * table.  A ring all-reduce is a reduce-scatter plus an all-gather, Psi
+ * each: plain data parallelism (stage 0) and stages 1-2 (gradient
+ * reduce-scatter, fp16 parameter all-gather) move 2 Psi; stage 3 adds the
+ * parameter all-gathers before the forward and the backward pass: 3 Psi.
+ * Volumes count elements (each fp16 element is 2 bytes).  ring_send_elems
+ * is the exact count over the padded layout: every ring pass has each rank
+ * send nd - 1 shards of shard_len elements.
+ * Pure host function.  Errors: EINVAL (out NULL, stage > 3, nd = 0,
+ * align = 0); EOVERFLOW.
+ */
+int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
+                     zero_comm *out);
 
 /*
  * zero_plan_create -- chunk table for a list of tensors of mixed sizes.
@@ -239,6 +265,27 @@ int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n
                           void *param_f16, float *master, float *m, float *v,
                           void *grad_out_f16, const zero_adam_hparams *hp,
                           uint64_t t, int32_t *nonfinite_flag, void *stream);
+
+/*
+ * zero_gather_shards -- the receive side of the all-gather of updated fp16
+ * parameters: after it every rank holds the whole fp16 buffer, rank r's
+ * shard at element r * shard_len ([16B] "The part that sounds too good:
+ * communication": the ranks all-gather the updated fp16 parameters).
+ * Here the nd shards are given in local device memory:
+ *   full[r * shard_len + i] = shards[r][i],  r < nd, i < shard_len
+ * A shard whose pointer already equals full + r * shard_len (this rank's
+ * own shard, when its parameter is a view into the full buffer) is left
+ * where it is and not read.
+ * shards_f16: host array of nd device pointers (read only; they may
+ *   overlap each other but not the part of full they are not copied to).
+ * full_f16: device pointer to nd * shard_len fp16, written.
+ * Asynchronous; allocates nothing.  shard_len = 0 launches nothing.
+ * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not
+ * 2-byte aligned, a shard that is not in place overlapping full); EOVERFLOW;
+ * EHIP.
+ */
+int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shard_len,
+                       void *full_f16, void *stream);
 
 /* zero_status_str -- static description of a status code. */
 const char *zero_status_str(int status);

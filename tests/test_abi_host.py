@@ -247,3 +247,54 @@ def test_fused_rejects_before_any_device_call(zs):
     # two ranks' slices may be the same read-only memory: passes validation
     # (n = 0 stops before any device call)
     assert call(sl=(P * 2)(0x100000, 0x100000), n=0) == 0
+
+
+def test_comm_volume_matches_oracle(zs, orc):
+    for stage in range(4):
+        for psi in (0, 1, 7, 1000, 7_500_000_000, 2 ** 40 + 3):
+            for nd in (1, 2, 8, 64, 256, 65535):
+                for align in (1, 3, 512):
+                    got = zs.zero_comm_volume(stage, psi, nd, align)
+                    want = orc.comm_volume(stage, psi, nd, align)
+                    assert (got["passes"], got["volume_elems"], got["ring_send_elems"]) == \
+                        (want["passes"], want["volume"], want["ring_send"]), (stage, psi, nd, align)
+
+
+def test_comm_volume_rejects(zs, orc):
+    import ctypes
+    for args in ((4, 10, 2, 1), (0, 10, 0, 1), (0, 10, 2, 0)):
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_comm_volume(*args)
+        assert e.value.status == -1
+        with pytest.raises(orc.OracleError):
+            orc.comm_volume(*args)
+    assert zs.lib().zero_comm_volume(0, 10, 2, 1, None) == -1
+    # 3 * psi overflows 64 bits in stage 3 only
+    psi = 2 ** 63
+    zs.zero_comm_volume(1, psi - 1, 1, 1)
+    for stage in (0, 3):
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_comm_volume(stage, psi, 1, 1)
+        assert e.value.status == -2
+
+
+def test_gather_rejects_before_any_device_call(zs):
+    import ctypes
+    L = zs.lib()
+    P = ctypes.c_void_p
+    S = 64
+    full = 0x1000000
+    sh = (P * 2)(0x100000, 0x200000)
+    assert L.zero_gather_shards(None, 2, S, full, None) == -1
+    assert L.zero_gather_shards(sh, 0, S, full, None) == -1
+    assert L.zero_gather_shards(sh, 257, S, full, None) == -1
+    assert L.zero_gather_shards(sh, 2, S, None, None) == -1
+    assert L.zero_gather_shards(sh, 2, S, full + 1, None) == -1                  # misaligned full
+    assert L.zero_gather_shards((P * 2)(0x100001, 0x200000), 2, S, full, None) == -1
+    assert L.zero_gather_shards((P * 2)(0x100000, 0), 2, S, full, None) == -1   # null shard
+    # shard 0 sits inside full but not at its own place (it is shard 1's place)
+    assert L.zero_gather_shards((P * 2)(full + 2 * S, 0x200000), 2, S, full, None) == -1
+    assert L.zero_gather_shards(sh, 2, 2 ** 63, full, None) == -2
+    # nothing to move: zero length, or every shard already in place
+    assert L.zero_gather_shards(sh, 2, 0, full, None) == 0
+    assert L.zero_gather_shards((P * 2)(full, full + 2 * S), 2, S, full, None) == 0

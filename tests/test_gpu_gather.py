@@ -1,0 +1,150 @@
+"""GPU parity of the parameter gather (zero_gather_shards) and of a whole
+ZeRO stage-2 step simulated over N_d ranks on one GPU.
+
+The gather's reference is the oracle's gather (concatenation); every
+element is compared, bit for bit.  The stage-2 simulation runs this
+library's reduce, Adam step and gather rank by rank and must reproduce, bit
+for bit, one plain data-parallel step run with the same kernels over the
+whole buffer (the equality the oracle's pins establish on the CPU).  Each
+case prints its name and sizes before it touches the GPU."""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import host16, to_dev16, to_dev32
+from zero_partitioned_mixed_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+HP = dict(W.ADAM_HP)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_partitioned_mixed_layout_amd import zero_shard
+    torch.cuda.set_device(0)
+    return zero_shard
+
+
+@pytest.mark.parametrize("nd", [1, 2, 3, 8, 64])
+def test_gather_matches_oracle(zs, nd):
+    """Shards at every source phase (so each takes its own access width),
+    ragged lengths, and one shard already in place in the full buffer."""
+    import torch
+    rng = np.random.default_rng(nd)
+    for S in (1, 7, 511, 512, 513, 4099, 70001):
+        say(f"gather nd={nd} S={S}")
+        hs = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(nd)]
+        full = torch.zeros(nd * S, dtype=torch.float16, device="cuda")
+        shards = []
+        for r in range(nd):
+            if r == nd // 2:           # this rank's own shard: a view in place
+                v = full[r * S:(r + 1) * S]
+            else:
+                off = (r * 3) % 8
+                v = torch.zeros(S + 8, dtype=torch.float16, device="cuda")[off:off + S]
+            v.copy_(to_dev16(hs[r]))
+            shards.append(v)
+        zs.zero_gather_shards(shards, full)
+        want = oracle.gather(hs)
+        torch.cuda.synchronize()
+        assert np.array_equal(host16(full), want)
+
+
+def _zero2_vs_dp(zs, torch, psi, nd, align, t, seed):
+    lay = zs.zero_shard_layout(psi, nd, 0, align)
+    P, S = lay.padded_total, lay.shard_len
+    rng = np.random.default_rng(seed)
+    grads = []
+    for _ in range(nd):
+        g = np.zeros(P, np.float64)
+        g[:psi] = rng.standard_normal(psi) * 1e-3
+        grads.append(to_dev16(g.astype(np.float16).view(np.uint16)))
+    w0 = to_dev32((rng.standard_normal(P) * 0.02).astype(np.float32))
+    m0 = to_dev32((rng.standard_normal(P) * 1e-4).astype(np.float32))
+    v0 = to_dev32((rng.random(P) * 1e-6).astype(np.float32))
+    hp = zs.AdamHParams(**HP)
+    # plain data parallelism: mean over ranks of the full gradients, one
+    # update of the whole buffer
+    g_dp = torch.empty(P, dtype=torch.float16, device="cuda")
+    p_dp = torch.zeros(P, dtype=torch.float16, device="cuda")
+    w_dp, m_dp, v_dp = w0.clone(), m0.clone(), v0.clone()
+    flag_dp = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard(grads, g_dp, flag_dp)
+    plan = zs.zero_plan_create([(p_dp, g_dp, w_dp, m_dp, v_dp)])
+    zs.zero_adam_step(plan, hp, t, flag_dp)
+    # ZeRO stage 2: rank q reduces its partition, updates its shard into a
+    # buffer of its own, and the shards are gathered
+    flag_z = torch.zeros(1, dtype=torch.int32, device="cuda")
+    shards, states, plans = [], [], []
+    for q in range(nd):
+        lq = zs.zero_shard_layout(psi, nd, q, align)
+        lo, hi = lq.offset, lq.offset + S
+        g_q = torch.empty(S, dtype=torch.float16, device="cuda")
+        zs.zero_reduce_grad_shard([g[lo:hi] for g in grads], g_q, flag_z)
+        p_q = torch.zeros(S, dtype=torch.float16, device="cuda")
+        st = (w0[lo:hi].clone(), m0[lo:hi].clone(), v0[lo:hi].clone())
+        pq = zs.zero_plan_create([(p_q, g_q, *st)])
+        zs.zero_adam_step(pq, hp, t, flag_z)
+        shards.append(p_q)
+        states.append(st)
+        plans.append(pq)
+    full = torch.zeros(P, dtype=torch.float16, device="cuda")
+    zs.zero_gather_shards(shards, full)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), p_dp.view(torch.int16))
+    for k, ref in enumerate((w_dp, m_dp, v_dp)):
+        got = torch.cat([st[k] for st in states])
+        assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    assert int(flag_z.item()) == int(flag_dp.item())
+    for pq in plans + [plan]:
+        pq.destroy()
+
+
+@pytest.mark.parametrize("psi,nd,align", [(1_000_003, 4, 1), (1_000_003, 8, 512),
+                                          (262_144, 64, 1), (77, 5, 3)])
+def test_zero2_step_equals_data_parallel_step(zs, psi, nd, align):
+    """Every rank's reduce + Adam on its shard, then the gather, reproduce
+    one data-parallel step bit for bit (fp16 params, master, m, v, flag)."""
+    import torch
+    say(f"zero2 vs dp psi={psi} nd={nd} align={align}")
+    _zero2_vs_dp(zs, torch, psi, nd, align, t=3, seed=psi + nd)
+
+
+def test_gather_full_size(zs):
+    """Psi = 7.5e9 over 64 ranks: this rank's shard in place, 63 other
+    117,187,500-element shards (the gradient slices stand in for the other
+    ranks' updated parameters) copied into the 15 GB fp16 buffer; every
+    shard checked whole on the device, a sample against the oracle."""
+    import torch
+    wl = W.WORKLOADS["flat_7p5b_nd64"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, 0, wl.align)
+    S = lay.shard_len
+    say(f"gather full size nd={wl.nd} S={S}")
+    full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total)
+    sh.p.copy_(sh.w)                      # some nonzero fp16 content in place
+    buf, rows = W.device_slices(wl, S)
+    shards = [sh.p] + rows[1:]
+    own = sh.p.clone()
+    zs.zero_gather_shards(shards, full)
+    torch.cuda.synchronize()
+    assert torch.equal(full[:S].view(torch.int16), own.view(torch.int16))
+    for r in range(1, wl.nd):
+        assert torch.equal(full[r * S:(r + 1) * S].view(torch.int16), rows[r].view(torch.int16)), r
+    idx = W.sample_indices(S, 4096, seed=5)
+    d = torch.from_numpy(idx).cuda()
+    hs = [host16(s.index_select(0, d)) for s in shards]
+    want = oracle.gather(hs)
+    got = np.concatenate([host16(full[r * S:(r + 1) * S].index_select(0, d)) for r in range(wl.nd)])
+    assert np.array_equal(got, want)
+    del full, sh, buf, rows, shards, own
+    gc.collect()
+    torch.cuda.empty_cache()

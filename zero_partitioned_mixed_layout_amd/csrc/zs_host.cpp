@@ -60,6 +60,28 @@ extern "C" int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint3
     return ZERO_OK;
 }
 
+extern "C" int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
+                                zero_comm *out) {
+    if (!out || stage > 3)
+        return ZERO_EINVAL;
+    zero_layout lay;
+    int rc = zero_shard_layout(psi, nd, 0, align, &lay);
+    if (rc != ZERO_OK)
+        return rc;
+    // [16B] "The part that sounds too good: communication": a reduce-scatter
+    // and an all-gather per step (stages 0-2), one more all-gather of the
+    // parameters in stage 3; each ring pass sends nd - 1 shards per rank.
+    const uint64_t passes = stage == 3 ? 3 : 2;
+    uint64_t volume, per_pass, ring;
+    if (!mul_ok(passes, psi, &volume) || !mul_ok((uint64_t)(nd - 1), lay.shard_len, &per_pass) ||
+        !mul_ok(passes, per_pass, &ring))
+        return ZERO_EOVERFLOW;
+    out->passes = passes;
+    out->volume_elems = volume;
+    out->ring_send_elems = ring;
+    return ZERO_OK;
+}
+
 extern "C" int zero_adam_scalars(const zero_adam_hparams *hp, uint64_t t, float out[8]) {
     if (!hp || !out || t == 0)
         return ZERO_EINVAL;

@@ -60,6 +60,13 @@ constexpr uint64_t kMaxGrid = 1u << 24;
 // list of 118M; the 6.7G-element Llama-7B list alone prefers 6 (by 2%).
 constexpr uint32_t kAdamPerCU = 7;
 
+// Elements one wave of the parameter gather moves per tile: four 16-byte
+// loads per lane in flight on the widest path.
+constexpr uint32_t kGatherTile = 2048;
+
+// Resident one-wave workgroups per CU for the parameter gather (0: no cap).
+constexpr uint32_t kGatherPerCU = 12;
+
 // Slices whose fp16 vectors one lane keeps in flight at once when reducing
 // nd slices (the kernels load batches of 16, 8, 4, then 1).
 inline uint32_t slices_in_flight(uint32_t nd) {

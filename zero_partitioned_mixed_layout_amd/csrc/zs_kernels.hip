@@ -570,6 +570,75 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
 }
 
 // ---------------------------------------------------------------------------
+// Parameter gather: nd shards of S fp16 elements into the full buffer.
+// ---------------------------------------------------------------------------
+struct GatherArgs {
+    const uint16_t *src[ZERO_MAX_SLICES];
+    uint8_t vec[ZERO_MAX_SLICES];  // 8, 4, 2 or 1 elements per access; 0: in place, skip
+    uint8_t head[ZERO_MAX_SLICES]; // leading elements copied singly
+};
+
+template <typename V>
+__device__ __forceinline__ void copy_vec(const uint16_t *src, uint16_t *dst, uint64_t i) {
+    st_nt(ld_nt(reinterpret_cast<const V *>(src + i)), reinterpret_cast<V *>(dst + i));
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Tile j of shard r: after the shard's head, kGatherTile consecutive
+// elements.  A full tile has each lane load kGatherTile / (64 VEC) groups of
+// VEC elements (lane L's groups at L, L + 64, ...: every wave instruction
+// contiguous), all before the first store; the shard's last, partial tile
+// moves its whole groups of VEC, then single elements.
+template <int VEC, typename V>
+__device__ __forceinline__ void gather_tile(const uint16_t *src, uint16_t *dst, uint64_t S,
+                                            uint32_t head, uint64_t j) {
+    const uint32_t lane = threadIdx.x;
+    const uint64_t h = head < S ? head : S;
+    if (j == 0 && lane < h)
+        as_global(dst)[lane] = as_global(src)[lane];
+    const uint64_t lo = h + j * zs::kGatherTile;
+    if (lo >= S)
+        return;
+    const uint64_t hi = min(S, lo + zs::kGatherTile);
+    if (VEC > 1 && hi - lo == zs::kGatherTile) {
+        constexpr int G = zs::kGatherTile / (kWave * VEC);
+        V x[G];
+#pragma unroll
+        for (int k = 0; k < G; k++)
+            x[k] = ld_nt(reinterpret_cast<const V *>(src + lo + (lane + kWave * k) * VEC));
+#pragma unroll
+        for (int k = 0; k < G; k++)
+            st_nt(x[k], reinterpret_cast<V *>(dst + lo + (lane + kWave * k) * VEC));
+        return;
+    }
+    const uint64_t ngroups = (hi - lo) / VEC;
+    for (uint64_t q = lane; q < ngroups; q += kWave)
+        copy_vec<V>(src, dst, lo + q * VEC);
+    for (uint64_t i = lo + ngroups * VEC + lane; i < hi; i += kWave)
+        as_global(dst)[i] = as_global(src)[i];
+}
+
+__global__ __launch_bounds__(kWave) void zs_gather_kernel(GatherArgs a, uint32_t nd, uint64_t S,
+                                                          uint64_t tiles_per_shard,
+                                                          uint16_t *__restrict__ full) {
+    const uint64_t n_virtual = (uint64_t)nd * tiles_per_shard;
+    for (uint64_t b = blockIdx.x; b < n_virtual; b += gridDim.x) {
+        const uint32_t r = (uint32_t)(b / tiles_per_shard);
+        const uint64_t j = b - (uint64_t)r * tiles_per_shard;
+        const uint16_t *src = a.src[r];
+        uint16_t *dst = full + (uint64_t)r * S;
+        switch (a.vec[r]) {
+        case 8: gather_tile<8, f16x8>(src, dst, S, a.head[r], j); break;
+        case 4: gather_tile<4, f16x4>(src, dst, S, a.head[r], j); break;
+        case 2: gather_tile<2, u16x2>(src, dst, S, a.head[r], j); break;
+        case 1: gather_tile<1, uint16_t>(src, dst, S, 0, j); break;
+        default: break; // in place
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch shapes.
 // ---------------------------------------------------------------------------
 
@@ -847,6 +916,70 @@ extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd,
     else
         hipLaunchKernelGGL(zs_fused_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
                            0u, ntiles, F, c, nonfinite_flag);
+    if (hipGetLastError() != hipSuccess)
+        return ZERO_EHIP;
+    return ZERO_OK;
+}
+
+extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shard_len,
+                                  void *full_f16, void *stream) {
+    if (!shards_f16 || !full_f16 || nd == 0 || nd > ZERO_MAX_SLICES)
+        return ZERO_EINVAL;
+    uint64_t sb, fb;
+    if (__builtin_mul_overflow(shard_len, (uint64_t)2, &sb) ||
+        __builtin_mul_overflow(sb, (uint64_t)nd, &fb))
+        return ZERO_EOVERFLOW;
+    const uintptr_t f = (uintptr_t)full_f16;
+    if (f % 2 || f + fb < f)
+        return ZERO_EINVAL;
+    GatherArgs args;
+    uint32_t moving = 0;
+    for (uint32_t r = 0; r < nd; r++) {
+        const uintptr_t s = (uintptr_t)shards_f16[r];
+        if (!s || s % 2 || s + sb < s)
+            return ZERO_EINVAL;
+        const uintptr_t d = f + (uintptr_t)r * sb;
+        args.src[r] = (const uint16_t *)shards_f16[r];
+        args.head[r] = 0;
+        if (s == d) {
+            args.vec[r] = 0; // already in place
+            continue;
+        }
+        // a shard that moves must not overlap the buffer it is copied into
+        if (shard_len > 0 && s < f + fb && f < s + sb)
+            return ZERO_EINVAL;
+        // widest access for which source and destination share a phase
+        uint32_t vec = 1, head = 0;
+        for (uint32_t w : {8u, 4u, 2u}) {
+            if ((s - d) % (2u * w) == 0) {
+                vec = w;
+                head = (uint32_t)(((2u * w - d % (2u * w)) % (2u * w)) / 2u);
+                break;
+            }
+        }
+        args.vec[r] = (uint8_t)vec;
+        args.head[r] = (uint8_t)head;
+        moving++;
+    }
+    for (uint32_t r = nd; r < ZERO_MAX_SLICES; r++) {
+        args.src[r] = nullptr;
+        args.vec[r] = 0;
+        args.head[r] = 0;
+    }
+    if (shard_len == 0 || moving == 0)
+        return ZERO_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ZERO_EHIP;
+    }
+    // tiles per shard, with room for a head of up to 7 elements
+    const uint64_t tps = (shard_len + 7 + zs::kGatherTile - 1) / zs::kGatherTile;
+    const uint64_t n_virtual = (uint64_t)nd * tps;
+    const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
+    const size_t lds = zs::kGatherPerCU ? lds_cap_bytes(dev, zs::kGatherPerCU) : 0;
+    hipLaunchKernelGGL(zs_gather_kernel, dim3(grid), dim3(kWave), lds, (hipStream_t)stream, args,
+                       nd, shard_len, tps, (uint16_t *)full_f16);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;

@@ -40,6 +40,11 @@ class _Layout(ctypes.Structure):
                 ("offset", ctypes.c_uint64), ("real_len", ctypes.c_uint64)]
 
 
+class _Comm(ctypes.Structure):
+    _fields_ = [("passes", ctypes.c_uint64), ("volume_elems", ctypes.c_uint64),
+                ("ring_send_elems", ctypes.c_uint64)]
+
+
 class _Tensor(ctypes.Structure):
     _fields_ = [("param_f16", ctypes.c_void_p), ("grad_f16", ctypes.c_void_p),
                 ("master", ctypes.c_void_p), ("m", ctypes.c_void_p),
@@ -68,6 +73,8 @@ def _load() -> ctypes.CDLL:
     sig = {
         "zero_shard_layout": [u64, u32, u32, u32, ctypes.POINTER(_Layout)],
         "zero_state_bytes": [u32, u64, u32, u32, ctypes.POINTER(ctypes.c_uint64)],
+        "zero_comm_volume": [u32, u64, u32, u32, ctypes.POINTER(_Comm)],
+        "zero_gather_shards": [ctypes.POINTER(vp), u32, u64, vp, vp],
         "zero_plan_create": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(vp)],
         "zero_plan_stats_of": [vp, ctypes.POINTER(_Stats)],
         "zero_plan_describe": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(_Stats)],
@@ -90,7 +97,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 
 # Every symbol include/zero_shard.h declares.
-EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_plan_create",
+EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
+           "zero_gather_shards", "zero_plan_create",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
            "zero_reduce_adam_step", "zero_status_str")
@@ -126,6 +134,13 @@ def zero_state_bytes(stage: int, psi: int, nd: int, align: int = 1) -> int:
     out = ctypes.c_uint64()
     _check("zero_state_bytes", _lib.zero_state_bytes(stage, psi, nd, align, ctypes.byref(out)))
     return out.value
+
+
+def zero_comm_volume(stage: int, psi: int, nd: int, align: int = 1) -> dict:
+    """Elements one rank moves per step: {passes, volume_elems, ring_send_elems}."""
+    out = _Comm()
+    _check("zero_comm_volume", _lib.zero_comm_volume(stage, psi, nd, align, ctypes.byref(out)))
+    return {k: getattr(out, k) for k, _ in _Comm._fields_}
 
 
 @dataclass(frozen=True)
@@ -332,3 +347,23 @@ def zero_reduce_adam_step(slices: Sequence[torch.Tensor], param: torch.Tensor,
            _lib.zero_reduce_adam_step(ptrs, nd, n, param.data_ptr(), master.data_ptr(),
                                       m.data_ptr(), v.data_ptr(), go, ctypes.byref(h), int(t), f,
                                       _stream_handle(stream)))
+
+
+def zero_gather_shards(shards: Sequence[torch.Tensor], full: torch.Tensor, stream=None) -> None:
+    """full[r * S:(r + 1) * S] = shards[r] for every rank r (fp16); shards
+    that are already views at their place in full are left alone."""
+    _need(full, torch.float16, "full")
+    nd = len(shards)
+    if nd == 0 or nd > ZERO_MAX_SLICES:
+        raise ValueError(f"need 1..{ZERO_MAX_SLICES} shards, got {nd}")
+    S = shards[0].numel()
+    if full.numel() != nd * S:
+        raise ValueError(f"full has {full.numel()} elements, {nd} shards of {S} need {nd * S}")
+    ptrs = (ctypes.c_void_p * nd)()
+    for r, s in enumerate(shards):
+        _need(s, torch.float16, f"shard {r}", full.device)
+        if s.numel() != S:
+            raise ValueError(f"shard {r} has {s.numel()} elements, shard 0 has {S}")
+        ptrs[r] = s.data_ptr()
+    _check("zero_gather_shards",
+           _lib.zero_gather_shards(ptrs, nd, S, full.data_ptr(), _stream_handle(stream)))
