@@ -76,6 +76,12 @@ def parse():
                     help="workloads with gradient slices: end the step with zero_gather_shards "
                          "of the N_d fp16 shards into the full parameter buffer (this rank's "
                          "shard in place; the other ranks' shards stood in for by the slices)")
+    ap.add_argument("--offload", action="store_true",
+                    help="ZeRO-Offload: fp32 master, m, v in host memory and the Adam update "
+                         "on the host CPU (zero_offload_step); the fp16 gradient and "
+                         "parameters stay on the GPU")
+    ap.add_argument("--offload-threads", type=int, default=0,
+                    help="host threads of the offload update (0: min(16, hardware threads))")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="elements per chunk of the Adam plan (0: library default)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
@@ -112,7 +118,8 @@ def copy_calibration(nbytes: int, reps: int) -> None:
 class Step:
     """Device state and the launches of one step for a workload."""
 
-    def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False):
+    def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
+                 offload_threads=0):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         wl = W.WORKLOADS[name]
@@ -138,6 +145,16 @@ class Step:
         self.n_params = self.plan.stats()["n_params"]
         self.t = 0
         self.fused = fused and self.rows is not None
+        self.offload = None
+        if offload:
+            if len(self.tensors) != 1:
+                raise SystemExit("--offload runs on the flat workloads")
+            sh = self.tensors[0]
+            self.host = [x.cpu().numpy().copy() for x in (sh.w, sh.m, sh.v)]
+            self.hflag = __import__("numpy").zeros(1, dtype="int32")
+            self.offload = zs.zero_offload_create(0, offload_threads)
+            self.offload_threads_used = offload_threads or min(16, os.cpu_count() or 1)
+            self.fused = False
         self.gather = gather and self.rows is not None
         if self.gather:
             # this rank's fp16 shard is the view of the full buffer at its
@@ -153,6 +170,11 @@ class Step:
         self.t += 1
         skip = self.rflag if self.rows is not None else None
         self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip)
+
+    def offload_step(self):
+        self.t += 1
+        sh = self.tensors[0]
+        self.offload.step(sh.g, sh.p, *self.host, self.hp, self.t, nonfinite_flag=self.hflag)
 
     def reduce_adam(self):
         self.t += 1
@@ -170,7 +192,10 @@ class Step:
             ks = []
             if self.rows is not None:
                 ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
-            ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
+            if self.offload is not None:
+                ks.append(("zero_offload_step", self.offload_step, 4 * self.n_params))
+            else:
+                ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
         if self.gather:
             ks.append(("zs_gather_kernel", self.gather_full,
                        4 * self.layout.shard_len * (self.wl.nd - 1)))
@@ -226,6 +251,43 @@ def cpu_baseline(step, sample_n: int, min_seconds: float):
                       f"{dt:.2f} s wall"}
 
 
+PCIE_PEAK_GBPS = 128.0  # PCIe Gen5 x16 host link, both directions together
+
+
+def pcie_copy_rates(nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """Pinned host <-> device copy rates (GB/s): each direction alone and
+    both at once on two streams."""
+    import torch
+    n = nbytes // 2
+    dev = torch.empty(n, dtype=torch.float16, device="cuda")
+    dev2 = torch.empty(n, dtype=torch.float16, device="cuda")
+    hin = torch.empty(n, dtype=torch.float16, pin_memory=True)
+    hout = torch.empty(n, dtype=torch.float16, pin_memory=True)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    t_d2h = timed(lambda: hout.copy_(dev, non_blocking=True))
+    t_h2d = timed(lambda: dev.copy_(hin, non_blocking=True))
+
+    def both():
+        with torch.cuda.stream(s1):
+            hout.copy_(dev, non_blocking=True)
+        with torch.cuda.stream(s2):
+            dev2.copy_(hin, non_blocking=True)
+
+    t_both = timed(both)
+    return {"d2h_gbps": nbytes / t_d2h / 1e9, "h2d_gbps": nbytes / t_h2d / 1e9,
+            "both_gbps": 2 * nbytes / t_both / 1e9, "bytes": nbytes}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -244,7 +306,8 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather)
+    step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
+                args.offload_threads)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -280,25 +343,40 @@ def main():
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
     cfg = {"workload": args.workload + ("+fused" if step.fused else "") +
-           ("+gather" if step.gather else ""), "psi": step.wl.psi, "nd": step.wl.nd,
+           ("+gather" if step.gather else "") + ("+offload" if step.offload else ""),
+           "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
            "chunk_elems": step.plan.stats()["chunk_elems"],
            "kernels_per_step": [k for k, _, _ in ks],
            "alg_bytes_per_step": bytes_per_step,
            "step_hbm_gbps": bytes_per_step * args.steps / wall / 1e9}
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": d["gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
+    offload = None
+    if step.offload is not None:
+        rates = pcie_copy_rates()
+        o = kstats["zero_offload_step"]
+        offload = {"avg_ms": o["avg_us"] / 1e3, "params_per_s": step.n_params / (o["avg_us"] / 1e6),
+                   "pcie_bytes_per_param": 4, "pcie_gbps": o["gbps"],
+                   "host_state_gbps": 24 * step.n_params / (o["avg_us"] / 1e6) / 1e9,
+                   "threads": step.offload_threads_used, "pinned_copy": rates}
+        if dom == "zero_offload_step":
+            roofline = {"bound": "pcie", "kernel": dom, "achieved": o["gbps"],
+                        "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                        "frac": o["gbps"] / PCIE_PEAK_GBPS, "traffic": None}
     out = {
         "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": cfg,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": d["gbps"],
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["frac"],
-                     "traffic": traffic},
+        "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in s.items() if kk != "total_s"} for k, s in kstats.items()},
         "cpu_baseline": cpu,
     }
+    if offload is not None:
+        out["offload"] = offload
     print(json.dumps(out), flush=True)
     step.plan.destroy()
 

@@ -36,7 +36,8 @@ extern "C" {
 #define ZERO_EINVAL (-1)    /* bad argument (null, range, alignment, aliasing) */
 #define ZERO_EOVERFLOW (-2) /* a byte or element count exceeds 64 bits */
 #define ZERO_EHIP (-3)      /* HIP runtime or launch error (captured, cleared) */
-#define ZERO_ENOMEM (-4)    /* device allocation failed (plan creation only) */
+#define ZERO_ENOMEM (-4)    /* allocation failed (plan or offload creation only) */
+#define ZERO_ENOTSUP (-5)   /* host CPU lacks AVX2 and F16C (host Adam, offload) */
 
 /* Largest N_d zero_reduce_grad_shard accepts (slice pointers travel as
  * kernel arguments). */
@@ -286,6 +287,69 @@ int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n
  */
 int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shard_len,
                        void *full_f16, void *stream);
+
+/*
+ * zero_adam_step_host -- the Adam step of zero_adam_step computed by the
+ * host CPU over host arrays: the update that ZeRO-Offload moves to the CPU
+ * together with the fp32 state ([ER10] "The Breakthrough": the optimizer's
+ * fp32 states and the update run in host RAM on the CPU; [DSZ] "Offload
+ * trades capacity against movement").  Same per-element operations in the
+ * same order as zero_adam_step, so the results are bit-identical.
+ * grad_f16: n fp16 (read); param_f16: n fp16 (written); master, m, v: n fp32
+ * each, updated in place; all host memory, borrowed.  threads: 0 for
+ * min(16, hardware threads), else the number of threads to use (the calling
+ * thread is one of them).  nonfinite_flag: NULL or a host int32 that 1 is
+ * OR-ed into if any gradient is infinite or NaN.  Synchronous.
+ * Errors: EINVAL (NULL or misaligned arrays, written arrays overlapping,
+ * bad hyperparameters as zero_adam_scalars); EOVERFLOW; ENOTSUP (no AVX2 or
+ * F16C); ENOMEM (threads could not start).
+ */
+int zero_adam_step_host(const void *grad_f16, void *param_f16, float *master, float *m,
+                        float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
+                        uint32_t threads, int32_t *nonfinite_flag);
+
+/* Opaque ZeRO-Offload pipeline: pinned staging, two copy streams and the
+ * host threads of the CPU update. */
+typedef struct zero_offload zero_offload;
+
+/*
+ * zero_offload_create -- set up the offload pipeline on the current device.
+ * chunk_elems: elements per pipeline chunk (0: 4 Mi; else a multiple of 8,
+ * at most 2^32); three chunks of fp16 gradients and three of fp16
+ * parameters are staged in pinned host memory (hipHostMalloc, 12 bytes per
+ * chunk element).  threads: as zero_adam_step_host.  *out belongs to the
+ * caller until zero_offload_destroy.
+ * Errors: EINVAL; ENOTSUP; ENOMEM; EHIP.
+ */
+int zero_offload_create(uint64_t chunk_elems, uint32_t threads, zero_offload **out);
+
+/* zero_offload_destroy -- wait for its copies and free everything.  NULL is
+ * accepted.  Errors: EHIP. */
+int zero_offload_destroy(zero_offload *off);
+
+/*
+ * zero_offload_step -- one ZeRO-Offload step over an n-element shard: the
+ * GPU keeps the fp16 parameters and gradients, the host keeps the fp32
+ * master, m and v and runs the update ([ER10] "The Breakthrough", "The
+ * Mathematics", the ZeRO-Offload paragraph).  The fp16 gradients go to the
+ * host, zero_adam_step_host's update runs there, the fresh fp16 parameters
+ * come back: 4 bytes per parameter over PCIe, pipelined in chunks so the
+ * copies in both directions overlap the CPU work.
+ * grad_f16, param_f16: device arrays of n fp16 (grad read, param written);
+ *   the gradients are read once the work already enqueued on `stream` is
+ *   done.
+ * master, m, v: host arrays of n fp32, updated in place.
+ * nonfinite_flag: NULL or a host int32 (as zero_adam_step_host).
+ * Host-synchronous: returns after the last parameters have reached the
+ * device (any later work on any stream sees them).  An offload object runs
+ * one step at a time.  Results are bit-identical to zero_adam_step.
+ * Errors: EINVAL (NULL, misaligned or overlapping arrays, offload made on
+ * another device, bad hyperparameters); EOVERFLOW; EHIP.
+ */
+int zero_offload_step(zero_offload *off, const void *grad_f16, void *param_f16,
+                      float *master, float *m, float *v, uint64_t n,
+                      const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
+                      void *stream);
 
 /* zero_status_str -- static description of a status code. */
 const char *zero_status_str(int status);

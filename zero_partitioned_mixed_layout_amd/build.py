@@ -17,7 +17,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzeroshard.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("zs_host.cpp", "zs_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f)
+           for f in ("zs_host.cpp", "zs_kernels.hip", "zs_offload.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "zero_shard.h"),
            os.path.join(HERE, "csrc", "zs_internal.h")]
 

@@ -109,7 +109,8 @@ extern "C" const char *zero_status_str(int status) {
     case ZERO_EINVAL: return "invalid argument";
     case ZERO_EOVERFLOW: return "size overflows 64 bits";
     case ZERO_EHIP: return "HIP runtime or launch error";
-    case ZERO_ENOMEM: return "device allocation failed";
+    case ZERO_ENOMEM: return "allocation failed";
+    case ZERO_ENOTSUP: return "host CPU lacks AVX2 and F16C";
     default: return "unknown status";
     }
 }

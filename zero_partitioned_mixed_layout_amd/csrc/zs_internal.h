@@ -64,6 +64,10 @@ constexpr uint32_t kAdamPerCU = 7;
 // loads per lane in flight on the widest path.
 constexpr uint32_t kGatherTile = 2048;
 
+// Elements per chunk of the offload pipeline (8 MiB of fp16 per staging
+// buffer).
+constexpr uint64_t kOffloadChunk = 4ull << 20;
+
 // Resident one-wave workgroups per CU for the parameter gather (0: no cap).
 constexpr uint32_t kGatherPerCU = 12;
 

@@ -26,6 +26,7 @@ ZERO_EINVAL = -1
 ZERO_EOVERFLOW = -2
 ZERO_EHIP = -3
 ZERO_ENOMEM = -4
+ZERO_ENOTSUP = -5
 ZERO_MAX_SLICES = 256
 
 
@@ -84,6 +85,10 @@ def _load() -> ctypes.CDLL:
         "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
         "zero_reduce_adam_step": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(_HParams), u64, vp, vp],
+        "zero_adam_step_host": [vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, u32, vp],
+        "zero_offload_create": [u64, u32, ctypes.POINTER(vp)],
+        "zero_offload_destroy": [vp],
+        "zero_offload_step": [vp, vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -101,7 +106,8 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_gather_shards", "zero_plan_create",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
-           "zero_reduce_adam_step", "zero_status_str")
+           "zero_reduce_adam_step", "zero_adam_step_host", "zero_offload_create",
+           "zero_offload_destroy", "zero_offload_step", "zero_status_str")
 
 
 def lib() -> ctypes.CDLL:
@@ -367,3 +373,83 @@ def zero_gather_shards(shards: Sequence[torch.Tensor], full: torch.Tensor, strea
         ptrs[r] = s.data_ptr()
     _check("zero_gather_shards",
            _lib.zero_gather_shards(ptrs, nd, S, full.data_ptr(), _stream_handle(stream)))
+
+
+def _host(a, dtype, what: str, n: Optional[int] = None) -> int:
+    """Address of a contiguous host numpy array of the given element type."""
+    import numpy as np
+    if not isinstance(a, np.ndarray):
+        raise TypeError(f"{what}: expected a numpy array")
+    if a.dtype.itemsize != np.dtype(dtype).itemsize or a.dtype.kind != np.dtype(dtype).kind:
+        if not (np.dtype(dtype) == np.uint16 and a.dtype == np.float16):
+            raise TypeError(f"{what}: expected {np.dtype(dtype)}, got {a.dtype}")
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError(f"{what}: must be contiguous")
+    if n is not None and a.size != n:
+        raise ValueError(f"{what}: has {a.size} elements, expected {n}")
+    return a.ctypes.data
+
+
+def zero_adam_step_host(grad16, param16, master, m, v, hp, t: int, threads: int = 0,
+                        nonfinite_flag=None) -> None:
+    """The Adam step on the host CPU over numpy arrays (fp16 as uint16 or
+    float16; fp32 state updated in place); bit-identical to zero_adam_step."""
+    import numpy as np
+    n = master.size
+    ptrs = [_host(grad16, np.uint16, "grad", n), _host(param16, np.uint16, "param", n),
+            _host(master, np.float32, "master", n), _host(m, np.float32, "m", n),
+            _host(v, np.float32, "v", n)]
+    f = None if nonfinite_flag is None else _host(nonfinite_flag, np.int32, "nonfinite_flag", 1)
+    h = _hp(hp)
+    _check("zero_adam_step_host",
+           _lib.zero_adam_step_host(*ptrs, n, ctypes.byref(h), int(t), int(threads), f))
+
+
+class Offload:
+    """A zero_offload pipeline (pinned staging, copy streams, host threads)."""
+
+    def __init__(self, handle: int, device):
+        self._h = handle
+        self.device = device
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("offload was destroyed")
+        return self._h
+
+    def step(self, grad: torch.Tensor, param: torch.Tensor, master, m, v, hp, t: int,
+             nonfinite_flag=None, stream=None) -> None:
+        """grad, param: device fp16 tensors; master, m, v: host numpy fp32
+        arrays updated in place; nonfinite_flag: None or a numpy int32[1]."""
+        import numpy as np
+        n = master.size
+        _need(grad, torch.float16, "grad", self.device)
+        _need(param, torch.float16, "param", self.device)
+        if grad.numel() != n or param.numel() != n:
+            raise ValueError("grad, param and the host state differ in size")
+        hs = [_host(master, np.float32, "master", n), _host(m, np.float32, "m", n),
+              _host(v, np.float32, "v", n)]
+        f = None if nonfinite_flag is None else _host(nonfinite_flag, np.int32, "nonfinite_flag", 1)
+        h = _hp(hp)
+        _check("zero_offload_step",
+               _lib.zero_offload_step(self.handle, grad.data_ptr(), param.data_ptr(), *hs, n,
+                                      ctypes.byref(h), int(t), f, _stream_handle(stream)))
+
+    def destroy(self) -> None:
+        if self._h:
+            h, self._h = self._h, None
+            _check("zero_offload_destroy", _lib.zero_offload_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def zero_offload_create(chunk_elems: int = 0, threads: int = 0) -> Offload:
+    h = ctypes.c_void_p()
+    _check("zero_offload_create", _lib.zero_offload_create(int(chunk_elems), int(threads),
+                                                           ctypes.byref(h)))
+    return Offload(h.value, torch.device("cuda", torch.cuda.current_device()))
