@@ -69,6 +69,18 @@ def lib() -> ctypes.CDLL:
         L.orc_adam_step.restype = i32
         L.orc_reduce.argtypes = [u32, vp, u64, vp]
         L.orc_reduce.restype = i32
+        L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_bf16.restype = ctypes.c_uint16
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_bf16_array.argtypes = [vp, vp, u64]
+        L.orc_f32_to_bf16_array.restype = None
+        L.orc_bf16_to_f32_array.argtypes = [vp, vp, u64]
+        L.orc_bf16_to_f32_array.restype = None
+        L.orc_adam_step_fmt.argtypes = [i32, u64, vp, vp, vp, vp, vp, vp, u64, i32]
+        L.orc_adam_step_fmt.restype = i32
+        L.orc_reduce_fmt.argtypes = [i32, u32, vp, u64, vp]
+        L.orc_reduce_fmt.restype = i32
         L.orc_comm_volume.argtypes = [u32, u64, u32, u32, vp]
         L.orc_comm_volume.restype = i32
         L.orc_gather.argtypes = [u32, vp, u64, vp]
@@ -99,6 +111,22 @@ def f16_to_f32(h: np.ndarray) -> np.ndarray:
     h = np.ascontiguousarray(h).view(np.uint16)
     out = np.empty(h.shape, dtype=np.float32)
     lib().orc_f16_to_f32_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 bit patterns (uint16), nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to fp32, exactly."""
+    h = np.ascontiguousarray(h).view(np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().orc_bf16_to_f32_array(_ptr(h), _ptr(out), h.size)
     return out
 
 
@@ -133,9 +161,14 @@ def adam_scalars(lr, beta1, beta2, eps, t, weight_decay=0.0) -> np.ndarray:
     return out
 
 
+_FMT = {"f16": 0, "bf16": 1}
+
+
 def adam_step(grad16, param16, master, m, v, *, lr, beta1, beta2, eps, t,
-              weight_decay=0.0, skip=False) -> int:
-    """One Adam step in place over this shard; returns the non-finite flag."""
+              weight_decay=0.0, skip=False, fmt="f16") -> int:
+    """One Adam step in place over this shard; returns the non-finite flag.
+    fmt: "f16" (the pages' ledger) or "bf16": the format of the 16-bit
+    gradient and parameter bit patterns (uint16 arrays)."""
     n = master.size
     g = np.ascontiguousarray(grad16).view(np.uint16)
     for a, dt in ((param16, np.uint16), (master, np.float32), (m, np.float32),
@@ -143,15 +176,20 @@ def adam_step(grad16, param16, master, m, v, *, lr, beta1, beta2, eps, t,
         assert a.dtype.itemsize == np.dtype(dt).itemsize and a.size == n
     assert g.size == n
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
-    rc = lib().orc_adam_step(n, _ptr(g), _ptr(param16), _ptr(master), _ptr(m),
-                             _ptr(v), _ptr(hp), t, int(bool(skip)))
+    if fmt == "f16":
+        rc = lib().orc_adam_step(n, _ptr(g), _ptr(param16), _ptr(master), _ptr(m),
+                                 _ptr(v), _ptr(hp), t, int(bool(skip)))
+    else:
+        rc = lib().orc_adam_step_fmt(_FMT[fmt], n, _ptr(g), _ptr(param16), _ptr(master),
+                                     _ptr(m), _ptr(v), _ptr(hp), t, int(bool(skip)))
     if rc < 0:
         raise OracleError(f"orc_adam_step rc={rc}")
     return rc
 
 
-def reduce_grad(slices, out=None):
-    """Average N_d fp16 slices into fp16; returns (out, flag)."""
+def reduce_grad(slices, out=None, fmt="f16"):
+    """Average N_d 16-bit slices (fmt "f16" or "bf16") into the same format;
+    returns (out, flag)."""
     arrs = [np.ascontiguousarray(s).view(np.uint16) for s in slices]
     nd = len(arrs)
     n = arrs[0].size if nd else 0
@@ -159,7 +197,10 @@ def reduce_grad(slices, out=None):
     if out is None:
         out = np.empty(n, dtype=np.uint16)
     ptrs = (ctypes.c_void_p * max(nd, 1))(*[_ptr(a) for a in arrs])
-    rc = lib().orc_reduce(nd, ctypes.cast(ptrs, ctypes.c_void_p), n, _ptr(out))
+    if fmt == "f16":
+        rc = lib().orc_reduce(nd, ctypes.cast(ptrs, ctypes.c_void_p), n, _ptr(out))
+    else:
+        rc = lib().orc_reduce_fmt(_FMT[fmt], nd, ctypes.cast(ptrs, ctypes.c_void_p), n, _ptr(out))
     if rc < 0:
         raise OracleError(f"orc_reduce rc={rc}")
     return out, rc

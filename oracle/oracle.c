@@ -118,6 +118,101 @@ static int orc_f16_is_finite(uint16_t h)
 }
 
 /* ------------------------------------------------------------------------ */
+/* bfloat16 <-> binary32.                                                    */
+/* [DSZ] "Why parameter count is not training memory": BF16 setups differ   */
+/* in which states they keep; this variant keeps the 16-byte ledger with    */
+/* bfloat16 parameters and gradients in place of fp16.  bfloat16: 1 sign    */
+/* bit, binary32's 8 exponent bits (bias 127) and 7 fraction bits.  A       */
+/* normal value is (1 + F/128) * 2^(E-127) for E in 1..254; a subnormal     */
+/* (E = 0) is F * 2^-133; E = 255 is infinity (F = 0) or NaN.               */
+/* ------------------------------------------------------------------------ */
+float orc_bf16_to_f32(uint16_t h)
+{
+    int negative = (h >> 15) & 1;
+    int E = (h >> 7) & 0xff;
+    int F = h & 0x7f;
+    double mag;
+    if (E == 0) {
+        mag = ldexp((double)F, -133);
+    } else if (E == 255) {
+        if (F != 0)
+            return negative ? -NAN : NAN;
+        mag = INFINITY;
+    } else {
+        mag = ldexp(128.0 + (double)F, E - 134);
+    }
+    return (float)(negative ? -mag : mag); /* exact: every bfloat16 fits */
+}
+
+/*
+ * Round a binary32 value to the nearest bfloat16 value, ties to the one with
+ * an even last fraction bit.  The quantum at a magnitude a in [2^(e-1), 2^e)
+ * is 2^(e-8) for normal numbers and 2^-133 in the subnormal range; the
+ * rounded magnitude is rint(a / quantum) * quantum (rint: half to even).
+ * Magnitudes from (2 - 2^-8) * 2^127 up (halfway between the largest finite
+ * value (2 - 2^-7) * 2^127 and 2^128, a tie that goes to the even 2^128)
+ * overflow to infinity.
+ */
+uint16_t orc_f32_to_bf16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return sign | 0x7fc0; /* a quiet NaN; the payload is not kept */
+    double a = fabs((double)x);
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))
+        return sign | 0x7f80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int q = e - 8;
+    if (q < -133)
+        q = -133;
+    double quanta = nearbyint(ldexp(a, -q)); /* ties to even */
+    double r = ldexp(quanta, q);
+    if (r == 0.0)
+        return sign;
+    if (r < ldexp(1.0, -126)) /* subnormal: F quanta of 2^-133 */
+        return sign | (uint16_t)ldexp(r, 133);
+    int er;
+    double fr = frexp(r, &er);
+    int E = er - 1 + 127;
+    int F = (int)((2.0 * fr - 1.0) * 128.0);
+    return sign | (uint16_t)(E << 7) | (uint16_t)F;
+}
+
+void orc_f32_to_bf16_array(const float *x, uint16_t *out, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; i++)
+        out[i] = orc_f32_to_bf16(x[i]);
+}
+
+void orc_bf16_to_f32_array(const uint16_t *h, float *out, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; i++)
+        out[i] = orc_bf16_to_f32(h[i]);
+}
+
+/* The two 16-bit formats of the parameters and gradients. */
+#define ORC_FMT_F16 0
+#define ORC_FMT_BF16 1
+
+static float orc_widen(int fmt, uint16_t h)
+{
+    return fmt == ORC_FMT_BF16 ? orc_bf16_to_f32(h) : orc_f16_to_f32(h);
+}
+
+static uint16_t orc_narrow(int fmt, float x)
+{
+    return fmt == ORC_FMT_BF16 ? orc_f32_to_bf16(x) : orc_f32_to_f16(x);
+}
+
+static int orc_is_finite(int fmt, uint16_t h)
+{
+    return fmt == ORC_FMT_BF16 ? ((h >> 7) & 0xff) != 255 : orc_f16_is_finite(h);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Shard layout of the flat buffer.                                          */
 /* Each of the N_d ranks owns one contiguous slice of the flattened state    */
 /* ([16B] "The replication nobody questioned", "The part that sounds too     */
@@ -223,10 +318,12 @@ int orc_adam_scalars(const double hp[5], uint64_t t, float out[8])
  * element.  Returns 1 if any gradient is infinite or NaN, else 0; if skip is
  * nonzero nothing is read or written and 0 is returned.
  */
-int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
-                  float *w, float *m, float *v, const double hp[5], uint64_t t,
-                  int skip)
+int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
+                      float *w, float *m, float *v, const double hp[5], uint64_t t,
+                      int skip)
 {
+    if (fmt != ORC_FMT_F16 && fmt != ORC_FMT_BF16)
+        return ORC_EINVAL;
     float s[8];
     int rc = orc_adam_scalars(hp, t, s);
     if (rc != ORC_OK)
@@ -237,9 +334,9 @@ int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
     const float bc1 = s[5], bc2 = s[6], eps = s[7];
     int flag = 0;
     for (uint64_t i = 0; i < n; i++) {
-        if (!orc_f16_is_finite(grad16[i]))
+        if (!orc_is_finite(fmt, grad16[i]))
             flag = 1;
-        float g = orc_f16_to_f32(grad16[i]);
+        float g = orc_widen(fmt, grad16[i]);
 
         float m_old = b1 * m[i];
         float m_in = omb1 * g;
@@ -261,9 +358,17 @@ int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
         m[i] = m_new;
         v[i] = v_new;
         w[i] = w_new;
-        param16[i] = orc_f32_to_f16(w_new);
+        param16[i] = orc_narrow(fmt, w_new);
     }
     return flag;
+}
+
+/* The fp16 step above (the pages' 16-byte ledger). */
+int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
+                  float *w, float *m, float *v, const double hp[5], uint64_t t,
+                  int skip)
+{
+    return orc_adam_step_fmt(ORC_FMT_F16, n, grad16, param16, w, m, v, hp, t, skip);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -277,23 +382,30 @@ int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
 /* to fp16 (the stage-2 ledger keeps 2 bytes of gradient per parameter).     */
 /* Returns 1 if any output is infinite or NaN, else 0.                       */
 /* ------------------------------------------------------------------------ */
-int orc_reduce(uint32_t nd, const uint16_t *const *slices, uint64_t n,
-               uint16_t *out)
+int orc_reduce_fmt(int fmt, uint32_t nd, const uint16_t *const *slices, uint64_t n,
+                   uint16_t *out)
 {
-    if (nd == 0)
+    if (nd == 0 || (fmt != ORC_FMT_F16 && fmt != ORC_FMT_BF16))
         return ORC_EINVAL;
     const float count = (float)nd;
     int flag = 0;
     for (uint64_t i = 0; i < n; i++) {
-        float acc = orc_f16_to_f32(slices[0][i]);
+        float acc = orc_widen(fmt, slices[0][i]);
         for (uint32_t r = 1; r < nd; r++)
-            acc = acc + orc_f16_to_f32(slices[r][i]);
+            acc = acc + orc_widen(fmt, slices[r][i]);
         float mean = acc / count;
-        out[i] = orc_f32_to_f16(mean);
-        if (!orc_f16_is_finite(out[i]))
+        out[i] = orc_narrow(fmt, mean);
+        if (!orc_is_finite(fmt, out[i]))
             flag = 1;
     }
     return flag;
+}
+
+/* The fp16 reduction (the pages' 2-byte gradients). */
+int orc_reduce(uint32_t nd, const uint16_t *const *slices, uint64_t n,
+               uint16_t *out)
+{
+    return orc_reduce_fmt(ORC_FMT_F16, nd, slices, n, out);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -38,19 +38,28 @@ MUTANTS = {
     "ledger_stage1": ("case 1: b = 4 * P + 12 * S; break;", "case 1: b = 4 * P + 12 * P; break;"),
     "reduce_divisor": ("const float count = (float)nd;", "const float count = (float)(nd + 1);"),
     "reduce_skip_first": ("for (uint32_t r = 1; r < nd; r++)", "for (uint32_t r = 2; r < nd; r++)"),
-    "reduce_reverse": ("float acc = orc_f16_to_f32(slices[0][i]);\n"
+    "reduce_reverse": ("float acc = orc_widen(fmt, slices[0][i]);\n"
                        "        for (uint32_t r = 1; r < nd; r++)\n"
-                       "            acc = acc + orc_f16_to_f32(slices[r][i]);",
-                       "float acc = orc_f16_to_f32(slices[nd - 1][i]);\n"
+                       "            acc = acc + orc_widen(fmt, slices[r][i]);",
+                       "float acc = orc_widen(fmt, slices[nd - 1][i]);\n"
                        "        for (uint32_t r = nd - 1; r-- > 0;)\n"
-                       "            acc = acc + orc_f16_to_f32(slices[r][i]);"),
-    "flag_ignores_nan": ("if (!orc_f16_is_finite(grad16[i]))",
+                       "            acc = acc + orc_widen(fmt, slices[r][i]);"),
+    "flag_ignores_nan": ("if (!orc_is_finite(fmt, grad16[i]))",
                          "if (((grad16[i] >> 10) & 0x1f) == 31 && (grad16[i] & 0x3ff) == 0)"),
-    "reduce_flag_ignores_nan": ("if (!orc_f16_is_finite(out[i]))",
+    "reduce_flag_ignores_nan": ("if (!orc_is_finite(fmt, out[i]))",
                                 "if (((out[i] >> 10) & 0x1f) == 31 && (out[i] & 0x3ff) == 0)"),
     "comm_stage3_two_passes": ("uint64_t passes = stage == 3 ? 3 : 2;", "uint64_t passes = 2;"),
     "comm_ring_nd_shards": ("ring = (unsigned __int128)passes * (nd - 1) * lay[1];",
                             "ring = (unsigned __int128)passes * nd * lay[1];"),
+    "bf16_round_trunc": ("double quanta = nearbyint(ldexp(a, -q));",
+                         "double quanta = trunc(ldexp(a, -q));"),
+    "bf16_quantum": ("int q = e - 8;\n    if (q < -133)", "int q = e - 7;\n    if (q < -133)"),
+    "bf16_overflow_edge": ("if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))",
+                           "if (a > ldexp(2.0 - ldexp(1.0, -7), 127))"),
+    "bf16_widen_bias": ("mag = ldexp(128.0 + (double)F, E - 134);",
+                        "mag = ldexp(128.0 + (double)F, E - 133);"),
+    "bf16_flag_exponent": ("return fmt == ORC_FMT_BF16 ? ((h >> 7) & 0xff) != 255 : orc_f16_is_finite(h);",
+                           "return fmt == ORC_FMT_BF16 ? ((h >> 7) & 0xff) != 254 : orc_f16_is_finite(h);"),
     "gather_reversed": ("full[(uint64_t)r * shard_len + i] = shards[r][i];",
                         "full[(uint64_t)r * shard_len + i] = shards[nd - 1 - r][i];"),
 }
@@ -75,7 +84,8 @@ def test_pins_catch_planted_mistake(tmp_path, name):
     env = dict(os.environ, ZERO_ORACLE_LIB=str(so))
     files = [os.path.join(HERE, f) for f in (
         "test_oracle_fp16.py", "test_oracle_ledger_layout.py",
-        "test_oracle_adam.py", "test_oracle_reduce.py", "test_oracle_comm.py")]
+        "test_oracle_adam.py", "test_oracle_reduce.py", "test_oracle_comm.py",
+        "test_oracle_bf16.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-k", "not every_fp32_pattern", *files],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
