@@ -82,6 +82,9 @@ def parse():
                          "parameters stay on the GPU")
     ap.add_argument("--offload-threads", type=int, default=0,
                     help="host threads of the offload update (0: min(16, hardware threads))")
+    ap.add_argument("--bf16", action="store_true",
+                    help="the bfloat16 variant: bfloat16 parameters, gradients and slices "
+                         "(fp32 master, m, v as before)")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="elements per chunk of the Adam plan (0: library default)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
@@ -119,9 +122,12 @@ class Step:
     """Device state and the launches of one step for a workload."""
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
-                 offload_threads=0):
+                 offload_threads=0, bf16=False):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
+        half = torch.bfloat16 if bf16 else torch.float16
+        if bf16 and (fused or offload):
+            raise SystemExit("--bf16 runs the separate reduce and Adam kernels only")
         wl = W.WORKLOADS[name]
         self.wl = wl
         self.hp = zs.AdamHParams(**W.ADAM_HP)
@@ -131,15 +137,16 @@ class Step:
         if len(wl.tensors) == 1:
             lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
             self.layout = lay
-            self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total)
+            self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total,
+                                                half=half)
             self.tensors = [sh]
             if wl.reduce_slices:
-                self.slice_buf, self.rows = W.device_slices(wl, lay.real_len)
+                self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half)
             else:
                 W.device_fill_grads(wl, self.tensors, 1)
         else:
             self.layout = None
-            self.tensors = W.device_list_state(wl)
+            self.tensors = W.device_list_state(wl, half=half)
             W.device_fill_grads(wl, self.tensors, 1)
         self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors], chunk_elems)
         self.n_params = self.plan.stats()["n_params"]
@@ -307,7 +314,7 @@ def main():
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
-                args.offload_threads)
+                args.offload_threads, args.bf16)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -343,7 +350,8 @@ def main():
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
     cfg = {"workload": args.workload + ("+fused" if step.fused else "") +
-           ("+gather" if step.gather else "") + ("+offload" if step.offload else ""),
+           ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
+           ("+bf16" if args.bf16 else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),

@@ -166,6 +166,19 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
 int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
                      uint32_t chunk_elems, zero_plan **out);
 
+/*
+ * zero_plan_create_bf16 -- as zero_plan_create, for tensors whose parameter
+ * and gradient arrays hold bfloat16 values (param_f16 and grad_f16 then
+ * point to bfloat16): the variant that keeps the 16-byte ledger with
+ * bfloat16 in place of fp16 ([DSZ] "Why parameter count is not training
+ * memory": BF16 setups differ in which states they keep).  zero_adam_step
+ * on such a plan widens the gradient from bfloat16 (exact), runs the same
+ * fp32 update and rounds the parameter to the nearest bfloat16 (ties to
+ * even); the non-finite flag tests the bfloat16 exponent field.
+ */
+int zero_plan_create_bf16(const zero_tensor *tensors, uint32_t n_tensors,
+                          uint32_t chunk_elems, zero_plan **out);
+
 /* zero_plan_stats_of -- fill *out for an existing plan.  Host only. */
 int zero_plan_stats_of(const zero_plan *plan, zero_plan_stats *out);
 
@@ -237,6 +250,17 @@ int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp,
 int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd,
                            uint64_t n, void *out_f16, int32_t *nonfinite_flag,
                            void *stream);
+
+/*
+ * zero_reduce_grad_shard_bf16 -- zero_reduce_grad_shard for bfloat16
+ * slices and output: the same fp32 sum in rank order and one division by
+ * nd, rounded to the nearest bfloat16 (the bfloat16 variant of the ledger,
+ * see zero_plan_create_bf16).  Arguments and errors as
+ * zero_reduce_grad_shard.
+ */
+int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
+                                uint64_t n, void *out_bf16, int32_t *nonfinite_flag,
+                                void *stream);
 
 /*
  * zero_reduce_adam_step -- the stage-2 step of one rank over a flat shard

@@ -3,9 +3,9 @@ helpers.  The bar:
   fp32 master, m, v: relative error <= 1e-6 where the oracle's value is
     nonzero, equal (either sign of zero) where it is zero, and non-finite
     values in the same places with the same class (NaN, +inf, -inf);
-  fp16 params and reduced gradients: within 1 ulp, measured on an ordered
-    integer image of the bits (+0 and -0 both map to 0), non-finite classes
-    matching.
+  fp16 (or bfloat16) params and reduced gradients: within 1 ulp, measured
+    on an ordered integer image of the bits (+0 and -0 both map to 0),
+    non-finite classes matching.
 Bit-exact counts are reported next to the bar (the design target is
 bit-exact: both sides do the same IEEE operations in the same order).
 """
@@ -69,10 +69,14 @@ def _ordered16(b: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
-def _class16(b):
+_FMT16 = {"f16": (0x7C00, 0x03FF), "bf16": (0x7F80, 0x007F)}
+
+
+def _class16(b, fmt="f16"):
     b = np.asarray(b, np.uint16)
-    exp_all = (b & 0x7C00) == 0x7C00
-    frac = (b & 0x03FF) != 0
+    em, fm = _FMT16[fmt]
+    exp_all = (b & em) == em
+    frac = (b & fm) != 0
     c = np.zeros(b.shape, np.int8)
     c[exp_all & frac] = 1
     c[exp_all & ~frac & ((b & 0x8000) == 0)] = 2
@@ -80,11 +84,12 @@ def _class16(b):
     return c
 
 
-def check16(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
+def check16(got: np.ndarray, ref: np.ndarray, what: str, fmt: str = "f16") -> dict:
+    """fmt: "f16" or "bf16", the format of both bit-pattern arrays."""
     got = np.asarray(got).view(np.uint16)
     ref = np.asarray(ref).view(np.uint16)
     assert got.shape == ref.shape, what
-    cg, cr = _class16(got), _class16(ref)
+    cg, cr = _class16(got, fmt), _class16(ref, fmt)
     bad_class = np.flatnonzero(cg != cr)
     assert bad_class.size == 0, f"{what}: non-finite class differs at {bad_class[:8]}"
     fin = cr == 0

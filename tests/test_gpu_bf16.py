@@ -1,0 +1,207 @@
+"""GPU parity of the bfloat16 variant (bfloat16 parameters and gradients,
+fp32 master, m and v) through the C ABI, against the oracle's bfloat16 step
+and reduce: ragged sizes at every alignment class, every bfloat16 gradient
+pattern, the reduce over N_d from 1 to 64, the skip chain, and the full
+7.5e9 / N_d = 64 rank's shard on sampled elements.  Each case prints its
+name and sizes before it touches the GPU."""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import check16, check32, host16, host32, to_dev32
+from zero_partitioned_mixed_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+HP = dict(W.ADAM_HP)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_partitioned_mixed_layout_amd import zero_shard
+    torch.cuda.set_device(0)
+    return zero_shard
+
+
+def to_devbf(bits, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(x):
+    return oracle.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def _step_ref(g, p, w, m, v, t):
+    return oracle.adam_step(g, p, w, m, v, t=t, fmt="bf16", **HP)
+
+
+def _cmp(dev, ref, what):
+    p, w, m, v = dev
+    P, Wr, M, V = ref
+    res = [check16(host16(p), P, what + " param", fmt="bf16"), check32(host32(w), Wr, what + " master"),
+           check32(host32(m), M, what + " m"), check32(host32(v), V, what + " v")]
+    return sum(r["not_bit_exact"] for r in res)
+
+
+SIZES = [1, 7, 8, 9, 31, 4095, 4096, 4097, 70001]
+OFFSETS = [(0, 0, 0, 0, 0), (4, 0, 0, 0, 0), (3, 3, 3, 3, 3), (2, 6, 2, 2, 6),
+           (1, 0, 0, 0, 0), (0, 0, 1, 0, 0)]
+
+
+@pytest.mark.parametrize("chunk", [0, 512])
+def test_bf16_ragged_sizes_and_alignments(zs, chunk):
+    import torch
+    rng = np.random.default_rng(31 + chunk)
+    dev, ref = [], []
+    for i, n in enumerate(SIZES):
+        offs = OFFSETS[i % len(OFFSETS)]
+        bufs = [torch.zeros(n + o + 8, dtype=dt, device="cuda")[o:o + n] for o, dt in
+                zip(offs, (torch.bfloat16, torch.bfloat16, torch.float32, torch.float32,
+                           torch.float32))]
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v0 = (rng.random(n) * 1e-6).astype(np.float32)
+        bufs[2].copy_(to_dev32(w0))
+        bufs[3].copy_(to_dev32(m0))
+        bufs[4].copy_(to_dev32(v0))
+        dev.append(bufs)
+        ref.append([np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy()])
+    say(f"bf16 ragged chunk={chunk} tensors={len(dev)}")
+    plan = zs.zero_plan_create([tuple(b) for b in dev], chunk)
+    st = plan.stats()
+    assert st["vector_elems"] and st["scalar_elems"]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    inexact = 0
+    for t in (4, 5, 6):
+        gs = []
+        for b in dev:
+            gh = bf16_bits(rng.standard_normal(b[2].numel()) * 1e-3)
+            b[1].copy_(to_devbf(gh))
+            gs.append(gh)
+        zs.zero_adam_step(plan, zs.AdamHParams(**HP), t, flag)
+        for gh, r in zip(gs, ref):
+            _step_ref(gh, r[0], r[1], r[2], r[3], t)
+        torch.cuda.synchronize()
+        for k, (b, r) in enumerate(zip(dev, ref)):
+            inexact += _cmp((b[0], b[2], b[3], b[4]), r, f"bf16 tensor {k} t={t}")
+    assert int(flag.item()) == 0 and inexact == 0
+    plan.destroy()
+
+
+def test_bf16_every_gradient_pattern(zs):
+    import torch
+    n = 1 << 16
+    say("bf16 every gradient pattern")
+    rng = np.random.default_rng(8)
+    g = np.arange(n, dtype=np.uint32).astype(np.uint16)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = (rng.random(n) * 1e-6).astype(np.float32)
+    dp = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    dw, dm, dv = to_dev32(w0), to_dev32(m0), to_dev32(v0)
+    plan = zs.zero_plan_create([(dp, to_devbf(g), dw, dm, dv)])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 3, flag)
+    ref = [np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy()]
+    assert _step_ref(g, *ref, 3) == 1
+    torch.cuda.synchronize()
+    assert _cmp((dp, dw, dm, dv), ref, "bf16 all patterns") == 0
+    assert int(flag.item()) == 1
+    plan.destroy()
+
+
+@pytest.mark.parametrize("nd", [1, 2, 3, 8, 16, 17, 64])
+@pytest.mark.parametrize("layout", ["aligned", "phase3", "odd"])
+def test_bf16_reduce_matches_oracle(zs, nd, layout):
+    import torch
+    rng = np.random.default_rng(100 + nd)
+    for n in (1, 9, 4097, 65537):
+        say(f"bf16 reduce nd={nd} layout={layout} n={n}")
+        hs = [bf16_bits(rng.standard_normal(n) * 1e-3) for _ in range(nd)]
+        offs = {"aligned": [0] * (nd + 1), "phase3": [3] * (nd + 1),
+                "odd": [r % 3 for r in range(nd + 1)]}[layout]
+        ds = []
+        for r in range(nd):
+            b = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")[offs[r]:offs[r] + n]
+            b.copy_(to_devbf(hs[r]))
+            ds.append(b)
+        out = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")[offs[nd]:offs[nd] + n]
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        zs.zero_reduce_grad_shard(ds, out, flag)
+        ref, rflag = oracle.reduce_grad(hs, fmt="bf16")
+        torch.cuda.synchronize()
+        assert check16(host16(out), ref, f"bf16 reduce nd={nd} n={n}", fmt="bf16")["not_bit_exact"] == 0
+        assert int(flag.item()) == rflag == 0
+
+
+def test_bf16_reduce_then_step_skips_on_nonfinite(zs):
+    """An infinite bfloat16 slice value raises the reduce's flag, which as
+    the step's skip input leaves every array untouched."""
+    import torch
+    say("bf16 reduce -> skip")
+    n = 5000
+    rng = np.random.default_rng(3)
+    hs = [bf16_bits(rng.standard_normal(n) * 1e-3) for _ in range(4)]
+    hs[2][1234] = 0x7F80
+    ds = [to_devbf(h) for h in hs]
+    g = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard(ds, g, rflag)
+    p = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w, m, v = to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    plan = zs.zero_plan_create([(p, g, w, m, v)])
+    aflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, aflag, rflag)
+    torch.cuda.synchronize()
+    assert int(rflag.item()) == 1 and int(aflag.item()) == 0
+    assert np.array_equal(host32(w).view(np.uint32), w0.view(np.uint32))
+    assert int(torch.count_nonzero(m).item()) == 0 and int(torch.count_nonzero(p).item()) == 0
+    plan.destroy()
+
+
+def test_bf16_flat_7p5b_nd64_full_size(zs):
+    """Psi = 7.5e9 over 64 ranks, rank 0's 117,187,500 elements in bfloat16:
+    reduce of 64 bfloat16 slices, then the step at t = 1; 200,000 sampled
+    elements (both ends included) against the oracle's bfloat16 reduce and
+    step on the same inputs."""
+    import torch
+    wl = W.WORKLOADS["flat_7p5b_nd64"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, 0, wl.align)
+    n = lay.real_len
+    say(f"bf16 flat_7p5b_nd64 n={n}")
+    full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total, half=torch.bfloat16)
+    buf, rows = W.device_slices(wl, n, half=torch.bfloat16)
+    idx = W.sample_indices(n, 200_000, seed=wl.seed + 7)
+    d = torch.from_numpy(idx).cuda()
+    w0 = host32(sh.w.index_select(0, d))
+    slices = [host16(r.index_select(0, d)) for r in rows]
+    rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    aflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard(rows, sh.g, rflag)
+    plan = zs.zero_plan_create([sh.arrays()])
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, aflag, rflag)
+    torch.cuda.synchronize()
+    g_ref, f1 = oracle.reduce_grad(slices, fmt="bf16")
+    ref = [np.zeros(idx.size, np.uint16), w0.copy(), np.zeros(idx.size, np.float32),
+           np.zeros(idx.size, np.float32)]
+    f2 = _step_ref(g_ref, *ref, 1)
+    assert check16(host16(sh.g.index_select(0, d)), g_ref, "bf16 grad", fmt="bf16")["not_bit_exact"] == 0
+    got = (sh.p.index_select(0, d), sh.w.index_select(0, d), sh.m.index_select(0, d),
+           sh.v.index_select(0, d))
+    assert _cmp(got, ref, "bf16 full size") == 0
+    assert int(rflag.item()) == f1 == 0 and int(aflag.item()) == f2 == 0
+    assert int(torch.count_nonzero(full[n:]).item()) == 0
+    plan.destroy()
+    del full, sh, buf, rows
+    gc.collect()
+    torch.cuda.empty_cache()

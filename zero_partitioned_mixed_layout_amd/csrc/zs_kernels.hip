@@ -44,6 +44,26 @@ using zs::TensorDesc;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// The 16-bit formats of parameters and gradients: IEEE binary16 (the
+// pages' ledger) and bfloat16 (the variant that keeps the same ledger with
+// bfloat16 in their place).  Widening is exact in both; narrowing rounds
+// to nearest even (v_cvt_f16_f32, v_cvt_pk_bf16_f32).  A value is infinite
+// or NaN when its exponent field is all ones.
+struct FmtF16 {
+    typedef _Float16 T;
+    typedef f16x4 V4;
+    typedef f16x8 V8;
+    static constexpr uint16_t kExp = 0x7C00;
+};
+struct FmtBF16 {
+    typedef __bf16 T;
+    typedef bf16x4 V4;
+    typedef bf16x8 V8;
+    static constexpr uint16_t kExp = 0x7F80;
+};
 
 // Pointers read from the chunk table are generic; the arrays live in device
 // global memory, and saying so lets the compiler use global_load/store
@@ -71,8 +91,13 @@ __device__ __forceinline__ void st_nt(T v, T *p) {
     __builtin_nontemporal_store(v, as_global(p));
 }
 
+template <class Fmt = FmtF16>
+__device__ __forceinline__ bool bits_nonfinite(uint16_t b) {
+    return (b & Fmt::kExp) == Fmt::kExp;
+}
+
 __device__ __forceinline__ bool f16_bits_nonfinite(uint16_t b) {
-    return (b & 0x7C00u) == 0x7C00u;
+    return bits_nonfinite<FmtF16>(b);
 }
 
 // Raise the non-finite flag once for this wave if any lane saw a non-finite
@@ -93,9 +118,10 @@ __device__ __forceinline__ void raise_flag(int32_t *flag, int bad) {
 // ---------------------------------------------------------------------------
 
 // One element of the Adam step (Kingma and Ba, Algorithm 1, with bias
-// correction and eps outside the root).  Returns the new fp16 parameter.
-__device__ __forceinline__ _Float16 adam_elem(float g, float &w, float &m, float &v,
-                                              const AdamConsts &c) {
+// correction and eps outside the root).  Returns the new 16-bit parameter.
+template <class Fmt = FmtF16>
+__device__ __forceinline__ typename Fmt::T adam_elem(float g, float &w, float &m, float &v,
+                                                     const AdamConsts &c) {
     const float m_old = c.b1 * m;
     const float m_in = c.omb1 * g;
     m = m_old + m_in;
@@ -109,17 +135,18 @@ __device__ __forceinline__ _Float16 adam_elem(float g, float &w, float &m, float
     const float u = m_hat / denom;
     const float step = c.lr * u;
     w = w - step;
-    return (_Float16)w;
+    return (typename Fmt::T)w;
 }
 
+template <class Fmt>
 __device__ __forceinline__ void adam_single(const TensorDesc &T, uint64_t i,
                                             const AdamConsts &c, int &bad) {
     const uint16_t gb = as_global(T.g)[i];
-    bad |= f16_bits_nonfinite(gb);
-    _Float16 gh;
+    bad |= bits_nonfinite<Fmt>(gb);
+    typename Fmt::T gh;
     memcpy(&gh, &gb, 2);
     float w = as_global(T.w)[i], m = as_global(T.m)[i], v = as_global(T.v)[i];
-    const _Float16 p = adam_elem((float)gh, w, m, v, c);
+    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c);
     as_global(T.w)[i] = w;
     as_global(T.m)[i] = m;
     as_global(T.v)[i] = v;
@@ -130,29 +157,32 @@ __device__ __forceinline__ void adam_single(const TensorDesc &T, uint64_t i,
 
 // Four consecutive elements held in registers: fp16 gradient (8 bytes) and
 // fp32 master, m, v (16 bytes each).
+template <class Fmt>
 struct Quad {
-    f16x4 g;
+    typename Fmt::V4 g;
     f32x4 w, m, v;
 };
 
-__device__ __forceinline__ void quad_load(const TensorDesc &T, uint64_t i, Quad &q) {
-    q.g = ld_nt(reinterpret_cast<const f16x4 *>(T.g + i));
+template <class Fmt>
+__device__ __forceinline__ void quad_load(const TensorDesc &T, uint64_t i, Quad<Fmt> &q) {
+    q.g = ld_nt(reinterpret_cast<const typename Fmt::V4 *>(T.g + i));
     q.w = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i));
     q.m = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i));
     q.v = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
 }
 
-__device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t i, Quad &q,
+template <class Fmt>
+__device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t i, Quad<Fmt> &q,
                                                   const AdamConsts &c, int &bad) {
-    f16x4 p;
+    typename Fmt::V4 p;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const _Float16 gj = q.g[j];
+        const typename Fmt::T gj = q.g[j];
         uint16_t gb;
         memcpy(&gb, &gj, 2);
-        bad |= f16_bits_nonfinite(gb);
+        bad |= bits_nonfinite<Fmt>(gb);
         float w = q.w[j], m = q.m[j], v = q.v[j];
-        p[j] = adam_elem((float)gj, w, m, v, c);
+        p[j] = adam_elem<Fmt>((float)gj, w, m, v, c);
         q.w[j] = w;
         q.m[j] = m;
         q.v[j] = v;
@@ -160,22 +190,23 @@ __device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t 
     st_nt(q.w, reinterpret_cast<f32x4 *>(T.w + i));
     st_nt(q.m, reinterpret_cast<f32x4 *>(T.m + i));
     st_nt(q.v, reinterpret_cast<f32x4 *>(T.v + i));
-    st_nt(p, reinterpret_cast<f16x4 *>(T.p + i));
+    st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + i));
 }
 
 // A full wave tile: kTile consecutive elements from `base` (vector-aligned).
 // Lane L takes elements 4L..4L+3 and kTile/2+4L..kTile/2+4L+3, so each of the
 // wave's load and store instructions covers one contiguous 512-byte (fp16)
 // or 1-KiB (fp32) range.  All eight loads are issued before any arithmetic.
+template <class Fmt>
 __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, uint32_t lane,
                                           const AdamConsts &c, int &bad) {
     const uint64_t i0 = base + 4u * lane, i1 = i0 + kTile / 2;
-    Quad a, b;
-    quad_load(T, i0, a);
-    quad_load(T, i1, b);
+    Quad<Fmt> a, b;
+    quad_load<Fmt>(T, i0, a);
+    quad_load<Fmt>(T, i1, b);
     __builtin_amdgcn_sched_barrier(0);
-    quad_update_store(T, i0, a, c, bad);
-    quad_update_store(T, i1, b, c, bad);
+    quad_update_store<Fmt>(T, i0, a, c, bad);
+    quad_update_store<Fmt>(T, i1, b, c, bad);
 }
 
 // Tile j of a chunk on the vector path.  The tensor's peeled head (fewer
@@ -183,17 +214,18 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
 // chunk and is done by tile 0; every other chunk starts vector-aligned.  The
 // chunk's last, partial tile goes four elements per lane, then the final
 // fewer-than-four singly.
+template <class Fmt>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
     const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
     if (j == 0 && lane < head)
-        adam_single(T, lane, c, bad);
+        adam_single<Fmt>(T, lane, c, bad);
     const uint64_t base = ch.start + head;
     const uint32_t body = ch.count - head;
     const uint32_t nfull = body / kTile;
     if (j < nfull) {
-        adam_tile(T, base + (uint64_t)j * kTile, lane, c, bad);
+        adam_tile<Fmt>(T, base + (uint64_t)j * kTile, lane, c, bad);
         return;
     }
     if (j > nfull)
@@ -202,30 +234,32 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
     const uint32_t rem = body - nfull * kTile; // < kTile
     const uint32_t nquads = rem / 4u;
     for (uint32_t q = lane; q < nquads; q += kWave) {
-        Quad x;
-        quad_load(T, rbase + 4u * q, x);
-        quad_update_store(T, rbase + 4u * q, x, c, bad);
+        Quad<Fmt> x;
+        quad_load<Fmt>(T, rbase + 4u * q, x);
+        quad_update_store<Fmt>(T, rbase + 4u * q, x, c, bad);
     }
     const uint32_t tail = rem - 4u * nquads;
     if (lane < tail)
-        adam_single(T, rbase + 4u * nquads + lane, c, bad);
+        adam_single<Fmt>(T, rbase + 4u * nquads + lane, c, bad);
 }
 
 // Tile j of a chunk of a tensor whose arrays disagree in alignment: the
 // tile's elements one at a time, lane-strided so each access instruction of
 // the wave stays contiguous.
+template <class Fmt>
 __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chunk &ch,
                                                  uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lo = j * kTile;
     const uint32_t hi = min(ch.count, lo + kTile);
     for (uint32_t k = lo + threadIdx.x; k < hi; k += kWave)
-        adam_single(T, ch.start + k, c, bad);
+        adam_single<Fmt>(T, ch.start + k, c, bad);
 }
 
 // The fused step over a plan.  Each workgroup is one wave and takes one wave
 // tile: virtual workgroup b is tile b % tiles_per_chunk of chunk
 // b / tiles_per_chunk.  Launches with fewer workgroups than virtual ones
-// stride over them.
+// stride over them.  Fmt: the 16-bit format of parameters and gradients.
+template <class Fmt>
 __global__ __launch_bounds__(kWave) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
     uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
@@ -239,9 +273,9 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
         const Chunk ch = chunks[ci];
         const TensorDesc T = tensors[ch.tensor];
         if (T.vec == 4)
-            adam_tile_of_chunk(T, ch, j, c, bad);
+            adam_tile_of_chunk<Fmt>(T, ch, j, c, bad);
         else
-            adam_tile_single(T, ch, j, c, bad);
+            adam_tile_single<Fmt>(T, ch, j, c, bad);
     }
     raise_flag(flag, bad);
 }
@@ -250,34 +284,41 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
 // Gradient reduction over N_d slices.
 // ---------------------------------------------------------------------------
 struct SliceArgs {
-    const _Float16 *p[ZERO_MAX_SLICES];
+    const uint16_t *p[ZERO_MAX_SLICES]; // 16-bit values of the kernel's format
 };
 
-template <int VEC>
+// Vector of VEC values of a format.
+template <class Fmt, int VEC>
 struct HVec;
-template <>
-struct HVec<8> {
-    typedef f16x8 T;
+template <class Fmt>
+struct HVec<Fmt, 8> {
+    typedef typename Fmt::V8 T;
 };
-template <>
-struct HVec<4> {
-    typedef f16x4 T;
+template <class Fmt>
+struct HVec<Fmt, 4> {
+    typedef typename Fmt::V4 T;
 };
 
+template <class Fmt = FmtF16>
+__device__ __forceinline__ float widen(const uint16_t *p, uint64_t i) {
+    return (float)as_global(reinterpret_cast<const typename Fmt::T *>(p))[i];
+}
+
+template <class Fmt = FmtF16>
 __device__ __forceinline__ float reduce_single(const SliceArgs &s, uint32_t nd, uint64_t i) {
-    float acc = (float)as_global(s.p[0])[i];
+    float acc = widen<Fmt>(s.p[0], i);
     for (uint32_t r = 1; r < nd; r++)
-        acc = acc + (float)as_global(s.p[r])[i];
+        acc = acc + widen<Fmt>(s.p[r], i);
     return acc;
 }
 
 // Adds slices r0 .. r0+B-1, in rank order, at group start i into acc; the B
 // loads are all issued before the first add.  With `first`, slice r0
 // initialises the sum instead of being added to it.
-template <int VEC, int B>
+template <int VEC, int B, class Fmt = FmtF16>
 __device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, uint64_t i,
                                              bool first, float (&acc)[VEC]) {
-    typedef typename HVec<VEC>::T hv;
+    typedef typename HVec<Fmt, VEC>::T hv;
     hv x[B];
 #pragma unroll
     for (int q = 0; q < B; q++)
@@ -293,48 +334,49 @@ __device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, ui
 // One vector group of VEC outputs at element i: the sum over the nd slices
 // in rank order, in batches of 16, 8, 4 and 1 slices in flight per lane,
 // then one division by nd.
-template <int VEC>
+template <class Fmt, int VEC>
 __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, uint64_t i,
-                                             float count, _Float16 *out, int &bad) {
-    typedef typename HVec<VEC>::T hv;
+                                             float count, uint16_t *out, int &bad) {
+    typedef typename HVec<Fmt, VEC>::T hv;
     float acc[VEC];
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
-        reduce_batch<VEC, 16>(s, r, i, r == 0, acc);
+        reduce_batch<VEC, 16, Fmt>(s, r, i, r == 0, acc);
     for (; r + 8 <= nd; r += 8)
-        reduce_batch<VEC, 8>(s, r, i, r == 0, acc);
+        reduce_batch<VEC, 8, Fmt>(s, r, i, r == 0, acc);
     for (; r + 4 <= nd; r += 4)
-        reduce_batch<VEC, 4>(s, r, i, r == 0, acc);
+        reduce_batch<VEC, 4, Fmt>(s, r, i, r == 0, acc);
     for (; r < nd; r++)
-        reduce_batch<VEC, 1>(s, r, i, r == 0, acc);
+        reduce_batch<VEC, 1, Fmt>(s, r, i, r == 0, acc);
     hv o;
 #pragma unroll
     for (int j = 0; j < VEC; j++) {
-        o[j] = (_Float16)(acc[j] / count);
+        o[j] = (typename Fmt::T)(acc[j] / count);
         uint16_t b;
-        _Float16 oj = o[j];
+        typename Fmt::T oj = o[j];
         memcpy(&b, &oj, 2);
-        bad |= f16_bits_nonfinite(b);
+        bad |= bits_nonfinite<Fmt>(b);
     }
     st_nt(o, reinterpret_cast<hv *>(out + i));
 }
 
+template <class Fmt>
 __device__ __forceinline__ void reduce_one(const SliceArgs &s, uint32_t nd, uint64_t i,
-                                           float count, _Float16 *out, int &bad) {
-    const _Float16 o = (_Float16)(reduce_single(s, nd, i) / count);
-    as_global(out)[i] = o;
+                                           float count, uint16_t *out, int &bad) {
+    const typename Fmt::T o = (typename Fmt::T)(reduce_single<Fmt>(s, nd, i) / count);
     uint16_t b;
     memcpy(&b, &o, 2);
-    bad |= f16_bits_nonfinite(b);
+    as_global(out)[i] = b;
+    bad |= bits_nonfinite<Fmt>(b);
 }
 
 // Each lane reduces one vector group of VEC elements (grid-striding when the
 // launch is smaller than the work); the unaligned head (fewer than VEC
 // leading elements) and the tail past the last whole group go one element
 // per lane.  VEC = 1: every element singly.
-template <int VEC>
+template <class Fmt, int VEC>
 __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t nd, uint64_t n,
-                                                          uint32_t head, _Float16 *__restrict__ out,
+                                                          uint32_t head, uint16_t *__restrict__ out,
                                                           int32_t *__restrict__ flag) {
     const float count = (float)nd;
     const uint64_t gtid = (uint64_t)blockIdx.x * kWave + threadIdx.x;
@@ -344,12 +386,12 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
     const uint64_t ngroups = VEC > 1 ? (n - h) / VEC : 0;
     const uint64_t body_end = h + ngroups * VEC;
     if (gtid < h)
-        reduce_one(s, nd, gtid, count, out, bad);
+        reduce_one<Fmt>(s, nd, gtid, count, out, bad);
     for (uint64_t i = body_end + gtid; i < n; i += gstride)
-        reduce_one(s, nd, i, count, out, bad);
+        reduce_one<Fmt>(s, nd, i, count, out, bad);
     if (VEC > 1)
         for (uint64_t k = gtid; k < ngroups; k += gstride)
-            reduce_group<VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
+            reduce_group<Fmt, VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
     raise_flag(flag, bad);
 }
 
@@ -673,10 +715,13 @@ struct zero_plan {
     zero_plan_stats stats;
     int device;
     size_t lds_cap; // dynamic LDS per Adam workgroup (the occupancy cap)
+    bool bf16;      // parameters and gradients are bfloat16 (else fp16)
 };
 
-extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
-                                uint32_t chunk_elems, zero_plan **out) {
+namespace {
+
+int plan_create(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems, bool bf16,
+                zero_plan **out) {
     if (!out)
         return ZERO_EINVAL;
     zs::HostPlan hp;
@@ -697,6 +742,7 @@ extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
     plan->stats = hp.stats;
     plan->device = dev;
     plan->lds_cap = lds_cap_bytes(dev, zs::kAdamPerCU);
+    plan->bf16 = bf16;
     const size_t tb = hp.tensors.size() * sizeof(zs::TensorDesc);
     const size_t cb = hp.chunks.size() * sizeof(zs::Chunk);
     if (tb + cb > 0) {
@@ -717,6 +763,18 @@ extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
     }
     *out = plan;
     return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_plan_create(const zero_tensor *tensors, uint32_t n_tensors,
+                                uint32_t chunk_elems, zero_plan **out) {
+    return plan_create(tensors, n_tensors, chunk_elems, false, out);
+}
+
+extern "C" int zero_plan_create_bf16(const zero_tensor *tensors, uint32_t n_tensors,
+                                     uint32_t chunk_elems, zero_plan **out) {
+    return plan_create(tensors, n_tensors, chunk_elems, true, out);
 }
 
 extern "C" int zero_plan_stats_of(const zero_plan *plan, zero_plan_stats *out) {
@@ -764,16 +822,24 @@ extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp
     const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / kTile);
     const uint64_t n_virtual = plan->stats.n_chunks * tpc;
     const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
-    hipLaunchKernelGGL(zs_adam_kernel, dim3(grid), dim3(kWave), plan->lds_cap,
-                       (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c,
-                       nonfinite_flag, skip_if_nonzero);
+    if (plan->bf16)
+        hipLaunchKernelGGL(zs_adam_kernel<FmtBF16>, dim3(grid), dim3(kWave), plan->lds_cap,
+                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
+                           c, nonfinite_flag, skip_if_nonzero);
+    else
+        hipLaunchKernelGGL(zs_adam_kernel<FmtF16>, dim3(grid), dim3(kWave), plan->lds_cap,
+                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
+                           c, nonfinite_flag, skip_if_nonzero);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
 }
 
-extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n,
-                                      void *out_f16, int32_t *nonfinite_flag, void *stream) {
+namespace {
+
+template <class Fmt>
+int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, void *out_f16,
+                      int32_t *nonfinite_flag, void *stream) {
     if (!slices_f16 || !out_f16 || nd == 0 || nd > ZERO_MAX_SLICES)
         return ZERO_EINVAL;
     uint64_t bytes;
@@ -791,7 +857,7 @@ extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd
         // the output must not overlap any slice
         if (n > 0 && a < o + bytes && o < a + bytes)
             return ZERO_EINVAL;
-        args.p[r] = (const _Float16 *)slices_f16[r];
+        args.p[r] = (const uint16_t *)slices_f16[r];
         addr[r] = a;
     }
     for (uint32_t r = nd; r < ZERO_MAX_SLICES; r++)
@@ -813,17 +879,30 @@ extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd
     const size_t lds = lds_cap_bytes(dev, zs::reduce_per_cu(nd));
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
-        hipLaunchKernelGGL(zs_reduce_kernel<8>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           head, (_Float16 *)out_f16, nonfinite_flag);
+        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, head, (uint16_t *)out_f16, nonfinite_flag);
     else if (vec == 4)
-        hipLaunchKernelGGL(zs_reduce_kernel<4>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           head, (_Float16 *)out_f16, nonfinite_flag);
+        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 4>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, head, (uint16_t *)out_f16, nonfinite_flag);
     else
-        hipLaunchKernelGGL(zs_reduce_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           0u, (_Float16 *)out_f16, nonfinite_flag);
+        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 1>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, 0u, (uint16_t *)out_f16, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n,
+                                      void *out_f16, int32_t *nonfinite_flag, void *stream) {
+    return reduce_grad_shard<FmtF16>(slices_f16, nd, n, out_f16, nonfinite_flag, stream);
+}
+
+extern "C" int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
+                                           uint64_t n, void *out_bf16, int32_t *nonfinite_flag,
+                                           void *stream) {
+    return reduce_grad_shard<FmtBF16>(slices_bf16, nd, n, out_bf16, nonfinite_flag, stream);
 }
 
 extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n,
@@ -853,7 +932,7 @@ extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd,
         const uintptr_t a = (uintptr_t)slices_f16[r];
         if (!a || a % 2)
             return ZERO_EINVAL;
-        args.p[r] = (const _Float16 *)slices_f16[r];
+        args.p[r] = (const uint16_t *)slices_f16[r];
         a16[r] = a;
         ranges.push_back({a, a + b2, false});
     }

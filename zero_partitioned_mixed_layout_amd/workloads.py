@@ -233,13 +233,16 @@ def sample_indices(n: int, k: int, seed: int, must: Optional[np.ndarray] = None,
 # caller (the shard layout is not computed here).
 # ---------------------------------------------------------------------------
 class DeviceTensor:
-    """The five arrays of one tensor of the shard, on the device."""
+    """The five arrays of one tensor of the shard, on the device.  half: the
+    16-bit dtype of the parameter and gradient (torch.float16 by default;
+    torch.bfloat16 for the bfloat16 variant)."""
 
-    def __init__(self, n: int, device, param=None):
+    def __init__(self, n: int, device, param=None, half=None):
         import torch
+        half = half or torch.float16
         self.n = n
-        self.p = param if param is not None else torch.zeros(n, dtype=torch.float16, device=device)
-        self.g = torch.zeros(n, dtype=torch.float16, device=device)
+        self.p = param if param is not None else torch.zeros(n, dtype=half, device=device)
+        self.g = torch.zeros(n, dtype=half, device=device)
         self.w = torch.empty(n, dtype=torch.float32, device=device)
         self.m = torch.zeros(n, dtype=torch.float32, device=device)
         self.v = torch.zeros(n, dtype=torch.float32, device=device)
@@ -248,25 +251,25 @@ class DeviceTensor:
         return (self.p, self.g, self.w, self.m, self.v)
 
 
-def device_list_state(wl: Workload, device="cuda") -> List[DeviceTensor]:
+def device_list_state(wl: Workload, device="cuda", half=None) -> List[DeviceTensor]:
     """One DeviceTensor per tensor of a list workload; master ~ N(0, 0.02)."""
     out = []
     for k, (_, n) in enumerate(wl.tensors):
-        t = DeviceTensor(n, device)
+        t = DeviceTensor(n, device, half=half)
         device_normal(n, MASTER_STD, master_seed(wl.seed, k), None, device, out=t.w)
         out.append(t)
     return out
 
 
 def device_flat_state(wl: Workload, offset: int, length: int, padded_total: int,
-                      device="cuda"):
+                      device="cuda", half=None):
     """The flat workloads: the full fp16 parameter buffer of padded_total
     elements (every rank holds all fp16 parameters under stages 1-2) and this
     rank's shard of `length` elements at `offset` in it.  Returns
     (param_full, DeviceTensor)."""
     import torch
-    full = torch.zeros(padded_total, dtype=torch.float16, device=device)
-    t = DeviceTensor(length, device, param=full[offset:offset + length])
+    full = torch.zeros(padded_total, dtype=half or torch.float16, device=device)
+    t = DeviceTensor(length, device, param=full[offset:offset + length], half=half)
     device_normal(length, MASTER_STD, master_seed(wl.seed), None, device, out=t.w)
     return full, t
 
@@ -282,17 +285,17 @@ def device_inject_inf(grad, positions: np.ndarray, signs: np.ndarray) -> None:
     import torch
     pos = torch.from_numpy(positions).to(grad.device)
     val = torch.from_numpy(signs.astype(np.float32) * np.float32(np.inf)).to(grad.device)
-    grad.index_copy_(0, pos, val.to(torch.float16))
+    grad.index_copy_(0, pos, val.to(grad.dtype))
 
 
-def device_slices(wl: Workload, length: int, device="cuda"):
+def device_slices(wl: Workload, length: int, device="cuda", half=None):
     """N_d fp16 gradient slices of this rank's partition, ~ N(0, 1e-3), as
     rows of one buffer whose row pitch is rounded up to 64 elements (so every
     row starts 128-byte aligned, as separately allocated receive buffers
     would).  Returns (buffer, [row views])."""
     import torch
     pitch = (length + 63) // 64 * 64
-    buf = torch.zeros(wl.nd, pitch, dtype=torch.float16, device=device)
+    buf = torch.zeros(wl.nd, pitch, dtype=half or torch.float16, device=device)
     rows = [buf[r, :length] for r in range(wl.nd)]
     for r in range(wl.nd):
         device_normal(length, GRAD_STD, slice_seed(wl.seed, r), None, device, out=rows[r])

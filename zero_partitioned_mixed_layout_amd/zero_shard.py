@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "zero_comm_volume": [u32, u64, u32, u32, ctypes.POINTER(_Comm)],
         "zero_gather_shards": [ctypes.POINTER(vp), u32, u64, vp, vp],
         "zero_plan_create": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(vp)],
+        "zero_plan_create_bf16": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(vp)],
+        "zero_reduce_grad_shard_bf16": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
         "zero_plan_stats_of": [vp, ctypes.POINTER(_Stats)],
         "zero_plan_describe": [ctypes.POINTER(_Tensor), u32, u32, ctypes.POINTER(_Stats)],
         "zero_plan_destroy": [vp],
@@ -103,7 +105,8 @@ _lib = _load()
 
 # Every symbol include/zero_shard.h declares.
 EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
-           "zero_gather_shards", "zero_plan_create",
+           "zero_gather_shards", "zero_plan_create", "zero_plan_create_bf16",
+           "zero_reduce_grad_shard_bf16",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
            "zero_reduce_adam_step", "zero_adam_step_host", "zero_offload_create",
@@ -203,15 +206,17 @@ def _flag_ptr(flag: Optional[torch.Tensor], what: str, device) -> Optional[int]:
     return flag.data_ptr()
 
 
-def _tensor_entries(tensors: Sequence[Sequence[torch.Tensor]]):
+def _tensor_entries(tensors: Sequence[Sequence[torch.Tensor]], half=torch.float16):
+    """half: the 16-bit dtype of every parameter and gradient (float16 or
+    bfloat16)."""
     arr = (_Tensor * max(1, len(tensors)))()
     device = None
     for k, group in enumerate(tensors):
         if len(group) != 5:
-            raise ValueError("each tensor is (param_f16, grad_f16, master, m, v)")
+            raise ValueError("each tensor is (param, grad, master, m, v)")
         p, g, w, m, v = group
         device = device or w.device
-        for x, dt, nm in ((p, torch.float16, "param"), (g, torch.float16, "grad"),
+        for x, dt, nm in ((p, half, "param"), (g, half, "grad"),
                           (w, torch.float32, "master"), (m, torch.float32, "m"),
                           (v, torch.float32, "v")):
             _need(x, dt, f"tensor {k} {nm}", device)
@@ -257,13 +262,18 @@ class Plan:
 
 
 def zero_plan_create(tensors: Sequence[Sequence[torch.Tensor]], chunk_elems: int = 0) -> Plan:
-    """tensors: sequence of (param_f16, grad_f16, master_f32, m_f32, v_f32).
-    chunk_elems: 0 for the library default, else a multiple of 512."""
-    arr, device = _tensor_entries(tensors)
+    """tensors: sequence of (param, grad, master_f32, m_f32, v_f32) where
+    every param and grad is float16 (the pages' ledger) or every one is
+    bfloat16 (the bfloat16 variant).  chunk_elems: 0 for the library
+    default, else a multiple of 512."""
+    half = tensors[0][0].dtype if len(tensors) else torch.float16
+    if half not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"param: expected torch.float16 or torch.bfloat16, got {half}")
+    arr, device = _tensor_entries(tensors, half)
+    fn = "zero_plan_create_bf16" if half == torch.bfloat16 else "zero_plan_create"
     h = ctypes.c_void_p()
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        _check("zero_plan_create", _lib.zero_plan_create(arr, len(tensors), int(chunk_elems),
-                                                         ctypes.byref(h)))
+        _check(fn, getattr(_lib, fn)(arr, len(tensors), int(chunk_elems), ctypes.byref(h)))
     return Plan(h.value, tensors, device)
 
 
@@ -301,21 +311,23 @@ def zero_adam_step(plan: Plan, hp, t: int, nonfinite_flag: Optional[torch.Tensor
 
 def zero_reduce_grad_shard(slices: Sequence[torch.Tensor], out: torch.Tensor,
                            nonfinite_flag: Optional[torch.Tensor] = None, stream=None) -> None:
-    """out = fp16(mean over ranks of the fp16 slices), fp32 sum in rank order."""
-    _need(out, torch.float16, "out")
+    """out = mean over ranks of the slices, fp32 sum in rank order, rounded
+    to out's format: float16, or bfloat16 (the bfloat16 variant)."""
+    half = out.dtype if out.dtype in (torch.float16, torch.bfloat16) else torch.float16
+    _need(out, half, "out")
     n = out.numel()
     nd = len(slices)
     if nd == 0 or nd > ZERO_MAX_SLICES:
         raise ValueError(f"need 1..{ZERO_MAX_SLICES} slices, got {nd}")
     ptrs = (ctypes.c_void_p * nd)()
     for r, s in enumerate(slices):
-        _need(s, torch.float16, f"slice {r}", out.device)
+        _need(s, half, f"slice {r}", out.device)
         if s.numel() != n:
             raise ValueError(f"slice {r} has {s.numel()} elements, out has {n}")
         ptrs[r] = s.data_ptr()
     f = _flag_ptr(nonfinite_flag, "nonfinite_flag", out.device)
-    _check("zero_reduce_grad_shard",
-           _lib.zero_reduce_grad_shard(ptrs, nd, n, out.data_ptr(), f, _stream_handle(stream)))
+    fn = "zero_reduce_grad_shard_bf16" if half == torch.bfloat16 else "zero_reduce_grad_shard"
+    _check(fn, getattr(_lib, fn)(ptrs, nd, n, out.data_ptr(), f, _stream_handle(stream)))
 
 
 def zero_reduce_adam_step(slices: Sequence[torch.Tensor], param: torch.Tensor,
