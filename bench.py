@@ -66,7 +66,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="flat_7p5b_nd64",
                     choices=["flat_7p5b_nd64", "flat_7p5b_nd8", "gpt2_xl", "llama_7b", "tiny_flat"])
     ap.add_argument("--fused", action="store_true",
