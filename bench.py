@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--bf16", action="store_true",
                     help="the bfloat16 variant: bfloat16 parameters, gradients and slices "
                          "(fp32 master, m, v as before)")
+    ap.add_argument("--list-layout", choices=["flat", "separate"], default="flat",
+                    help="tensor-list workloads: views into five flattened buffers (the "
+                         "state a ZeRO rank holds) or five allocations per tensor")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="elements per chunk of the Adam plan (0: library default)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
@@ -118,11 +121,35 @@ def copy_calibration(nbytes: int, reps: int) -> None:
           flush=True)
 
 
+def plain_copy(stream, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """A plain stream for context: torch's device-to-device copy of nbytes
+    (read nbytes, write nbytes; the runtime's copy kernel), timed with HIP
+    events on `stream` after the timed region.  Not the roofline's
+    denominator, which is the published 8 TB/s."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    b.synchronize()
+    s = a.elapsed_time(b) / reps / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * nbytes / s / 1e9
+    return {"kernel": "torch device-to-device copy (__amd_rocclr_copyBuffer)", "bytes_per_launch": 2 * nbytes,
+            "avg_us": s * 1e6, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+
+
 class Step:
     """Device state and the launches of one step for a workload."""
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
-                 offload_threads=0, bf16=False):
+                 offload_threads=0, bf16=False, list_layout="flat"):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         half = torch.bfloat16 if bf16 else torch.float16
@@ -146,7 +173,7 @@ class Step:
                 W.device_fill_grads(wl, self.tensors, 1)
         else:
             self.layout = None
-            self.tensors = W.device_list_state(wl, half=half)
+            self.tensors = W.device_list_state(wl, half=half, layout=list_layout)
             W.device_fill_grads(wl, self.tensors, 1)
         self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors], chunk_elems)
         self.n_params = self.plan.stats()["n_params"]
@@ -314,7 +341,7 @@ def main():
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
-                args.offload_threads, args.bf16)
+                args.offload_threads, args.bf16, args.list_layout)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -347,6 +374,7 @@ def main():
     traffic = measured_traffic(dom, args.workload)
     value = step.n_params * args.steps / wall
     bytes_per_step = sum(b for _, _, b in ks)
+    copy = plain_copy(stream)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
     cfg = {"workload": args.workload + ("+fused" if step.fused else "") +
@@ -355,6 +383,7 @@ def main():
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
+           "list_layout": args.list_layout if len(step.wl.tensors) > 1 else None,
            "chunk_elems": step.plan.stats()["chunk_elems"],
            "kernels_per_step": [k for k, _, _ in ks],
            "alg_bytes_per_step": bytes_per_step,
@@ -382,6 +411,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in s.items() if kk != "total_s"} for k, s in kstats.items()},
         "cpu_baseline": cpu,
+        "plain_copy": copy,
     }
     if offload is not None:
         out["offload"] = offload

@@ -73,16 +73,20 @@ def _check_all(got, ref, what):
     return inexact
 
 
-@pytest.mark.parametrize("name", ["gpt2_xl", "llama_7b"])
-def test_tensor_list_workload(zs, name):
+@pytest.mark.parametrize("name,layout", [("gpt2_xl", "flat"), ("gpt2_xl", "separate"),
+                                         ("llama_7b", "flat"), ("llama_7b", "separate")])
+def test_tensor_list_workload(zs, name, layout):
     """GPT-2-XL (580 tensors, 1.56e9 params) and Llama-7B (291 tensors,
     6.74e9 params, 108 GB of state in HBM): 5 warm-up steps, then step 6,
-    one plan over the whole list, N_d = 1."""
+    one plan over the whole list, N_d = 1.  Both caller layouts: views into
+    five flattened buffers, and five allocations per tensor."""
     import torch
     wl = W.WORKLOADS[name]
-    say(f"{name}: {len(wl.tensors)} tensors, {wl.n_params} params")
+    say(f"{name} ({layout}): {len(wl.tensors)} tensors, {wl.n_params} params")
     assert zs.zero_state_bytes(0, wl.n_params, 1) == 16 * wl.n_params
-    tensors = W.device_list_state(wl)
+    tensors = W.device_list_state(wl, layout=layout)
+    if layout == "flat":
+        assert tensors[1].w.data_ptr() == tensors[0].w.data_ptr() + 4 * tensors[0].n
     plan = zs.zero_plan_create([t.arrays() for t in tensors])
     st = plan.stats()
     assert st["n_params"] == wl.n_params and st["vector_elems"] == wl.n_params

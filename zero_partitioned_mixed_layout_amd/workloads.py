@@ -237,10 +237,13 @@ class DeviceTensor:
     16-bit dtype of the parameter and gradient (torch.float16 by default;
     torch.bfloat16 for the bfloat16 variant)."""
 
-    def __init__(self, n: int, device, param=None, half=None):
+    def __init__(self, n: int, device, param=None, half=None, views=None):
         import torch
         half = half or torch.float16
         self.n = n
+        if views is not None:                 # five existing arrays of n elements
+            self.p, self.g, self.w, self.m, self.v = views
+            return
         self.p = param if param is not None else torch.zeros(n, dtype=half, device=device)
         self.g = torch.zeros(n, dtype=half, device=device)
         self.w = torch.empty(n, dtype=torch.float32, device=device)
@@ -251,11 +254,35 @@ class DeviceTensor:
         return (self.p, self.g, self.w, self.m, self.v)
 
 
-def device_list_state(wl: Workload, device="cuda", half=None) -> List[DeviceTensor]:
-    """One DeviceTensor per tensor of a list workload; master ~ N(0, 0.02)."""
-    out = []
+LIST_LAYOUTS = ("flat", "separate")
+
+
+def device_list_state(wl: Workload, device="cuda", half=None,
+                      layout="flat") -> List[DeviceTensor]:
+    """One DeviceTensor per tensor of a list workload; master ~ N(0, 0.02).
+
+    layout "flat": the flattened state a ZeRO rank holds -- five buffers of
+    n_params elements (fp16 parameters, fp16 gradients, fp32 master, m, v),
+    each tensor a view at its running offset, in list order.
+    layout "separate": five allocations per tensor, in the order p, g, w, m,
+    v, as a model that owns its parameters one tensor at a time holds them.
+    Both draw the same values from the same seeds."""
+    import torch
+    if layout not in LIST_LAYOUTS:
+        raise ValueError(f"layout must be one of {LIST_LAYOUTS}")
+    half = half or torch.float16
+    bufs = None
+    if layout == "flat":
+        total = wl.n_params
+        bufs = [torch.zeros(total, dtype=dt, device=device)
+                for dt in (half, half, torch.float32, torch.float32, torch.float32)]
+    out, off = [], 0
     for k, (_, n) in enumerate(wl.tensors):
-        t = DeviceTensor(n, device, half=half)
+        if bufs is None:
+            t = DeviceTensor(n, device, half=half)
+        else:
+            t = DeviceTensor(n, device, half=half, views=[b[off:off + n] for b in bufs])
+            off += n
         device_normal(n, MASTER_STD, master_seed(wl.seed, k), None, device, out=t.w)
         out.append(t)
     return out
