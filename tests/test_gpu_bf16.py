@@ -119,7 +119,7 @@ def test_bf16_every_gradient_pattern(zs):
     plan.destroy()
 
 
-@pytest.mark.parametrize("nd", [1, 2, 3, 8, 16, 17, 64])
+@pytest.mark.parametrize("nd", [1, 2, 3, 8, 16, 17, 64, 256])
 @pytest.mark.parametrize("layout", ["aligned", "phase3", "odd"])
 def test_bf16_reduce_matches_oracle(zs, nd, layout):
     import torch

@@ -34,7 +34,7 @@ def zs():
     return zero_shard
 
 
-@pytest.mark.parametrize("nd", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("nd", [1, 2, 3, 8, 64, 256])
 def test_gather_matches_oracle(zs, nd):
     """Shards at every source phase (so each takes its own access width),
     ragged lengths, and one shard already in place in the full buffer."""

@@ -1,0 +1,176 @@
+"""GPU parity past 2^32 elements in one array: the Adam step over a single
+tensor of 2^32 + 1027 elements (under the default chunk and under the
+largest chunk the plan accepts, 2^24), the reduce and the fused step over
+2^32 + 1027 elements, and the gather into a 2^32 + 1034-element buffer.
+Element indices, chunk starts and tile bases must all be 64-bit for these
+to pass.  The oracle recomputes sampled elements one by one from the same
+seeded inputs (both ends of every array, the 2^32 boundary, random
+positions); the gather, a concatenation, is also compared whole on the
+device.  Each case prints its name and sizes before it touches the GPU."""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import check16, check32, host16, host32
+from zero_partitioned_mixed_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+HP = dict(W.ADAM_HP)
+N = (1 << 32) + 1027          # vector body n - 3, then a 3-element tail
+BOUNDARY = np.arange((1 << 32) - 2048, (1 << 32) + 1027, dtype=np.int64)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_partitioned_mixed_layout_amd import zero_shard
+    torch.cuda.set_device(0)
+    return zero_shard
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    import torch
+    gc.collect()
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def _samples(n, seed):
+    return W.sample_indices(n, 60_000, seed, must=BOUNDARY[BOUNDARY < n])
+
+
+def _at16(t, d):
+    return host16(t.index_select(0, d))
+
+
+def _at32(t, d):
+    return host32(t.index_select(0, d))
+
+
+def _bit_exact(got, ref, what):
+    p, w, m, v = got
+    rp, rw, rm, rv = ref
+    res = [check16(p, rp, what + " param"), check32(w, rw, what + " master"),
+           check32(m, rm, what + " m"), check32(v, rv, what + " v")]
+    return sum(r["not_bit_exact"] for r in res)
+
+
+def test_adam_one_tensor_past_2_32(zs):
+    """Two steps over one 2^32 + 1027-element tensor: t = 1 under the default
+    chunk, t = 2 under 2^24-element chunks (257 of them)."""
+    import torch
+    say(f"adam n={N}: allocating 16 B/param ({16 * N / 1e9:.1f} GB)")
+    t_ = W.DeviceTensor(N, "cuda")
+    W.device_normal(N, W.MASTER_STD, 91, None, out=t_.w)
+    idx = _samples(N, 91)
+    d = torch.from_numpy(idx).cuda()
+    w0 = _at32(t_.w, d)
+    plans = [zs.zero_plan_create([t_.arrays()]), zs.zero_plan_create([t_.arrays()], 1 << 24)]
+    st = plans[1].stats()
+    assert st["n_chunks"] == (N + (1 << 24) - 1) >> 24 == 257
+    assert st["n_params"] == N and st["vector_elems"] == N - 3 and st["scalar_elems"] == 3
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grads = []
+    for t, plan in ((1, plans[0]), (2, plans[1])):
+        W.device_normal(N, W.GRAD_STD, 910 + t, None, out=t_.g)
+        grads.append(_at16(t_.g, d))
+        say(f"adam n={N} t={t} chunk={plan.stats()['chunk_elems']}")
+        zs.zero_adam_step(plan, zs.AdamHParams(**HP), t, flag)
+    torch.cuda.synchronize()
+    got = (_at16(t_.p, d), _at32(t_.w, d), _at32(t_.m, d), _at32(t_.v, d))
+    k = idx.size
+    rp, rw = np.zeros(k, np.uint16), w0.copy()
+    rm, rv = np.zeros(k, np.float32), np.zeros(k, np.float32)
+    rflag = 0
+    for t, g in enumerate(grads, start=1):
+        rflag |= oracle.adam_step(g, rp, rw, rm, rv, t=t, **HP)
+    assert int(flag.item()) == rflag == 0
+    assert _bit_exact(got, (rp, rw, rm, rv), f"adam n={N}") == 0
+    for p in plans:
+        p.destroy()
+
+
+def test_reduce_past_2_32(zs):
+    """Three fp16 slices of 2^32 + 1027 elements averaged into the shard."""
+    import torch
+    nd = 3
+    say(f"reduce nd={nd} n={N}")
+    slices = [W.device_normal(N, W.GRAD_STD, 920 + r, torch.float16) for r in range(nd)]
+    out = torch.zeros(N, dtype=torch.float16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx = _samples(N, 92)
+    d = torch.from_numpy(idx).cuda()
+    hs = [_at16(s, d) for s in slices]
+    zs.zero_reduce_grad_shard(slices, out, flag)
+    torch.cuda.synchronize()
+    ref, rflag = oracle.reduce_grad(hs)
+    res = check16(_at16(out, d), ref, f"reduce nd={nd} n={N}")
+    assert res["not_bit_exact"] == 0
+    assert int(flag.item()) == rflag == 0
+
+
+def test_fused_past_2_32(zs):
+    """The fused reduce + Adam step over 2^32 + 1027 elements, N_d = 2, with
+    the fp16 gradient output."""
+    import torch
+    nd = 2
+    say(f"fused nd={nd} n={N}")
+    slices = [W.device_normal(N, W.GRAD_STD, 930 + r, torch.float16) for r in range(nd)]
+    p = torch.zeros(N, dtype=torch.float16, device="cuda")
+    gout = torch.zeros(N, dtype=torch.float16, device="cuda")
+    w = W.device_normal(N, W.MASTER_STD, 93, torch.float32)
+    m = torch.zeros(N, dtype=torch.float32, device="cuda")
+    v = torch.zeros(N, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx = _samples(N, 93)
+    d = torch.from_numpy(idx).cuda()
+    hs = [_at16(s, d) for s in slices]
+    w0 = _at32(w, d)
+    zs.zero_reduce_adam_step(slices, p, w, m, v, zs.AdamHParams(**HP), 1, grad_out=gout,
+                             nonfinite_flag=flag)
+    torch.cuda.synchronize()
+    g_ref, rflag = oracle.reduce_grad(hs)
+    k = idx.size
+    rp, rw = np.zeros(k, np.uint16), w0.copy()
+    rm, rv = np.zeros(k, np.float32), np.zeros(k, np.float32)
+    aflag = oracle.adam_step(g_ref, rp, rw, rm, rv, t=1, **HP)
+    got = (_at16(p, d), _at32(w, d), _at32(m, d), _at32(v, d))
+    assert _bit_exact(got, (rp, rw, rm, rv), f"fused n={N}") == 0
+    assert check16(_at16(gout, d), g_ref, f"fused n={N} grad")["not_bit_exact"] == 0
+    assert int(flag.item()) == (rflag | aflag) == 0
+
+
+def test_gather_past_2_32(zs):
+    """Two shards of 2^31 + 517 elements into a 2^32 + 1034-element buffer:
+    shard 0 already in place, shard 1 from its own allocation three elements
+    off a 16-byte boundary, so its copy crosses element 2^32 of the
+    buffer."""
+    import torch
+    nd, S = 2, (1 << 31) + 517
+    say(f"gather nd={nd} S={S} full={nd * S}")
+    full = torch.zeros(nd * S, dtype=torch.float16, device="cuda")
+    other = torch.zeros(S + 8, dtype=torch.float16, device="cuda")[3:3 + S]
+    W.device_normal(S, W.GRAD_STD, 940, None, out=full[:S])
+    W.device_normal(S, W.GRAD_STD, 941, None, out=other)
+    cross = (1 << 32) - S
+    idx = W.sample_indices(S, 60_000, 94, must=np.arange(cross - 1024, cross + 1024))
+    d = torch.from_numpy(idx).cuda()
+    h0, h1 = _at16(full[:S], d), _at16(other, d)
+    zs.zero_gather_shards([full[:S], other], full)
+    torch.cuda.synchronize()
+    want = oracle.gather([h0, h1])
+    got = np.concatenate([_at16(full[:S], d), _at16(full[S:], d)])
+    assert np.array_equal(got, want)
+    # a concatenation: the whole copied shard, compared bit for bit on the device
+    assert torch.equal(full[S:].view(torch.int16), other.view(torch.int16))
