@@ -279,10 +279,30 @@ def cpu_baseline(step, sample_n: int, min_seconds: float):
             dt = time.perf_counter() - t0
             if dt >= min_seconds or steps >= 8:
                 break
+    # one more step over the first partition alone, on this thread
+    t1 = time.perf_counter()
+    part(bounds[0], steps + 1)
+    dt1 = time.perf_counter() - t1
+    n1 = bounds[0][1] - bounds[0][0]
     what = ("reduce of %d fp16 slices + Adam step" % step.wl.nd) if sl is not None else "Adam step"
+    per_param = 28 + ((2 * step.wl.nd + 2) if sl is not None else 0)
     return {"value": n * steps / dt, "unit": "params/s", "cores": T, "kind": "oracle",
+            "gbps": per_param * n * steps / dt / 1e9, "alg_bytes_per_param": per_param,
+            "single_thread_value": n1 / dt1, "cpu_model": cpu_model(),
             "sample": f"first {n} elements of the shard: {steps} x ({what}), {T} host threads, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall; then one step over the first {n1} elements on one "
+                      f"thread, {dt1:.2f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 PCIE_PEAK_GBPS = 128.0  # PCIe Gen5 x16 host link, both directions together
