@@ -321,12 +321,12 @@ int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shar
  * same order as zero_adam_step, so the results are bit-identical.
  * grad_f16: n fp16 (read); param_f16: n fp16 (written); master, m, v: n fp32
  * each, updated in place; all host memory, borrowed.  threads: 0 for
- * min(16, hardware threads), else the number of threads to use (the calling
- * thread is one of them).  nonfinite_flag: NULL or a host int32 that 1 is
+ * min(16, hardware threads), else the number of threads to use, at most
+ * 1024 (the calling thread is one of them).  nonfinite_flag: NULL or a host int32 that 1 is
  * OR-ed into if any gradient is infinite or NaN.  Synchronous.
  * Errors: EINVAL (NULL or misaligned arrays, written arrays overlapping,
- * bad hyperparameters as zero_adam_scalars); EOVERFLOW; ENOTSUP (no AVX2 or
- * F16C); ENOMEM (threads could not start).
+ * threads above 1024, bad hyperparameters as zero_adam_scalars); EOVERFLOW;
+ * ENOTSUP (no AVX2 or F16C); ENOMEM (threads could not start).
  */
 int zero_adam_step_host(const void *grad_f16, void *param_f16, float *master, float *m,
                         float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,

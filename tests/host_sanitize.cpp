@@ -88,6 +88,14 @@ int main() {
             EXPECT(rc == 0 || rc == ZERO_ENOTSUP);
         }
     }
+    {   // the thread bound: 1025 is rejected, 1024 runs
+        std::vector<uint16_t> g(100, 0x3C00), p(100);
+        std::vector<float> w(100, 1.f), m(100), v(100);
+        EXPECT(zero_adam_step_host(g.data(), p.data(), w.data(), m.data(), v.data(), 100, &hp, 1, 1025, nullptr) == ZERO_EINVAL);
+        EXPECT(zero_adam_step_host(g.data(), p.data(), w.data(), m.data(), v.data(), 100, &hp, 1, 1024, nullptr) == 0);
+        zero_offload *o = nullptr;
+        EXPECT(zero_offload_create(0, 1025, &o) == ZERO_EINVAL && o == nullptr);
+    }
     for (int st = -7; st <= 1; st++) EXPECT(zero_status_str(st) != nullptr);
     printf("asan driver: %d failures\n", fails);
     return fails != 0;

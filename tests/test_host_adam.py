@@ -117,6 +117,10 @@ def test_rejects(zs):
         zs.zero_adam_step_host(g, p, w_odd, m, v, hp, 1)
     with pytest.raises(ValueError):
         zs.zero_adam_step_host(g[:10], p, w, m, v, hp, 1)
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_adam_step_host(g, p, w, m, v, hp, 1, threads=1025)   # above the bound
+    assert e.value.status == -1
+    zs.zero_adam_step_host(g, p, w, m, v, hp, 1, threads=1024)       # at the bound
     # n = 0 does nothing
     e16, e32 = np.zeros(0, np.uint16), np.zeros(0, np.float32)
     zs.zero_adam_step_host(e16, e16.copy(), e32, e32.copy(), e32.copy(), hp, 1)

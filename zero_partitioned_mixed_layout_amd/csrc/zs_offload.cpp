@@ -103,23 +103,25 @@ __attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, ui
     return bad != 0;
 }
 
+// Most host threads an update may use.
+constexpr uint32_t kMaxHostThreads = 1024;
+
 // A fixed set of worker threads; run(f) calls f(0..parts-1) with the calling
-// thread taking part 0 and returns when every part is done.
+// thread taking part 0 and returns when every part is done.  If a thread
+// cannot start, the ones already started are stopped and joined before the
+// exception leaves the constructor.
 class Pool {
 public:
     explicit Pool(uint32_t parts) : parts_(parts) {
-        for (uint32_t k = 1; k < parts; k++)
-            threads_.emplace_back([this, k] { work(k); });
-    }
-    ~Pool() {
-        {
-            std::lock_guard<std::mutex> lk(mu_);
-            stop_ = true;
+        try {
+            for (uint32_t k = 1; k < parts; k++)
+                threads_.emplace_back([this, k] { work(k); });
+        } catch (...) {
+            shutdown();
+            throw;
         }
-        cv_.notify_all();
-        for (std::thread &t : threads_)
-            t.join();
     }
+    ~Pool() { shutdown(); }
     uint32_t parts() const { return parts_; }
     void run(const std::function<void(uint32_t)> &f) {
         {
@@ -136,6 +138,17 @@ public:
     }
 
 private:
+    void shutdown() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (std::thread &t : threads_)
+            if (t.joinable())
+                t.join();
+        threads_.clear();
+    }
     void work(uint32_t k) {
         uint64_t seen = 0;
         for (;;) {
@@ -218,6 +231,8 @@ extern "C" int zero_adam_step_host(const void *grad_f16, void *param_f16, float 
     int rc = zero_adam_scalars(hp, t, s);
     if (rc != ZERO_OK)
         return rc;
+    if (threads > kMaxHostThreads)
+        return ZERO_EINVAL;
     rc = check_host_arrays(grad_f16, param_f16, master, m, v, n);
     if (rc != ZERO_OK)
         return rc;
@@ -287,7 +302,7 @@ extern "C" int zero_offload_create(uint64_t chunk_elems, uint32_t threads, zero_
         return ZERO_EINVAL;
     if (chunk_elems == 0)
         chunk_elems = zs::kOffloadChunk;
-    if (chunk_elems % 8 != 0 || chunk_elems > (1ull << 32))
+    if (chunk_elems % 8 != 0 || chunk_elems > (1ull << 32) || threads > kMaxHostThreads)
         return ZERO_EINVAL;
     if (!cpu_has_avx2_f16c())
         return ZERO_ENOTSUP;
