@@ -80,6 +80,8 @@ def parse():
                     help="ZeRO-Offload: fp32 master, m, v in host memory and the Adam update "
                          "on the host CPU (zero_offload_step); the fp16 gradient and "
                          "parameters stay on the GPU")
+    ap.add_argument("--offload-chunk", type=int, default=0,
+                    help="elements per offload pipeline chunk (0: library default)")
     ap.add_argument("--offload-threads", type=int, default=0,
                     help="host threads of the offload update (0: min(16, hardware threads))")
     ap.add_argument("--bf16", action="store_true",
@@ -149,7 +151,7 @@ class Step:
     """Device state and the launches of one step for a workload."""
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
-                 offload_threads=0, bf16=False, list_layout="flat"):
+                 offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         half = torch.bfloat16 if bf16 else torch.float16
@@ -186,7 +188,7 @@ class Step:
             sh = self.tensors[0]
             self.host = [x.cpu().numpy().copy() for x in (sh.w, sh.m, sh.v)]
             self.hflag = __import__("numpy").zeros(1, dtype="int32")
-            self.offload = zs.zero_offload_create(0, offload_threads)
+            self.offload = zs.zero_offload_create(offload_chunk, offload_threads)
             self.offload_threads_used = offload_threads or min(16, os.cpu_count() or 1)
             self.fused = False
         self.gather = gather and self.rows is not None
@@ -361,7 +363,7 @@ def main():
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
-                args.offload_threads, args.bf16, args.list_layout)
+                args.offload_threads, args.bf16, args.list_layout, args.offload_chunk)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -417,7 +419,8 @@ def main():
         offload = {"avg_ms": o["avg_us"] / 1e3, "params_per_s": step.n_params / (o["avg_us"] / 1e6),
                    "pcie_bytes_per_param": 4, "pcie_gbps": o["gbps"],
                    "host_state_gbps": 24 * step.n_params / (o["avg_us"] / 1e6) / 1e9,
-                   "threads": step.offload_threads_used, "pinned_copy": rates}
+                   "threads": step.offload_threads_used,
+                   "chunk_elems": args.offload_chunk or 4 << 20, "pinned_copy": rates}
         if dom == "zero_offload_step":
             roofline = {"bound": "pcie", "kernel": dom, "achieved": o["gbps"],
                         "peak": PCIE_PEAK_GBPS, "unit": "GB/s",

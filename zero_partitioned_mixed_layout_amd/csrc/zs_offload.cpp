@@ -77,6 +77,10 @@ __attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, ui
     const __m128i expo = _mm_set1_epi16(0x7C00);
     int bad = 0;
     uint64_t i = 0;
+    // The fp16 parameters are written only: streamed past the caches when
+    // 16-byte aligned (no read for ownership of their lines; in the offload
+    // pipeline the staging slot is read next by the copy engine, not the CPU).
+    const bool p_aligned = ((uintptr_t)p16 & 15) == 0;
     for (; i + 8 <= n; i += 8) {
         const __m128i gh = _mm_loadu_si128(reinterpret_cast<const __m128i *>(g16 + i));
         bad |= _mm_movemask_epi8(_mm_cmpeq_epi16(_mm_and_si128(gh, expo), expo));
@@ -93,9 +97,13 @@ __attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, ui
         _mm256_storeu_ps(m + i, m_new);
         _mm256_storeu_ps(v + i, v_new);
         _mm256_storeu_ps(w + i, w_new);
-        _mm_storeu_si128(reinterpret_cast<__m128i *>(p16 + i),
-                         _mm256_cvtps_ph(w_new, _MM_FROUND_TO_NEAREST_INT));
+        const __m128i ph = _mm256_cvtps_ph(w_new, _MM_FROUND_TO_NEAREST_INT);
+        if (p_aligned)
+            _mm_stream_si128(reinterpret_cast<__m128i *>(p16 + i), ph);
+        else
+            _mm_storeu_si128(reinterpret_cast<__m128i *>(p16 + i), ph);
     }
+    _mm_sfence(); // the streamed parameters are visible before this range returns
     for (; i < n; i++) {
         bad |= (g16[i] & 0x7C00u) == 0x7C00u;
         p16[i] = adam_elem_host(g16[i], w[i], m[i], v[i], c);
