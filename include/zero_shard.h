@@ -244,6 +244,9 @@ int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp,
  * nonfinite_flag: NULL or a device int32; 1 is OR-ed into it if any output
  *   is infinite or NaN.
  * Asynchronous; allocates nothing.  n = 0 launches nothing.
+ * Fastest with every slice 16-byte aligned at the same phase as out; slices
+ * spaced an exact power of two apart (256 MiB, say) read about a fifth
+ * slower than with a few KiB more between them.
  * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not
  * 2-byte aligned, out overlapping a slice); EHIP.
  */
