@@ -389,6 +389,7 @@ def main():
         avg_s = sum(ms) / len(ms) / 1e3
         gbps = alg_bytes / avg_s / 1e9
         kstats[name] = {"avg_us": avg_s * 1e6, "min_us": min(ms) * 1e3,
+                        "median_us": sorted(ms)[len(ms) // 2] * 1e3,
                         "alg_bytes_per_launch": alg_bytes, "gbps": gbps,
                         "frac": gbps / HBM_PEAK_GBPS, "total_s": sum(ms) / 1e3}
     dom = max(kstats, key=lambda k: kstats[k]["total_s"])
