@@ -295,6 +295,21 @@ int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n
                           uint64_t t, int32_t *nonfinite_flag, void *stream);
 
 /*
+ * zero_reduce_adam_step_bf16 -- zero_reduce_adam_step with bfloat16
+ * slices, parameter and gradient output (fp32 master, m, v as before): the
+ * reduction of zero_reduce_grad_shard_bf16 followed by the update of
+ * zero_adam_step over a zero_plan_create_bf16 plan, bit-identical to those
+ * two calls in sequence ([DSZ] "Why parameter count is not training
+ * memory": BF16 setups keep different states; the variant keeps the whole
+ * 16-byte ledger).  Arguments, ownership and errors as
+ * zero_reduce_adam_step.
+ */
+int zero_reduce_adam_step_bf16(const void *const *slices_bf16, uint32_t nd, uint64_t n,
+                               void *param_bf16, float *master, float *m, float *v,
+                               void *grad_out_bf16, const zero_adam_hparams *hp,
+                               uint64_t t, int32_t *nonfinite_flag, void *stream);
+
+/*
  * zero_gather_shards -- the receive side of the all-gather of updated fp16
  * parameters: after it every rank holds the whole fp16 buffer, rank r's
  * shard at element r * shard_len ([16B] "The part that sounds too good:

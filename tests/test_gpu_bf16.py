@@ -205,3 +205,82 @@ def test_bf16_flat_7p5b_nd64_full_size(zs):
     del full, sh, buf, rows
     gc.collect()
     torch.cuda.empty_cache()
+
+
+# element offsets of ((even slices, odd slices), param, grad_out, master, m, v)
+# inside their buffers, and the access path of the fused kernel each selects
+FUSED_LAYOUTS = {
+    "aligned": ((0, 0), 0, 0, 0, 0, 0),   # 16-byte slice loads, no head
+    "phase2": ((2, 2), 2, 2, 2, 2, 2),    # 16-byte slice loads after a head of 6
+    "split": ((0, 4), 0, 0, 0, 0, 0),     # slices agree only mod 8 bytes: 8-byte loads
+    "odd": ((1, 1), 0, 0, 0, 0, 0),       # no common phase: single elements
+}
+
+
+def _fused_case(zs, n, nd, layout, with_gout, t, rng, inject=None):
+    import torch
+    so, po, go, wo, mo, vo = FUSED_LAYOUTS[layout]
+
+    def view(off, dt):
+        return torch.zeros(n + off + 8, dtype=dt, device="cuda")[off:off + n]
+
+    hs = [bf16_bits(rng.standard_normal(n) * 1e-3) for _ in range(nd)]
+    if inject is not None:
+        r, i, bits = inject
+        hs[r][i] = bits
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = (rng.random(n) * 1e-6).astype(np.float32)
+    ds = []
+    for r in range(nd):
+        b = view(so[r % 2], torch.bfloat16)
+        b.copy_(to_devbf(hs[r]))
+        ds.append(b)
+    p = view(po, torch.bfloat16)
+    gout = view(go, torch.bfloat16) if with_gout else None
+    w, m, v = view(wo, torch.float32), view(mo, torch.float32), view(vo, torch.float32)
+    w.copy_(to_dev32(w0))
+    m.copy_(to_dev32(m0))
+    v.copy_(to_dev32(v0))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_adam_step(ds, p, w, m, v, zs.AdamHParams(**HP), t, grad_out=gout,
+                             nonfinite_flag=flag)
+    g_ref, rflag = oracle.reduce_grad(hs, fmt="bf16")
+    ref = (np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy())
+    aflag = _step_ref(g_ref, *ref, t)
+    torch.cuda.synchronize()
+    what = f"bf16 fused n={n} nd={nd} {layout} gout={with_gout}"
+    inexact = _cmp((p, w, m, v), ref, what)
+    if with_gout:
+        inexact += check16(host16(gout), g_ref, what + " grad", fmt="bf16")["not_bit_exact"]
+    assert int(flag.item()) == (rflag | aflag)
+    return inexact, rflag | aflag
+
+
+@pytest.mark.parametrize("nd", [1, 3, 16, 17, 64, 256])
+@pytest.mark.parametrize("layout", list(FUSED_LAYOUTS))
+def test_bf16_fused_matches_oracle(zs, nd, layout):
+    """The fused reduce + Adam step in bfloat16 against the oracle's
+    bfloat16 reduce then its bfloat16 step: sizes from 1 to 70,001 (partial
+    tiles, heads and tails), each access path, with and without the
+    gradient output; every element."""
+    rng = np.random.default_rng(8000 + nd)
+    inexact = 0
+    for n in (1, 5, 511, 512, 513, 70001):
+        for with_gout in (False, True):
+            say(f"bf16 fused nd={nd} layout={layout} n={n} gout={with_gout}")
+            k, f = _fused_case(zs, n, nd, layout, with_gout, 3, rng)
+            inexact += k
+            assert f == 0
+    assert inexact == 0, f"{inexact} elements within tolerance but not bit-exact"
+
+
+@pytest.mark.parametrize("bits", [0x7F80, 0xFF80, 0x7FC0])
+def test_bf16_fused_nonfinite(zs, bits):
+    """An infinite or NaN bfloat16 slice value raises the flag and
+    propagates per IEEE at its position only (the oracle decides which
+    arrays turn non-finite)."""
+    rng = np.random.default_rng(bits)
+    say(f"bf16 fused inject {bits:#06x}")
+    k, f = _fused_case(zs, 4099, 5, "aligned", True, 2, rng, inject=(3, 2050, bits))
+    assert f == 1 and k == 0

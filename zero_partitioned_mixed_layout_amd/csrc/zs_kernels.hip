@@ -96,10 +96,6 @@ __device__ __forceinline__ bool bits_nonfinite(uint16_t b) {
     return (b & Fmt::kExp) == Fmt::kExp;
 }
 
-__device__ __forceinline__ bool f16_bits_nonfinite(uint16_t b) {
-    return bits_nonfinite<FmtF16>(b);
-}
-
 // Raise the non-finite flag once for this wave if any lane saw a non-finite
 // value.  The flag only ever goes from 0 to 1, so a wave that reads 1 (an
 // agent-coherent load) skips its atomic: with many waves seeing infinities
@@ -398,28 +394,30 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
 // ---------------------------------------------------------------------------
 // Fused stage-2 step over a flat shard: the reduce and the Adam step in one
 // pass.  Element i's gradient is exactly what zs_reduce_kernel would store
-// (fp32 sum of the slices in rank order, one division by nd, rounded to
-// fp16), widened again and fed to the same Adam element, so results are
-// bit-identical to the two kernels run in sequence; the fp16 gradient is
-// stored only if the caller asks for it.
+// (fp32 sum of the slices in rank order, one division by nd, rounded to the
+// 16-bit format), widened again and fed to the same Adam element, so results
+// are bit-identical to the two kernels run in sequence; the 16-bit gradient
+// is stored only if the caller asks for it.  Fmt: fp16 or bfloat16, for the
+// slices, the parameter and the gradient alike.
 // ---------------------------------------------------------------------------
 struct FlatState {
-    uint16_t *p;    // fp16 parameter (written)
+    uint16_t *p;    // 16-bit parameter (written)
     float *w, *m, *v;
-    uint16_t *gout; // fp16 reduced gradient (written), or null
+    uint16_t *gout; // 16-bit reduced gradient (written), or null
 };
 
+template <class Fmt>
 __device__ __forceinline__ void fused_single(const SliceArgs &s, uint32_t nd, uint64_t i,
                                              float count, const FlatState &F,
                                              const AdamConsts &c, int &bad) {
-    const _Float16 gh = (_Float16)(reduce_single(s, nd, i) / count);
+    const typename Fmt::T gh = (typename Fmt::T)(reduce_single<Fmt>(s, nd, i) / count);
     uint16_t gb;
     memcpy(&gb, &gh, 2);
-    bad |= f16_bits_nonfinite(gb);
+    bad |= bits_nonfinite<Fmt>(gb);
     if (F.gout != nullptr)
         as_global(F.gout)[i] = gb;
     float w = as_global(F.w)[i], m = as_global(F.m)[i], v = as_global(F.v)[i];
-    const _Float16 p = adam_elem((float)gh, w, m, v, c);
+    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c);
     as_global(F.w)[i] = w;
     as_global(F.m)[i] = m;
     as_global(F.v)[i] = v;
@@ -431,15 +429,16 @@ __device__ __forceinline__ void fused_single(const SliceArgs &s, uint32_t nd, ui
 // Adds slices r0 .. r0+B-1 (rank order) at the Q four-element groups
 // starting at i[0..Q-1] into acc; all B*Q loads are issued before the first
 // add.  With `first`, slice r0 initialises the sums.
-template <int B, int Q>
+template <class Fmt, int B, int Q>
 __device__ __forceinline__ void fused_batch(const SliceArgs &s, uint32_t r0, const uint64_t (&i)[Q],
                                             bool first, f32x4 (&acc)[Q]) {
-    f16x4 x[B][Q];
+    typedef typename Fmt::V4 hv;
+    hv x[B][Q];
 #pragma unroll
     for (int q = 0; q < B; q++)
 #pragma unroll
         for (int k = 0; k < Q; k++)
-            x[q][k] = ld_nt(reinterpret_cast<const f16x4 *>(s.p[r0 + q] + i[k]));
+            x[q][k] = ld_nt(reinterpret_cast<const hv *>(s.p[r0 + q] + i[k]));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < B; q++)
@@ -454,7 +453,7 @@ __device__ __forceinline__ void fused_batch(const SliceArgs &s, uint32_t r0, con
 // loaded first, then the slices in batches of 16, 8, 4 and 1; then the
 // reduced gradient,
 // the update and the stores.
-template <int Q>
+template <class Fmt, int Q>
 __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
                                              const uint64_t (&i)[Q], float count,
                                              const FlatState &F, const AdamConsts &c, int &bad) {
@@ -469,35 +468,35 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
     f32x4 acc[Q];
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
-        fused_batch<16, Q>(s, r, i, r == 0, acc);
+        fused_batch<Fmt, 16, Q>(s, r, i, r == 0, acc);
     for (; r + 8 <= nd; r += 8)
-        fused_batch<8, Q>(s, r, i, r == 0, acc);
+        fused_batch<Fmt, 8, Q>(s, r, i, r == 0, acc);
     for (; r + 4 <= nd; r += 4)
-        fused_batch<4, Q>(s, r, i, r == 0, acc);
+        fused_batch<Fmt, 4, Q>(s, r, i, r == 0, acc);
     for (; r < nd; r++)
-        fused_batch<1, Q>(s, r, i, r == 0, acc);
+        fused_batch<Fmt, 1, Q>(s, r, i, r == 0, acc);
 #pragma unroll
     for (int k = 0; k < Q; k++) {
-        f16x4 g, p;
+        typename Fmt::V4 g, p;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            g[j] = (_Float16)(acc[k][j] / count);
-            const _Float16 gj = g[j];
+            g[j] = (typename Fmt::T)(acc[k][j] / count);
+            const typename Fmt::T gj = g[j];
             uint16_t gb;
             memcpy(&gb, &gj, 2);
-            bad |= f16_bits_nonfinite(gb);
+            bad |= bits_nonfinite<Fmt>(gb);
             float ww = w[k][j], mm = m[k][j], vv = v[k][j];
-            p[j] = adam_elem((float)gj, ww, mm, vv, c);
+            p[j] = adam_elem<Fmt>((float)gj, ww, mm, vv, c);
             w[k][j] = ww;
             m[k][j] = mm;
             v[k][j] = vv;
         }
         if (F.gout != nullptr)
-            st_nt(g, reinterpret_cast<f16x4 *>(F.gout + i[k]));
+            st_nt(g, reinterpret_cast<typename Fmt::V4 *>(F.gout + i[k]));
         st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
         st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
         st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
-        st_nt(p, reinterpret_cast<f16x4 *>(F.p + i[k]));
+        st_nt(p, reinterpret_cast<typename Fmt::V4 *>(F.p + i[k]));
     }
 }
 
@@ -510,6 +509,7 @@ extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
 // instruction, as zs_reduce_kernel), the fp16 gradients go through LDS to
 // the Adam tile's mapping (lane L: 4L..4L+3 and kTile/2+4L..), and the
 // update runs there.  The fp32 state loads are issued first.
+template <class Fmt>
 __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uint64_t lo,
                                             uint32_t lane, float count, const FlatState &F,
                                             const AdamConsts &c, int &bad) {
@@ -526,44 +526,46 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
     float acc[8];
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
-        reduce_batch<8, 16>(s, r, j, r == 0, acc);
+        reduce_batch<8, 16, Fmt>(s, r, j, r == 0, acc);
     for (; r + 8 <= nd; r += 8)
-        reduce_batch<8, 8>(s, r, j, r == 0, acc);
+        reduce_batch<8, 8, Fmt>(s, r, j, r == 0, acc);
     for (; r + 4 <= nd; r += 4)
-        reduce_batch<8, 4>(s, r, j, r == 0, acc);
+        reduce_batch<8, 4, Fmt>(s, r, j, r == 0, acc);
     for (; r < nd; r++)
-        reduce_batch<8, 1>(s, r, j, r == 0, acc);
-    f16x8 g8;
+        reduce_batch<8, 1, Fmt>(s, r, j, r == 0, acc);
+    typedef typename Fmt::V8 hv8;
+    typedef typename Fmt::V4 hv4;
+    hv8 g8;
 #pragma unroll
     for (int q = 0; q < 8; q++)
-        g8[q] = (_Float16)(acc[q] / count);
-    reinterpret_cast<f16x8 *>(zs_lds)[lane] = g8;
+        g8[q] = (typename Fmt::T)(acc[q] / count);
+    reinterpret_cast<hv8 *>(zs_lds)[lane] = g8;
     __syncthreads(); // one wave per workgroup: orders the LDS write and reads
-    f16x4 g[2];
-    g[0] = reinterpret_cast<const f16x4 *>(zs_lds)[lane];
-    g[1] = reinterpret_cast<const f16x4 *>(zs_lds)[kWave + lane];
+    hv4 g[2];
+    g[0] = reinterpret_cast<const hv4 *>(zs_lds)[lane];
+    g[1] = reinterpret_cast<const hv4 *>(zs_lds)[kWave + lane];
     __syncthreads(); // the next tile of this workgroup rewrites the buffer
 #pragma unroll
     for (int k = 0; k < 2; k++) {
-        f16x4 p;
+        hv4 p;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const _Float16 gj = g[k][q];
+            const typename Fmt::T gj = g[k][q];
             uint16_t gb;
             memcpy(&gb, &gj, 2);
-            bad |= f16_bits_nonfinite(gb);
+            bad |= bits_nonfinite<Fmt>(gb);
             float ww = w[k][q], mm = m[k][q], vv = v[k][q];
-            p[q] = adam_elem((float)gj, ww, mm, vv, c);
+            p[q] = adam_elem<Fmt>((float)gj, ww, mm, vv, c);
             w[k][q] = ww;
             m[k][q] = mm;
             v[k][q] = vv;
         }
         if (F.gout != nullptr)
-            st_nt(g[k], reinterpret_cast<f16x4 *>(F.gout + i[k]));
+            st_nt(g[k], reinterpret_cast<hv4 *>(F.gout + i[k]));
         st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
         st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
         st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
-        st_nt(p, reinterpret_cast<f16x4 *>(F.p + i[k]));
+        st_nt(p, reinterpret_cast<hv4 *>(F.p + i[k]));
     }
 }
 
@@ -573,7 +575,7 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
 // of four (slices 8-byte aligned).  Both: the last partial tile four per
 // lane, then singly.  VEC = 1: the tile's elements one at a time.  Tiles
 // beyond the grid stride.
-template <int VEC>
+template <class Fmt, int VEC>
 __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t nd, uint64_t n,
                                                          uint32_t head, uint64_t ntiles,
                                                          FlatState F, AdamConsts c,
@@ -584,28 +586,28 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
     int bad = 0;
     for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
         if (b == 0 && lane < h)
-            fused_single(s, nd, lane, count, F, c, bad);
+            fused_single<Fmt>(s, nd, lane, count, F, c, bad);
         const uint64_t lo = h + b * kTile;
         const uint64_t hi = min(n, lo + kTile);
         if (VEC > 1) {
             if (hi - lo == kTile && VEC == 8) {
-                fused_tile8(s, nd, lo, lane, count, F, c, bad);
+                fused_tile8<Fmt>(s, nd, lo, lane, count, F, c, bad);
             } else if (hi - lo == kTile) {
                 const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
-                fused_groups<2>(s, nd, i, count, F, c, bad);
+                fused_groups<Fmt, 2>(s, nd, i, count, F, c, bad);
             } else {
                 const uint32_t nquads = (uint32_t)(hi - lo) / 4u;
                 for (uint32_t q = lane; q < nquads; q += kWave) {
                     const uint64_t i[1] = {lo + 4u * q};
-                    fused_groups<1>(s, nd, i, count, F, c, bad);
+                    fused_groups<Fmt, 1>(s, nd, i, count, F, c, bad);
                 }
                 const uint64_t t0 = lo + 4u * (uint64_t)nquads;
                 if (t0 + lane < hi)
-                    fused_single(s, nd, t0 + lane, count, F, c, bad);
+                    fused_single<Fmt>(s, nd, t0 + lane, count, F, c, bad);
             }
         } else {
             for (uint64_t k = lo + lane; k < hi; k += kWave)
-                fused_single(s, nd, k, count, F, c, bad);
+                fused_single<Fmt>(s, nd, k, count, F, c, bad);
         }
     }
     raise_flag(flag, bad);
@@ -905,10 +907,13 @@ extern "C" int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint3
     return reduce_grad_shard<FmtBF16>(slices_bf16, nd, n, out_bf16, nonfinite_flag, stream);
 }
 
-extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n,
-                                     void *param_f16, float *master, float *m, float *v,
-                                     void *grad_out_f16, const zero_adam_hparams *hp,
-                                     uint64_t t, int32_t *nonfinite_flag, void *stream) {
+namespace {
+
+template <class Fmt>
+int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, void *param_f16,
+                     float *master, float *m, float *v, void *grad_out_f16,
+                     const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
+                     void *stream) {
     if (!slices_f16 || nd == 0 || nd > ZERO_MAX_SLICES || !hp)
         return ZERO_EINVAL;
     float sc[8];
@@ -987,17 +992,36 @@ extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd,
     const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]};
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
-        hipLaunchKernelGGL(zs_fused_kernel<8>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           head, ntiles, F, c, nonfinite_flag);
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, head, ntiles, F, c, nonfinite_flag);
     else if (vec == 4)
-        hipLaunchKernelGGL(zs_fused_kernel<4>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           head, ntiles, F, c, nonfinite_flag);
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 4>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, head, ntiles, F, c, nonfinite_flag);
     else
-        hipLaunchKernelGGL(zs_fused_kernel<1>, dim3(grid), dim3(kWave), lds, st, args, nd, n,
-                           0u, ntiles, F, c, nonfinite_flag);
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 1>), dim3(grid), dim3(kWave), lds, st, args, nd,
+                           n, 0u, ntiles, F, c, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n,
+                                     void *param_f16, float *master, float *m, float *v,
+                                     void *grad_out_f16, const zero_adam_hparams *hp,
+                                     uint64_t t, int32_t *nonfinite_flag, void *stream) {
+    return reduce_adam_step<FmtF16>(slices_f16, nd, n, param_f16, master, m, v, grad_out_f16,
+                                    hp, t, nonfinite_flag, stream);
+}
+
+extern "C" int zero_reduce_adam_step_bf16(const void *const *slices_bf16, uint32_t nd,
+                                          uint64_t n, void *param_bf16, float *master, float *m,
+                                          float *v, void *grad_out_bf16,
+                                          const zero_adam_hparams *hp, uint64_t t,
+                                          int32_t *nonfinite_flag, void *stream) {
+    return reduce_adam_step<FmtBF16>(slices_bf16, nd, n, param_bf16, master, m, v,
+                                     grad_out_bf16, hp, t, nonfinite_flag, stream);
 }
 
 extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shard_len,

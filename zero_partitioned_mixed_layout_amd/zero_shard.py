@@ -87,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
         "zero_reduce_adam_step": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(_HParams), u64, vp, vp],
+        "zero_reduce_adam_step_bf16": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(_HParams), u64, vp, vp],
         "zero_adam_step_host": [vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, u32, vp],
         "zero_offload_create": [u64, u32, ctypes.POINTER(vp)],
         "zero_offload_destroy": [vp],
@@ -109,7 +111,8 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_reduce_grad_shard_bf16",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
-           "zero_reduce_adam_step", "zero_adam_step_host", "zero_offload_create",
+           "zero_reduce_adam_step", "zero_reduce_adam_step_bf16", "zero_adam_step_host",
+           "zero_offload_create",
            "zero_offload_destroy", "zero_offload_step", "zero_status_str")
 
 
@@ -334,12 +337,15 @@ def zero_reduce_adam_step(slices: Sequence[torch.Tensor], param: torch.Tensor,
                           master: torch.Tensor, m: torch.Tensor, v: torch.Tensor, hp, t: int,
                           grad_out: Optional[torch.Tensor] = None,
                           nonfinite_flag: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Reduce the fp16 slices and apply the Adam step in one pass over a flat
-    shard (bit-identical to zero_reduce_grad_shard then zero_adam_step)."""
+    """Reduce the 16-bit slices and apply the Adam step in one pass over a
+    flat shard (bit-identical to zero_reduce_grad_shard then
+    zero_adam_step).  param, the slices and grad_out are all float16 or all
+    bfloat16 (the bfloat16 variant)."""
     _need(master, torch.float32, "master")
     dev = master.device
     n = master.numel()
-    for x, dt, nm in ((param, torch.float16, "param"), (m, torch.float32, "m"),
+    half = param.dtype if param.dtype in (torch.float16, torch.bfloat16) else torch.float16
+    for x, dt, nm in ((param, half, "param"), (m, torch.float32, "m"),
                       (v, torch.float32, "v")):
         _need(x, dt, nm, dev)
         if x.numel() != n:
@@ -349,22 +355,22 @@ def zero_reduce_adam_step(slices: Sequence[torch.Tensor], param: torch.Tensor,
         raise ValueError(f"need 1..{ZERO_MAX_SLICES} slices, got {nd}")
     ptrs = (ctypes.c_void_p * nd)()
     for r, s in enumerate(slices):
-        _need(s, torch.float16, f"slice {r}", dev)
+        _need(s, half, f"slice {r}", dev)
         if s.numel() != n:
             raise ValueError(f"slice {r} has {s.numel()} elements, master has {n}")
         ptrs[r] = s.data_ptr()
     go = None
     if grad_out is not None:
-        _need(grad_out, torch.float16, "grad_out", dev)
+        _need(grad_out, half, "grad_out", dev)
         if grad_out.numel() != n:
             raise ValueError(f"grad_out has {grad_out.numel()} elements, master has {n}")
         go = grad_out.data_ptr()
     h = _hp(hp)
     f = _flag_ptr(nonfinite_flag, "nonfinite_flag", dev)
-    _check("zero_reduce_adam_step",
-           _lib.zero_reduce_adam_step(ptrs, nd, n, param.data_ptr(), master.data_ptr(),
-                                      m.data_ptr(), v.data_ptr(), go, ctypes.byref(h), int(t), f,
-                                      _stream_handle(stream)))
+    name = "zero_reduce_adam_step_bf16" if half == torch.bfloat16 else "zero_reduce_adam_step"
+    _check(name, getattr(_lib, name)(ptrs, nd, n, param.data_ptr(), master.data_ptr(),
+                                     m.data_ptr(), v.data_ptr(), go, ctypes.byref(h), int(t), f,
+                                     _stream_handle(stream)))
 
 
 def zero_gather_shards(shards: Sequence[torch.Tensor], full: torch.Tensor, stream=None) -> None:
