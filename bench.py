@@ -155,8 +155,6 @@ class Step:
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         half = torch.bfloat16 if bf16 else torch.float16
-        if bf16 and offload:
-            raise SystemExit("--offload runs in fp16 only")
         wl = W.WORKLOADS[name]
         self.wl = wl
         self.hp = zs.AdamHParams(**W.ADAM_HP)

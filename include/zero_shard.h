@@ -350,6 +350,18 @@ int zero_adam_step_host(const void *grad_f16, void *param_f16, float *master, fl
                         float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
                         uint32_t threads, int32_t *nonfinite_flag);
 
+/*
+ * zero_adam_step_host_bf16 -- zero_adam_step_host with bfloat16 gradient and
+ * parameter (the bfloat16 variant of the ledger): the gradient widened
+ * exactly, the parameter rounded to the nearest bfloat16, ties to even (a
+ * NaN stays a quiet NaN with its sign); bit-identical to zero_adam_step over
+ * a zero_plan_create_bf16 plan, NaN payloads aside.  Arguments, ownership
+ * and errors as zero_adam_step_host.
+ */
+int zero_adam_step_host_bf16(const void *grad_bf16, void *param_bf16, float *master, float *m,
+                             float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
+                             uint32_t threads, int32_t *nonfinite_flag);
+
 /* Opaque ZeRO-Offload pipeline: pinned staging, two copy streams and the
  * host threads of the CPU update. */
 typedef struct zero_offload zero_offload;
@@ -392,6 +404,16 @@ int zero_offload_step(zero_offload *off, const void *grad_f16, void *param_f16,
                       float *master, float *m, float *v, uint64_t n,
                       const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
                       void *stream);
+
+/*
+ * zero_offload_step_bf16 -- zero_offload_step with bfloat16 gradient and
+ * parameter on the device and the update of zero_adam_step_host_bf16 on the
+ * host.  Arguments, ownership and errors as zero_offload_step.
+ */
+int zero_offload_step_bf16(zero_offload *off, const void *grad_bf16, void *param_bf16,
+                           float *master, float *m, float *v, uint64_t n,
+                           const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
+                           void *stream);
 
 /* zero_status_str -- static description of a status code. */
 const char *zero_status_str(int status);

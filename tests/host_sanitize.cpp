@@ -86,6 +86,8 @@ int main() {
             int32_t flag = 0;
             int rc = zero_adam_step_host(g.data(), p.data(), w.data(), m.data(), v.data(), n, &hp, 1, th, &flag);
             EXPECT(rc == 0 || rc == ZERO_ENOTSUP);
+            rc = zero_adam_step_host_bf16(g.data(), p.data(), w.data(), m.data(), v.data(), n, &hp, 2, th, &flag);
+            EXPECT(rc == 0 || rc == ZERO_ENOTSUP);
         }
     }
     {   // the thread bound: 1025 is rejected, 1024 runs

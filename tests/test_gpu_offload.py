@@ -133,3 +133,36 @@ def test_offload_equals_gpu_step_at_full_size(zs):
     del t_, dp, w, m, v
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _to_devbf(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("chunk,threads", [(64, 1), (0, 0)])
+def test_offload_bf16_matches_oracle(zs, chunk, threads):
+    """The bfloat16 offload step (zero_offload_step_bf16): bfloat16 gradient
+    and parameter on the device, the host update over fp32 state, against
+    the oracle's bfloat16 step, with an infinity and a NaN injected."""
+    import torch
+    off = zs.zero_offload_create(chunk, threads)
+    rng = np.random.default_rng(300 + chunk + threads)
+    for n in (1, 7, 65, 4097, 70001):
+        say(f"offload bf16 chunk={chunk} threads={threads} n={n}")
+        g = oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        if n > 100:
+            g[[5, n // 2]] = [0x7F80, 0xFFC0]          # an inf and a NaN
+        w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v = (rng.random(n) * 1e-6).astype(np.float32)
+        W_, M_, V_, P_ = w.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16)
+        dp = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        flag = np.zeros(1, np.int32)
+        off.step(_to_devbf(g), dp, w, m, v, zs.AdamHParams(**HP), 4, nonfinite_flag=flag)
+        rflag = oracle.adam_step(g, P_, W_, M_, V_, t=4, fmt="bf16", **HP)
+        res = [check16(host16(dp), P_, "param", fmt="bf16"), check32(w, W_, "master"),
+               check32(m, M_, "m"), check32(v, V_, "v")]
+        assert sum(r["not_bit_exact"] for r in res) == 0
+        assert int(flag[0]) == rflag == (1 if n > 100 else 0)
+    off.destroy()

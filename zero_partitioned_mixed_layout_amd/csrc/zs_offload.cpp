@@ -20,6 +20,7 @@
 #include <immintrin.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <algorithm>
 #include <condition_variable>
@@ -42,12 +43,64 @@ bool cpu_has_avx2_f16c() {
     return __builtin_cpu_supports("avx2") && __builtin_cpu_supports("f16c");
 }
 
+// The 16-bit formats of parameters and gradients, as on the device: IEEE
+// binary16 (F16C conversions) and bfloat16 (widening is a 16-bit shift;
+// narrowing rounds to nearest even in integer arithmetic, and a NaN stays a
+// quiet NaN with its sign).  A value is infinite or NaN when its exponent
+// field is all ones.
+struct HostF16 {
+    static constexpr uint16_t kExp = 0x7C00;
+};
+struct HostBF16 {
+    static constexpr uint16_t kExp = 0x7F80;
+};
+
+#define ZS_HOST_SIMD __attribute__((target("avx2,f16c")))
+
+ZS_HOST_SIMD inline float widen1(HostF16, uint16_t b) { return _cvtsh_ss(b); }
+ZS_HOST_SIMD inline uint16_t narrow1(HostF16, float x) {
+    return _cvtss_sh(x, _MM_FROUND_TO_NEAREST_INT);
+}
+ZS_HOST_SIMD inline __m256 widen8(HostF16, __m128i h) { return _mm256_cvtph_ps(h); }
+ZS_HOST_SIMD inline __m128i narrow8(HostF16, __m256 x) {
+    return _mm256_cvtps_ph(x, _MM_FROUND_TO_NEAREST_INT);
+}
+
+ZS_HOST_SIMD inline float widen1(HostBF16, uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, 4);
+    return x;
+}
+ZS_HOST_SIMD inline uint16_t narrow1(HostBF16, float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+ZS_HOST_SIMD inline __m256 widen8(HostBF16, __m128i h) {
+    return _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
+}
+ZS_HOST_SIMD inline __m128i narrow8(HostBF16, __m256 x) {
+    const __m256i u = _mm256_castps_si256(x);
+    const __m256i hi = _mm256_srli_epi32(u, 16);
+    const __m256i lsb = _mm256_and_si256(hi, _mm256_set1_epi32(1));
+    __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, _mm256_set1_epi32(0x7FFF)),
+                                                   lsb), 16);
+    const __m256i qnan = _mm256_or_si256(hi, _mm256_set1_epi32(0x0040));
+    r = _mm256_blendv_epi8(r, qnan, _mm256_castps_si256(_mm256_cmp_ps(x, x, _CMP_UNORD_Q)));
+    // eight 32-bit values below 2^16 to eight 16-bit ones, in order
+    const __m256i packed = _mm256_packus_epi32(r, r);
+    return _mm256_castsi256_si128(_mm256_permute4x64_epi64(packed, 0x08));
+}
+
 // One element: the Adam step of Kingma and Ba's Algorithm 1 with bias
 // correction, eps outside the root, in the GPU kernel's operation order.
-__attribute__((target("avx2,f16c"))) inline uint16_t adam_elem_host(uint16_t gb, float &w,
-                                                                    float &m, float &v,
-                                                                    const HostConsts &c) {
-    const float g = _cvtsh_ss(gb);
+template <class Fmt>
+ZS_HOST_SIMD inline uint16_t adam_elem_host(uint16_t gb, float &w, float &m, float &v,
+                                            const HostConsts &c) {
+    const float g = widen1(Fmt(), gb);
     const float m_old = c.b1 * m;
     const float m_in = c.omb1 * g;
     m = m_old + m_in;
@@ -62,29 +115,29 @@ __attribute__((target("avx2,f16c"))) inline uint16_t adam_elem_host(uint16_t gb,
     const float u = m_hat / denom;
     const float step = c.lr * u;
     w = w - step;
-    return _cvtss_sh(w, _MM_FROUND_TO_NEAREST_INT);
+    return narrow1(Fmt(), w);
 }
 
 // Elements [0, n) of one range, eight at a time, then singly.  Returns 1 if
 // any gradient is infinite or NaN.
-__attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, uint16_t *p16,
-                                                         float *w, float *m, float *v,
-                                                         uint64_t n, const HostConsts &c) {
+template <class Fmt>
+ZS_HOST_SIMD int adam_range_host(const uint16_t *g16, uint16_t *p16, float *w, float *m,
+                                 float *v, uint64_t n, const HostConsts &c) {
     const __m256 lr = _mm256_set1_ps(c.lr), b1 = _mm256_set1_ps(c.b1),
                  omb1 = _mm256_set1_ps(c.omb1), b2 = _mm256_set1_ps(c.b2),
                  omb2 = _mm256_set1_ps(c.omb2), bc1 = _mm256_set1_ps(c.bc1),
                  bc2 = _mm256_set1_ps(c.bc2), eps = _mm256_set1_ps(c.eps);
-    const __m128i expo = _mm_set1_epi16(0x7C00);
+    const __m128i expo = _mm_set1_epi16((short)Fmt::kExp);
     int bad = 0;
     uint64_t i = 0;
-    // The fp16 parameters are written only: streamed past the caches when
+    // The 16-bit parameters are written only: streamed past the caches when
     // 16-byte aligned (no read for ownership of their lines; in the offload
     // pipeline the staging slot is read next by the copy engine, not the CPU).
     const bool p_aligned = ((uintptr_t)p16 & 15) == 0;
     for (; i + 8 <= n; i += 8) {
         const __m128i gh = _mm_loadu_si128(reinterpret_cast<const __m128i *>(g16 + i));
         bad |= _mm_movemask_epi8(_mm_cmpeq_epi16(_mm_and_si128(gh, expo), expo));
-        const __m256 g = _mm256_cvtph_ps(gh);
+        const __m256 g = widen8(Fmt(), gh);
         const __m256 m_new = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + i)),
                                            _mm256_mul_ps(omb1, g));
         const __m256 v_new = _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + i)),
@@ -97,7 +150,7 @@ __attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, ui
         _mm256_storeu_ps(m + i, m_new);
         _mm256_storeu_ps(v + i, v_new);
         _mm256_storeu_ps(w + i, w_new);
-        const __m128i ph = _mm256_cvtps_ph(w_new, _MM_FROUND_TO_NEAREST_INT);
+        const __m128i ph = narrow8(Fmt(), w_new);
         if (p_aligned)
             _mm_stream_si128(reinterpret_cast<__m128i *>(p16 + i), ph);
         else
@@ -105,8 +158,8 @@ __attribute__((target("avx2,f16c"))) int adam_range_host(const uint16_t *g16, ui
     }
     _mm_sfence(); // the streamed parameters are visible before this range returns
     for (; i < n; i++) {
-        bad |= (g16[i] & 0x7C00u) == 0x7C00u;
-        p16[i] = adam_elem_host(g16[i], w[i], m[i], v[i], c);
+        bad |= (g16[i] & Fmt::kExp) == Fmt::kExp;
+        p16[i] = adam_elem_host<Fmt>(g16[i], w[i], m[i], v[i], c);
     }
     return bad != 0;
 }
@@ -185,6 +238,7 @@ private:
 
 // The update of n elements split over the pool's parts in contiguous ranges
 // of whole groups of eight.  Returns 1 if any gradient is non-finite.
+template <class Fmt>
 int adam_parallel(Pool &pool, const uint16_t *g16, uint16_t *p16, float *w, float *m, float *v,
                   uint64_t n, const HostConsts &c) {
     const uint32_t P = pool.parts();
@@ -194,7 +248,8 @@ int adam_parallel(Pool &pool, const uint16_t *g16, uint16_t *p16, float *w, floa
         const uint64_t lo = std::min(n, groups * k / P * 8);
         const uint64_t hi = std::min(n, groups * (k + 1) / P * 8);
         if (hi > lo)
-            bad[k] = adam_range_host(g16 + lo, p16 + lo, w + lo, m + lo, v + lo, hi - lo, c);
+            bad[k] = adam_range_host<Fmt>(g16 + lo, p16 + lo, w + lo, m + lo, v + lo, hi - lo,
+                                          c);
     });
     int any = 0;
     for (int b : bad)
@@ -228,11 +283,10 @@ int check_host_arrays(const void *grad, const void *param, const float *w, const
     return zs::writes_overlap(r) ? ZERO_EINVAL : ZERO_OK;
 }
 
-} // namespace
-
-extern "C" int zero_adam_step_host(const void *grad_f16, void *param_f16, float *master, float *m,
-                                   float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
-                                   uint32_t threads, int32_t *nonfinite_flag) {
+template <class Fmt>
+int adam_step_host(const void *grad_f16, void *param_f16, float *master, float *m, float *v,
+                   uint64_t n, const zero_adam_hparams *hp, uint64_t t, uint32_t threads,
+                   int32_t *nonfinite_flag) {
     if (!hp)
         return ZERO_EINVAL;
     float s[8];
@@ -251,14 +305,31 @@ extern "C" int zero_adam_step_host(const void *grad_f16, void *param_f16, float 
     const HostConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
     try {
         Pool pool(threads ? threads : default_threads());
-        const int bad = adam_parallel(pool, (const uint16_t *)grad_f16, (uint16_t *)param_f16,
-                                      master, m, v, n, c);
+        const int bad = adam_parallel<Fmt>(pool, (const uint16_t *)grad_f16,
+                                           (uint16_t *)param_f16, master, m, v, n, c);
         if (bad && nonfinite_flag)
             *nonfinite_flag |= 1;
     } catch (...) {
         return ZERO_ENOMEM;
     }
     return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_adam_step_host(const void *grad_f16, void *param_f16, float *master, float *m,
+                                   float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
+                                   uint32_t threads, int32_t *nonfinite_flag) {
+    return adam_step_host<HostF16>(grad_f16, param_f16, master, m, v, n, hp, t, threads,
+                                   nonfinite_flag);
+}
+
+extern "C" int zero_adam_step_host_bf16(const void *grad_bf16, void *param_bf16, float *master,
+                                        float *m, float *v, uint64_t n,
+                                        const zero_adam_hparams *hp, uint64_t t,
+                                        uint32_t threads, int32_t *nonfinite_flag) {
+    return adam_step_host<HostBF16>(grad_bf16, param_bf16, master, m, v, n, hp, t, threads,
+                                    nonfinite_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,10 +432,12 @@ extern "C" int zero_offload_destroy(zero_offload *o) {
     return rc;
 }
 
-extern "C" int zero_offload_step(zero_offload *o, const void *grad_f16, void *param_f16,
-                                 float *master, float *m, float *v, uint64_t n,
-                                 const zero_adam_hparams *hp, uint64_t t,
-                                 int32_t *nonfinite_flag, void *stream) {
+namespace {
+
+template <class Fmt>
+int offload_step(zero_offload *o, const void *grad_f16, void *param_f16, float *master, float *m,
+                 float *v, uint64_t n, const zero_adam_hparams *hp, uint64_t t,
+                 int32_t *nonfinite_flag, void *stream) {
     if (!o || !hp)
         return ZERO_EINVAL;
     float s[8];
@@ -427,7 +500,7 @@ extern "C" int zero_offload_step(zero_offload *o, const void *grad_f16, void *pa
         if (!ok)
             break;
         try {
-            bad |= adam_parallel(*o->pool, o->g_stage[slot], o->p_stage[slot], master + k * C,
+            bad |= adam_parallel<Fmt>(*o->pool, o->g_stage[slot], o->p_stage[slot], master + k * C,
                                  m + k * C, v + k * C, count(k), c);
         } catch (...) {
             ok = false;
@@ -449,4 +522,22 @@ extern "C" int zero_offload_step(zero_offload *o, const void *grad_f16, void *pa
     if (bad && nonfinite_flag)
         *nonfinite_flag |= 1;
     return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_offload_step(zero_offload *o, const void *grad_f16, void *param_f16,
+                                 float *master, float *m, float *v, uint64_t n,
+                                 const zero_adam_hparams *hp, uint64_t t,
+                                 int32_t *nonfinite_flag, void *stream) {
+    return offload_step<HostF16>(o, grad_f16, param_f16, master, m, v, n, hp, t, nonfinite_flag,
+                                 stream);
+}
+
+extern "C" int zero_offload_step_bf16(zero_offload *o, const void *grad_bf16, void *param_bf16,
+                                      float *master, float *m, float *v, uint64_t n,
+                                      const zero_adam_hparams *hp, uint64_t t,
+                                      int32_t *nonfinite_flag, void *stream) {
+    return offload_step<HostBF16>(o, grad_bf16, param_bf16, master, m, v, n, hp, t,
+                                  nonfinite_flag, stream);
 }

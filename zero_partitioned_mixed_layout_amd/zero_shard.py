@@ -90,9 +90,13 @@ def _load() -> ctypes.CDLL:
         "zero_reduce_adam_step_bf16": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
                                        ctypes.POINTER(_HParams), u64, vp, vp],
         "zero_adam_step_host": [vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, u32, vp],
+        "zero_adam_step_host_bf16": [vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, u32,
+                                     vp],
         "zero_offload_create": [u64, u32, ctypes.POINTER(vp)],
         "zero_offload_destroy": [vp],
         "zero_offload_step": [vp, vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, vp, vp],
+        "zero_offload_step_bf16": [vp, vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, vp,
+                                   vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -112,7 +116,7 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_plan_stats_of", "zero_plan_describe", "zero_plan_destroy",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
            "zero_reduce_adam_step", "zero_reduce_adam_step_bf16", "zero_adam_step_host",
-           "zero_offload_create",
+           "zero_adam_step_host_bf16", "zero_offload_create", "zero_offload_step_bf16",
            "zero_offload_destroy", "zero_offload_step", "zero_status_str")
 
 
@@ -409,9 +413,13 @@ def _host(a, dtype, what: str, n: Optional[int] = None) -> int:
 
 
 def zero_adam_step_host(grad16, param16, master, m, v, hp, t: int, threads: int = 0,
-                        nonfinite_flag=None) -> None:
-    """The Adam step on the host CPU over numpy arrays (fp16 as uint16 or
-    float16; fp32 state updated in place); bit-identical to zero_adam_step."""
+                        nonfinite_flag=None, fmt: str = "f16") -> None:
+    """The Adam step on the host CPU over numpy arrays (16-bit values as
+    uint16, or float16 for fmt "f16"; fp32 state updated in place);
+    bit-identical to zero_adam_step.  fmt: "f16", or "bf16" for the
+    bfloat16 variant (gradient and parameter as bfloat16 bit patterns)."""
+    if fmt not in ("f16", "bf16"):
+        raise ValueError('fmt must be "f16" or "bf16"')
     import numpy as np
     n = master.size
     ptrs = [_host(grad16, np.uint16, "grad", n), _host(param16, np.uint16, "param", n),
@@ -419,8 +427,8 @@ def zero_adam_step_host(grad16, param16, master, m, v, hp, t: int, threads: int 
             _host(v, np.float32, "v", n)]
     f = None if nonfinite_flag is None else _host(nonfinite_flag, np.int32, "nonfinite_flag", 1)
     h = _hp(hp)
-    _check("zero_adam_step_host",
-           _lib.zero_adam_step_host(*ptrs, n, ctypes.byref(h), int(t), int(threads), f))
+    name = "zero_adam_step_host_bf16" if fmt == "bf16" else "zero_adam_step_host"
+    _check(name, getattr(_lib, name)(*ptrs, n, ctypes.byref(h), int(t), int(threads), f))
 
 
 class Offload:
@@ -438,21 +446,23 @@ class Offload:
 
     def step(self, grad: torch.Tensor, param: torch.Tensor, master, m, v, hp, t: int,
              nonfinite_flag=None, stream=None) -> None:
-        """grad, param: device fp16 tensors; master, m, v: host numpy fp32
-        arrays updated in place; nonfinite_flag: None or a numpy int32[1]."""
+        """grad, param: device tensors, both float16 or both bfloat16 (the
+        bfloat16 variant); master, m, v: host numpy fp32 arrays updated in
+        place; nonfinite_flag: None or a numpy int32[1]."""
         import numpy as np
         n = master.size
-        _need(grad, torch.float16, "grad", self.device)
-        _need(param, torch.float16, "param", self.device)
+        half = grad.dtype if grad.dtype in (torch.float16, torch.bfloat16) else torch.float16
+        _need(grad, half, "grad", self.device)
+        _need(param, half, "param", self.device)
         if grad.numel() != n or param.numel() != n:
             raise ValueError("grad, param and the host state differ in size")
         hs = [_host(master, np.float32, "master", n), _host(m, np.float32, "m", n),
               _host(v, np.float32, "v", n)]
         f = None if nonfinite_flag is None else _host(nonfinite_flag, np.int32, "nonfinite_flag", 1)
         h = _hp(hp)
-        _check("zero_offload_step",
-               _lib.zero_offload_step(self.handle, grad.data_ptr(), param.data_ptr(), *hs, n,
-                                      ctypes.byref(h), int(t), f, _stream_handle(stream)))
+        name = "zero_offload_step_bf16" if half == torch.bfloat16 else "zero_offload_step"
+        _check(name, getattr(_lib, name)(self.handle, grad.data_ptr(), param.data_ptr(), *hs, n,
+                                         ctypes.byref(h), int(t), f, _stream_handle(stream)))
 
     def destroy(self) -> None:
         if self._h:
