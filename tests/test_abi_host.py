@@ -315,3 +315,32 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libzeroshard.so is missing" in r.stderr
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/zero_shard.h compiles as strict C99 and C11 with every warning
+    an error, and a C program links against the library and calls a host
+    entry point through it."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("needs gcc")
+    src = tmp_path / "use.c"
+    src.write_text('#include "zero_shard.h"\n'
+                   "int main(void) {\n"
+                   "    zero_layout l;\n"
+                   "    uint64_t b = 0;\n"
+                   "    if (zero_shard_layout(7500000000ull, 64, 0, 1, &l) != ZERO_OK) return 1;\n"
+                   "    if (l.shard_len != 117187500ull) return 2;\n"
+                   "    if (zero_state_bytes(2, 7500000000ull, 64, 1, &b) != ZERO_OK) return 3;\n"
+                   "    return b == 16640625000ull ? 0 : 4;\n"
+                   "}\n")
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.join(ROOT, "zero_partitioned_mixed_layout_amd")
+    for std in ("c99", "c11"):
+        subprocess.run(["gcc", f"-std={std}", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", inc, "-fsyntax-only", str(src)], check=True, capture_output=True)
+    exe = str(tmp_path / "use")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-L", libdir, "-lzeroshard",
+                    f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True)
+    assert subprocess.run([exe], timeout=120).returncode == 0
