@@ -84,9 +84,18 @@ def test_tensor_list_workload(zs, name, layout):
     wl = W.WORKLOADS[name]
     say(f"{name} ({layout}): {len(wl.tensors)} tensors, {wl.n_params} params")
     assert zs.zero_state_bytes(0, wl.n_params, 1) == 16 * wl.n_params
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
     tensors = W.device_list_state(wl, layout=layout)
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - before
     if layout == "flat":
         assert tensors[1].w.data_ptr() == tensors[0].w.data_ptr() + 4 * tensors[0].n
+    if layout == "flat":
+        # the stage-0 ledger, 16 bytes per parameter, against what the
+        # allocator holds for the five buffers (torch hands out large blocks
+        # in 2 MiB segments: under 2 MiB of rounding each)
+        assert 0 <= held - 16 * wl.n_params < 5 * (2 << 20), (held, 16 * wl.n_params)
     plan = zs.zero_plan_create([t.arrays() for t in tensors])
     st = plan.stats()
     assert st["n_params"] == wl.n_params and st["vector_elems"] == wl.n_params
@@ -125,10 +134,17 @@ def test_flat_7p5b_nd64_reduce_then_step(zs, rank):
     assert lay._asdict() == oracle.shard_layout(wl.psi, wl.nd, rank, wl.align)
     n = lay.real_len
     say(f"flat_7p5b_nd64 rank={rank} n={n} offset={lay.offset}")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
     full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total)
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - before     # what the allocator holds for the state
     buf, rows = W.device_slices(wl, n)
     ledger = full.numel() * 2 + sh.g.numel() * 2 + 3 * 4 * sh.w.numel()
     assert ledger == zs.zero_state_bytes(2, wl.psi, wl.nd, wl.align) == 16_640_625_000
+    # five allocations, each rounded up by under 2 MiB (the allocator's
+    # segment size for large blocks)
+    assert 0 <= held - ledger < 5 * (2 << 20), (held, ledger)
     plan = zs.zero_plan_create([sh.arrays()])
     st = plan.stats()
     assert st["vector_elems"] >= n - 3
