@@ -64,12 +64,18 @@ constexpr uint32_t kAdamPerCU = 7;
 // loads per lane in flight on the widest path.
 constexpr uint32_t kGatherTile = 2048;
 
+// Resident one-wave workgroups per CU for the parameter gather.  Measured on
+// MI355X with 64 shards of 117,187,500 elements: 16 is 1-5% ahead of 8 and
+// 12; 1024-element tiles at 16 or 24 and 4096 at 8 were no faster, and
+// 512-element tiles without a cap (one vector per lane) 7-12% slower.
+constexpr uint32_t kGatherPerCU = 16;
+
+// Bytes of a cache line (the unit of the gather's destination alignment).
+constexpr uint32_t kLine = 128;
+
 // Elements per chunk of the offload pipeline (8 MiB of fp16 per staging
 // buffer).
 constexpr uint64_t kOffloadChunk = 4ull << 20;
-
-// Resident one-wave workgroups per CU for the parameter gather (0: no cap).
-constexpr uint32_t kGatherPerCU = 12;
 
 // Slices whose fp16 vectors one lane keeps in flight at once when reducing
 // nd slices (the kernels load batches of 16, 8, 4, then 1).

@@ -629,11 +629,12 @@ __device__ __forceinline__ void copy_vec(const uint16_t *src, uint16_t *dst, uin
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
-// Tile j of shard r: after the shard's head, kGatherTile consecutive
-// elements.  A full tile has each lane load kGatherTile / (64 VEC) groups of
-// VEC elements (lane L's groups at L, L + 64, ...: every wave instruction
-// contiguous), all before the first store; the shard's last, partial tile
-// moves its whole groups of VEC, then single elements.
+// Tile j of shard r: after the shard's head (the elements before the
+// destination's first 128-byte line), kGatherTile consecutive
+// elements.  A full tile has each lane move kGatherTile / (64 VEC) groups
+// of VEC elements (lane L's groups at L, L + 64, ...: every wave instruction
+// contiguous), all loads before the first store; the shard's last, partial
+// tile moves its whole groups of VEC, then single elements.
 template <int VEC, typename V>
 __device__ __forceinline__ void gather_tile(const uint16_t *src, uint16_t *dst, uint64_t S,
                                             uint32_t head, uint64_t j) {
@@ -645,7 +646,7 @@ __device__ __forceinline__ void gather_tile(const uint16_t *src, uint16_t *dst, 
     if (lo >= S)
         return;
     const uint64_t hi = min(S, lo + zs::kGatherTile);
-    if (VEC > 1 && hi - lo == zs::kGatherTile) {
+    if (hi - lo == zs::kGatherTile) {
         constexpr int G = zs::kGatherTile / (kWave * VEC);
         V x[G];
 #pragma unroll
@@ -663,21 +664,26 @@ __device__ __forceinline__ void gather_tile(const uint16_t *src, uint16_t *dst, 
         as_global(dst)[i] = as_global(src)[i];
 }
 
-__global__ __launch_bounds__(kWave) void zs_gather_kernel(GatherArgs a, uint32_t nd, uint64_t S,
+// Grid: x over a shard's tiles (striding when a shard has more than the
+// launch's x extent), y over the shards, so consecutive workgroups take
+// consecutive tiles of one shard and no workgroup divides to find its
+// shard.  Workgroups of a shard that is already in place return at once.
+__global__ __launch_bounds__(kWave) void zs_gather_kernel(GatherArgs a, uint64_t S,
                                                           uint64_t tiles_per_shard,
                                                           uint16_t *__restrict__ full) {
-    const uint64_t n_virtual = (uint64_t)nd * tiles_per_shard;
-    for (uint64_t b = blockIdx.x; b < n_virtual; b += gridDim.x) {
-        const uint32_t r = (uint32_t)(b / tiles_per_shard);
-        const uint64_t j = b - (uint64_t)r * tiles_per_shard;
-        const uint16_t *src = a.src[r];
-        uint16_t *dst = full + (uint64_t)r * S;
-        switch (a.vec[r]) {
-        case 8: gather_tile<8, f16x8>(src, dst, S, a.head[r], j); break;
-        case 4: gather_tile<4, f16x4>(src, dst, S, a.head[r], j); break;
-        case 2: gather_tile<2, u16x2>(src, dst, S, a.head[r], j); break;
-        case 1: gather_tile<1, uint16_t>(src, dst, S, 0, j); break;
-        default: break; // in place
+    const uint32_t r = blockIdx.y;
+    const uint32_t vec = a.vec[r];
+    if (vec == 0)
+        return; // in place
+    const uint16_t *src = a.src[r];
+    uint16_t *dst = full + (uint64_t)r * S;
+    const uint32_t head = a.head[r];
+    for (uint64_t j = blockIdx.x; j < tiles_per_shard; j += gridDim.x) {
+        switch (vec) {
+        case 8: gather_tile<8, f16x8>(src, dst, S, head, j); break;
+        case 4: gather_tile<4, f16x4>(src, dst, S, head, j); break;
+        case 2: gather_tile<2, u16x2>(src, dst, S, head, j); break;
+        default: gather_tile<1, uint16_t>(src, dst, S, head, j); break;
         }
     }
 }
@@ -1051,15 +1057,18 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
         // a shard that moves must not overlap the buffer it is copied into
         if (shard_len > 0 && s < f + fb && f < s + sb)
             return ZERO_EINVAL;
-        // widest access for which source and destination share a phase
-        uint32_t vec = 1, head = 0;
+        // widest access for which source and destination share a phase; the
+        // head (fewer than 64 elements, copied singly) puts the destination
+        // of every tile on a 128-byte line, so no two workgroups write parts
+        // of one line (the source keeps its phase relative to it)
+        uint32_t vec = 1;
         for (uint32_t w : {8u, 4u, 2u}) {
             if ((s - d) % (2u * w) == 0) {
                 vec = w;
-                head = (uint32_t)(((2u * w - d % (2u * w)) % (2u * w)) / 2u);
                 break;
             }
         }
+        const uint32_t head = (uint32_t)(((zs::kLine - d % zs::kLine) % zs::kLine) / 2u);
         args.vec[r] = (uint8_t)vec;
         args.head[r] = (uint8_t)head;
         moving++;
@@ -1076,13 +1085,13 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
         (void)hipGetLastError();
         return ZERO_EHIP;
     }
-    // tiles per shard, with room for a head of up to 7 elements
-    const uint64_t tps = (shard_len + 7 + zs::kGatherTile - 1) / zs::kGatherTile;
-    const uint64_t n_virtual = (uint64_t)nd * tps;
-    const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
-    const size_t lds = zs::kGatherPerCU ? lds_cap_bytes(dev, zs::kGatherPerCU) : 0;
-    hipLaunchKernelGGL(zs_gather_kernel, dim3(grid), dim3(kWave), lds, (hipStream_t)stream, args,
-                       nd, shard_len, tps, (uint16_t *)full_f16);
+    // tiles per shard, with room for a head of up to 63 elements; one
+    // workgroup per tile and shard, kGatherPerCU of them resident per CU
+    const uint64_t tps = (shard_len + zs::kLine / 2 - 1 + zs::kGatherTile - 1) / zs::kGatherTile;
+    const uint32_t gx = (uint32_t)(tps < zs::kMaxGrid ? tps : zs::kMaxGrid);
+    const size_t lds = lds_cap_bytes(dev, zs::kGatherPerCU);
+    hipLaunchKernelGGL(zs_gather_kernel, dim3(gx, nd), dim3(kWave), lds, (hipStream_t)stream,
+                       args, shard_len, tps, (uint16_t *)full_f16);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
