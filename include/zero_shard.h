@@ -105,7 +105,10 @@ typedef struct zero_plan_stats {
  * padded_total = ceil(psi / (nd * align)) * nd * align elements; every rank
  * gets shard_len = padded_total / nd elements starting at rank * shard_len,
  * of which real_len lie below psi (the padding sits in the last shards).
- * align is in elements.  psi = 0 is allowed (all zero).
+ * align is in elements.  psi = 0 is allowed (all zero).  align = 64 puts
+ * every rank's fp16 view of a line-aligned buffer on a 128-byte line, which
+ * the kernels stream fastest (a view off its lines costs the Adam step a
+ * few percent and the gather more).
  * Pure host function.  Errors: EINVAL if out is NULL, nd = 0, align = 0 or
  * rank >= nd; EOVERFLOW if padded_total exceeds 2^64 - 1.
  */
