@@ -35,11 +35,43 @@ KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", f
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
-def kernel_src_sha() -> str:
+def code_tokens(text: str) -> str:
+    """C/C++/HIP source with comments removed and every run of whitespace
+    made one space (string and character literals kept whole), so that the
+    hash below changes with the code, not with its comments or layout."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_src_sha(read=None) -> str:
+    """Hash of the code (not the comments) of the kernel sources; `read`
+    maps a path to its text (default: the working tree)."""
     h = hashlib.sha256()
     for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(p, encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(p)
+        h.update(code_tokens(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,23 +1,28 @@
 // zs_kernels.hip -- the device side of libzeroshard.so for gfx950 (CDNA4):
-// the fused multi-tensor Adam step and the N_d-slice gradient reduction, plus
+// the fused multi-tensor Adam step, the N_d-slice gradient reduction, the
+// reduction and the Adam step fused over a flat shard, and the gather of
+// updated shards, each for fp16 or bfloat16 parameters and gradients; plus
 // the plan upload and the launches behind the C ABI.
 //
-// Both kernels are elementwise HBM streams (Adam: 28 bytes per parameter;
-// reduce: 2 N_d + 2 bytes), so they use no matrix cores.  Every load and
-// store instruction of a 64-lane wave covers one contiguous, line-aligned
-// range (Adam: 512 bytes of fp16 or 1 KiB of fp32; reduce: 1 KiB of fp16),
-// and streamed data moves with the nontemporal hint.  On gfx950 nontemporal
-// stores only stream at full rate when each instruction writes whole lines,
-// which is why the Adam wave tile interleaves its two four-element groups
-// across the wave instead of giving each lane eight neighbours.
+// All four kernels are elementwise HBM streams (Adam: 28 bytes per
+// parameter; reduce: 2 N_d + 2 bytes; fused: 2 N_d + 26; gather: 4), so they
+// use no matrix cores.  Every load and store instruction of a 64-lane wave
+// covers one contiguous range (Adam: 512 bytes of fp16 or 1 KiB of fp32;
+// reduce: 1 KiB of fp16), and streamed data moves with the nontemporal hint.
+// On gfx950 nontemporal stores only stream at full rate when each
+// instruction writes whole lines, which is why the Adam wave tile
+// interleaves its two four-element groups across the wave instead of giving
+// each lane eight neighbours, and why the gather aligns its tiles to the
+// destination's 128-byte lines.
 //
-// Occupancy is capped on purpose.  Both kernels run one 64-lane wave per
+// Occupancy is capped on purpose.  The kernels run one 64-lane wave per
 // workgroup, and each launch reserves dynamic LDS that the kernel never
-// touches, so that only a few workgroups are resident per CU (Adam 7; reduce
-// 4 when 16 slices are in flight per lane).  Measured on MI355X, HBM3E
-// streams these many-array patterns fastest with just enough bytes in
-// flight to cover latency (about 45 KB per CU); with the 20-30 waves per CU
-// that registers alone would allow, the same streams run 10-15% slower.
+// touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
+// are resident per CU (Adam 7; reduce 4 when 16 slices are in flight per
+// lane; fused 4; gather 16).  Measured on MI355X, HBM3E streams these
+// many-array patterns fastest with just enough bytes in flight to cover
+// latency (about 45 KB per CU); with the 20-30 waves per CU that registers
+// alone would allow, the same streams run 10-15% slower.
 //
 // Exactness: every arithmetic step is one IEEE binary32 operation in a fixed
 // order; the library is built with -ffp-contract=off (no fused multiply-add),
