@@ -46,3 +46,12 @@ def test_traffic_lookup_requires_matching_hash(tmp_path, monkeypatch):
     assert b.measured_traffic("zs_adam_kernel", "w1") == 123.0
     assert b.measured_traffic("zs_reduce_kernel", "w1") is None      # taken on other code
     assert b.measured_traffic("zs_adam_kernel", "w2") is None        # another workload
+
+
+def test_committed_counters_match_the_current_kernels():
+    """profiles/hbm_traffic.md was taken on the kernels as they are now, so
+    the default bench line carries measured HBM traffic for both kernels of
+    the step (re-take the counters after any change to the kernels' code)."""
+    b = _bench()
+    for k in ("zs_reduce_kernel", "zs_adam_kernel"):
+        assert b.measured_traffic(k, "flat_7p5b_nd64") is not None, k
