@@ -372,3 +372,52 @@ def test_rejects_through_binding(zs, torch_mod):
         zs.zero_plan_create([(a, a.clone(), w, w, torch.zeros(16, device="cuda"))])
     with pytest.raises(TypeError):
         zs.zero_plan_create([(a, a.clone(), w.half(), w.clone(), w.clone())])
+
+
+def test_two_plans_on_two_streams(zs, torch_mod):
+    """The library keeps no mutable state between calls: two ranks' shards,
+    each with its own plan, slices and flags, stepped on two streams at once
+    (reduce, then Adam with the reduce's flag as skip input, three steps
+    each, launches interleaved across the streams) equal the oracle run
+    separately on each."""
+    torch = torch_mod
+    say("two plans on two streams")
+    rng = np.random.default_rng(77)
+    sizes = (300_001, 123_457)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    nd = 3
+    shards, hosts, plans = [], [], []
+    for n in sizes:
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        dev = dict(p=torch.zeros(n, dtype=torch.float16, device="cuda"),
+                   g=torch.zeros(n, dtype=torch.float16, device="cuda"),
+                   w=to_dev32(w0), m=torch.zeros(n, device="cuda"), v=torch.zeros(n, device="cuda"),
+                   rflag=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                   aflag=torch.zeros(1, dtype=torch.int32, device="cuda"))
+        shards.append(dev)
+        hosts.append(HostShard(np.zeros(n, np.uint16), np.zeros(n, np.uint16), w0.copy(),
+                               np.zeros(n, np.float32), np.zeros(n, np.float32)))
+        plans.append(zs.zero_plan_create([(dev["p"], dev["g"], dev["w"], dev["m"], dev["v"])]))
+    torch.cuda.synchronize()
+    for t in (1, 2, 3):
+        slices = []
+        for k, n in enumerate(sizes):
+            hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
+            slices.append((hs, [to_dev16(h) for h in hs]))
+        torch.cuda.synchronize()                  # inputs are in place before either stream starts
+        for k in (0, 1):                          # the two reduces, one per stream
+            with torch.cuda.stream(streams[k]):
+                zs.zero_reduce_grad_shard(slices[k][1], shards[k]["g"], shards[k]["rflag"])
+        for k in (0, 1):                          # then the two steps, each after its own reduce
+            with torch.cuda.stream(streams[k]):
+                zs.zero_adam_step(plans[k], _hp(zs), t, shards[k]["aflag"], shards[k]["rflag"])
+        for k in (0, 1):
+            g_ref, _ = oracle.reduce_grad(slices[k][0])
+            hosts[k].g[:] = g_ref
+            hosts[k].step(t)
+        torch.cuda.synchronize()
+    for k in (0, 1):
+        d = shards[k]
+        assert _compare((d["p"], d["g"], d["w"], d["m"], d["v"]), hosts[k], f"stream {k}") == 0
+        assert int(d["rflag"].item()) == 0 and int(d["aflag"].item()) == 0
+        plans[k].destroy()
