@@ -32,7 +32,7 @@ METRIC = "params updated/sec and achieved HBM GB/s (% of roofline) per Adam shar
 # the sources that decide what the kernels do and how they are launched
 KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", f)
                for f in ("zs_kernels.hip", "zs_internal.h", "zs_host.cpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_flat_7p5b_nd64.md")
 
 
 def code_tokens(text: str) -> str:

@@ -49,7 +49,7 @@ def test_traffic_lookup_requires_matching_hash(tmp_path, monkeypatch):
 
 
 def test_committed_counters_match_the_current_kernels():
-    """profiles/hbm_traffic.md was taken on the kernels as they are now, so
+    """profiles/hbm_traffic_flat_7p5b_nd64.md was taken on the kernels as they are now, so
     the default bench line carries measured HBM traffic for both kernels of
     the step (re-take the counters after any change to the kernels' code)."""
     b = _bench()
