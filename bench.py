@@ -101,6 +101,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="flat_7p5b_nd64",
                     choices=["flat_7p5b_nd64", "flat_7p5b_nd8", "gpt2_xl", "llama_7b", "tiny_flat"])
+    ap.add_argument("--slices", action="store_true",
+                    help="flat workloads without gradient slices (flat_7p5b_nd8): give the step "
+                         "the reduce of N_d simulated fp16 slices too, as flat_7p5b_nd64 has")
     ap.add_argument("--fused", action="store_true",
                     help="workloads with gradient slices: one zero_reduce_adam_step launch per "
                          "step instead of zero_reduce_grad_shard + zero_adam_step")
@@ -183,7 +186,8 @@ class Step:
     """Device state and the launches of one step for a workload."""
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
-                 offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0):
+                 offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
+                 slices=False):
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         half = torch.bfloat16 if bf16 else torch.float16
@@ -199,7 +203,7 @@ class Step:
             self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total,
                                                 half=half)
             self.tensors = [sh]
-            if wl.reduce_slices:
+            if wl.reduce_slices or slices:
                 self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half)
             else:
                 W.device_fill_grads(wl, self.tensors, 1)
@@ -393,7 +397,8 @@ def main():
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
-                args.offload_threads, args.bf16, args.list_layout, args.offload_chunk)
+                args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
+                args.slices)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -430,7 +435,9 @@ def main():
     copy = plain_copy(stream)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
-    cfg = {"workload": args.workload + ("+fused" if step.fused else "") +
+    cfg = {"workload": args.workload +
+           ("+slices" if args.slices and not step.wl.reduce_slices and step.rows is not None else "") +
+           ("+fused" if step.fused else "") +
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
            ("+bf16" if args.bf16 else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
