@@ -188,6 +188,7 @@ class Step:
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
                  slices=False):
+        import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
         half = torch.bfloat16 if bf16 else torch.float16
@@ -221,7 +222,7 @@ class Step:
                 raise SystemExit("--offload runs on the flat workloads")
             sh = self.tensors[0]
             self.host = [x.cpu().numpy().copy() for x in (sh.w, sh.m, sh.v)]
-            self.hflag = __import__("numpy").zeros(1, dtype="int32")
+            self.hflag = np.zeros(1, dtype=np.int32)
             self.offload = zs.zero_offload_create(offload_chunk, offload_threads)
             self.offload_threads_used = offload_threads or min(16, os.cpu_count() or 1)
             self.fused = False
