@@ -55,3 +55,10 @@ def test_committed_counters_match_the_current_kernels():
     b = _bench()
     for k in ("zs_reduce_kernel", "zs_adam_kernel"):
         assert b.measured_traffic(k, "flat_7p5b_nd64") is not None, k
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
