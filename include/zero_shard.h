@@ -133,10 +133,11 @@ int zero_state_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * zero_comm_volume -- elements one rank moves per training step.
  * [16B] "The part that sounds too good: communication"; [ER10] "The
  * Mathematics", communication paragraph, and "What It Enabled", stage
- * table.  A ring all-reduce is a reduce-scatter plus an all-gather, Psi
- * each: plain data parallelism (stage 0) and stages 1-2 (gradient
- * reduce-scatter, fp16 parameter all-gather) move 2 Psi; stage 3 adds the
- * parameter all-gathers before the forward and the backward pass: 3 Psi.
+ * table.  Each pass (a reduce-scatter or an all-gather; a ring all-reduce
+ * runs one of each) moves Psi elements: plain data parallelism (stage 0)
+ * and stages 1-2 (gradient reduce-scatter, fp16 parameter all-gather) move
+ * 2 Psi; stage 3 adds the parameter all-gathers before the forward and the
+ * backward pass: 3 Psi.
  * Volumes count elements (each fp16 element is 2 bytes).  ring_send_elems
  * is the exact count over the padded layout: every ring pass has each rank
  * send nd - 1 shards of shard_len elements.
@@ -316,7 +317,8 @@ int zero_reduce_adam_step_bf16(const void *const *slices_bf16, uint32_t nd, uint
  * zero_gather_shards -- the receive side of the all-gather of updated fp16
  * parameters: after it every rank holds the whole fp16 buffer, rank r's
  * shard at element r * shard_len ([16B] "The part that sounds too good:
- * communication": the ranks all-gather the updated fp16 parameters).
+ * communication": after the update, every rank receives every other
+ * rank's fresh fp16 shard).
  * Here the nd shards are given in local device memory:
  *   full[r * shard_len + i] = shards[r][i],  r < nd, i < shard_len
  * A shard whose pointer already equals full + r * shard_len (this rank's

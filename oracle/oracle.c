@@ -373,8 +373,8 @@ int orc_adam_step(uint64_t n, const uint16_t *grad16, uint16_t *param16,
 
 /* ------------------------------------------------------------------------ */
 /* Gradient reduction for this rank's partition.                             */
-/* Each rank ends up owning the final gradients for its partition after a    */
-/* reduce-scatter ([16B] "The part that sounds too good: communication";     */
+/* After the reduce-scatter, a rank holds the summed gradient of its own    */
+/* partition only ([16B] "The part that sounds too good: communication";     */
 /* [ER10] "The Mathematics", communication paragraph).  Here the N_d ranks'  */
 /* fp16 slices of this partition are given as N_d arrays.  The pages do not  */
 /* fix order, precision or scaling; this oracle sums in fp32 in rank order   */
@@ -412,8 +412,8 @@ int orc_reduce(uint32_t nd, const uint16_t *const *slices, uint64_t n,
 /* Communication volume of one training step, per rank.                      */
 /* [16B] "The part that sounds too good: communication"; [ER10] "The         */
 /* Mathematics", communication paragraph, and "What It Enabled", stage      */
-/* table.  A ring all-reduce is a reduce-scatter followed by an all-gather,  */
-/* each moving Psi, so plain data parallelism (stage 0) moves 2 Psi per      */
+/* table.  Plain data parallelism (stage 0) all-reduces, which in a ring   */
+/* takes two passes of Psi each (reduce-scatter, then all-gather): 2 Psi per */
 /* step.  Stages 1 and 2 reduce-scatter the gradients (Psi) and all-gather   */
 /* the updated fp16 parameters (Psi): 2 Psi.  Stage 3 also all-gathers the   */
 /* parameters on demand in the forward and in the backward pass, besides the */
