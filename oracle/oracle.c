@@ -414,11 +414,12 @@ int orc_reduce(uint32_t nd, const uint16_t *const *slices, uint64_t n,
 /* Mathematics", communication paragraph, and "What It Enabled", stage      */
 /* table.  Plain data parallelism (stage 0) all-reduces, which in a ring   */
 /* takes two passes of Psi each (reduce-scatter, then all-gather): 2 Psi per */
-/* step.  Stages 1 and 2 reduce-scatter the gradients (Psi) and all-gather   */
-/* the updated fp16 parameters (Psi): 2 Psi.  Stage 3 also all-gathers the   */
-/* parameters on demand in the forward and in the backward pass, besides the */
-/* gradient reduce-scatter: 3 Psi, 1.5x.  Volumes count elements (the pages' */
-/* multiples of Psi); with fp16 gradients and parameters each is 2 bytes.   */
+/* step.  Stages 1 and 2 reduce-scatter the gradients (Psi) and gather the  */
+/* fresh fp16 parameter shards to every rank (Psi): 2 Psi.  Stage 3 also     */
+/* all-gathers the parameters on demand in the forward and in the backward   */
+/* pass, besides the gradient reduce-scatter: 3 Psi, 1.5x.  Volumes count    */
+/* elements (the pages' multiples of Psi); with fp16 gradients and          */
+/* parameters each is 2 bytes.                                               */
 /* out = {passes, volume = passes * Psi, ring_send = passes * (nd - 1) * S}  */
 /* where one ring pass over the padded layout has every rank send nd - 1     */
 /* shards of S elements to its neighbour.                                    */
