@@ -104,6 +104,12 @@ def parse():
     ap.add_argument("--slices", action="store_true",
                     help="flat workloads without gradient slices (flat_7p5b_nd8): give the step "
                          "the reduce of N_d simulated fp16 slices too, as flat_7p5b_nd64 has")
+    ap.add_argument("--inject-inf", action="store_true",
+                    help="flat workloads without slices: set the workload's fraction of the "
+                         "gradients (0.01%% if it names none) to +inf or -inf at seeded positions "
+                         "and clear the non-finite flag before every step, so that each Adam "
+                         "launch raises it afresh (for counting the flag's atomics; the clear "
+                         "is timed with the step)")
     ap.add_argument("--fused", action="store_true",
                     help="workloads with gradient slices: one zero_reduce_adam_step launch per "
                          "step instead of zero_reduce_grad_shard + zero_adam_step")
@@ -187,7 +193,7 @@ class Step:
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
-                 slices=False):
+                 slices=False, inject_inf=False):
         import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
@@ -208,10 +214,15 @@ class Step:
                 self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half)
             else:
                 W.device_fill_grads(wl, self.tensors, 1)
+                if inject_inf:
+                    pos, sign = W.inf_positions(lay.real_len, wl.inf_frac or 1e-4, wl.seed)
+                    W.device_inject_inf(sh.g, pos, sign)
+                    self.n_inf = int(pos.size)
         else:
             self.layout = None
             self.tensors = W.device_list_state(wl, half=half, layout=list_layout)
             W.device_fill_grads(wl, self.tensors, 1)
+        self.inject_inf = inject_inf and self.rows is None and len(self.tensors) == 1
         self.plan = zs.zero_plan_create([t.arrays() for t in self.tensors], chunk_elems)
         self.n_params = self.plan.stats()["n_params"]
         self.t = 0
@@ -239,6 +250,8 @@ class Step:
 
     def adam(self):
         self.t += 1
+        if self.inject_inf:
+            self.flag.zero_()
         skip = self.rflag if self.rows is not None else None
         self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip)
 
@@ -399,7 +412,7 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
                 args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
-                args.slices)
+                args.slices, args.inject_inf)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -438,12 +451,14 @@ def main():
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
     cfg = {"workload": args.workload +
            ("+slices" if args.slices and not step.wl.reduce_slices and step.rows is not None else "") +
+           ("+inf" if step.inject_inf else "") +
            ("+fused" if step.fused else "") +
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
            ("+bf16" if args.bf16 else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
+           "injected_inf": step.n_inf if step.inject_inf else None,
            "list_layout": args.list_layout if len(step.wl.tensors) > 1 else None,
            "chunk_elems": step.plan.stats()["chunk_elems"],
            "kernels_per_step": [k for k, _, _ in ks],
