@@ -325,7 +325,9 @@ int zero_reduce_adam_step_bf16(const void *const *slices_bf16, uint32_t nd, uint
  * own shard, when its parameter is a view into the full buffer) is left
  * where it is and not read.
  * shards_f16: host array of nd device pointers (read only; they may
- *   overlap each other but not the part of full they are not copied to).
+ *   overlap each other; a shard not already in place must not overlap any
+ *   part of full).  Fastest when full sits on a 128-byte line and
+ *   shard_len is a multiple of 64 (every destination on a line).
  * full_f16: device pointer to nd * shard_len fp16, written.
  * Asynchronous; allocates nothing.  shard_len = 0 launches nothing.
  * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not
