@@ -235,10 +235,10 @@ int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp,
 
 /*
  * zero_reduce_grad_shard -- this rank's final gradient for its partition
- * from the nd ranks' fp16 slices of it: after a reduce-scatter each rank
- * owns the final gradients of its partition ([16B] "The part that sounds
- * too good: communication"; [ER10] "The Mathematics", communication
- * paragraph).  Here the nd slices are given in local device memory.
+ * from the nd ranks' fp16 slices of it: the reduce-scatter leaves every
+ * rank with the summed gradient of its own partition only ([16B] "The part
+ * that sounds too good: communication"; [ER10] "The Mathematics",
+ * communication paragraph).  Here the nd slices are given in local device memory.
  *   out[i] = fp16( (s_0[i] + s_1[i] + ... + s_{nd-1}[i]) / nd )
  * summed in fp32 in rank order starting from s_0, one IEEE division by nd,
  * rounded to nearest even fp16.
