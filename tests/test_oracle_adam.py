@@ -376,3 +376,53 @@ def test_swamping_set_over_ten_steps(orc):
     assert moved_any.all()
     # the fp32 master accumulated what fp16 could not: some params moved
     assert (p16[swamp] != start).sum() > 0
+
+
+def test_every_fp16_gradient_pattern_against_fp64(orc):
+    """One step from m = v = 0 over a tensor holding every one of the 65,536
+    fp16 gradient bit patterns (zeros, all subnormals, normals, infinities,
+    NaNs).  Finite g: the exact values are m = (1 - b1) g, v = (1 - b2) g^2
+    and w1 = w0 - lr g / (|g| + eps) (the bias corrections cancel at t = 1),
+    computed in fp64 from the widened g; the fp32 results must lie within
+    1e-6 relative of them (a handful of binary32 roundings) and the fp16
+    parameter within one ulp of fp16(w1).  Non-finite g: m, v, w and the
+    parameter take the IEEE classes (+-inf -> m = +-inf, v = +inf, w = NaN;
+    NaN -> NaN everywhere) and the flag is raised.  w0 is drawn from
+    [0.5, 1) so that w1 stays far from zero."""
+    n = 1 << 16
+    bits = np.arange(n, dtype=np.uint32).astype(np.uint16)
+    g64 = bits.view(np.float16).astype(np.float64)
+    rng = np.random.default_rng(65536)
+    w0 = (0.5 + 0.5 * rng.random(n)).astype(np.float32)
+    w, m, v = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p = np.zeros(n, np.uint16)
+    flag = orc.adam_step(bits, p, w, m, v, t=1, **HP)
+    assert flag == 1
+    fin = np.isfinite(g64)
+    b1, b2, lr, eps = HP["beta1"], HP["beta2"], HP["lr"], HP["eps"]
+    m_ex = (1 - b1) * g64[fin]
+    v_ex = (1 - b2) * g64[fin] ** 2
+    w_ex = w0[fin].astype(np.float64) - lr * g64[fin] / (np.abs(g64[fin]) + eps)
+
+    def rel_ok(got, ex):
+        got = got.astype(np.float64)
+        nz = ex != 0
+        assert np.all(got[~nz] == 0)
+        return float(np.max(np.abs(got[nz] - ex[nz]) / np.abs(ex[nz])))
+
+    assert rel_ok(m[fin], m_ex) <= 1e-6
+    assert rel_ok(v[fin], v_ex) <= 1e-6
+    assert rel_ok(w[fin], w_ex) <= 1e-6
+    # the fp16 parameter: within one ulp (ordered-integer distance) of fp16(w1)
+    want16 = w_ex.astype(np.float16).view(np.uint16).astype(np.int64)
+    got16 = p[fin].astype(np.int64)
+    assert np.all(np.abs(got16 - want16) <= 1)      # all positive, so bits order the values
+    # non-finite gradients: IEEE classes
+    inf = np.isinf(g64)
+    nan = np.isnan(g64)
+    assert inf.sum() == 2 and nan.sum() == 2046
+    assert np.array_equal(m[inf], np.sign(g64[inf]).astype(np.float32) * np.float32(np.inf))
+    assert np.all(v[inf] == np.inf) and np.all(np.isnan(w[inf]))
+    assert np.all(np.isnan(m[nan])) and np.all(np.isnan(v[nan])) and np.all(np.isnan(w[nan]))
+    pv = p.view(np.float16)
+    assert np.all(np.isnan(pv[~fin]))
