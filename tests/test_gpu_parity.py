@@ -421,3 +421,48 @@ def test_two_plans_on_two_streams(zs, torch_mod):
         assert _compare((d["p"], d["g"], d["w"], d["m"], d["v"]), hosts[k], f"stream {k}") == 0
         assert int(d["rflag"].item()) == 0 and int(d["aflag"].item()) == 0
         plans[k].destroy()
+
+
+def test_fp32_subnormal_state_is_kept(zs, torch_mod):
+    """Master, m and v at fp32 subnormals and just above the smallest normal,
+    gradients 0, +-2^-24 (the smallest fp16 subnormal) or small normals, at
+    t = 7: the kernel keeps subnormals (built without flushing them to
+    zero), bit for bit with the oracle.  The oracle's results must contain
+    subnormal m and v, so the case is exercised."""
+    torch = torch_mod
+    say("fp32 subnormal state")
+    n = 70_001
+    rng = np.random.default_rng(38)
+
+    def tiny(k):
+        # subnormal bit patterns and the first normals, either sign
+        b = rng.integers(1, 0x01000000, size=k, dtype=np.uint64).astype(np.uint32)
+        b |= (rng.random(k) < 0.5).astype(np.uint32) << 31
+        return b.view(np.float32)
+
+    w0, m0 = tiny(n), tiny(n)
+    v0 = np.abs(tiny(n))
+    choice = rng.integers(0, 4, n)
+    g = np.where(choice == 0, 0, np.where(choice == 1, 0x0001, np.where(choice == 2, 0x8001, 0x0400))).astype(np.uint16)
+    host = HostShard(g.copy(), np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy())
+    flag_ref = host.step(7)
+    m_sub = (host.m != 0) & (np.abs(host.m) < np.finfo(np.float32).tiny)
+    v_sub = (host.v != 0) & (host.v < np.finfo(np.float32).tiny)
+    assert m_sub.sum() > 1000 and v_sub.sum() > 1000
+    p = torch.zeros(n, dtype=torch.float16, device="cuda")
+    dev = (p, to_dev16(g), to_dev32(w0), to_dev32(m0), to_dev32(v0))
+    plan = zs.zero_plan_create([dev])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, _hp(zs), 7, flag)
+    torch.cuda.synchronize()
+    assert _compare(dev, host, "subnormal state") == 0
+    assert int(flag.item()) == flag_ref == 0
+    plan.destroy()
+    # the reduce keeps fp16 subnormal slices exact too (sums of a few 2^-24)
+    hs = [rng.choice(np.array([0x0000, 0x0001, 0x8001, 0x0002, 0x03FF], np.uint16), size=n) for _ in range(3)]
+    out = torch.zeros(n, dtype=torch.float16, device="cuda")
+    rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard([to_dev16(h) for h in hs], out, rflag)
+    ref, _ = oracle.reduce_grad(hs)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(out), ref)
