@@ -284,3 +284,29 @@ def test_bf16_fused_nonfinite(zs, bits):
     say(f"bf16 fused inject {bits:#06x}")
     k, f = _fused_case(zs, 4099, 5, "aligned", True, 2, rng, inject=(3, 2050, bits))
     assert f == 1 and k == 0
+
+
+def test_bf16_subnormal_masters_narrow_exactly(zs):
+    """Masters at fp32 subnormals (and the first normals), g = 0 and m = v = 0
+    at t = 1: the master is unchanged and the bfloat16 parameter is its
+    round-to-nearest-even narrowing, subnormal results included (gfx950's
+    conversion with denormals kept), bit for bit with the oracle."""
+    import torch
+    say("bf16 subnormal masters")
+    n = 65_537
+    rng = np.random.default_rng(16)
+    b = rng.integers(1, 0x01000000, size=n, dtype=np.uint64).astype(np.uint32)
+    b |= (rng.random(n) < 0.5).astype(np.uint32) << 31
+    w0 = b.view(np.float32)
+    g = np.zeros(n, np.uint16)
+    P, Wr, M, V = np.zeros(n, np.uint16), w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    assert _step_ref(g, P, Wr, M, V, 1) == 0
+    sub = (P & 0x7F80) == 0
+    assert (sub & ((P & 0x7F) != 0)).sum() > 10000        # many subnormal bfloat16 results
+    p = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    dev = (p, to_devbf(g), to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda"))
+    plan = zs.zero_plan_create([dev])
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1)
+    torch.cuda.synchronize()
+    assert _cmp((dev[0], dev[2], dev[3], dev[4]), (P, Wr, M, V), "bf16 subnormal masters") == 0
+    plan.destroy()
