@@ -466,3 +466,39 @@ def test_fp32_subnormal_state_is_kept(zs, torch_mod):
     ref, _ = oracle.reduce_grad(hs)
     torch.cuda.synchronize()
     assert np.array_equal(host16(out), ref)
+
+
+@pytest.mark.parametrize("hp", [
+    dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8),
+    dict(lr=0.1, beta1=0.0, beta2=0.0, eps=1e-3),      # no averaging at all
+    dict(lr=1.0, beta1=0.5, beta2=0.25, eps=0.0),      # eps = 0: 0 / 0 is NaN where g = m = 0
+    dict(lr=3e-4, beta1=0.95, beta2=0.98, eps=1e-6),
+])
+def test_hyperparameters_and_step_counts(zs, torch_mod, hp):
+    """The step's constants as the kernel receives them, for several
+    hyperparameter sets and step counts t = 1, 2, 1000, 2^40 (bias
+    corrections from 1 - beta down to exactly 1): bit for bit with the
+    oracle, NaN compared by class."""
+    torch = torch_mod
+    rng = np.random.default_rng(int(hp["lr"] * 1e4) + int(hp["beta1"] * 100))
+    n = 20_011
+    for t in (1, 2, 1000, 1 << 40):
+        say(f"hyperparameters {hp} t={t}")
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16)
+        g[:7] = 0                                        # g = 0 rows (NaN when eps = 0 and m = v = 0)
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v0 = (rng.random(n) * 1e-6).astype(np.float32)
+        m0[:3] = 0
+        v0[:3] = 0
+        host = HostShard(g.copy(), np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy())
+        ref_flag = oracle.adam_step(host.g, host.p, host.w, host.m, host.v, t=t, **hp)
+        dev = (torch.zeros(n, dtype=torch.float16, device="cuda"), to_dev16(g), to_dev32(w0),
+               to_dev32(m0), to_dev32(v0))
+        plan = zs.zero_plan_create([dev])
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        zs.zero_adam_step(plan, zs.AdamHParams(**hp), t, flag)
+        torch.cuda.synchronize()
+        assert _compare(dev, host, f"hp {hp} t={t}") == 0
+        assert int(flag.item()) == ref_flag == 0
+        plan.destroy()
