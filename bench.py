@@ -444,6 +444,9 @@ def main():
     dom = max(kstats, key=lambda k: kstats[k]["total_s"])
     d = kstats[dom]
     traffic = measured_traffic(dom, args.workload)
+    if traffic is None:
+        print(f"[bench] no HBM counters for {dom} on {args.workload} taken on the current kernel "
+              f"code ({kernel_src_sha()}): traffic is null", file=sys.stderr, flush=True)
     value = step.n_params * args.steps / wall
     bytes_per_step = sum(b for _, _, b in ks)
     copy = plain_copy(stream)
