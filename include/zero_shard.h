@@ -153,8 +153,11 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * keep the host array).  Each tensor is cut into chunks of chunk_elems
  * elements (its last chunk may be shorter); the step runs one 64-lane wave
  * per 512 consecutive elements of a chunk.
- * chunk_elems: 0 selects the library default (16384); otherwise a multiple
- * of 512 between 512 and 2^24.  Per tensor the library takes the vector
+ * chunk_elems: 0 lets the library choose: the largest of 16384, 8192, ...,
+ * 512 whose workgroups (one per 512 elements of every chunk, a tensor's
+ * last chunk included) exceed those with work by at most one eighth, so
+ * 16384 for big tensors and smaller chunks for many small ones; otherwise a
+ * multiple of 512 between 512 and 2^24.  Per tensor the library takes the vector
  * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree
  * in alignment after peeling at most 3 leading elements, else it moves
  * single elements.  The table is allocated on the current device

@@ -131,9 +131,11 @@ def test_plan_describe_paths(zs):
 
 def test_plan_chunking(zs):
     """Chunk counts: a tensor's first chunk holds its peeled head plus up to
-    chunk_elems elements, then chunk_elems each; the default is 16384."""
-    d = zs.zero_plan_describe([_fake(40000)])
-    assert d["chunk_elems"] == 16384 and d["n_chunks"] == 3
+    chunk_elems elements, then chunk_elems each."""
+    d = zs.zero_plan_describe([_fake(1 << 20, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44)])
+    assert d["chunk_elems"] == 16384 and d["n_chunks"] == 64
+    d = zs.zero_plan_describe([_fake(40000)])            # 16384 would leave 17 of 96 slots idle
+    assert d["chunk_elems"] == 8192 and d["n_chunks"] == 5
     for C in (512, 1024, 4096, 1 << 24):
         for n in (1, 511, 512, 513, 5000, 100003):
             d = zs.zero_plan_describe([_fake(n)], C)
@@ -147,6 +149,52 @@ def test_plan_chunking(zs):
         with pytest.raises(zs.ZeroError) as e:
             zs.zero_plan_describe([_fake(10)], C)
         assert e.value.status == -1
+
+
+def _slots_and_work(sizes, C):
+    """Workgroup slots (chunks x tiles per chunk) and tiles holding work, for
+    aligned tensors (no head), counted tile by tile."""
+    slots = work = 0
+    for n in sizes:
+        chunks = max(1, -(-n // C))
+        slots += chunks * (C // 512)
+        for c in range(chunks):
+            cnt = min(C, n - c * C)
+            work += max(1, -(-cnt // 512))
+    return slots, work
+
+
+def test_plan_chunk_choice(zs):
+    """With chunk_elems = 0 the plan takes the largest of 16384 ... 512 whose
+    workgroup slots exceed the tiles with work by at most one eighth: model
+    lists and big shards keep 16384, many small tensors get small chunks,
+    and an explicit chunk size is kept as given."""
+    rng = np.random.default_rng(12)
+    cases = [[1 << 26], [1024] * 100000, list(rng.integers(1, 601, 4000)),
+             [50_000_000] + [4096] * 10000, list(rng.integers(1, 100_000, 300)),
+             [n for _, n in W.WORKLOADS["llama_7b"].tensors],
+             [n for _, n in W.WORKLOADS["gpt2_xl"].tensors]]
+    for sizes in cases:
+        ents, base = [], 1 << 40
+        for n in sizes:
+            n = int(n)
+            step = (n * 4 + 255) // 256 * 256
+            ents.append(_fake(n, base, base + step, base + 2 * step, base + 3 * step,
+                              base + 4 * step))
+            base += 5 * step
+        C = zs.zero_plan_describe(ents)["chunk_elems"]
+        want = 512
+        for c in (16384, 8192, 4096, 2048, 1024):
+            sl, wk = _slots_and_work([int(n) for n in sizes], c)
+            if sl <= wk + wk // 8:
+                want = c
+                break
+        assert C == want, (len(sizes), C, want)
+    assert zs.zero_plan_describe([_fake(1024)] * 1)["chunk_elems"] == 1024
+    big = [_fake(1024, (1 << 40) + k * (1 << 20), (1 << 41) + k * (1 << 20), (1 << 42) + k * (1 << 20),
+                 (1 << 43) + k * (1 << 20), (1 << 44) + k * (1 << 20)) for k in range(1000)]
+    assert zs.zero_plan_describe(big)["chunk_elems"] == 1024
+    assert zs.zero_plan_describe(big, 16384)["chunk_elems"] == 16384
 
 
 def test_plan_describe_workload_lists(zs):

@@ -502,3 +502,59 @@ def test_hyperparameters_and_step_counts(zs, torch_mod, hp):
         assert _compare(dev, host, f"hp {hp} t={t}") == 0
         assert int(flag.item()) == ref_flag == 0
         plan.destroy()
+
+
+@pytest.mark.parametrize("chunk", [0, 512])
+def test_four_thousand_small_tensors(zs, torch_mod, chunk):
+    """One plan over 4,000 tensors of 1 to 600 elements, each a view into
+    five flat buffers at its own random gap (0-7 elements) in every buffer,
+    so the five arrays of a tensor agree or disagree in alignment at random
+    (vector path or single elements).  Two steps; the whole buffers are
+    compared with the oracle applied tensor by tensor, and the gaps, filled
+    with sentinels, must come back untouched."""
+    torch = torch_mod
+    rng = np.random.default_rng(4000 + chunk)
+    T = 4000
+    sizes = rng.integers(1, 601, T)
+    offs = np.zeros((5, T), np.int64)
+    ends = np.zeros(5, np.int64)
+    for a in range(5):
+        for k in range(T):
+            offs[a, k] = ends[a] + rng.integers(0, 8)
+            ends[a] = offs[a, k] + sizes[k]
+    say(f"{T} small tensors chunk={chunk}: {int(sizes.sum())} elements")
+    hp16 = np.full(ends[0] + 8, 0x7E01, np.uint16)                 # NaN sentinel in the gaps
+    hg16 = np.full(ends[1] + 8, 0x3C00, np.uint16)
+    hw = np.full(ends[2] + 8, 7.0, np.float32)
+    hm = np.full(ends[3] + 8, -3.0, np.float32)
+    hv = np.full(ends[4] + 8, 5.0, np.float32)
+    for k in range(T):
+        n = sizes[k]
+        hw[offs[2, k]:offs[2, k] + n] = rng.standard_normal(n) * 0.02
+        hm[offs[3, k]:offs[3, k] + n] = rng.standard_normal(n) * 1e-4
+        hv[offs[4, k]:offs[4, k] + n] = rng.random(n) * 1e-6
+    dp, dg, dw, dm, dv = to_dev16(hp16), to_dev16(hg16), to_dev32(hw), to_dev32(hm), to_dev32(hv)
+    views = [(dp[offs[0, k]:offs[0, k] + sizes[k]], dg[offs[1, k]:offs[1, k] + sizes[k]],
+              dw[offs[2, k]:offs[2, k] + sizes[k]], dm[offs[3, k]:offs[3, k] + sizes[k]],
+              dv[offs[4, k]:offs[4, k] + sizes[k]]) for k in range(T)]
+    plan = zs.zero_plan_create(views, chunk)
+    st = plan.stats()
+    assert st["n_tensors"] == T and st["n_params"] == int(sizes.sum())
+    assert st["vector_elems"] and st["scalar_elems"]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t in (3, 4):
+        for k in range(T):
+            n = sizes[k]
+            hg16[offs[1, k]:offs[1, k] + n] = (rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16)
+        dg.copy_(to_dev16(hg16))
+        zs.zero_adam_step(plan, _hp(zs), t, flag)
+        for k in range(T):
+            n = sizes[k]
+            sl = [slice(offs[a, k], offs[a, k] + n) for a in range(5)]
+            oracle.adam_step(hg16[sl[1]], hp16[sl[0]], hw[sl[2]], hm[sl[3]], hv[sl[4]], t=t, **HP)
+        torch.cuda.synchronize()
+        assert np.array_equal(host16(dp), hp16), f"fp16 parameters differ at t={t}"
+        for d, h, nm in ((dw, hw, "master"), (dm, hm, "m"), (dv, hv, "v")):
+            assert np.array_equal(host32(d).view(np.uint32), h.view(np.uint32)), f"{nm} differs at t={t}"
+    assert int(flag.item()) == 0
+    plan.destroy()

@@ -156,13 +156,35 @@ bool writes_overlap(std::vector<Range> &r) {
     return false;
 }
 
+// The chunk a plan gets when the caller leaves it to the library: the
+// largest of kDefaultChunk, kDefaultChunk / 2, ..., kTile whose workgroup
+// slots (chunks times tiles per chunk, the launch's virtual workgroups)
+// exceed the tiles that hold work by at most one eighth.  Big tensors keep
+// the compact table of kDefaultChunk; many small tensors get small chunks,
+// so that few workgroups start only to find their tile past the end of a
+// short chunk.
+uint32_t pick_chunk(const std::vector<TensorDesc> &tensors) {
+    for (uint32_t C = kDefaultChunk; C > kTile; C /= 2) {
+        uint64_t slots = 0, work = 0;
+        for (const TensorDesc &d : tensors) {
+            const uint64_t body = d.n - std::min<uint64_t>(d.head, d.n);
+            const uint64_t chunks = body == 0 ? 1 : (body + C - 1) / C;
+            slots += chunks * (C / kTile);
+            work += body == 0 ? 1 : (body + kTile - 1) / kTile;
+        }
+        if (slots <= work + work / 8)
+            return C;
+    }
+    return kTile;
+}
+
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out) {
     if (!out || (n_tensors > 0 && !tensors))
         return ZERO_EINVAL;
-    if (chunk_elems == 0)
-        chunk_elems = kDefaultChunk;
-    if (chunk_elems % kTile != 0 || chunk_elems < kMinChunk || chunk_elems > kMaxChunk)
+    const bool automatic = chunk_elems == 0;
+    if (!automatic &&
+        (chunk_elems % kTile != 0 || chunk_elems < kMinChunk || chunk_elems > kMaxChunk))
         return ZERO_EINVAL;
     HostPlan plan;
     memset(&plan.stats, 0, sizeof(plan.stats));
@@ -209,7 +231,7 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
     if (writes_overlap(ranges))
         return ZERO_EINVAL;
 
-    const uint64_t C = chunk_elems;
+    const uint64_t C = automatic ? pick_chunk(plan.tensors) : chunk_elems;
     zero_plan_stats &s = plan.stats;
     s.n_tensors = n_tensors;
     s.n_params = n_params;

@@ -108,8 +108,9 @@ struct HostPlan {
     zero_plan_stats stats;
 };
 
-// Validate and classify; fills `out`.  chunk_elems: 0 for kDefaultChunk,
-// else a multiple of kTile in [kMinChunk, kMaxChunk].  Pure host code.
+// Validate and classify; fills `out`.  chunk_elems: 0 for the library's
+// choice (kDefaultChunk unless the tensors are small: see pick_chunk), else
+// a multiple of kTile in [kMinChunk, kMaxChunk].  Pure host code.
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out);
 

@@ -244,14 +244,47 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
         adam_single<Fmt>(T, rbase + 4u * nquads + lane, c, bad);
 }
 
-// Tile j of a chunk of a tensor whose arrays disagree in alignment: the
-// tile's elements one at a time, lane-strided so each access instruction of
-// the wave stays contiguous.
+// Tile j of a chunk of a tensor whose arrays disagree in alignment: single
+// elements, lane-strided so each access instruction of the wave stays
+// contiguous.  A full tile loads all of a lane's kTile / 64 elements before
+// the first update (the same per-element operations as adam_single), so
+// the wave keeps as many loads in flight as on the vector path; a partial
+// tile goes element by element.
 template <class Fmt>
 __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chunk &ch,
                                                  uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lo = j * kTile;
     const uint32_t hi = min(ch.count, lo + kTile);
+    if (hi - lo == kTile) {
+        constexpr int G = kTile / kWave;
+        const uint64_t i0 = ch.start + lo + threadIdx.x;
+        uint16_t gb[G];
+        float w[G], m[G], v[G];
+#pragma unroll
+        for (int k = 0; k < G; k++) {
+            const uint64_t i = i0 + (uint64_t)kWave * k;
+            gb[k] = as_global(T.g)[i];
+            w[k] = as_global(T.w)[i];
+            m[k] = as_global(T.m)[i];
+            v[k] = as_global(T.v)[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < G; k++) {
+            const uint64_t i = i0 + (uint64_t)kWave * k;
+            bad |= bits_nonfinite<Fmt>(gb[k]);
+            typename Fmt::T gh;
+            memcpy(&gh, &gb[k], 2);
+            const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c);
+            as_global(T.w)[i] = w[k];
+            as_global(T.m)[i] = m[k];
+            as_global(T.v)[i] = v[k];
+            uint16_t pb;
+            memcpy(&pb, &p, 2);
+            as_global(T.p)[i] = pb;
+        }
+        return;
+    }
     for (uint32_t k = lo + threadIdx.x; k < hi; k += kWave)
         adam_single<Fmt>(T, ch.start + k, c, bad);
 }
