@@ -120,14 +120,15 @@ def test_bf16_every_gradient_pattern(zs):
 
 
 @pytest.mark.parametrize("nd", [1, 2, 3, 8, 16, 17, 64, 256])
-@pytest.mark.parametrize("layout", ["aligned", "phase3", "odd"])
+@pytest.mark.parametrize("layout", ["aligned", "phase3", "mixed4h", "odd"])
 def test_bf16_reduce_matches_oracle(zs, nd, layout):
     import torch
     rng = np.random.default_rng(100 + nd)
-    for n in (1, 9, 4097, 65537):
+    for n in (1, 9, 1027, 4097, 65537):
         say(f"bf16 reduce nd={nd} layout={layout} n={n}")
         hs = [bf16_bits(rng.standard_normal(n) * 1e-3) for _ in range(nd)]
         offs = {"aligned": [0] * (nd + 1), "phase3": [3] * (nd + 1),
+                "mixed4h": [1 + 4 * (r % 2) for r in range(nd + 1)],
                 "odd": [r % 3 for r in range(nd + 1)]}[layout]
         ds = []
         for r in range(nd):

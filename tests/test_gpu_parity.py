@@ -282,18 +282,21 @@ def test_resume_is_bit_exact(zs, torch_mod):
 # Gradient reduction.
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 9, 16, 17, 64, 256])
-@pytest.mark.parametrize("layout", ["aligned", "phase3", "mixed4", "odd"])
+@pytest.mark.parametrize("layout", ["aligned", "phase3", "mixed4", "mixed4h", "odd"])
 def test_reduce_matches_oracle(zs, torch_mod, nd, layout):
     """Every output element of the N_d-slice average, for N_d from 1 to
-    256, sizes with ragged tails, and slice alignments that select each
-    access path (16-byte, peeled head, 8-byte, single element)."""
+    256, sizes with ragged tails (1027 = a head of 3 and two whole 512-element
+    tiles under "mixed4h"), and slice alignments that select each access
+    path (16-byte, peeled head, 8-byte with and without a head, single
+    element)."""
     torch = torch_mod
     rng = np.random.default_rng(1000 + nd)
-    for n in (1, 7, 9, 4097, 65537):
+    for n in (1, 7, 9, 1027, 4097, 65537):
         say(f"reduce nd={nd} layout={layout} n={n}")
         hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
         offs = {"aligned": [0] * (nd + 1), "phase3": [3] * (nd + 1),
                 "mixed4": [4 * (r % 2) for r in range(nd + 1)],
+                "mixed4h": [1 + 4 * (r % 2) for r in range(nd + 1)],
                 "odd": [r % 3 for r in range(nd + 1)]}[layout]
         ds = []
         for r in range(nd):

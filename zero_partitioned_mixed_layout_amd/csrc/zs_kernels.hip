@@ -429,6 +429,71 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
     raise_flag(flag, bad);
 }
 
+// Adds slices r0 .. r0+B-1 (rank order) at a lane's eight single elements
+// i0 + 64k into acc; all 8B two-byte loads are issued before the first add.
+template <int B, class Fmt>
+__device__ __forceinline__ void reduce_batch_single(const SliceArgs &s, uint32_t r0, uint64_t i0,
+                                                    bool first, float (&acc)[8]) {
+    uint16_t x[B][8];
+#pragma unroll
+    for (int q = 0; q < B; q++)
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            x[q][k] = as_global(s.p[r0 + q])[i0 + (uint64_t)kWave * k];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < B; q++)
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            typename Fmt::T h;
+            memcpy(&h, &x[q][k], 2);
+            acc[k] = (first && q == 0) ? (float)h : acc[k] + (float)h;
+        }
+}
+
+// The reduction when the slices and the output share no common phase: one
+// wave per kTile elements, lane L taking elements L + 64k (k < 8), so every
+// two-byte load and store instruction of the wave is one contiguous
+// 128-byte range; slices in batches of 8, 4 and 1, each batch's loads all
+// in flight before its adds; the sum in rank order and one division, as
+// reduce_single.  A partial last tile goes element by element.
+template <class Fmt>
+__global__ __launch_bounds__(kWave) void zs_reduce_single_kernel(SliceArgs s, uint32_t nd,
+                                                                 uint64_t n,
+                                                                 uint16_t *__restrict__ out,
+                                                                 int32_t *__restrict__ flag) {
+    const float count = (float)nd;
+    const uint32_t lane = threadIdx.x;
+    const uint64_t ntiles = (n + kTile - 1) / kTile;
+    int bad = 0;
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t lo = t * kTile;
+        if (lo + kTile > n) {
+            for (uint64_t i = lo + lane; i < n; i += kWave)
+                reduce_one<Fmt>(s, nd, i, count, out, bad);
+            continue;
+        }
+        const uint64_t i0 = lo + lane;
+        float acc[8];
+        uint32_t r = 0;
+        for (; r + 8 <= nd; r += 8)
+            reduce_batch_single<8, Fmt>(s, r, i0, r == 0, acc);
+        for (; r + 4 <= nd; r += 4)
+            reduce_batch_single<4, Fmt>(s, r, i0, r == 0, acc);
+        for (; r < nd; r++)
+            reduce_batch_single<1, Fmt>(s, r, i0, r == 0, acc);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const typename Fmt::T o = (typename Fmt::T)(acc[k] / count);
+            uint16_t b;
+            memcpy(&b, &o, 2);
+            bad |= bits_nonfinite<Fmt>(b);
+            as_global(out)[i0 + (uint64_t)kWave * k] = b;
+        }
+    }
+    raise_flag(flag, bad);
+}
+
 // ---------------------------------------------------------------------------
 // Fused stage-2 step over a flat shard: the reduce and the Adam step in one
 // pass.  Element i's gradient is exactly what zs_reduce_kernel would store
@@ -538,6 +603,64 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
     }
 }
 
+// The reduction when the slices and the output share an 8-byte phase but
+// not a 16-byte one: one wave per kTile elements after the head, each lane
+// reducing two groups of four (elements 4L..4L+3 and kTile/2+4L..), so a
+// lane keeps as many bytes per slice in flight as on the 16-byte path; the
+// rank-order sum and the division of reduce_single.  The last, partial tile
+// goes by groups of four, then singly; tile 0 also does the head.
+template <class Fmt>
+__global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint32_t nd,
+                                                               uint64_t n, uint32_t head,
+                                                               uint64_t ntiles,
+                                                               uint16_t *__restrict__ out,
+                                                               int32_t *__restrict__ flag) {
+    const float count = (float)nd;
+    const uint32_t lane = threadIdx.x;
+    const uint64_t h = head < n ? head : n;
+    int bad = 0;
+    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        if (b == 0 && lane < h)
+            reduce_one<Fmt>(s, nd, lane, count, out, bad);
+        const uint64_t lo = h + b * kTile;
+        if (lo >= n)
+            continue;
+        const uint64_t hi = min(n, lo + kTile);
+        if (hi - lo == kTile) {
+            const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
+            f32x4 acc[2];
+            uint32_t r = 0;
+            for (; r + 8 <= nd; r += 8)
+                fused_batch<Fmt, 8, 2>(s, r, i, r == 0, acc);
+            for (; r + 4 <= nd; r += 4)
+                fused_batch<Fmt, 4, 2>(s, r, i, r == 0, acc);
+            for (; r < nd; r++)
+                fused_batch<Fmt, 1, 2>(s, r, i, r == 0, acc);
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                typename Fmt::V4 o;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    o[j] = (typename Fmt::T)(acc[k][j] / count);
+                    const typename Fmt::T oj = o[j];
+                    uint16_t ob;
+                    memcpy(&ob, &oj, 2);
+                    bad |= bits_nonfinite<Fmt>(ob);
+                }
+                st_nt(o, reinterpret_cast<typename Fmt::V4 *>(out + i[k]));
+            }
+            continue;
+        }
+        const uint32_t nquads = (uint32_t)(hi - lo) / 4u;
+        for (uint32_t q = lane; q < nquads; q += kWave)
+            reduce_group<Fmt, 4>(s, nd, lo + 4u * q, count, out, bad);
+        const uint64_t t0 = lo + 4u * (uint64_t)nquads;
+        if (t0 + lane < hi)
+            reduce_one<Fmt>(s, nd, t0 + lane, count, out, bad);
+    }
+    raise_flag(flag, bad);
+}
+
 // Dynamic LDS of the launch: the part of the occupancy reservation that the
 // fused kernel uses (1 KiB per one-wave workgroup).
 extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
@@ -607,6 +730,53 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
     }
 }
 
+// A full tile of the fused step when the slices, parameter and state share
+// no common phase: lane L takes elements L + 64k (k < 8), every access
+// instruction of the wave contiguous; the fp32 state is loaded first, the
+// slices in batches of 8, 4 and 1 (loads in flight before the adds), then
+// the same per-element reduction, narrowing and update as fused_single.
+template <class Fmt>
+__device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t nd, uint64_t lo,
+                                                  uint32_t lane, float count,
+                                                  const FlatState &F, const AdamConsts &c,
+                                                  int &bad) {
+    const uint64_t i0 = lo + lane;
+    float w[8], m[8], v[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint64_t i = i0 + (uint64_t)kWave * k;
+        w[k] = as_global(F.w)[i];
+        m[k] = as_global(F.m)[i];
+        v[k] = as_global(F.v)[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[8];
+    uint32_t r = 0;
+    for (; r + 8 <= nd; r += 8)
+        reduce_batch_single<8, Fmt>(s, r, i0, r == 0, acc);
+    for (; r + 4 <= nd; r += 4)
+        reduce_batch_single<4, Fmt>(s, r, i0, r == 0, acc);
+    for (; r < nd; r++)
+        reduce_batch_single<1, Fmt>(s, r, i0, r == 0, acc);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint64_t i = i0 + (uint64_t)kWave * k;
+        const typename Fmt::T gh = (typename Fmt::T)(acc[k] / count);
+        uint16_t gb;
+        memcpy(&gb, &gh, 2);
+        bad |= bits_nonfinite<Fmt>(gb);
+        if (F.gout != nullptr)
+            as_global(F.gout)[i] = gb;
+        const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c);
+        as_global(F.w)[i] = w[k];
+        as_global(F.m)[i] = m[k];
+        as_global(F.v)[i] = v[k];
+        uint16_t pb;
+        memcpy(&pb, &p, 2);
+        as_global(F.p)[i] = pb;
+    }
+}
+
 // One wave per tile of kTile elements after the peeled head (tile 0 also
 // does the head).  VEC = 8: full tiles by fused_tile8 (slices 16-byte
 // aligned).  VEC = 4: full tiles with each lane reducing its own two groups
@@ -643,6 +813,8 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
                 if (t0 + lane < hi)
                     fused_single<Fmt>(s, nd, t0 + lane, count, F, c, bad);
             }
+        } else if (hi - lo == kTile) {
+            fused_tile_single<Fmt>(s, nd, lo, lane, count, F, c, bad);
         } else {
             for (uint64_t k = lo + lane; k < hi; k += kWave)
                 fused_single<Fmt>(s, nd, k, count, F, c, bad);
@@ -918,21 +1090,27 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     addr[nd] = o;
     uint32_t vec, head;
     zs::pick_vector_path(addr, (int)nd + 1, nullptr, 0, 8, &vec, &head);
-    // one vector group per lane, one wave per workgroup
-    const uint64_t items = vec > 1 ? (n - (head < n ? head : n)) / vec + 1 : n;
-    const uint64_t want = (items + kWave - 1) / kWave;
+    // 16-byte path: one vector group per lane, one wave per workgroup;
+    // 8-byte path: one 512-element tile per wave (two groups per lane);
+    // single elements: one 512-element tile per wave, half the bytes per
+    // wave in flight, so twice as many workgroups stay resident
+    const uint64_t hh = head < n ? head : n;
+    const uint64_t tiles4 = (n - hh + kTile - 1) / kTile + (n == hh ? 1 : 0);
+    const uint64_t want = vec == 8 ? ((n - hh) / 8 + 1 + kWave - 1) / kWave
+                          : vec == 4 ? tiles4 : (n + kTile - 1) / kTile;
     const uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
-    const size_t lds = lds_cap_bytes(dev, zs::reduce_per_cu(nd));
+    const uint32_t per_cu = zs::reduce_per_cu(nd) * (vec == 1 ? 2u : 1u);
+    const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
         hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
                            n, head, (uint16_t *)out_f16, nonfinite_flag);
     else if (vec == 4)
-        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 4>), dim3(grid), dim3(kWave), lds, st, args, nd,
-                           n, head, (uint16_t *)out_f16, nonfinite_flag);
+        hipLaunchKernelGGL((zs_reduce_vec4_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
+                           nd, n, head, tiles4, (uint16_t *)out_f16, nonfinite_flag);
     else
-        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 1>), dim3(grid), dim3(kWave), lds, st, args, nd,
-                           n, 0u, (uint16_t *)out_f16, nonfinite_flag);
+        hipLaunchKernelGGL((zs_reduce_single_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
+                           nd, n, (uint16_t *)out_f16, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -1029,7 +1207,9 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     const uint64_t h = head < n ? head : n;
     const uint64_t ntiles = (n - h + kTile - 1) / kTile + (n == h ? 1 : 0);
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
-    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd));
+    // the single-element path keeps fewer bytes per wave in flight: twice the
+    // resident workgroups
+    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd) * (vec == 1 ? 2u : 1u));
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
