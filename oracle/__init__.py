@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.orc_bf16_to_f32_array.restype = None
         L.orc_adam_step_fmt.argtypes = [i32, u64, vp, vp, vp, vp, vp, vp, u64, i32]
         L.orc_adam_step_fmt.restype = i32
+        L.orc_adam_step_scaled.argtypes = [i32, u64, vp, vp, vp, vp, vp, vp, u64, ctypes.c_int32,
+                                           i32]
+        L.orc_adam_step_scaled.restype = i32
         L.orc_reduce_fmt.argtypes = [i32, u32, vp, u64, vp]
         L.orc_reduce_fmt.restype = i32
         L.orc_comm_volume.argtypes = [u32, u64, u32, u32, vp]
@@ -185,6 +188,43 @@ def adam_step(grad16, param16, master, m, v, *, lr, beta1, beta2, eps, t,
     if rc < 0:
         raise OracleError(f"orc_adam_step rc={rc}")
     return rc
+
+
+def adam_step_scaled(grad16, param16, master, m, v, *, lr, beta1, beta2, eps, t,
+                     log2_scale, weight_decay=0.0, skip=False, fmt="f16") -> int:
+    """adam_step on gradients that carry a loss scale of 2^log2_scale: each
+    widened gradient is multiplied by 2^-log2_scale first (|log2_scale| <=
+    100).  Returns the non-finite flag of the scaled gradients."""
+    n = master.size
+    g = np.ascontiguousarray(grad16).view(np.uint16)
+    for a, dt in ((param16, np.uint16), (master, np.float32), (m, np.float32),
+                  (v, np.float32)):
+        assert a.dtype.itemsize == np.dtype(dt).itemsize and a.size == n
+    assert g.size == n
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    rc = lib().orc_adam_step_scaled(_FMT[fmt], n, _ptr(g), _ptr(param16), _ptr(master), _ptr(m),
+                                    _ptr(v), _ptr(hp), t, int(log2_scale), int(bool(skip)))
+    if rc < 0:
+        raise OracleError(f"orc_adam_step_scaled rc={rc}")
+    return rc
+
+
+def loss_scale_update(state, flag, *, interval, min_log2, max_log2):
+    """One update of a dynamic loss scale after a step whose gradients had
+    the non-finite flag ``flag``.  ``state`` = (log2_scale, good_steps,
+    skipped_steps, applied_steps); returns the new tuple.
+
+    Not on the pages (a reading): a step with a non-finite gradient is
+    skipped and the scale halves, down to 2^min_log2; every ``interval``-th
+    finite step in a row doubles it, up to 2^max_log2, and restarts the
+    count.  Powers of two keep the unscaling multiply exact."""
+    k, good, skipped, applied = state
+    if flag:
+        return (max(min_log2, k - 1), 0, skipped + 1, applied)
+    good += 1
+    if good >= interval:
+        return (min(max_log2, k + 1), 0, skipped, applied + 1)
+    return (k, good, skipped, applied + 1)
 
 
 def reduce_grad(slices, out=None, fmt="f16"):

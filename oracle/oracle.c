@@ -318,9 +318,9 @@ int orc_adam_scalars(const double hp[5], uint64_t t, float out[8])
  * element.  Returns 1 if any gradient is infinite or NaN, else 0; if skip is
  * nonzero nothing is read or written and 0 is returned.
  */
-int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
-                      float *w, float *m, float *v, const double hp[5], uint64_t t,
-                      int skip)
+static int adam_over(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
+                     float *w, float *m, float *v, const double hp[5], uint64_t t,
+                     int skip, int scaled, float unscale)
 {
     if (fmt != ORC_FMT_F16 && fmt != ORC_FMT_BF16)
         return ORC_EINVAL;
@@ -337,6 +337,8 @@ int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *par
         if (!orc_is_finite(fmt, grad16[i]))
             flag = 1;
         float g = orc_widen(fmt, grad16[i]);
+        if (scaled)
+            g = g * unscale;
 
         float m_old = b1 * m[i];
         float m_in = omb1 * g;
@@ -361,6 +363,34 @@ int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *par
         param16[i] = orc_narrow(fmt, w_new);
     }
     return flag;
+}
+
+int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
+                      float *w, float *m, float *v, const double hp[5], uint64_t t,
+                      int skip)
+{
+    return adam_over(fmt, n, grad16, param16, w, m, v, hp, t, skip, 0, 1.0f);
+}
+
+/*
+ * The same step on gradients that carry a loss scale of 2^k.  The pages do
+ * not treat loss scaling; they do say that fp16 loses gradient values below
+ * 2^-24 ([16B] "Why you can't just delete the fp32 copies"), which is what a
+ * scale on the loss, and so on every gradient, works against.  Reading: the
+ * widened gradient is multiplied by 2^-k in fp32 before the update above.
+ * For |k| <= 100 this product is exact for every finite fp16 value (it stays
+ * a normal fp32 number), so the step equals the unscaled step on the true
+ * gradient whenever that gradient is itself an fp16 value.  Other k are
+ * rejected.
+ */
+int orc_adam_step_scaled(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
+                         float *w, float *m, float *v, const double hp[5], uint64_t t,
+                         int32_t log2_scale, int skip)
+{
+    if (log2_scale < -100 || log2_scale > 100)
+        return ORC_EINVAL;
+    const float unscale = (float)ldexp(1.0, -log2_scale);
+    return adam_over(fmt, n, grad16, param16, w, m, v, hp, t, skip, 1, unscale);
 }
 
 /* The fp16 step above (the pages' 16-byte ledger). */

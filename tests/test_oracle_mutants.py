@@ -60,6 +60,10 @@ MUTANTS = {
                         "mag = ldexp(128.0 + (double)F, E - 133);"),
     "bf16_flag_exponent": ("return fmt == ORC_FMT_BF16 ? ((h >> 7) & 0xff) != 255 : orc_f16_is_finite(h);",
                            "return fmt == ORC_FMT_BF16 ? ((h >> 7) & 0xff) != 254 : orc_f16_is_finite(h);"),
+    "unscale_divides": ("            g = g * unscale;", "            g = g / unscale;"),
+    "unscale_sign": ("ldexp(1.0, -log2_scale)", "ldexp(1.0, log2_scale)"),
+    "unscale_dropped": ("        if (scaled)\n            g = g * unscale;\n", ""),
+    "unscale_off_by_one": ("ldexp(1.0, -log2_scale)", "ldexp(1.0, -log2_scale - 1)"),
     "gather_reversed": ("full[(uint64_t)r * shard_len + i] = shards[r][i];",
                         "full[(uint64_t)r * shard_len + i] = shards[nd - 1 - r][i];"),
 }
@@ -85,7 +89,7 @@ def test_pins_catch_planted_mistake(tmp_path, name):
     files = [os.path.join(HERE, f) for f in (
         "test_oracle_fp16.py", "test_oracle_ledger_layout.py",
         "test_oracle_adam.py", "test_oracle_reduce.py", "test_oracle_comm.py",
-        "test_oracle_bf16.py")]
+        "test_oracle_bf16.py", "test_oracle_loss_scale.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-k", "not every_fp32_pattern", *files],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
