@@ -237,6 +237,65 @@ int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp,
                    const int32_t *skip_if_nonzero, void *stream);
 
 /*
+ * Dynamic loss scale.  The pages do not treat loss scaling; they say that
+ * fp16 loses gradient values below 2^-24 ([16B] "Why you can't just delete
+ * the fp32 copies"), which a power-of-two factor on the loss, and so on
+ * every gradient, keeps inside fp16's range.  The scale is 2^log2_scale.
+ * Lives in device memory (16 bytes, 4-byte aligned); the caller writes the
+ * initial value (e.g. {16, 0, 0, 0}) and afterwards only
+ * zero_loss_scale_update changes it.
+ */
+typedef struct zero_loss_scale {
+    int32_t log2_scale;     /* the gradients carry a factor 2^log2_scale   */
+    uint32_t good_steps;    /* finite steps since the scale last changed   */
+    uint32_t skipped_steps; /* steps skipped for a non-finite gradient     */
+    uint32_t applied_steps; /* steps applied (both counts wrap at 2^32)    */
+} zero_loss_scale;
+
+#define ZERO_LOG2_SCALE_MAX 100 /* |log2_scale| bound: 2^-k stays normal fp32 */
+
+/*
+ * zero_adam_step_scaled -- zero_adam_step on gradients that carry the loss
+ * scale *scale: each widened gradient is multiplied by 2^-log2_scale in fp32
+ * before the update (exact for every finite fp16 value), so the step equals
+ * the unscaled step on the true gradient wherever that is representable.
+ * log2_scale is read on the device when the step starts and clamped to
+ * [-ZERO_LOG2_SCALE_MAX, ZERO_LOG2_SCALE_MAX].  Plans of either format.
+ * A step skipped through skip_if_nonzero leaves everything unchanged; the
+ * caller chooses t, so a caller that wants t to count applied steps reads
+ * the flag (or applied_steps) before the next step.
+ * scale: device pointer (required, 4-byte aligned, read only); no other
+ *   argument may point into it.
+ * Errors: those of zero_adam_step; EINVAL (NULL or misaligned scale, the
+ * flag or skip pointer inside *scale).
+ */
+int zero_adam_step_scaled(const zero_plan *plan, const zero_adam_hparams *hp,
+                          uint64_t t, const zero_loss_scale *scale,
+                          int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
+                          void *stream);
+
+/*
+ * zero_loss_scale_update -- one update of *scale after a step, from the
+ * non-finite flag of that step's gradients, then the flag is set to 0 so
+ * that the next step's kernels can OR into it again.  On the device, one
+ * thread:
+ *   flag != 0:  log2_scale = max(min_log2, log2_scale - 1); good_steps = 0;
+ *               skipped_steps += 1
+ *   flag == 0:  applied_steps += 1; good_steps += 1;
+ *               if good_steps >= interval:
+ *                   log2_scale = min(max_log2, log2_scale + 1); good_steps = 0
+ * Used as: reduce (flag) -> zero_adam_step_scaled (skip = the same flag) ->
+ * zero_loss_scale_update (flag), all on one stream.
+ * scale, nonfinite_flag: device pointers, 4-byte aligned, not overlapping.
+ * Asynchronous; allocates nothing.  Errors: EINVAL (NULL or misaligned
+ * pointer, overlap, interval = 0, min_log2 > max_log2, either outside
+ * [-ZERO_LOG2_SCALE_MAX, ZERO_LOG2_SCALE_MAX]); EHIP.
+ */
+int zero_loss_scale_update(zero_loss_scale *scale, int32_t *nonfinite_flag,
+                           uint32_t interval, int32_t min_log2, int32_t max_log2,
+                           void *stream);
+
+/*
  * zero_reduce_grad_shard -- this rank's final gradient for its partition
  * from the nd ranks' fp16 slices of it: the reduce-scatter leaves every
  * rank with the summed gradient of its own partition only ([16B] "The part

@@ -262,6 +262,37 @@ def test_step_and_reduce_reject_before_any_device_call(zs):
     assert L.zero_reduce_grad_shard(p, 2, 0, 0x3000, None, None) == 0
 
 
+def test_loss_scale_rejects_before_any_device_call(zs):
+    """zero_adam_step_scaled and zero_loss_scale_update check their
+    pointers and ranges on the host first (fake addresses, never used)."""
+    import ctypes
+    L = zs.lib()
+    hp = zs.AdamHParams()._c()
+    S = 0x10000                                   # a fake 16-byte scale record
+    assert L.zero_adam_step_scaled(None, ctypes.byref(hp), 1, None, None, None, None) == -1
+    assert L.zero_adam_step_scaled(None, ctypes.byref(hp), 1, S, None, None, None) == -1
+
+    def upd(scale=S, flag=0x20000, interval=2000, lo=0, hi=24):
+        return L.zero_loss_scale_update(scale, flag, interval, lo, hi, None)
+
+    assert upd(scale=None) == -1
+    assert upd(flag=None) == -1
+    assert upd(scale=S + 2) == -1                 # misaligned
+    assert upd(flag=0x20002) == -1
+    for f in (S, S + 4, S + 8, S + 12):           # the flag inside the record
+        assert upd(flag=f) == -1
+    assert upd(interval=0) == -1
+    assert upd(lo=5, hi=4) == -1
+    assert upd(lo=-101) == -1
+    assert upd(hi=101) == -1
+    with pytest.raises(ValueError):
+        zs.LossScale(min_log2=3, max_log2=2)
+    with pytest.raises(ValueError):
+        zs.LossScale(max_log2=101)
+    with pytest.raises(ValueError):
+        zs.LossScale(interval=0)
+
+
 def test_fused_rejects_before_any_device_call(zs):
     """zero_reduce_adam_step validates everything on the host first."""
     import ctypes

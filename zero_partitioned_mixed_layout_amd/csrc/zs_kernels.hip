@@ -85,6 +85,7 @@ __device__ __forceinline__ const ZS_GLOBAL T *as_global(const T *p) {
 
 struct AdamConsts {
     float lr, b1, omb1, b2, omb2, bc1, bc2, eps;
+    float unscale; // 2^-k for gradients that carry a loss scale 2^k, else 1
 };
 
 template <typename T>
@@ -123,6 +124,7 @@ __device__ __forceinline__ void raise_flag(int32_t *flag, int bad) {
 template <class Fmt = FmtF16>
 __device__ __forceinline__ typename Fmt::T adam_elem(float g, float &w, float &m, float &v,
                                                      const AdamConsts &c) {
+    g = g * c.unscale; // exact: a power of two, the product a normal fp32
     const float m_old = c.b1 * m;
     const float m_in = c.omb1 * g;
     m = m_old + m_in;
@@ -297,9 +299,13 @@ template <class Fmt>
 __global__ __launch_bounds__(kWave) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
     uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
-    const int32_t *__restrict__ skip) {
+    const int32_t *__restrict__ skip, const int32_t *__restrict__ log2_scale) {
     if (skip != nullptr && *skip != 0)
         return; // the same value for every wave: the whole step is skipped
+    if (log2_scale != nullptr) {
+        const int k = min(max(*log2_scale, -ZERO_LOG2_SCALE_MAX), ZERO_LOG2_SCALE_MAX);
+        c.unscale = __uint_as_float((uint32_t)(127 - k) << 23); // 2^-k, a normal fp32
+    }
     int bad = 0;
     for (uint64_t vb = blockIdx.x; vb < n_virtual; vb += gridDim.x) {
         const uint64_t ci = vb / tiles_per_chunk;
@@ -1014,9 +1020,9 @@ extern "C" int zero_plan_destroy(zero_plan *plan) {
     return rc;
 }
 
-extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
-                              int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
-                              void *stream) {
+static int adam_step_launch(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
+                            int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
+                            const int32_t *log2_scale, void *stream) {
     if (!plan || !hp)
         return ZERO_EINVAL;
     if (nonfinite_flag != nullptr && (const void *)nonfinite_flag == (const void *)skip_if_nonzero)
@@ -1034,7 +1040,7 @@ extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp
     }
     if (dev != plan->device)
         return ZERO_EINVAL;
-    const AdamConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
+    const AdamConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7], 1.0f};
     // one one-wave workgroup per wave tile, dispatched in order and balanced
     // over the CUs by the hardware; only plans beyond kMaxGrid tiles stride
     const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / kTile);
@@ -1043,11 +1049,73 @@ extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp
     if (plan->bf16)
         hipLaunchKernelGGL(zs_adam_kernel<FmtBF16>, dim3(grid), dim3(kWave), plan->lds_cap,
                            (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
-                           c, nonfinite_flag, skip_if_nonzero);
+                           c, nonfinite_flag, skip_if_nonzero, log2_scale);
     else
         hipLaunchKernelGGL(zs_adam_kernel<FmtF16>, dim3(grid), dim3(kWave), plan->lds_cap,
                            (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
-                           c, nonfinite_flag, skip_if_nonzero);
+                           c, nonfinite_flag, skip_if_nonzero, log2_scale);
+    if (hipGetLastError() != hipSuccess)
+        return ZERO_EHIP;
+    return ZERO_OK;
+}
+
+extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
+                              int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
+                              void *stream) {
+    return adam_step_launch(plan, hp, t, nonfinite_flag, skip_if_nonzero, nullptr, stream);
+}
+
+// true when the 4-byte word at p lies inside the loss-scale record at s
+static bool inside_scale(const void *p, const zero_loss_scale *s) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)s;
+    return p != nullptr && a + 4 > b && a < b + sizeof(zero_loss_scale);
+}
+
+extern "C" int zero_adam_step_scaled(const zero_plan *plan, const zero_adam_hparams *hp,
+                                     uint64_t t, const zero_loss_scale *scale,
+                                     int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
+                                     void *stream) {
+    if (!scale || (uintptr_t)scale % 4 || inside_scale(nonfinite_flag, scale) ||
+        inside_scale(skip_if_nonzero, scale))
+        return ZERO_EINVAL;
+    return adam_step_launch(plan, hp, t, nonfinite_flag, skip_if_nonzero, &scale->log2_scale,
+                            stream);
+}
+
+// One update of the dynamic loss scale from the step's non-finite flag, by
+// one thread; the flag is then cleared for the next step.
+__global__ __launch_bounds__(kWave) void zs_loss_scale_kernel(zero_loss_scale *__restrict__ s,
+                                                              int32_t *__restrict__ flag,
+                                                              uint32_t interval, int32_t lo,
+                                                              int32_t hi) {
+    if (threadIdx.x != 0)
+        return;
+    zero_loss_scale st = *s;
+    if (*flag != 0) {
+        st.log2_scale = (int32_t)max((int64_t)lo, (int64_t)st.log2_scale - 1);
+        st.good_steps = 0;
+        st.skipped_steps += 1;
+    } else {
+        st.applied_steps += 1;
+        st.good_steps += 1;
+        if (st.good_steps >= interval) {
+            st.log2_scale = (int32_t)min((int64_t)hi, (int64_t)st.log2_scale + 1);
+            st.good_steps = 0;
+        }
+    }
+    *s = st;
+    *flag = 0;
+}
+
+extern "C" int zero_loss_scale_update(zero_loss_scale *scale, int32_t *nonfinite_flag,
+                                      uint32_t interval, int32_t min_log2, int32_t max_log2,
+                                      void *stream) {
+    if (!scale || !nonfinite_flag || (uintptr_t)scale % 4 || (uintptr_t)nonfinite_flag % 4 ||
+        inside_scale(nonfinite_flag, scale) || interval == 0 || min_log2 > max_log2 ||
+        min_log2 < -ZERO_LOG2_SCALE_MAX || max_log2 > ZERO_LOG2_SCALE_MAX)
+        return ZERO_EINVAL;
+    hipLaunchKernelGGL(zs_loss_scale_kernel, dim3(1), dim3(kWave), 0, (hipStream_t)stream, scale,
+                       nonfinite_flag, interval, min_log2, max_log2);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -1213,7 +1281,7 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
-    const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]};
+    const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7], 1.0f};
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,

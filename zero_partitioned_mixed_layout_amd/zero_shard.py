@@ -28,6 +28,7 @@ ZERO_EHIP = -3
 ZERO_ENOMEM = -4
 ZERO_ENOTSUP = -5
 ZERO_MAX_SLICES = 256
+ZERO_LOG2_SCALE_MAX = 100
 
 
 class ZeroError(RuntimeError):
@@ -84,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "zero_plan_destroy": [vp],
         "zero_adam_scalars": [ctypes.POINTER(_HParams), u64, ctypes.POINTER(ctypes.c_float)],
         "zero_adam_step": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp],
+        "zero_adam_step_scaled": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp, vp],
+        "zero_loss_scale_update": [vp, vp, u32, ctypes.c_int32, ctypes.c_int32, vp],
         "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
         "zero_reduce_adam_step": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(_HParams), u64, vp, vp],
@@ -117,7 +120,8 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
            "zero_reduce_adam_step", "zero_reduce_adam_step_bf16", "zero_adam_step_host",
            "zero_adam_step_host_bf16", "zero_offload_create", "zero_offload_step_bf16",
-           "zero_offload_destroy", "zero_offload_step", "zero_status_str")
+           "zero_offload_destroy", "zero_offload_step", "zero_status_str",
+           "zero_adam_step_scaled", "zero_loss_scale_update")
 
 
 def lib() -> ctypes.CDLL:
@@ -306,14 +310,56 @@ def zero_plan_destroy(plan: Plan) -> None:
 
 
 def zero_adam_step(plan: Plan, hp, t: int, nonfinite_flag: Optional[torch.Tensor] = None,
-                   skip_if_nonzero: Optional[torch.Tensor] = None, stream=None) -> None:
+                   skip_if_nonzero: Optional[torch.Tensor] = None, stream=None,
+                   loss_scale: Optional["LossScale"] = None) -> None:
     """Enqueue one Adam step over the plan on `stream` (torch's current stream
-    by default)."""
+    by default).  With `loss_scale`, the gradients carry its factor 2^k and
+    are multiplied by 2^-k first (zero_adam_step_scaled)."""
     h = _hp(hp)
     f = _flag_ptr(nonfinite_flag, "nonfinite_flag", plan.device)
     s = _flag_ptr(skip_if_nonzero, "skip_if_nonzero", plan.device)
-    _check("zero_adam_step", _lib.zero_adam_step(plan.handle, ctypes.byref(h), int(t), f, s,
-                                                 _stream_handle(stream)))
+    if loss_scale is None:
+        _check("zero_adam_step", _lib.zero_adam_step(plan.handle, ctypes.byref(h), int(t), f, s,
+                                                     _stream_handle(stream)))
+        return
+    if loss_scale.state.device != plan.device:
+        raise ValueError(f"loss_scale: on {loss_scale.state.device}, expected {plan.device}")
+    _check("zero_adam_step_scaled",
+           _lib.zero_adam_step_scaled(plan.handle, ctypes.byref(h), int(t),
+                                      loss_scale.state.data_ptr(), f, s, _stream_handle(stream)))
+
+
+class LossScale:
+    """A dynamic loss scale 2^k held on the device as the four int32 of
+    zero_loss_scale: (log2_scale, good_steps, skipped_steps, applied_steps).
+
+    One step: zero_reduce_grad_shard(..., flag); zero_adam_step(plan, hp, t,
+    skip_if_nonzero=flag, loss_scale=ls); ls.update(flag) -- which halves the
+    scale after a non-finite gradient, doubles it after `interval` finite
+    steps in a row, and clears the flag."""
+
+    def __init__(self, log2_scale: int = 16, interval: int = 2000, min_log2: int = 0,
+                 max_log2: int = 24, device=None):
+        if not -ZERO_LOG2_SCALE_MAX <= min_log2 <= max_log2 <= ZERO_LOG2_SCALE_MAX:
+            raise ValueError("need -100 <= min_log2 <= max_log2 <= 100")
+        if interval < 1:
+            raise ValueError("interval must be >= 1")
+        self.interval, self.min_log2, self.max_log2 = int(interval), int(min_log2), int(max_log2)
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        self.state = torch.tensor([int(log2_scale), 0, 0, 0], dtype=torch.int32, device=device)
+
+    def update(self, nonfinite_flag: torch.Tensor, stream=None) -> None:
+        """Enqueue the scale's update from the step's flag (then set to 0)."""
+        f = _flag_ptr(nonfinite_flag, "nonfinite_flag", self.state.device)
+        _check("zero_loss_scale_update",
+               _lib.zero_loss_scale_update(self.state.data_ptr(), f, self.interval,
+                                           self.min_log2, self.max_log2, _stream_handle(stream)))
+
+    def read(self) -> tuple:
+        """(log2_scale, good_steps, skipped_steps, applied_steps); waits for
+        the device."""
+        v = self.state.cpu().tolist()
+        return (v[0], v[1] & 0xFFFFFFFF, v[2] & 0xFFFFFFFF, v[3] & 0xFFFFFFFF)
 
 
 def zero_reduce_grad_shard(slices: Sequence[torch.Tensor], out: torch.Tensor,
