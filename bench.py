@@ -110,6 +110,10 @@ def parse():
                          "and clear the non-finite flag before every step, so that each Adam "
                          "launch raises it afresh (for counting the flag's atomics; the clear "
                          "is timed with the step)")
+    ap.add_argument("--loss-scale", type=int, default=None, metavar="LOG2",
+                    help="the Adam step reads the gradients as carrying a loss scale of 2^LOG2 "
+                         "(zero_adam_step_scaled) and each step ends with the scale's update "
+                         "(zero_loss_scale_update), which consumes the step's flag")
     ap.add_argument("--fused", action="store_true",
                     help="workloads with gradient slices: one zero_reduce_adam_step launch per "
                          "step instead of zero_reduce_grad_shard + zero_adam_step")
@@ -193,7 +197,7 @@ class Step:
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
-                 slices=False, inject_inf=False):
+                 slices=False, inject_inf=False, loss_scale=None):
         import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
@@ -237,6 +241,11 @@ class Step:
             self.offload = zs.zero_offload_create(offload_chunk, offload_threads)
             self.offload_threads_used = offload_threads or min(16, os.cpu_count() or 1)
             self.fused = False
+        self.loss_scale = None
+        if loss_scale is not None and self.offload is None and not self.fused:
+            self.loss_scale = zs.LossScale(log2_scale=loss_scale, interval=2000,
+                                           min_log2=min(0, loss_scale),
+                                           max_log2=max(24, loss_scale))
         self.gather = gather and self.rows is not None
         if self.gather:
             # this rank's fp16 shard is the view of the full buffer at its
@@ -253,7 +262,13 @@ class Step:
         if self.inject_inf:
             self.flag.zero_()
         skip = self.rflag if self.rows is not None else None
-        self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip)
+        self.zs.zero_adam_step(self.plan, self.hp, self.t, self.flag, skip,
+                               loss_scale=self.loss_scale)
+
+    def scale_update(self):
+        # the reduce's flag when there is a reduce (the step's skip input),
+        # else the Adam step's own
+        self.loss_scale.update(self.rflag if self.rows is not None else self.flag)
 
     def offload_step(self):
         self.t += 1
@@ -280,6 +295,8 @@ class Step:
                 ks.append(("zero_offload_step", self.offload_step, 4 * self.n_params))
             else:
                 ks.append(("zs_adam_kernel", self.adam, 28 * self.n_params))
+            if self.loss_scale is not None:
+                ks.append(("zs_loss_scale_kernel", self.scale_update, 20))
         if self.gather:
             ks.append(("zs_gather_kernel", self.gather_full,
                        4 * self.layout.shard_len * (self.wl.nd - 1)))
@@ -412,7 +429,7 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
                 args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
-                args.slices, args.inject_inf)
+                args.slices, args.inject_inf, args.loss_scale)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -455,6 +472,7 @@ def main():
     cfg = {"workload": args.workload +
            ("+slices" if args.slices and not step.wl.reduce_slices and step.rows is not None else "") +
            ("+inf" if step.inject_inf else "") +
+           (f"+loss_scale_2^{args.loss_scale}" if step.loss_scale is not None else "") +
            ("+fused" if step.fused else "") +
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
            ("+bf16" if args.bf16 else ""),
