@@ -87,3 +87,77 @@ def test_captured_step_replays_match_the_oracle(zs):
         torch.cuda.synchronize()
         del scratch
     plan.destroy()
+
+
+def test_captured_loss_scaled_step_follows_the_scale(zs):
+    """reduce -> scaled Adam (skip = the reduce's flag) -> scale update,
+    captured once and replayed six times with new slice contents written
+    eagerly before each replay (infinities in replays 2 and 3).  The scale
+    lives on the device, so replays read the scale the previous replay left:
+    a skipped replay halves it and the next replays run with the new factor.
+    No flag clear is captured: the update kernel clears the flag."""
+    import torch
+    n, nd, t = 40_003, 4, 2
+    say(f"graph capture, loss-scaled step n={n} nd={nd}")
+    rng = np.random.default_rng(13)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    slices = [torch.zeros(n, dtype=torch.float16, device="cuda") for _ in range(nd)]
+    g = torch.empty(n, dtype=torch.float16, device="cuda")
+    p = torch.zeros(n, dtype=torch.float16, device="cuda")
+    w, m, v = to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = zs.zero_plan_create([(p, g, w, m, v)])
+    hp = zs.AdamHParams(**HP)
+    ls = zs.LossScale(log2_scale=10, interval=2, min_log2=0, max_log2=12)
+    init = ls.state.clone()
+
+    def step():
+        zs.zero_reduce_grad_shard(slices, g, rflag)
+        zs.zero_adam_step(plan, hp, t, skip_if_nonzero=rflag, loss_scale=ls)
+        ls.update(rflag)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    w.copy_(to_dev32(w0))
+    m.zero_()
+    v.zero_()
+    p.zero_()
+    ls.state.copy_(init)
+    rflag.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    assert ls.read() == (10, 0, 0, 0)
+    P, Wr, M, V = np.zeros(n, np.uint16), w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    st = (10, 0, 0, 0)
+    for k in range(6):
+        hs = [(rng.standard_normal(n) * 1e-3 * 2.0 ** st[0]).astype(np.float16).view(np.uint16)
+              for _ in range(nd)]
+        if k in (2, 3):
+            hs[k][(k * 7919) % n] = 0xFC00
+        for s_, h in zip(slices, hs):
+            s_.copy_(to_dev16(h))
+        torch.cuda.synchronize()
+        say(f"graph replay {k} (scale 2^{st[0]})")
+        graph.replay()
+        torch.cuda.synchronize()
+        g_ref, rf = oracle.reduce_grad(hs)
+        assert rf == int(k in (2, 3))
+        oracle.adam_step_scaled(g_ref, P, Wr, M, V, t=t, log2_scale=st[0], skip=bool(rf), **HP)
+        st = oracle.loss_scale_update(st, rf, interval=2, min_log2=0, max_log2=12)
+        assert ls.read() == st
+        assert int(rflag.item()) == 0
+        res = [check16(host16(p), P, "replay param"), check32(host32(w), Wr, "replay master"),
+               check32(host32(m), M, "replay m"), check32(host32(v), V, "replay v")]
+        assert sum(r["not_bit_exact"] for r in res) == 0, k
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        del scratch
+    assert st[2] == 2 and st[3] == 4
+    plan.destroy()
