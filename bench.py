@@ -482,6 +482,7 @@ def main():
            "injected_inf": step.n_inf if step.inject_inf else None,
            "list_layout": args.list_layout if len(step.wl.tensors) > 1 else None,
            "chunk_elems": step.plan.stats()["chunk_elems"],
+           "adam_tile_elems": step.plan.stats()["tile_elems"],
            "kernels_per_step": [k for k, _, _ in ks],
            "alg_bytes_per_step": bytes_per_step,
            "step_hbm_gbps": bytes_per_step * args.steps / wall / 1e9}

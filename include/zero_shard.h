@@ -95,6 +95,8 @@ typedef struct zero_plan_stats {
     uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
                                tensors whose arrays disagree in alignment) */
     uint64_t table_bytes;   /* device bytes of the chunk table */
+    uint64_t tile_elems;    /* elements one 64-lane wave of the step updates:
+                               256 or 512 (see zero_plan_create) */
 } zero_plan_stats;
 
 /*
@@ -152,10 +154,12 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * tensors: host array of n_tensors descriptors (copied; the table does not
  * keep the host array).  Each tensor is cut into chunks of chunk_elems
  * elements (its last chunk may be shorter); the step runs one 64-lane wave
- * per 512 consecutive elements of a chunk.
+ * per tile_elems consecutive elements of a chunk: 256 when at least 7/8 of
+ * the plan's elements take the vector path and chunk_elems is 16384, else
+ * 512 (the faster of the two, measured, for such plans).
  * chunk_elems: 0 lets the library choose: the largest of 16384, 8192, ...,
- * 512 whose workgroups (one per 512 elements of every chunk, a tensor's
- * last chunk included) exceed those with work by at most one eighth, so
+ * 512 whose 512-element tiles (counted over every chunk, a tensor's last
+ * chunk included) exceed those with work by at most one eighth, so
  * 16384 for big tensors and smaller chunks for many small ones; otherwise a
  * multiple of 512 between 512 and 2^24.  Per tensor the library takes the vector
  * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree

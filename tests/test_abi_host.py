@@ -151,16 +151,16 @@ def test_plan_chunking(zs):
         assert e.value.status == -1
 
 
-def _slots_and_work(sizes, C):
-    """Workgroup slots (chunks x tiles per chunk) and tiles holding work, for
-    aligned tensors (no head), counted tile by tile."""
+def _slots_and_work(sizes, C, tile=512):
+    """Tile slots (chunks x 512-element tiles per chunk) and tiles holding
+    work, for aligned tensors (no head), counted tile by tile."""
     slots = work = 0
     for n in sizes:
         chunks = max(1, -(-n // C))
-        slots += chunks * (C // 512)
+        slots += chunks * (C // tile)
         for c in range(chunks):
             cnt = min(C, n - c * C)
-            work += max(1, -(-cnt // 512))
+            work += max(1, -(-cnt // tile))
     return slots, work
 
 
@@ -195,6 +195,38 @@ def test_plan_chunk_choice(zs):
                  (1 << 43) + k * (1 << 20), (1 << 44) + k * (1 << 20)) for k in range(1000)]
     assert zs.zero_plan_describe(big)["chunk_elems"] == 1024
     assert zs.zero_plan_describe(big, 16384)["chunk_elems"] == 16384
+
+
+def test_plan_tile_choice(zs):
+    """The step's tile: 256 elements per wave when at least 7/8 of the
+    plan's elements take the vector path and the chunk is 16384 (big
+    tensors), else 512."""
+    def tile(ents, chunk=0):
+        return zs.zero_plan_describe(ents, chunk)["tile_elems"]
+    big = _fake(1 << 26, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44)
+    assert tile([big]) == 256
+    assert tile([big], 16384) == 256
+    assert tile([big], 8192) == 512                       # not the default chunk
+    single = _fake(1 << 26, 1 << 40, 1 << 41, (1 << 42) + 4, 1 << 43, 1 << 44)
+    assert zs.zero_plan_describe([single])["scalar_elems"] == 1 << 26
+    assert tile([single]) == 512                           # all single elements
+    small = [_fake(1024, (1 << 40) + k * (1 << 20), (1 << 41) + k * (1 << 20),
+                   (1 << 42) + k * (1 << 20), (1 << 43) + k * (1 << 20),
+                   (1 << 44) + k * (1 << 20)) for k in range(1000)]
+    assert tile(small) == 512                              # the plan takes 1024-element chunks
+    # exactly 1/8 of the elements single: still 256; a little more: 512
+    vec = _fake(7 << 20, 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44)
+    for n_single, want in ((1 << 20, 256), ((1 << 20) + 8, 512)):
+        one = _fake(n_single, 1 << 45, 3 << 44, (1 << 46) + 4, 5 << 44, 7 << 44)
+        d = zs.zero_plan_describe([vec, one])
+        assert d["scalar_elems"] == n_single and d["tile_elems"] == want, (n_single, d)
+    for name in ("llama_7b", "gpt2_xl"):
+        ents, base = [], 1 << 40
+        for _, n in W.WORKLOADS[name].tensors:
+            step = (n * 4 + 255) // 256 * 256
+            ents.append(_fake(n, base, base + step, base + 2 * step, base + 3 * step, base + 4 * step))
+            base += 5 * step
+        assert tile(ents) == 256, name
 
 
 def test_plan_describe_workload_lists(zs):

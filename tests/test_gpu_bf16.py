@@ -57,13 +57,21 @@ OFFSETS = [(0, 0, 0, 0, 0), (4, 0, 0, 0, 0), (3, 3, 3, 3, 3), (2, 6, 2, 2, 6),
            (1, 0, 0, 0, 0), (0, 0, 1, 0, 0)]
 
 
-@pytest.mark.parametrize("chunk", [0, 512])
+@pytest.mark.parametrize("chunk", [0, 512, "fine"])
 def test_bf16_ragged_sizes_and_alignments(zs, chunk):
+    """Tensors of sizes 1..70001 at every alignment class on 512-element
+    tiles (chunk 0 or 512), and the same after one aligned tensor of 8M
+    elements, which gives the plan 256-element tiles ("fine"); three steps,
+    every element compared."""
     import torch
-    rng = np.random.default_rng(31 + chunk)
+    fine = chunk == "fine"
+    rng = np.random.default_rng(31 + (7 if fine else chunk))
+    sizes_offs = [(n, OFFSETS[i % len(OFFSETS)]) for i, n in enumerate(SIZES)]
+    if fine:
+        sizes_offs = [(8 << 20, OFFSETS[0])] + sizes_offs
+        chunk = 0
     dev, ref = [], []
-    for i, n in enumerate(SIZES):
-        offs = OFFSETS[i % len(OFFSETS)]
+    for n, offs in sizes_offs:
         bufs = [torch.zeros(n + o + 8, dtype=dt, device="cuda")[o:o + n] for o, dt in
                 zip(offs, (torch.bfloat16, torch.bfloat16, torch.float32, torch.float32,
                            torch.float32))]
@@ -75,10 +83,11 @@ def test_bf16_ragged_sizes_and_alignments(zs, chunk):
         bufs[4].copy_(to_dev32(v0))
         dev.append(bufs)
         ref.append([np.zeros(n, np.uint16), w0.copy(), m0.copy(), v0.copy()])
-    say(f"bf16 ragged chunk={chunk} tensors={len(dev)}")
+    say(f"bf16 ragged chunk={chunk} fine={fine} tensors={len(dev)}")
     plan = zs.zero_plan_create([tuple(b) for b in dev], chunk)
     st = plan.stats()
     assert st["vector_elems"] and st["scalar_elems"]
+    assert st["tile_elems"] == (256 if fine else 512)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     inexact = 0
     for t in (4, 5, 6):

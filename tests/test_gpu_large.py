@@ -68,7 +68,8 @@ def _bit_exact(got, ref, what):
 
 def test_adam_one_tensor_past_2_32(zs):
     """Two steps over one 2^32 + 1027-element tensor: t = 1 under the default
-    chunk, t = 2 under 2^24-element chunks (257 of them)."""
+    chunk (256-element tiles), t = 2 under 2^24-element chunks (257 of them,
+    512-element tiles)."""
     import torch
     say(f"adam n={N}: allocating 16 B/param ({16 * N / 1e9:.1f} GB)")
     t_ = W.DeviceTensor(N, "cuda")
@@ -77,7 +78,9 @@ def test_adam_one_tensor_past_2_32(zs):
     d = torch.from_numpy(idx).cuda()
     w0 = _at32(t_.w, d)
     plans = [zs.zero_plan_create([t_.arrays()]), zs.zero_plan_create([t_.arrays()], 1 << 24)]
+    assert plans[0].stats()["tile_elems"] == 256
     st = plans[1].stats()
+    assert st["tile_elems"] == 512
     assert st["n_chunks"] == (N + (1 << 24) - 1) >> 24 == 257
     assert st["n_params"] == N and st["vector_elems"] == N - 3 and st["scalar_elems"] == 3
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -112,7 +112,7 @@ def _ragged_plan(zs, torch, sizes_offsets, seed, warm=False):
     return dev, host
 
 
-SIZES = [1, 7, 8, 9, 31, 4095, 4096, 4097, 2048 * 3 + 5, 70001, 0]
+SIZES = [1, 7, 8, 9, 31, 255, 256, 257, 511, 512, 513, 4095, 4096, 4097, 2048 * 3 + 5, 70001, 0]
 # element offsets of (param, grad, master, m, v) inside their buffers
 OFFSETS = [(0, 0, 0, 0, 0),      # all aligned: vector path, no head
            (4, 0, 0, 0, 0),      # param 8 mod 16 bytes, grad 0: vector path, no head
@@ -122,20 +122,29 @@ OFFSETS = [(0, 0, 0, 0, 0),      # all aligned: vector path, no head
            (0, 0, 1, 0, 0)]      # master 4 mod 16 bytes: single elements
 
 
-@pytest.mark.parametrize("chunk", [0, 512, 1536])
+@pytest.mark.parametrize("chunk", [0, 512, 1536, "fine"])
 @pytest.mark.parametrize("warm", [False, True])
 def test_ragged_sizes_and_alignments(zs, torch_mod, warm, chunk):
     """One plan over tensors of sizes 0..70001 whose arrays sit at every
-    alignment class, with the default chunk size and with chunks of one and
-    three wave tiles (many chunk boundaries inside small tensors); three
-    steps; every element compared."""
+    alignment class, with the default chunk size and with chunks of 512 and
+    1536 elements (one and three tiles: many chunk boundaries inside small
+    tensors), all on 512-element tiles; "fine": the same tensors after one
+    aligned tensor of 8M elements, which keeps the plan's chunk at 16384
+    and its tile at 256 elements.  Sizes on both sides of both tiles;
+    three steps; every element compared."""
     torch = torch_mod
     so = [(n, OFFSETS[i % len(OFFSETS)]) for i, n in enumerate(SIZES)]
     so += [(n, OFFSETS[(i + 2) % len(OFFSETS)]) for i, n in enumerate(SIZES)]
-    say(f"ragged warm={warm} chunk={chunk} tensors={len(so)}")
+    fine = chunk == "fine"
+    if fine:
+        so = [(8 << 20, OFFSETS[0])] + so
+        chunk = 0
+    say(f"ragged warm={warm} chunk={chunk} fine={fine} tensors={len(so)}")
     dev, host = _ragged_plan(zs, torch, so, seed=42 + warm, warm=warm)
     plan = zs.zero_plan_create(dev, chunk)
     st = plan.stats()
+    assert st["tile_elems"] == (256 if fine else 512)
+    assert (st["chunk_elems"] == 16384) if fine else True
     assert st["vector_elems"] and st["scalar_elems"]
     assert st["vector_elems"] + st["scalar_elems"] == st["n_params"]
     rng = np.random.default_rng(7)
@@ -560,4 +569,52 @@ def test_four_thousand_small_tensors(zs, torch_mod, chunk):
         for d, h, nm in ((dw, hw, "master"), (dm, hm, "m"), (dv, hv, "v")):
             assert np.array_equal(host32(d).view(np.uint32), h.view(np.uint32)), f"{nm} differs at t={t}"
     assert int(flag.item()) == 0
+    plan.destroy()
+
+
+def test_grid_at_its_limit_strides(zs, torch_mod):
+    """A plan with more virtual workgroups than the largest grid: 2100 small
+    tensors (1-299 elements, heads of 0-3) in 2^24-element chunks, 32,768
+    tiles of 512 elements per chunk and almost all of them empty, so
+    68,812,800 virtual workgroups on a grid of 2^26 - 1; the tensors from
+    2048 on are reached only by striding.  One step, every element of the
+    five buffers compared with the oracle (the gaps between tensors
+    untouched)."""
+    torch = torch_mod
+    rng = np.random.default_rng(77)
+    K = 2100
+    sizes = rng.integers(1, 300, K)
+    offs, pos = [], 0
+    for k in range(K):
+        pos += int(rng.integers(0, 4))
+        offs.append(pos)
+        pos += int(sizes[k])
+    total = pos
+    w0 = (rng.standard_normal(total) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(total) * 1e-3).astype(np.float16).view(np.uint16)
+    dp = torch.zeros(total, dtype=torch.float16, device="cuda")
+    dg = to_dev16(g)
+    dw = to_dev32(w0)
+    dm = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(total, dtype=torch.float32, device="cuda")
+    ents = [(dp[o:o + n], dg[o:o + n], dw[o:o + n], dm[o:o + n], dv[o:o + n])
+            for o, n in zip(offs, sizes.tolist())]
+    plan = zs.zero_plan_create(ents, 1 << 24)
+    st = plan.stats()
+    assert st["n_chunks"] == K and st["tile_elems"] == 512
+    assert K * ((1 << 24) // 512) > (1 << 26) - 1
+    say(f"grid limit: {K} tensors, {K * ((1 << 24) // 512)} virtual workgroups")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, _hp(zs), 1, flag)
+    torch.cuda.synchronize()
+    rp = np.zeros(total, np.uint16)
+    rw, rm, rv = w0.copy(), np.zeros(total, np.float32), np.zeros(total, np.float32)
+    rflag = 0
+    for o, n in zip(offs, sizes.tolist()):
+        rflag |= oracle.adam_step(g[o:o + n], rp[o:o + n], rw[o:o + n], rm[o:o + n],
+                                  rv[o:o + n], t=1, **W.ADAM_HP)
+    assert int(flag.item()) == rflag == 0
+    res = [check16(host16(dp), rp, "grid limit param"), check32(host32(dw), rw, "grid limit master"),
+           check32(host32(dm), rm, "grid limit m"), check32(host32(dv), rv, "grid limit v")]
+    assert sum(r["not_bit_exact"] for r in res) == 0
     plan.destroy()

@@ -158,8 +158,8 @@ bool writes_overlap(std::vector<Range> &r) {
 
 // The chunk a plan gets when the caller leaves it to the library: the
 // largest of kDefaultChunk, kDefaultChunk / 2, ..., kTile whose workgroup
-// slots (chunks times tiles per chunk, the launch's virtual workgroups)
-// exceed the tiles that hold work by at most one eighth.  Big tensors keep
+// slots (chunks times kTile-element tiles per chunk) exceed the tiles that
+// hold work by at most one eighth.  Big tensors keep
 // the compact table of kDefaultChunk; many small tensors get small chunks,
 // so that few workgroups start only to find their tile past the end of a
 // short chunk.
@@ -261,6 +261,7 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
         }
     }
     s.n_chunks = plan.chunks.size();
+    s.tile_elems = s.scalar_elems * 8 <= s.n_params && C == kDefaultChunk ? kAdamTileFine : kTile;
     s.table_bytes = plan.tensors.size() * sizeof(TensorDesc) + plan.chunks.size() * sizeof(Chunk);
     *out = std::move(plan);
     return ZERO_OK;

@@ -40,25 +40,46 @@ static_assert(sizeof(Chunk) == 16, "Chunk is 16 bytes");
 // per workgroup.
 constexpr uint32_t kWave = 64;
 
-// Elements of one Adam wave tile: 64 lanes x two groups of four.
+// Elements of one wave tile of the reduce and fused kernels (64 lanes x two
+// groups of four), and the unit of a plan's chunk sizes.
 constexpr uint32_t kTile = 512;
 
+// Elements of an Adam wave tile, chosen per plan: kAdamTileFine (64 lanes x
+// one group of four) when at least 7/8 of the plan's elements take the
+// vector path and its chunk is kDefaultChunk (big tensors), else kTile (two
+// groups of four per lane).  Measured on MI355X, each against the other in
+// one process: the fine tile is 1-5% faster on flat shards of 117M-937.5M
+// elements (1.4% slower on one of 102.4M), 0.6-2% on the Llama-7B and
+// GPT-2-XL lists in flattened buffers
+// and 7-10% on the same lists held as five allocations per tensor; the
+// coarse tile is 4-7% faster on the single-element path and 4% on 100,000
+// tensors of 1,024 elements, where a wave's descriptor loads weigh twice as
+// much per byte with the fine tile.
+constexpr uint32_t kAdamTileFine = 256;
+static_assert(kTile % kAdamTileFine == 0, "chunks hold whole Adam tiles");
+
 // Chunk sizes a plan accepts (multiples of kTile) and the default.  One
-// workgroup updates one tile; the chunk size only sets how many tiles share
-// a table entry (a tensor's short last chunk leaves some workgroups idle).
+// workgroup updates one Adam tile; the chunk size only sets how many tiles
+// share a table entry (a tensor's short last chunk leaves some workgroups
+// idle).
 constexpr uint32_t kMinChunk = kTile;
 constexpr uint32_t kMaxChunk = 1u << 24;
 constexpr uint32_t kDefaultChunk = 16384;
 
-// Largest grid of either kernel (64 * 2^24 lanes stays below 2^32); larger
-// work strides over it.
-constexpr uint64_t kMaxGrid = 1u << 24;
+// Largest grid of every kernel, in one-wave workgroups: the most whose
+// work-items (64 each) still fit the 32-bit grid size of a dispatch.  Larger
+// work strides over it.  Measured on MI355X with the Llama-7B list (26.3M
+// Adam tiles): a grid capped at 2^24 that strode over the rest ran 2-3%
+// slower than one workgroup per tile.
+constexpr uint64_t kMaxGrid = (1ull << 26) - 1;
+static_assert(kMaxGrid * kWave <= 0xFFFFFFFFull, "grid size fits 32 bits");
 
-// Resident one-wave workgroups per CU for the Adam step (each keeps eight
-// 8- or 16-byte loads per lane in flight).  Measured on MI355X over 5..8:
-// 7 is fastest on flat shards from 117M to 6.7G elements and on a 291-tensor
-// list of 118M; the 6.7G-element Llama-7B list alone prefers 6 (by 2%).
-constexpr uint32_t kAdamPerCU = 7;
+// Resident one-wave workgroups per CU for the Adam step, by tile: each
+// keeps four (fine) or eight (coarse) 8- or 16-byte loads per lane in
+// flight.  Measured on MI355X: the fine tile is fastest at 12 (over 10..14)
+// on flat shards of 117M-3G elements and on both lists in either layout;
+// the coarse tile at 7 (over 5..8) on flat shards of 117M-6.7G elements.
+inline uint32_t adam_per_cu(uint32_t tile) { return tile == kAdamTileFine ? 12u : 7u; }
 
 // Elements one wave of the parameter gather moves per tile: four 16-byte
 // loads per lane in flight on the widest path.

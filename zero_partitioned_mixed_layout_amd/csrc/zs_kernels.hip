@@ -10,19 +10,22 @@
 // covers one contiguous range (Adam: 512 bytes of fp16 or 1 KiB of fp32;
 // reduce: 1 KiB of fp16), and streamed data moves with the nontemporal hint.
 // On gfx950 nontemporal stores only stream at full rate when each
-// instruction writes whole lines, which is why the Adam wave tile
-// interleaves its two four-element groups across the wave instead of giving
-// each lane eight neighbours, and why the gather aligns its tiles to the
+// instruction writes whole lines, which is why a lane's four-element groups
+// of a wave tile are adjacent to its neighbours' (a 512-element tile
+// interleaves two such groups across the wave instead of giving each lane
+// eight neighbours), and why the gather aligns its tiles to the
 // destination's 128-byte lines.
 //
 // Occupancy is capped on purpose.  The kernels run one 64-lane wave per
 // workgroup, and each launch reserves dynamic LDS that the kernel never
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
-// are resident per CU (Adam 7; reduce 4 when 16 slices are in flight per
-// lane; fused 4; gather 16).  Measured on MI355X, HBM3E streams these
-// many-array patterns fastest with just enough bytes in flight to cover
-// latency (about 45 KB per CU); with the 20-30 waves per CU that registers
-// alone would allow, the same streams run 10-15% slower.
+// are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
+// tiles; reduce 4 when 16 slices are in flight per lane; fused 4; gather
+// 16).  Measured on
+// MI355X, HBM3E streams these many-array patterns fastest with just enough
+// bytes in flight to cover latency (about 45 KB per CU); with the 20-30
+// waves per CU that registers alone would allow, the same streams run
+// 10-15% slower.
 //
 // Exactness: every arithmetic step is one IEEE binary32 operation in a fixed
 // order; the library is built with -ffp-contract=off (no fused multiply-add),
@@ -42,6 +45,7 @@
 namespace {
 
 using zs::Chunk;
+using zs::kAdamTileFine;
 using zs::kTile;
 using zs::kWave;
 using zs::TensorDesc;
@@ -196,20 +200,24 @@ __device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t 
     st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + i));
 }
 
-// A full wave tile: kTile consecutive elements from `base` (vector-aligned).
-// Lane L takes elements 4L..4L+3 and kTile/2+4L..kTile/2+4L+3, so each of the
-// wave's load and store instructions covers one contiguous 512-byte (fp16)
-// or 1-KiB (fp32) range.  All eight loads are issued before any arithmetic.
-template <class Fmt>
+// A full Adam tile: TILE consecutive elements from `base` (vector-aligned),
+// TILE / 256 groups of four per lane.  Lane L takes elements 4L..4L+3 of
+// every 256, so each of the wave's load and store instructions covers one
+// contiguous 512-byte (16-bit) or 1-KiB (fp32) range.  All loads are issued
+// before any arithmetic.
+template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, uint32_t lane,
                                           const AdamConsts &c, int &bad) {
-    const uint64_t i0 = base + 4u * lane, i1 = i0 + kTile / 2;
-    Quad<Fmt> a, b;
-    quad_load<Fmt>(T, i0, a);
-    quad_load<Fmt>(T, i1, b);
+    constexpr int Q = TILE / (4 * kWave);
+    static_assert(Q * 4 * kWave == TILE, "whole groups of four per lane");
+    Quad<Fmt> a[Q];
+#pragma unroll
+    for (int k = 0; k < Q; k++)
+        quad_load<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k]);
     __builtin_amdgcn_sched_barrier(0);
-    quad_update_store<Fmt>(T, i0, a, c, bad);
-    quad_update_store<Fmt>(T, i1, b, c, bad);
+#pragma unroll
+    for (int k = 0; k < Q; k++)
+        quad_update_store<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k], c, bad);
 }
 
 // Tile j of a chunk on the vector path.  The tensor's peeled head (fewer
@@ -217,7 +225,7 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
 // chunk and is done by tile 0; every other chunk starts vector-aligned.  The
 // chunk's last, partial tile goes four elements per lane, then the final
 // fewer-than-four singly.
-template <class Fmt>
+template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
@@ -226,15 +234,15 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
         adam_single<Fmt>(T, lane, c, bad);
     const uint64_t base = ch.start + head;
     const uint32_t body = ch.count - head;
-    const uint32_t nfull = body / kTile;
+    const uint32_t nfull = body / TILE;
     if (j < nfull) {
-        adam_tile<Fmt>(T, base + (uint64_t)j * kTile, lane, c, bad);
+        adam_tile<Fmt, TILE>(T, base + (uint64_t)j * TILE, lane, c, bad);
         return;
     }
     if (j > nfull)
         return; // past the end of a short chunk
-    const uint64_t rbase = base + (uint64_t)nfull * kTile;
-    const uint32_t rem = body - nfull * kTile; // < kTile
+    const uint64_t rbase = base + (uint64_t)nfull * TILE;
+    const uint32_t rem = body - nfull * TILE; // < TILE
     const uint32_t nquads = rem / 4u;
     for (uint32_t q = lane; q < nquads; q += kWave) {
         Quad<Fmt> x;
@@ -248,17 +256,17 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
 
 // Tile j of a chunk of a tensor whose arrays disagree in alignment: single
 // elements, lane-strided so each access instruction of the wave stays
-// contiguous.  A full tile loads all of a lane's kTile / 64 elements before
+// contiguous.  A full tile loads all of a lane's TILE / 64 elements before
 // the first update (the same per-element operations as adam_single), so
 // the wave keeps as many loads in flight as on the vector path; a partial
 // tile goes element by element.
-template <class Fmt>
+template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chunk &ch,
                                                  uint32_t j, const AdamConsts &c, int &bad) {
-    const uint32_t lo = j * kTile;
-    const uint32_t hi = min(ch.count, lo + kTile);
-    if (hi - lo == kTile) {
-        constexpr int G = kTile / kWave;
+    const uint32_t lo = j * TILE;
+    const uint32_t hi = min(ch.count, lo + TILE);
+    if (hi - lo == TILE) {
+        constexpr int G = TILE / kWave;
         const uint64_t i0 = ch.start + lo + threadIdx.x;
         uint16_t gb[G];
         float w[G], m[G], v[G];
@@ -291,11 +299,12 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
         adam_single<Fmt>(T, ch.start + k, c, bad);
 }
 
-// The fused step over a plan.  Each workgroup is one wave and takes one wave
+// The fused step over a plan.  Each workgroup is one wave and takes one Adam
 // tile: virtual workgroup b is tile b % tiles_per_chunk of chunk
 // b / tiles_per_chunk.  Launches with fewer workgroups than virtual ones
-// stride over them.  Fmt: the 16-bit format of parameters and gradients.
-template <class Fmt>
+// stride over them.  Fmt: the 16-bit format of parameters and gradients;
+// TILE: the plan's Adam tile (kAdamTileFine or kTile elements).
+template <class Fmt, uint32_t TILE>
 __global__ __launch_bounds__(kWave) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
     uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
@@ -313,9 +322,9 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
         const Chunk ch = chunks[ci];
         const TensorDesc T = tensors[ch.tensor];
         if (T.vec == 4)
-            adam_tile_of_chunk<Fmt>(T, ch, j, c, bad);
+            adam_tile_of_chunk<Fmt, TILE>(T, ch, j, c, bad);
         else
-            adam_tile_single<Fmt>(T, ch, j, c, bad);
+            adam_tile_single<Fmt, TILE>(T, ch, j, c, bad);
     }
     raise_flag(flag, bad);
 }
@@ -965,7 +974,7 @@ int plan_create(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_e
     plan->d_chunks = nullptr;
     plan->stats = hp.stats;
     plan->device = dev;
-    plan->lds_cap = lds_cap_bytes(dev, zs::kAdamPerCU);
+    plan->lds_cap = lds_cap_bytes(dev, zs::adam_per_cu((uint32_t)hp.stats.tile_elems));
     plan->bf16 = bf16;
     const size_t tb = hp.tensors.size() * sizeof(zs::TensorDesc);
     const size_t cb = hp.chunks.size() * sizeof(zs::Chunk);
@@ -1041,19 +1050,30 @@ static int adam_step_launch(const zero_plan *plan, const zero_adam_hparams *hp, 
     if (dev != plan->device)
         return ZERO_EINVAL;
     const AdamConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7], 1.0f};
-    // one one-wave workgroup per wave tile, dispatched in order and balanced
+    // one one-wave workgroup per Adam tile, dispatched in order and balanced
     // over the CUs by the hardware; only plans beyond kMaxGrid tiles stride
-    const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / kTile);
+    const uint32_t tile = (uint32_t)plan->stats.tile_elems;
+    const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / tile);
     const uint64_t n_virtual = plan->stats.n_chunks * tpc;
     const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
-    if (plan->bf16)
-        hipLaunchKernelGGL(zs_adam_kernel<FmtBF16>, dim3(grid), dim3(kWave), plan->lds_cap,
-                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
-                           c, nonfinite_flag, skip_if_nonzero, log2_scale);
+    hipStream_t st = (hipStream_t)stream;
+    const size_t lds = plan->lds_cap;
+    if (plan->bf16 && tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+                           st, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
+                           skip_if_nonzero, log2_scale);
+    else if (plan->bf16)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kTile>), dim3(grid), dim3(kWave), lds, st,
+                           plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
+                           skip_if_nonzero, log2_scale);
+    else if (tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+                           st, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
+                           skip_if_nonzero, log2_scale);
     else
-        hipLaunchKernelGGL(zs_adam_kernel<FmtF16>, dim3(grid), dim3(kWave), plan->lds_cap,
-                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, n_virtual, tpc,
-                           c, nonfinite_flag, skip_if_nonzero, log2_scale);
+        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kTile>), dim3(grid), dim3(kWave), lds, st,
+                           plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
+                           skip_if_nonzero, log2_scale);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;

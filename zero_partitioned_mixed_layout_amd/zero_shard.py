@@ -62,7 +62,7 @@ class _HParams(ctypes.Structure):
 class _Stats(ctypes.Structure):
     _fields_ = [(k, ctypes.c_uint64) for k in (
         "n_tensors", "n_params", "n_chunks", "chunk_elems", "vector_elems",
-        "scalar_elems", "table_bytes")]
+        "scalar_elems", "table_bytes", "tile_elems")]
 
 
 def _load() -> ctypes.CDLL:
