@@ -194,3 +194,55 @@ def test_scaled_rejects(zs):
     with pytest.raises(ValueError):
         zs.LossScale(interval=0)
     plan.destroy()
+
+
+def test_flat_7p5b_nd64_loss_scaled_full_size(zs):
+    """The launch configuration bench.py times with --loss-scale 16, at full
+    size: rank 0's 117,187,500-element partition of Psi = 7.5e9 over 64
+    ranks, two steps of reduce of the 64 fp16 slices -> Adam on gradients
+    read as carrying 2^16 (skipped on the reduce's flag) -> the scale's
+    update (interval 2000, 2^0..2^24).  200,000 sampled elements (both ends
+    included) equal the oracle's, recomputed from the same slices; the
+    scale's state is (16, 2, 0, 2) after the two finite steps."""
+    import torch
+    wl = W.WORKLOADS["flat_7p5b_nd64"]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
+    n = lay.real_len
+    say(f"loss-scaled flat_7p5b_nd64 n={n}")
+    full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total)
+    buf, rows = W.device_slices(wl, n)
+    plan = zs.zero_plan_create([sh.arrays()])
+    ls = zs.LossScale(log2_scale=16, interval=2000, min_log2=0, max_log2=24)
+    idx = W.sample_indices(n, 200_000, seed=wl.seed + 16)
+    d = torch.from_numpy(idx).cuda()
+
+    def at16(t):
+        return host16(t.index_select(0, d))
+
+    def at32(t):
+        return host32(t.index_select(0, d))
+
+    w0 = at32(sh.w)
+    slices = [at16(r) for r in rows]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t in (1, 2):
+        zs.zero_reduce_grad_shard(rows, sh.g, flag)
+        zs.zero_adam_step(plan, zs.AdamHParams(**HP), t, skip_if_nonzero=flag, loss_scale=ls)
+        ls.update(flag)
+    torch.cuda.synchronize()
+    assert ls.read() == (16, 2, 0, 2) and int(flag.item()) == 0
+    g_ref, rflag = oracle.reduce_grad(slices)
+    assert rflag == 0
+    k = idx.size
+    rp, rw = np.zeros(k, np.uint16), w0.copy()
+    rm, rv = np.zeros(k, np.float32), np.zeros(k, np.float32)
+    for t in (1, 2):
+        oracle.adam_step_scaled(g_ref, rp, rw, rm, rv, t=t, log2_scale=16, **HP)
+    bad = (check16(at16(sh.p), rp, "loss-scaled nd64 param")["not_bit_exact"]
+           + check32(at32(sh.w), rw, "loss-scaled nd64 master")["not_bit_exact"]
+           + check32(at32(sh.m), rm, "loss-scaled nd64 m")["not_bit_exact"]
+           + check32(at32(sh.v), rv, "loss-scaled nd64 v")["not_bit_exact"])
+    assert bad == 0
+    plan.destroy()
+    del full, sh, buf, rows
+    torch.cuda.empty_cache()
