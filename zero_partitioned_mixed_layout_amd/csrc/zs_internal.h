@@ -113,12 +113,23 @@ inline uint32_t reduce_per_cu(uint32_t nd) {
     return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 
-// Resident one-wave workgroups per CU for the fused reduce + Adam step:
-// about 70 16-byte vectors per lane in flight per CU, counting the six fp32
-// state vectors issued with the first slice batch (4 workgroups at N_d >= 16,
-// 5 at N_d = 8: the measured optima), between 2 and 8 workgroups.
-inline uint32_t fused_per_cu(uint32_t nd) {
-    const uint32_t per_wave = 6 + slices_in_flight(nd);
+// Whether the fused step's 16-byte path loads a tile's fp32 state after the
+// slices (then it arrives while the reduced gradients cross the LDS) instead
+// of with the first slice batch.  Measured on MI355X, one process, 937.5M
+// elements: after is 3.6% faster at N_d = 4 and 2.5% at N_d = 8 (with the
+// caps below); before is 4-5% faster at N_d = 16 and equal at N_d = 64.
+inline bool fused_state_late(uint32_t nd) { return slices_in_flight(nd) < 16; }
+
+// Resident one-wave workgroups per CU for the fused reduce + Adam step.
+// State first: about 70 16-byte vectors per lane in flight per CU, counting
+// the six fp32 state vectors issued with the first slice batch (4 workgroups
+// at N_d >= 16, 5 at N_d = 8: the measured optima), between 2 and 8.  State
+// last: 6 at 8 slices in flight and 7 at 4 (measured over 5-8), else 8.
+inline uint32_t fused_per_cu(uint32_t nd, bool state_late) {
+    const uint32_t sif = slices_in_flight(nd);
+    if (state_late)
+        return sif == 8 ? 6u : (sif == 4 ? 7u : 8u);
+    const uint32_t per_wave = 6 + sif;
     const uint32_t k = (70 + per_wave - 1) / per_wave;
     return k < 2 ? 2 : (k > 8 ? 8 : k);
 }

@@ -684,20 +684,23 @@ extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
 // consecutive elements 8L..8L+7 (16-byte loads, 1 KiB per wave
 // instruction, as zs_reduce_kernel), the fp16 gradients go through LDS to
 // the Adam tile's mapping (lane L: 4L..4L+3 and kTile/2+4L..), and the
-// update runs there.  The fp32 state loads are issued first.
-template <class Fmt>
+// update runs there.  The fp32 state loads are issued before the slices, or
+// with LATE after them (before the LDS exchange).
+template <class Fmt, bool LATE>
 __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uint64_t lo,
                                             uint32_t lane, float count, const FlatState &F,
                                             const AdamConsts &c, int &bad) {
     const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
     f32x4 w[2], m[2], v[2];
+    if (!LATE) {
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-        w[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.w + i[k]));
-        m[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.m + i[k]));
-        v[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.v + i[k]));
+        for (int k = 0; k < 2; k++) {
+            w[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.w + i[k]));
+            m[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.m + i[k]));
+            v[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.v + i[k]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     const uint64_t j = lo + 8u * lane;
     float acc[8];
     uint32_t r = 0;
@@ -715,6 +718,14 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
 #pragma unroll
     for (int q = 0; q < 8; q++)
         g8[q] = (typename Fmt::T)(acc[q] / count);
+    if (LATE) {
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            w[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.w + i[k]));
+            m[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.m + i[k]));
+            v[k] = ld_nt(reinterpret_cast<const f32x4 *>(F.v + i[k]));
+        }
+    }
     reinterpret_cast<hv8 *>(zs_lds)[lane] = g8;
     __syncthreads(); // one wave per workgroup: orders the LDS write and reads
     hv4 g[2];
@@ -797,8 +808,9 @@ __device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t n
 // aligned).  VEC = 4: full tiles with each lane reducing its own two groups
 // of four (slices 8-byte aligned).  Both: the last partial tile four per
 // lane, then singly.  VEC = 1: the tile's elements one at a time.  Tiles
-// beyond the grid stride.
-template <class Fmt, int VEC>
+// beyond the grid stride.  LATE: fused_tile8 loads the state after the
+// slices.
+template <class Fmt, int VEC, bool LATE = false>
 __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t nd, uint64_t n,
                                                          uint32_t head, uint64_t ntiles,
                                                          FlatState F, AdamConsts c,
@@ -814,7 +826,7 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
         const uint64_t hi = min(n, lo + kTile);
         if (VEC > 1) {
             if (hi - lo == kTile && VEC == 8) {
-                fused_tile8<Fmt>(s, nd, lo, lane, count, F, c, bad);
+                fused_tile8<Fmt, LATE>(s, nd, lo, lane, count, F, c, bad);
             } else if (hi - lo == kTile) {
                 const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
                 fused_groups<Fmt, 2>(s, nd, i, count, F, c, bad);
@@ -1296,14 +1308,19 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     const uint64_t ntiles = (n - h + kTile - 1) / kTile + (n == h ? 1 : 0);
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
     // the single-element path keeps fewer bytes per wave in flight: twice the
-    // resident workgroups
-    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd) * (vec == 1 ? 2u : 1u));
+    // resident workgroups; the 16-byte path loads the state after the slices
+    // when fewer than 16 are in flight per batch
+    const bool late = vec == 8 && zs::fused_state_late(nd);
+    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late) * (vec == 1 ? 2u : 1u));
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
     const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7], 1.0f};
     hipStream_t st = (hipStream_t)stream;
-    if (vec == 8)
+    if (vec == 8 && late)
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8, true>), dim3(grid), dim3(kWave), lds, st, args,
+                           nd, n, head, ntiles, F, c, nonfinite_flag);
+    else if (vec == 8)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
                            n, head, ntiles, F, c, nonfinite_flag);
     else if (vec == 4)
