@@ -267,7 +267,7 @@ def _fused_case(zs, n, nd, layout, with_gout, t, rng, inject=None):
     return inexact, rflag | aflag
 
 
-@pytest.mark.parametrize("nd", [1, 3, 16, 17, 64, 256])
+@pytest.mark.parametrize("nd", [1, 3, 4, 8, 16, 17, 64, 256])
 @pytest.mark.parametrize("layout", list(FUSED_LAYOUTS))
 def test_bf16_fused_matches_oracle(zs, nd, layout):
     """The fused reduce + Adam step in bfloat16 against the oracle's

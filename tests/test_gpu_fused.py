@@ -83,7 +83,7 @@ def _run_case(zs, torch, n, nd, layout, with_gout, t, rng, warm=True):
     return sum(r["not_bit_exact"] for r in res)
 
 
-@pytest.mark.parametrize("nd", [1, 2, 3, 5, 16, 17, 64, 256])
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 15, 16, 17, 64, 256])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 def test_fused_matches_oracle(zs, nd, layout):
     """Sizes from 1 to 70,001 (partial tiles, heads and tails), each access
@@ -188,14 +188,17 @@ def test_fused_rejects_through_binding(zs):
     torch.cuda.synchronize()
 
 
-def test_fused_equals_separate_kernels_at_full_size(zs):
-    """Psi = 7.5e9 over 64 ranks, rank 0's 117,187,500 elements: the fused
-    kernel against zero_reduce_grad_shard + zero_adam_step on identical
-    copies of the state, every element of every array bit for bit; sampled
-    elements also against the oracle."""
+@pytest.mark.parametrize("name", ["flat_7p5b_nd64", "flat_7p5b_nd8"])
+def test_fused_equals_separate_kernels_at_full_size(zs, name):
+    """Psi = 7.5e9 over 64 ranks (rank 0's 117,187,500 elements, 64 slices:
+    the state loaded before the slices) and over 8 ranks (rank 3's
+    937,500,160 elements, 8 slices: the state loaded after them), as bench.py
+    times them with --fused: the fused kernel against zero_reduce_grad_shard
+    + zero_adam_step on identical copies of the state, every element of
+    every array bit for bit; sampled elements also against the oracle."""
     import torch
-    wl = W.WORKLOADS["flat_7p5b_nd64"]
-    lay = zs.zero_shard_layout(wl.psi, wl.nd, 0, wl.align)
+    wl = W.WORKLOADS[name]
+    lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
     n = lay.real_len
     say(f"fused full size n={n} nd={wl.nd}")
     full, sh = W.device_flat_state(wl, lay.offset, n, lay.padded_total)
@@ -234,7 +237,8 @@ def test_fused_equals_separate_kernels_at_full_size(zs):
            check32(host32(sh.v.index_select(0, d)), v_ref, "full v")]
     assert sum(r["not_bit_exact"] for r in res) == 0
     # other ranks' part of the full fp16 parameter buffer is untouched
-    assert int(torch.count_nonzero(full[n:]).item()) == 0
+    assert int(torch.count_nonzero(full[:lay.offset]).item()) == 0
+    assert int(torch.count_nonzero(full[lay.offset + n:]).item()) == 0
     plan.destroy()
     del full, sh, buf, rows, w2, m2, v2, p2, g2, gout
     gc.collect()
