@@ -17,6 +17,7 @@ oracle timed on a bounded sample on this host.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -32,7 +33,8 @@ METRIC = "params updated/sec and achieved HBM GB/s (% of roofline) per Adam shar
 # the sources that decide what the kernels do and how they are launched
 KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_layout_amd", "csrc", f)
                for f in ("zs_kernels.hip", "zs_internal.h", "zs_host.cpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_flat_7p5b_nd64.md")
+# committed rocprofv3 counter summaries, one per workload (lines "traffic: ...")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "hbm_traffic_*.md")
 
 
 def code_tokens(text: str) -> str:
@@ -76,21 +78,20 @@ def kernel_src_sha(read=None) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources (kernels, launch constants,
-    plan builder); else None."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+    """HBM bytes per launch from the committed rocprofv3 counter summaries,
+    if they were taken on the current kernel sources (kernels, launch
+    constants, plan builder); else None."""
     pat = re.compile(r"^traffic:\s+(.*)$")
-    for line in open(TRAFFIC_FILE):
-        m = pat.match(line.strip())
-        if not m:
-            continue
-        kv = dict(x.split("=", 1) for x in m.group(1).split())
-        if kv.get("kernel") == kernel and kv.get("workload") == workload:
-            if kv.get("src_sha256") != kernel_src_sha():
-                return None
-            return float(kv["hbm_bytes_per_launch"])
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        for line in open(path):
+            m = pat.match(line.strip())
+            if not m:
+                continue
+            kv = dict(x.split("=", 1) for x in m.group(1).split())
+            if kv.get("kernel") == kernel and kv.get("workload") == workload:
+                if kv.get("src_sha256") != kernel_src_sha():
+                    return None
+                return float(kv["hbm_bytes_per_launch"])
     return None
 
 

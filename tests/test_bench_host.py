@@ -38,23 +38,26 @@ def test_hash_ignores_comments_but_not_code():
 
 def test_traffic_lookup_requires_matching_hash(tmp_path, monkeypatch):
     b = _bench()
-    f = tmp_path / "traffic.md"
+    f = tmp_path / "hbm_traffic_w1.md"
     sha = b.kernel_src_sha()
     f.write_text(f"traffic: kernel=zs_adam_kernel workload=w1 src_sha256={sha} hbm_bytes_per_launch=123\n"
                  f"traffic: kernel=zs_reduce_kernel workload=w1 src_sha256=0000000000000000 hbm_bytes_per_launch=456\n")
-    monkeypatch.setattr(b, "TRAFFIC_FILE", str(f))
+    monkeypatch.setattr(b, "TRAFFIC_GLOB", str(tmp_path / "hbm_traffic_*.md"))
     assert b.measured_traffic("zs_adam_kernel", "w1") == 123.0
     assert b.measured_traffic("zs_reduce_kernel", "w1") is None      # taken on other code
     assert b.measured_traffic("zs_adam_kernel", "w2") is None        # another workload
 
 
 def test_committed_counters_match_the_current_kernels():
-    """profiles/hbm_traffic_flat_7p5b_nd64.md was taken on the kernels as they are now, so
+    """profiles/hbm_traffic_*.md were taken on the kernels as they are now, so
     the default bench line carries measured HBM traffic for both kernels of
-    the step (re-take the counters after any change to the kernels' code)."""
+    the step, and the N_d = 8 shard and the Llama-7B list for their Adam
+    step (re-take the counters after any change to the kernels' code)."""
     b = _bench()
     for k in ("zs_reduce_kernel", "zs_adam_kernel"):
         assert b.measured_traffic(k, "flat_7p5b_nd64") is not None, k
+    for w in ("flat_7p5b_nd8", "llama_7b"):
+        assert b.measured_traffic("zs_adam_kernel", w) is not None, w
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
