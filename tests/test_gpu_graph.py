@@ -44,7 +44,10 @@ def test_captured_step_replays_match_the_oracle(zs):
     w, m, v = to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
     rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
     aflag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    plan = zs.zero_plan_create([(p, g, w, m, v)])
+    # 16384-element chunks: this plan takes 256-element Adam tiles (the
+    # loss-scaled test below takes 512)
+    plan = zs.zero_plan_create([(p, g, w, m, v)], 16384)
+    assert plan.stats()["tile_elems"] == 256
     hp = zs.AdamHParams(**HP)
 
     def step():
@@ -107,6 +110,7 @@ def test_captured_loss_scaled_step_follows_the_scale(zs):
     w, m, v = to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
     rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
     plan = zs.zero_plan_create([(p, g, w, m, v)])
+    assert plan.stats()["tile_elems"] == 512
     hp = zs.AdamHParams(**HP)
     ls = zs.LossScale(log2_scale=10, interval=2, min_log2=0, max_log2=12)
     init = ls.state.clone()
