@@ -52,9 +52,8 @@ constexpr uint32_t kTile = 512;
 // elements (1.4% slower on one of 102.4M), 0.6-2% on the Llama-7B and
 // GPT-2-XL lists in flattened buffers
 // and 7-10% on the same lists held as five allocations per tensor; the
-// coarse tile is 4-7% faster on the single-element path and 4% on 100,000
-// tensors of 1,024 elements, where a wave's descriptor loads weigh twice as
-// much per byte with the fine tile.
+// coarse tile is 4-7% faster on the single-element path (a lane keeps
+// twice the loads in flight) and 4% on 100,000 tensors of 1,024 elements.
 constexpr uint32_t kAdamTileFine = 256;
 static_assert(kTile % kAdamTileFine == 0, "chunks hold whole Adam tiles");
 
