@@ -261,6 +261,9 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
         }
     }
     s.n_chunks = plan.chunks.size();
+    // at most 1/8 of the elements single and the default chunk: the fine
+    // tile.  scalar_elems * 8 cannot wrap: the three fp32 arrays of every
+    // tensor are disjoint ranges of the address space, so n_params < 2^64 / 12.
     s.tile_elems = s.scalar_elems * 8 <= s.n_params && C == kDefaultChunk ? kAdamTileFine : kTile;
     s.table_bytes = plan.tensors.size() * sizeof(TensorDesc) + plan.chunks.size() * sizeof(Chunk);
     *out = std::move(plan);
