@@ -345,7 +345,13 @@ int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
  *   g16 = fp16((s_0[i] + ... + s_{nd-1}[i]) / nd)   as zero_reduce_grad_shard
  *   then the Adam element of zero_adam_step with g = fp32(g16)
  * so the results are bit-identical to the two calls in sequence (without
- * a skip input).
+ * a skip input).  Below 32 slices one kernel does it all, reading the
+ * slices and the fp32 state in one pass (4 bytes per element less than the
+ * two calls); from 32 slices on, where that kernel's mix of state writes
+ * into the slice reads costs more than it saves, the call runs the reduce
+ * kernel and then the Adam kernel, with the fp16 gradient passing through
+ * grad_out_f16, or without it through param_f16, which then holds the
+ * gradient until the Adam kernel overwrites it with the new parameter.
  * slices_f16: host array of nd device pointers to n fp16 each (read only).
  * param_f16: n fp16, written.  master, m, v: n fp32 each, updated in place.
  * grad_out_f16: NULL, or n fp16 that receive g16.

@@ -1,9 +1,14 @@
 """The C ABI without a GPU: the library loads, exports every function the
 header declares, and its host-only functions (layout, ledger, step scalars,
 plan classification, argument checks) agree with the oracle and the header.
-No call here reaches a device."""
+No call here reaches a device: the checks that hand fake device addresses to
+entry points which launch once their arguments pass run in a child process
+that sees no GPU, so a check that regressed fails with EHIP instead of
+launching a kernel on made-up memory."""
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -34,6 +39,20 @@ def test_exports_every_declared_function(zs):
     missing = [n for n in names if not hasattr(zs.lib(), n)]
     assert not missing
     assert sorted(zs.EXPORTS) == names
+
+
+def _without_devices(body: str) -> None:
+    """Run the module-level function `body`(zs) in a child process in which
+    HIP sees no device."""
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="",
+               ROCR_VISIBLE_DEVICES="")
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = (f"import sys; sys.path[:0] = [{ROOT!r}, {here!r}]; import test_abi_host as t; "
+            f"from zero_partitioned_mixed_layout_amd import zero_shard as zs; "
+            f"t.{body}(zs); print('BODY_OK')")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "BODY_OK" in r.stdout, r.stdout + r.stderr
 
 
 def test_status_strings(zs):
@@ -277,6 +296,10 @@ def test_plan_describe_rejects(zs):
 
 
 def test_step_and_reduce_reject_before_any_device_call(zs):
+    _without_devices("_step_and_reduce_reject_before_any_device_call")
+
+
+def _step_and_reduce_reject_before_any_device_call(zs):
     import ctypes
     L = zs.lib()
     hp = zs.AdamHParams()._c()
@@ -295,6 +318,10 @@ def test_step_and_reduce_reject_before_any_device_call(zs):
 
 
 def test_loss_scale_rejects_before_any_device_call(zs):
+    _without_devices("_loss_scale_rejects_before_any_device_call")
+
+
+def _loss_scale_rejects_before_any_device_call(zs):
     """zero_adam_step_scaled and zero_loss_scale_update check their
     pointers and ranges on the host first (fake addresses, never used)."""
     import ctypes
@@ -326,6 +353,10 @@ def test_loss_scale_rejects_before_any_device_call(zs):
 
 
 def test_fused_rejects_before_any_device_call(zs):
+    _without_devices("_fused_rejects_before_any_device_call")
+
+
+def _fused_rejects_before_any_device_call(zs):
     """zero_reduce_adam_step validates everything on the host first."""
     import ctypes
     L = zs.lib()
@@ -390,6 +421,10 @@ def test_comm_volume_rejects(zs, orc):
 
 
 def test_gather_rejects_before_any_device_call(zs):
+    _without_devices("_gather_rejects_before_any_device_call")
+
+
+def _gather_rejects_before_any_device_call(zs):
     import ctypes
     L = zs.lib()
     P = ctypes.c_void_p
@@ -455,3 +490,4 @@ def test_header_is_plain_c_and_links(tmp_path):
     subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-L", libdir, "-lzeroshard",
                     f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True)
     assert subprocess.run([exe], timeout=120).returncode == 0
+

@@ -140,11 +140,12 @@ void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n
     *head = 0;
 }
 
-bool writes_overlap(std::vector<Range> &r) {
-    std::sort(r.begin(), r.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+bool writes_overlap(Range *r, size_t n) {
+    std::sort(r, r + n, [](const Range &a, const Range &b) { return a.lo < b.lo; });
     // Sweep keeping the furthest end seen among written and among all ranges.
     uintptr_t end_any = 0, end_written = 0;
-    for (const Range &x : r) {
+    for (size_t i = 0; i < n; i++) {
+        const Range &x = r[i];
         if (x.lo < end_written)
             return true;
         if (x.written && x.lo < end_any)
@@ -156,6 +157,8 @@ bool writes_overlap(std::vector<Range> &r) {
     return false;
 }
 
+bool writes_overlap(std::vector<Range> &r) { return writes_overlap(r.data(), r.size()); }
+
 // The chunk a plan gets when the caller leaves it to the library: the
 // largest of kDefaultChunk, kDefaultChunk / 2, ..., kTile whose workgroup
 // slots (chunks times kTile-element tiles per chunk) exceed the tiles that
@@ -163,10 +166,11 @@ bool writes_overlap(std::vector<Range> &r) {
 // the compact table of kDefaultChunk; many small tensors get small chunks,
 // so that few workgroups start only to find their tile past the end of a
 // short chunk.
-uint32_t pick_chunk(const std::vector<TensorDesc> &tensors) {
+uint32_t pick_chunk(const TensorDesc *tensors, size_t n) {
     for (uint32_t C = kDefaultChunk; C > kTile; C /= 2) {
         uint64_t slots = 0, work = 0;
-        for (const TensorDesc &d : tensors) {
+        for (size_t k = 0; k < n; k++) {
+            const TensorDesc &d = tensors[k];
             const uint64_t body = d.n - std::min<uint64_t>(d.head, d.n);
             const uint64_t chunks = body == 0 ? 1 : (body + C - 1) / C;
             slots += chunks * (C / kTile);
@@ -178,6 +182,68 @@ uint32_t pick_chunk(const std::vector<TensorDesc> &tensors) {
     return kTile;
 }
 
+int describe_tensor(const zero_tensor &t, TensorDesc *d, Range r[5]) {
+    const uintptr_t p = (uintptr_t)t.param_f16, g = (uintptr_t)t.grad_f16,
+                    w = (uintptr_t)t.master, m = (uintptr_t)t.m, v = (uintptr_t)t.v;
+    if (!p || !g || !w || !m || !v)
+        return ZERO_EINVAL;
+    if ((p | g) % 2 || (w | m | v) % 4)
+        return ZERO_EINVAL;
+    uint64_t b2, b4;
+    if (!mul_ok(t.n, 2, &b2) || !mul_ok(t.n, 4, &b4))
+        return ZERO_EOVERFLOW;
+    for (uintptr_t a : {p, g})
+        if (a + b2 < a)
+            return ZERO_EOVERFLOW;
+    for (uintptr_t a : {w, m, v})
+        if (a + b4 < a)
+            return ZERO_EOVERFLOW;
+    r[0] = {p, p + b2, true};
+    r[1] = {g, g + b2, false};
+    r[2] = {w, w + b4, true};
+    r[3] = {m, m + b4, true};
+    r[4] = {v, v + b4, true};
+    d->unused = 0;
+    d->p = (uint16_t *)t.param_f16;
+    d->g = (const uint16_t *)t.grad_f16;
+    d->w = t.master;
+    d->m = t.m;
+    d->v = t.v;
+    d->n = t.n;
+    const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
+    pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
+    return ZERO_OK;
+}
+
+void plan_stats(const TensorDesc *tensors, size_t n_desc, uint64_t n_tensors, uint64_t C,
+                zero_plan_stats *s) {
+    memset(s, 0, sizeof(*s));
+    s->n_tensors = n_tensors;
+    s->chunk_elems = C;
+    for (size_t k = 0; k < n_desc; k++) {
+        const TensorDesc &d = tensors[k];
+        const uint64_t head = std::min<uint64_t>(d.head, d.n);
+        s->n_params += d.n;
+        s->n_chunks += chunks_of(d, C);
+        if (d.vec == 1) {
+            s->scalar_elems += d.n;
+        } else {
+            // every chunk body but the tensor's last is a whole number of
+            // tiles, so only the tensor's last fewer-than-four elements (and
+            // its head) go singly
+            const uint64_t vec = (d.n - head) / 4 * 4;
+            s->vector_elems += vec;
+            s->scalar_elems += d.n - vec;
+        }
+    }
+    // at most 1/8 of the elements single and the default chunk: the fine
+    // tile.  scalar_elems * 8 cannot wrap: the three fp32 arrays of every
+    // tensor are disjoint ranges of the address space, so n_params < 2^64 / 12.
+    s->tile_elems =
+        s->scalar_elems * 8 <= s->n_params && C == kDefaultChunk ? kAdamTileFine : kTile;
+    s->table_bytes = n_desc * sizeof(TensorDesc) + s->n_chunks * sizeof(Chunk);
+}
+
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out) {
     if (!out || (n_tensors > 0 && !tensors))
@@ -187,85 +253,34 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
         (chunk_elems % kTile != 0 || chunk_elems < kMinChunk || chunk_elems > kMaxChunk))
         return ZERO_EINVAL;
     HostPlan plan;
-    memset(&plan.stats, 0, sizeof(plan.stats));
     std::vector<Range> ranges;
     uint64_t n_params = 0;
     for (uint32_t k = 0; k < n_tensors; k++) {
         const zero_tensor &t = tensors[k];
         if (t.n == 0)
             continue;
-        const uintptr_t p = (uintptr_t)t.param_f16, g = (uintptr_t)t.grad_f16,
-                        w = (uintptr_t)t.master, m = (uintptr_t)t.m, v = (uintptr_t)t.v;
-        if (!p || !g || !w || !m || !v)
-            return ZERO_EINVAL;
-        if ((p | g) % 2 || (w | m | v) % 4)
-            return ZERO_EINVAL;
-        uint64_t b2, b4;
-        if (!mul_ok(t.n, 2, &b2) || !mul_ok(t.n, 4, &b4))
-            return ZERO_EOVERFLOW;
-        for (uintptr_t a : {p, g})
-            if (a + b2 < a)
-                return ZERO_EOVERFLOW;
-        for (uintptr_t a : {w, m, v})
-            if (a + b4 < a)
-                return ZERO_EOVERFLOW;
-        ranges.push_back({p, p + b2, true});
-        ranges.push_back({g, g + b2, false});
-        ranges.push_back({w, w + b4, true});
-        ranges.push_back({m, m + b4, true});
-        ranges.push_back({v, v + b4, true});
+        TensorDesc d;
+        Range r[5];
+        const int rc = describe_tensor(t, &d, r);
+        if (rc != ZERO_OK)
+            return rc;
+        ranges.insert(ranges.end(), r, r + 5);
         if (!add_ok(n_params, t.n, &n_params))
             return ZERO_EOVERFLOW;
-        TensorDesc d;
-        d.unused = 0;
-        d.p = (uint16_t *)t.param_f16;
-        d.g = (const uint16_t *)t.grad_f16;
-        d.w = t.master;
-        d.m = t.m;
-        d.v = t.v;
-        d.n = t.n;
-        const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
-        pick_vector_path(a16, 2, a32, 3, 4, &d.vec, &d.head);
         plan.tensors.push_back(d);
     }
     if (writes_overlap(ranges))
         return ZERO_EINVAL;
 
-    const uint64_t C = automatic ? pick_chunk(plan.tensors) : chunk_elems;
-    zero_plan_stats &s = plan.stats;
-    s.n_tensors = n_tensors;
-    s.n_params = n_params;
-    s.chunk_elems = C;
+    const uint64_t C =
+        automatic ? pick_chunk(plan.tensors.data(), plan.tensors.size()) : chunk_elems;
     for (uint32_t k = 0; k < (uint32_t)plan.tensors.size(); k++) {
         const TensorDesc &d = plan.tensors[k];
-        const uint64_t head = std::min<uint64_t>(d.head, d.n);
-        // first chunk: the peeled head plus up to C elements; then C each
-        uint64_t start = 0;
-        uint64_t first = std::min<uint64_t>(d.n, head + C);
-        plan.chunks.push_back({k, (uint32_t)first, 0});
-        start = first;
-        while (start < d.n) {
-            const uint64_t cnt = std::min<uint64_t>(C, d.n - start);
-            plan.chunks.push_back({k, (uint32_t)cnt, start});
-            start += cnt;
-        }
-        if (d.vec == 1) {
-            s.scalar_elems += d.n;
-        } else {
-            // every chunk body but the tensor's last is a whole number of
-            // tiles, so only the tensor's last fewer-than-four elements (and
-            // its head) go singly
-            const uint64_t vec = (d.n - head) / 4 * 4;
-            s.vector_elems += vec;
-            s.scalar_elems += d.n - vec;
-        }
+        const uint64_t nc = chunks_of(d, C);
+        for (uint64_t j = 0; j < nc; j++)
+            plan.chunks.push_back(chunk_of(d, k, C, j));
     }
-    s.n_chunks = plan.chunks.size();
-    // at most 1/8 of the elements single and the default chunk: the fine
-    // tile.  scalar_elems * 8 cannot wrap: the three fp32 arrays of every
-    // tensor are disjoint ranges of the address space, so n_params < 2^64 / 12.
-    s.tile_elems = s.scalar_elems * 8 <= s.n_params && C == kDefaultChunk ? kAdamTileFine : kTile;
-    s.table_bytes = plan.tensors.size() * sizeof(TensorDesc) + plan.chunks.size() * sizeof(Chunk);
+    plan_stats(plan.tensors.data(), plan.tensors.size(), n_tensors, C, &plan.stats);
     *out = std::move(plan);
     return ZERO_OK;
 }

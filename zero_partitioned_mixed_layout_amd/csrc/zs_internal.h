@@ -119,6 +119,14 @@ inline uint32_t reduce_per_cu(uint32_t nd) {
 // caps below); before is 4-5% faster at N_d = 16 and equal at N_d = 64.
 inline bool fused_state_late(uint32_t nd) { return slices_in_flight(nd) < 16; }
 
+// Slices from which zero_reduce_adam_step runs the reduce and then the Adam
+// step (two kernels) instead of the fused kernel.  Measured on MI355X, one
+// process, 117,187,500 elements, against the two kernels: the fused kernel
+// is 6.9% faster at N_d = 8, 6.1% at 12, 4.2% at 16 and 3.6% at 24, and
+// 1.9% slower at 32, 6.9% at 48 and 9.8% at 64 (its mix of state writes
+// into the slice reads costs more than the 4 bytes per element it saves).
+constexpr uint32_t kFusedSplitSlices = 32;
+
 // Resident one-wave workgroups per CU for the fused reduce + Adam step.
 // State first: about 70 16-byte vectors per lane in flight per CU, counting
 // the six fp32 state vectors issued with the first slice batch (4 workgroups
@@ -133,10 +141,39 @@ inline uint32_t fused_per_cu(uint32_t nd, bool state_late) {
     return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 
+// A tensor's chunks: the first holds its peeled head plus up to C
+// elements, every later one C elements (the tensor's last may be shorter).
+// constexpr, so that the device code that fills a table on the GPU uses the
+// same formulas as the host plan builder (HIP compiles constexpr functions
+// for both sides).
+constexpr uint64_t first_chunk_count(const TensorDesc &d, uint64_t C) {
+    const uint64_t head = d.head < d.n ? d.head : d.n;
+    return d.n < head + C ? d.n : head + C;
+}
+constexpr uint64_t chunks_of(const TensorDesc &d, uint64_t C) {
+    const uint64_t first = first_chunk_count(d, C);
+    return 1 + (d.n - first + C - 1) / C;
+}
+// Chunk j of tensor k (j < chunks_of(d, C)).
+constexpr Chunk chunk_of(const TensorDesc &d, uint32_t k, uint64_t C, uint64_t j) {
+    const uint64_t first = first_chunk_count(d, C);
+    if (j == 0)
+        return {k, (uint32_t)first, 0};
+    const uint64_t start = first + (j - 1) * C;
+    const uint64_t left = d.n - start;
+    return {k, (uint32_t)(left < C ? left : C), start};
+}
+
 struct HostPlan {
     std::vector<TensorDesc> tensors;
     std::vector<Chunk> chunks;
     zero_plan_stats stats;
+};
+
+// A byte range [lo, hi) of one array, and whether the call writes it.
+struct Range {
+    uintptr_t lo, hi;
+    bool written;
 };
 
 // Validate and classify; fills `out`.  chunk_elems: 0 for the library's
@@ -145,14 +182,22 @@ struct HostPlan {
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out);
 
-// A byte range [lo, hi) of one array, and whether the call writes it.
-struct Range {
-    uintptr_t lo, hi;
-    bool written;
-};
+// One non-empty tensor: its descriptor (vector path and peeled head) and the
+// byte ranges of its five arrays (param, grad, master, m, v).  Errors:
+// EINVAL (a NULL or misaligned array), EOVERFLOW.
+int describe_tensor(const zero_tensor &t, TensorDesc *d, Range r[5]);
+
+// The library's chunk for these descriptors (see build_host_plan).
+uint32_t pick_chunk(const TensorDesc *tensors, size_t n);
+
+// Plan statistics of these descriptors cut into chunks of C elements;
+// n_tensors counts the caller's tensors, empty ones included.
+void plan_stats(const TensorDesc *tensors, size_t n_desc, uint64_t n_tensors, uint64_t C,
+                zero_plan_stats *s);
 
 // True if two of the ranges overlap where at least one of them is written
 // (read-only ranges may overlap each other).  Sorts r.
+bool writes_overlap(Range *r, size_t n);
 bool writes_overlap(std::vector<Range> &r);
 
 // Pick the widest vector width, at most max_width (8 or 4; else 1), and the

@@ -329,6 +329,35 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
     raise_flag(flag, bad);
 }
 
+// The Adam step over one tensor whose descriptor travels by value (no
+// table): workgroup b takes tile b of the tensor, which stands in for a
+// chunk of one tile (tile 0 also holds the peeled head), so the per-tile
+// code, and the results, are those of zs_adam_kernel.  Used where no table
+// exists: the second half of zero_reduce_adam_step at many slices.
+template <class Fmt, uint32_t TILE>
+__global__ __launch_bounds__(kWave) void zs_adam_flat_kernel(TensorDesc T, uint64_t ntiles,
+                                                             AdamConsts c,
+                                                             int32_t *__restrict__ flag) {
+    int bad = 0;
+    const uint64_t h = T.head < T.n ? T.head : T.n;
+    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        Chunk ch;
+        ch.tensor = 0;
+        if (T.vec == 4) {
+            const uint64_t start = b == 0 ? 0 : h + b * TILE;
+            const uint64_t want = b == 0 ? h + TILE : TILE;
+            ch.start = start;
+            ch.count = (uint32_t)(T.n - start < want ? T.n - start : want);
+            adam_tile_of_chunk<Fmt, TILE>(T, ch, 0, c, bad);
+        } else {
+            ch.start = b * TILE;
+            ch.count = (uint32_t)(T.n - ch.start < TILE ? T.n - ch.start : TILE);
+            adam_tile_single<Fmt, TILE>(T, ch, 0, c, bad);
+        }
+    }
+    raise_flag(flag, bad);
+}
+
 // ---------------------------------------------------------------------------
 // Gradient reduction over N_d slices.
 // ---------------------------------------------------------------------------
@@ -1041,6 +1070,57 @@ extern "C" int zero_plan_destroy(zero_plan *plan) {
     return rc;
 }
 
+namespace {
+
+// The Adam launch over a device table (descriptors and chunks) with the
+// given statistics: one one-wave workgroup per Adam tile, dispatched in
+// order and balanced over the CUs by the hardware; only tables beyond
+// kMaxGrid tiles stride.
+int launch_adam_table(const TensorDesc *d_tensors, const Chunk *d_chunks,
+                      const zero_plan_stats &stats, size_t lds, bool bf16, const AdamConsts &c,
+                      int32_t *flag, const int32_t *skip, const int32_t *log2_scale,
+                      hipStream_t st) {
+    const uint32_t tile = (uint32_t)stats.tile_elems;
+    const uint32_t tpc = (uint32_t)(stats.chunk_elems / tile);
+    const uint64_t n_virtual = stats.n_chunks * tpc;
+    const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
+    if (bf16 && tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+                           st, d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+    else if (bf16)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kTile>), dim3(grid), dim3(kWave), lds, st,
+                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+    else if (tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+                           st, d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+    else
+        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kTile>), dim3(grid), dim3(kWave), lds, st,
+                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+    if (hipGetLastError() != hipSuccess)
+        return ZERO_EHIP;
+    return ZERO_OK;
+}
+
+// The fp32 constants of step t, checked as zero_adam_scalars checks them.
+int adam_consts(const zero_adam_hparams *hp, uint64_t t, AdamConsts *c) {
+    float s[8];
+    const int rc = zero_adam_scalars(hp, t, s);
+    if (rc != ZERO_OK)
+        return rc;
+    *c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7], 1.0f};
+    return ZERO_OK;
+}
+
+int current_device(int *dev) {
+    if (hipGetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ZERO_EHIP;
+    }
+    return ZERO_OK;
+}
+
+} // namespace
+
 static int adam_step_launch(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
                             int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
                             const int32_t *log2_scale, void *stream) {
@@ -1048,47 +1128,20 @@ static int adam_step_launch(const zero_plan *plan, const zero_adam_hparams *hp, 
         return ZERO_EINVAL;
     if (nonfinite_flag != nullptr && (const void *)nonfinite_flag == (const void *)skip_if_nonzero)
         return ZERO_EINVAL;
-    float s[8];
-    int rc = zero_adam_scalars(hp, t, s);
+    AdamConsts c;
+    int rc = adam_consts(hp, t, &c);
     if (rc != ZERO_OK)
         return rc;
     if (plan->stats.n_chunks == 0)
         return ZERO_OK;
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return ZERO_EHIP;
-    }
+    if ((rc = current_device(&dev)) != ZERO_OK)
+        return rc;
     if (dev != plan->device)
         return ZERO_EINVAL;
-    const AdamConsts c = {s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7], 1.0f};
-    // one one-wave workgroup per Adam tile, dispatched in order and balanced
-    // over the CUs by the hardware; only plans beyond kMaxGrid tiles stride
-    const uint32_t tile = (uint32_t)plan->stats.tile_elems;
-    const uint32_t tpc = (uint32_t)(plan->stats.chunk_elems / tile);
-    const uint64_t n_virtual = plan->stats.n_chunks * tpc;
-    const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
-    hipStream_t st = (hipStream_t)stream;
-    const size_t lds = plan->lds_cap;
-    if (plan->bf16 && tile == kAdamTileFine)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
-                           st, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
-                           skip_if_nonzero, log2_scale);
-    else if (plan->bf16)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kTile>), dim3(grid), dim3(kWave), lds, st,
-                           plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
-                           skip_if_nonzero, log2_scale);
-    else if (tile == kAdamTileFine)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
-                           st, plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
-                           skip_if_nonzero, log2_scale);
-    else
-        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kTile>), dim3(grid), dim3(kWave), lds, st,
-                           plan->d_tensors, plan->d_chunks, n_virtual, tpc, c, nonfinite_flag,
-                           skip_if_nonzero, log2_scale);
-    if (hipGetLastError() != hipSuccess)
-        return ZERO_EHIP;
-    return ZERO_OK;
+    return launch_adam_table(plan->d_tensors, plan->d_chunks, plan->stats, plan->lds_cap,
+                             plan->bf16, c, nonfinite_flag, skip_if_nonzero, log2_scale,
+                             (hipStream_t)stream);
 }
 
 extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
@@ -1231,6 +1284,41 @@ extern "C" int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint3
 
 namespace {
 
+// The Adam step over one flat tensor (p, g, w, m, v of n elements) with
+// zs_adam_flat_kernel: the plan builder's access path and tile rule for a
+// one-tensor plan (256-element tiles on the vector path, else 512), and
+// its occupancy cap.
+template <class Fmt>
+int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *v, uint64_t n,
+                     const AdamConsts &c, int dev, hipStream_t st) {
+    TensorDesc T;
+    memset(&T, 0, sizeof(T));
+    T.p = p;
+    T.g = g;
+    T.w = w;
+    T.m = m;
+    T.v = v;
+    T.n = n;
+    const uintptr_t a16[2] = {(uintptr_t)p, (uintptr_t)g};
+    const uintptr_t a32[3] = {(uintptr_t)w, (uintptr_t)m, (uintptr_t)v};
+    zs::pick_vector_path(a16, 2, a32, 3, 4, &T.vec, &T.head);
+    const uint32_t tile = T.vec == 4 ? kAdamTileFine : kTile;
+    const uint64_t h = T.head < n ? T.head : n;
+    const uint64_t ntiles = T.vec == 4 ? (n == h ? 1 : (n - h + tile - 1) / tile)
+                                       : (n + tile - 1) / tile;
+    const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
+    const size_t lds = lds_cap_bytes(dev, zs::adam_per_cu(tile));
+    if (tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+                           st, T, ntiles, c, nullptr);
+    else
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kTile>), dim3(grid), dim3(kWave), lds, st, T,
+                           ntiles, c, nullptr);
+    if (hipGetLastError() != hipSuccess)
+        return ZERO_EHIP;
+    return ZERO_OK;
+}
+
 template <class Fmt>
 int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, void *param_f16,
                      float *master, float *m, float *v, void *grad_out_f16,
@@ -1284,6 +1372,19 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
         (void)hipGetLastError();
         return ZERO_EHIP;
     }
+    const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7], 1.0f};
+    if (nd >= zs::kFusedSplitSlices) {
+        // The reduce into the gradient output, or without one into the
+        // parameter array (every element of which the Adam step then reads
+        // as its gradient before writing the new parameter in its place),
+        // then the Adam step over it: the same values as the fused kernel.
+        void *gdst = grad_out_f16 != nullptr ? grad_out_f16 : param_f16;
+        rc = reduce_grad_shard<Fmt>(slices_f16, nd, n, gdst, nonfinite_flag, stream);
+        if (rc != ZERO_OK)
+            return rc;
+        return adam_flat_launch<Fmt>((uint16_t *)param_f16, (const uint16_t *)gdst, master, m, v,
+                                     n, c, dev, (hipStream_t)stream);
+    }
     // Access path: a common phase h (elements peeled singly) after which the
     // slices are 16-byte aligned (VEC 8) or 8-byte aligned (VEC 4), the fp16
     // outputs 8-byte and the fp32 state 16-byte aligned; else single elements.
@@ -1315,7 +1416,6 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
-    const AdamConsts c = {sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7], 1.0f};
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8 && late)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8, true>), dim3(grid), dim3(kWave), lds, st, args,
