@@ -20,8 +20,10 @@
  *  - `stream` is a hipStream_t (NULL: the default stream).  Device work is
  *    enqueued on it and the call returns without synchronising; results are
  *    ready once the stream reaches that point.
- *  - The library keeps no global mutable state; the step and reduce entry
- *    points allocate nothing.
+ *  - The step and reduce entry points allocate nothing.  The library's only
+ *    global state is, per device, the address of the fixed array that
+ *    zero_adam_step_noalloc builds its table in (set once, on that entry
+ *    point's first call on the device).
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
@@ -38,6 +40,7 @@ extern "C" {
 #define ZERO_EHIP (-3)      /* HIP runtime or launch error (captured, cleared) */
 #define ZERO_ENOMEM (-4)    /* allocation failed (plan or offload creation only) */
 #define ZERO_ENOTSUP (-5)   /* host CPU lacks AVX2 and F16C (host Adam, offload) */
+#define ZERO_ERANGE (-6)    /* beyond the fixed limits of zero_adam_step_noalloc */
 
 /* Largest N_d zero_reduce_grad_shard accepts (slice pointers travel as
  * kernel arguments). */
@@ -493,6 +496,46 @@ int zero_offload_step_bf16(zero_offload *off, const void *grad_bf16, void *param
                            float *master, float *m, float *v, uint64_t n,
                            const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
                            void *stream);
+
+/* Limits of zero_adam_step_noalloc: the bytes of its per-device table array
+ * (64 per non-empty tensor + 16 per chunk) and the tensors of one call. */
+#define ZERO_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define ZERO_NOALLOC_MAX_TENSORS 1024u
+
+/*
+ * zero_adam_step_noalloc -- zero_adam_step over a list of fp16 tensors
+ * without a plan, allocating nothing.  For callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.
+ * The chunk table that zero_plan_create keeps in an allocation of its own
+ * is instead rebuilt on the device at every call, in a fixed array of
+ * ZERO_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on until the process ends: the tensors' descriptors travel as
+ * kernel arguments (one small launch per 32 non-empty tensors), then the
+ * Adam kernel of zero_adam_step runs over that table.  The update, the
+ * flag and the skip are those of zero_adam_step, and the results are
+ * bit-identical to zero_plan_create (chunk_elems = 0) followed by
+ * zero_adam_step on the same tensors.
+ * tensors: host array of n_tensors descriptors, as zero_plan_create (read
+ *   during the call only).  hp, t, nonfinite_flag, skip_if_nonzero: as
+ *   zero_adam_step.
+ * The array is shared by every call on a device and keeps the last call's
+ * table: calls that may overlap on one device (two streams, or two threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe.  No device, pinned or heap memory is allocated:
+ * hipMalloc, hipFree and allocating library routines are never called
+ * (the host bookkeeping, about 190 KB, is on the calling thread's stack).
+ * The first call on a device takes the array's device address
+ * (hipGetSymbolAddress) with that device current.
+ * Asynchronous on `stream`.
+ * Errors: ERANGE (more than ZERO_NOALLOC_MAX_TENSORS tensors, or a table
+ * larger than ZERO_NOALLOC_SCRATCH_BYTES; zero_plan_describe's table_bytes
+ * gives its size), checked before anything is enqueued; EINVAL and
+ * EOVERFLOW as zero_plan_create and zero_adam_step; EHIP.
+ */
+int zero_adam_step_noalloc(const zero_tensor *tensors, uint32_t n_tensors,
+                           const zero_adam_hparams *hp, uint64_t t, int32_t *nonfinite_flag,
+                           const int32_t *skip_if_nonzero, void *stream);
 
 /* zero_status_str -- static description of a status code. */
 const char *zero_status_str(int status);

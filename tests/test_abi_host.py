@@ -56,7 +56,7 @@ def _without_devices(body: str) -> None:
 
 
 def test_status_strings(zs):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert zs.zero_status_str(code) != "unknown status"
     assert zs.zero_status_str(7) == "unknown status"
 
@@ -491,3 +491,61 @@ def test_header_is_plain_c_and_links(tmp_path):
                     f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True)
     assert subprocess.run([exe], timeout=120).returncode == 0
 
+
+def test_noalloc_rejects_before_any_device_call(zs):
+    _without_devices("_noalloc_rejects_before_any_device_call")
+
+
+def _noalloc_rejects_before_any_device_call(zs):
+    """zero_adam_step_noalloc checks its arguments and its fixed limits
+    (tensor count, table bytes) on the host before it enqueues anything
+    (fake addresses, never used)."""
+    import ctypes
+    L = zs.lib()
+    hp = zs.AdamHParams()._c()
+    bad_hp = zs.AdamHParams(weight_decay=0.1)._c()
+    T = zs._Tensor
+
+    def arr(ts):
+        a = (T * max(1, len(ts)))()
+        for k, x in enumerate(ts):
+            a[k] = x
+        return a
+
+    def tensor(base, n):
+        # five disjoint arrays spaced 16 n bytes apart
+        return T(base, base + 4 * n, base + 8 * n, base + 16 * n, base + 24 * n, n)
+
+    one = [tensor(1 << 30, 1000)]
+
+    def call(ts=one, h=hp, t=1, flag=None, skip=None, n=None):
+        a = arr(ts)
+        return L.zero_adam_step_noalloc(a, len(ts) if n is None else n,
+                                        ctypes.byref(h) if h is not None else None, t, flag,
+                                        skip, None)
+
+    assert call(h=None) == -1
+    assert call(h=bad_hp) == -1
+    assert call(t=0) == -1
+    assert call(flag=0x1000, skip=0x1000) == -1          # flag is the skip input
+    assert L.zero_adam_step_noalloc(None, 1, ctypes.byref(hp), 1, None, None, None) == -1
+    overlap = [tensor(1 << 30, 1000), tensor((1 << 30) + 64, 1000)]
+    assert call(ts=overlap) == -1                        # arrays of two tensors overlap
+    odd = [T((1 << 30) + 1, 1 << 31, 1 << 32, 1 << 33, 1 << 34, 8)]
+    assert call(ts=odd) == -1                            # fp16 array not 2-byte aligned
+    assert call(ts=[T(1 << 30, 0, 1 << 32, 1 << 33, 1 << 34, 8)]) == -1   # NULL gradient
+    assert call(ts=[tensor(1 << 30, 2 ** 62)]) == -2     # byte counts overflow
+    # the fixed limits: more tensors than the array holds descriptors for ...
+    many = [tensor((k + 1) << 24, 8) for k in range(zs.ZERO_NOALLOC_MAX_TENSORS + 1)]
+    assert call(ts=many) == -6
+    # ... and a table past ZERO_NOALLOC_SCRATCH_BYTES: 16384-element chunks
+    # of 16 bytes each, one tensor of (2^19 + 1) * 16384 elements
+    n_big = ((zs.ZERO_NOALLOC_SCRATCH_BYTES // 16) + 1) * 16384
+    big = tensor(1 << 40, n_big)
+    assert zs.zero_plan_describe([(big.param_f16, big.grad_f16, big.master, big.m, big.v,
+                                   big.n)])["table_bytes"] > \
+        zs.ZERO_NOALLOC_SCRATCH_BYTES
+    assert call(ts=[tensor(1 << 40, n_big)]) == -6
+    # nothing to do: no tensors, or only empty ones, returns before any device call
+    assert call(ts=[], n=0) == 0
+    assert call(ts=[T(0, 0, 0, 0, 0, 0), T(0, 0, 0, 0, 0, 0)]) == 0

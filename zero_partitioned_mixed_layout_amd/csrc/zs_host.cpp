@@ -111,6 +111,7 @@ extern "C" const char *zero_status_str(int status) {
     case ZERO_EHIP: return "HIP runtime or launch error";
     case ZERO_ENOMEM: return "allocation failed";
     case ZERO_ENOTSUP: return "host CPU lacks AVX2 and F16C";
+    case ZERO_ERANGE: return "beyond the fixed limits of the allocation-free step";
     default: return "unknown status";
     }
 }

@@ -36,6 +36,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1518,4 +1520,145 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The Adam step without a plan and without allocation: the chunk table is
+// rebuilt on the device at every call in a fixed array, then the Adam kernel
+// above runs over it.
+// ---------------------------------------------------------------------------
+
+// The table of zero_adam_step_noalloc: descriptors, then chunks.  One copy
+// per device, held until the process ends.  In host code this name is a
+// stand-in, not a device address: the host only ever uses the address that
+// hipGetSymbolAddress returns for the current device (noalloc_table below).
+static __device__ __align__(256) unsigned char scratch[ZERO_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Tensors whose descriptors one staging launch carries in its arguments
+// (2 KiB of descriptors and 264 bytes of chunk indices).
+constexpr uint32_t kStageBatch = 32;
+
+struct StageArgs {
+    TensorDesc d[kStageBatch];
+    uint64_t chunk0[kStageBatch + 1]; // table index of each tensor's first
+                                      // chunk; chunk0[count]: one past the last
+};
+
+// Writes the descriptors of tensors first .. first + count - 1 at their
+// places in the table and every chunk record of theirs, with the plan
+// builder's chunk formulas (zs::chunk_of).  Plain vector stores.
+__global__ __launch_bounds__(256) void zs_stage_table_kernel(StageArgs a, uint32_t first,
+                                                             uint32_t count, uint64_t C,
+                                                             TensorDesc *__restrict__ tensors,
+                                                             Chunk *__restrict__ chunks) {
+    const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    if (tid < count)
+        tensors[first + tid] = a.d[tid];
+    const uint64_t hi = a.chunk0[count];
+    for (uint64_t c = a.chunk0[0] + tid; c < hi; c += stride) {
+        uint32_t k = 0;
+        while (k + 1 < count && a.chunk0[k + 1] <= c)
+            k++;
+        chunks[c] = zs::chunk_of(a.d[k], first + k, C, c - a.chunk0[k]);
+    }
+}
+
+// Device address of the table array on device `dev`, taken once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_table_addr[kMaxDevices];
+std::mutex g_table_mu;
+
+int noalloc_table(int dev, unsigned char **out) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return ZERO_EHIP;
+    void *p = g_table_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_table_mu);
+        p = g_table_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return ZERO_EHIP;
+            }
+            g_table_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = (unsigned char *)p;
+    return ZERO_OK;
+}
+
+} // namespace
+
+extern "C" int zero_adam_step_noalloc(const zero_tensor *tensors, uint32_t n_tensors,
+                                      const zero_adam_hparams *hp, uint64_t t,
+                                      int32_t *nonfinite_flag, const int32_t *skip_if_nonzero,
+                                      void *stream) {
+    if (!hp || (n_tensors > 0 && !tensors))
+        return ZERO_EINVAL;
+    if (nonfinite_flag != nullptr && (const void *)nonfinite_flag == (const void *)skip_if_nonzero)
+        return ZERO_EINVAL;
+    AdamConsts c;
+    int rc = adam_consts(hp, t, &c);
+    if (rc != ZERO_OK)
+        return rc;
+    if (n_tensors > ZERO_NOALLOC_MAX_TENSORS)
+        return ZERO_ERANGE;
+    // the plan builder's classification and checks, on the stack
+    TensorDesc d[ZERO_NOALLOC_MAX_TENSORS];
+    zs::Range r[5 * ZERO_NOALLOC_MAX_TENSORS];
+    size_t nd = 0;
+    uint64_t n_params = 0;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        if (tensors[k].n == 0)
+            continue;
+        if ((rc = zs::describe_tensor(tensors[k], &d[nd], &r[5 * nd])) != ZERO_OK)
+            return rc;
+        if (__builtin_add_overflow(n_params, tensors[k].n, &n_params))
+            return ZERO_EOVERFLOW;
+        nd++;
+    }
+    if (zs::writes_overlap(r, 5 * nd))
+        return ZERO_EINVAL;
+    if (nd == 0)
+        return ZERO_OK;
+    const uint64_t C = zs::pick_chunk(d, nd);
+    zero_plan_stats stats;
+    zs::plan_stats(d, nd, n_tensors, C, &stats);
+    if (stats.table_bytes > ZERO_NOALLOC_SCRATCH_BYTES)
+        return ZERO_ERANGE;
+    int dev = -1;
+    if ((rc = current_device(&dev)) != ZERO_OK)
+        return rc;
+    unsigned char *table = nullptr;
+    if ((rc = noalloc_table(dev, &table)) != ZERO_OK)
+        return rc;
+    TensorDesc *d_tensors = (TensorDesc *)table;
+    Chunk *d_chunks = (Chunk *)(table + nd * sizeof(TensorDesc));
+    hipStream_t st = (hipStream_t)stream;
+    uint64_t c0 = 0;
+    for (size_t b = 0; b < nd; b += kStageBatch) {
+        const uint32_t count = (uint32_t)(nd - b < kStageBatch ? nd - b : kStageBatch);
+        StageArgs a;
+        memset(&a, 0, sizeof(a));
+        for (uint32_t j = 0; j < count; j++) {
+            a.d[j] = d[b + j];
+            a.chunk0[j] = c0;
+            c0 += zs::chunks_of(d[b + j], C);
+        }
+        a.chunk0[count] = c0;
+        const uint64_t work = a.chunk0[count] - a.chunk0[0];
+        const uint64_t want = ((work > count ? work : count) + 255) / 256;
+        const uint32_t grid = (uint32_t)(want < 1024 ? want : 1024);
+        hipLaunchKernelGGL(zs_stage_table_kernel, dim3(grid), dim3(256), 0, st, a, (uint32_t)b,
+                           count, C, d_tensors, d_chunks);
+        if (hipGetLastError() != hipSuccess)
+            return ZERO_EHIP;
+    }
+    const size_t lds = lds_cap_bytes(dev, zs::adam_per_cu((uint32_t)stats.tile_elems));
+    return launch_adam_table(d_tensors, d_chunks, stats, lds, false, c, nonfinite_flag,
+                             skip_if_nonzero, nullptr, st);
 }

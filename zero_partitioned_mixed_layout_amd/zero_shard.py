@@ -27,6 +27,9 @@ ZERO_EOVERFLOW = -2
 ZERO_EHIP = -3
 ZERO_ENOMEM = -4
 ZERO_ENOTSUP = -5
+ZERO_ERANGE = -6
+ZERO_NOALLOC_SCRATCH_BYTES = 8 << 20
+ZERO_NOALLOC_MAX_TENSORS = 1024
 ZERO_MAX_SLICES = 256
 ZERO_LOG2_SCALE_MAX = 100
 
@@ -86,6 +89,8 @@ def _load() -> ctypes.CDLL:
         "zero_adam_scalars": [ctypes.POINTER(_HParams), u64, ctypes.POINTER(ctypes.c_float)],
         "zero_adam_step": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp],
         "zero_adam_step_scaled": [vp, ctypes.POINTER(_HParams), u64, vp, vp, vp, vp],
+        "zero_adam_step_noalloc": [ctypes.POINTER(_Tensor), u32, ctypes.POINTER(_HParams), u64,
+                                   vp, vp, vp],
         "zero_loss_scale_update": [vp, vp, u32, ctypes.c_int32, ctypes.c_int32, vp],
         "zero_reduce_grad_shard": [ctypes.POINTER(vp), u32, u64, vp, vp, vp],
         "zero_reduce_adam_step": [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, vp,
@@ -121,7 +126,7 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_reduce_adam_step", "zero_reduce_adam_step_bf16", "zero_adam_step_host",
            "zero_adam_step_host_bf16", "zero_offload_create", "zero_offload_step_bf16",
            "zero_offload_destroy", "zero_offload_step", "zero_status_str",
-           "zero_adam_step_scaled", "zero_loss_scale_update")
+           "zero_adam_step_scaled", "zero_loss_scale_update", "zero_adam_step_noalloc")
 
 
 def lib() -> ctypes.CDLL:
@@ -327,6 +332,25 @@ def zero_adam_step(plan: Plan, hp, t: int, nonfinite_flag: Optional[torch.Tensor
     _check("zero_adam_step_scaled",
            _lib.zero_adam_step_scaled(plan.handle, ctypes.byref(h), int(t),
                                       loss_scale.state.data_ptr(), f, s, _stream_handle(stream)))
+
+
+def zero_adam_step_noalloc(tensors: Sequence[Sequence[torch.Tensor]], hp, t: int,
+                           nonfinite_flag: Optional[torch.Tensor] = None,
+                           skip_if_nonzero: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue one Adam step over float16 tensors (param, grad, master, m, v)
+    without a plan: the library rebuilds the chunk table in its fixed
+    per-device array and allocates nothing.  Calls that may overlap on one
+    device race for that array."""
+    arr, device = _tensor_entries(tensors, torch.float16)
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    h = _hp(hp)
+    f = _flag_ptr(nonfinite_flag, "nonfinite_flag", device)
+    s = _flag_ptr(skip_if_nonzero, "skip_if_nonzero", device)
+    with torch.cuda.device(device):
+        _check("zero_adam_step_noalloc",
+               _lib.zero_adam_step_noalloc(arr, len(tensors), ctypes.byref(h), int(t), f, s,
+                                           _stream_handle(stream)))
 
 
 class LossScale:
