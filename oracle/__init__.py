@@ -194,7 +194,8 @@ def adam_step_scaled(grad16, param16, master, m, v, *, lr, beta1, beta2, eps, t,
                      log2_scale, weight_decay=0.0, skip=False, fmt="f16") -> int:
     """adam_step on gradients that carry a loss scale of 2^log2_scale: each
     widened gradient is multiplied by 2^-log2_scale first (|log2_scale| <=
-    100).  Returns the non-finite flag of the scaled gradients."""
+    100).  Returns the non-finite flag of the gradients after 2^-log2_scale
+    (a finite bfloat16 value can overflow fp32 there when log2_scale < 0)."""
     n = master.size
     g = np.ascontiguousarray(grad16).view(np.uint16)
     for a, dt in ((param16, np.uint16), (master, np.float32), (m, np.float32),

@@ -315,8 +315,9 @@ int orc_adam_scalars(const double hp[5], uint64_t t, float out[8])
  * written fresh from the updated master ([16B] "Why you can't just delete the
  * fp32 copies": updates accumulate in the fp32 master, the fp16 weights are
  * derived from it).  Non-finite values follow IEEE arithmetic element by
- * element.  Returns 1 if any gradient is infinite or NaN, else 0; if skip is
- * nonzero nothing is read or written and 0 is returned.
+ * element.  Returns 1 if any gradient (after the loss scale's 2^-k, in the
+ * scaled step) is infinite or NaN, else 0; if skip is nonzero nothing is
+ * read or written and 0 is returned.
  */
 static int adam_over(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
                      float *w, float *m, float *v, const double hp[5], uint64_t t,
@@ -334,11 +335,14 @@ static int adam_over(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *para
     const float bc1 = s[5], bc2 = s[6], eps = s[7];
     int flag = 0;
     for (uint64_t i = 0; i < n; i++) {
-        if (!orc_is_finite(fmt, grad16[i]))
-            flag = 1;
         float g = orc_widen(fmt, grad16[i]);
         if (scaled)
             g = g * unscale;
+        /* the flag looks at the gradient the update uses: infinite or NaN
+           when the 16-bit value is, or when 2^-k carries a finite bfloat16
+           value past the fp32 range (k < 0) */
+        if (!isfinite(g))
+            flag = 1;
 
         float m_old = b1 * m[i];
         float m_in = omb1 * g;
@@ -378,10 +382,13 @@ int orc_adam_step_fmt(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *par
  * 2^-24 ([16B] "Why you can't just delete the fp32 copies"), which is what a
  * scale on the loss, and so on every gradient, works against.  Reading: the
  * widened gradient is multiplied by 2^-k in fp32 before the update above.
- * For |k| <= 100 this product is exact for every finite fp16 value (it stays
- * a normal fp32 number), so the step equals the unscaled step on the true
- * gradient whenever that gradient is itself an fp16 value.  Other k are
- * rejected.
+ * For fp16 and |k| <= 100 this product is exact for every finite value (it
+ * stays a normal fp32 number), so the step equals the unscaled step on the
+ * true gradient whenever that gradient is itself an fp16 value.  bfloat16
+ * has the fp32 exponent range: there the product is exact only while it
+ * stays a normal fp32 number (k > 0 can push small values into the
+ * subnormals or to zero, k < 0 large ones to infinity, which raises the
+ * flag).  Other k are rejected.
  */
 int orc_adam_step_scaled(int fmt, uint64_t n, const uint16_t *grad16, uint16_t *param16,
                          float *w, float *m, float *v, const double hp[5], uint64_t t,

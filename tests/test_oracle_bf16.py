@@ -157,6 +157,16 @@ def test_bf16_reduce(orc):
     assert out[0] == 0x0000
     out, _ = orc.reduce_grad(order[::-1], fmt="bf16")
     assert orc.bf16_to_f32(out)[0] == orc.bf16_to_f32(orc.f32_to_bf16(np.array([1 / 3], np.float32)))[0]
+    # the flag: values of the largest finite exponent leave it down, an
+    # infinite mean raises it, and so does a sum that leaves the fp32 range
+    # (twice the largest finite bfloat16 is past fp32's largest number)
+    big = np.array([0x7F7F, 0xFF7F, 0x7F00, 0x0001], np.uint16)
+    out, f = orc.reduce_grad([big], fmt="bf16")
+    assert f == 0 and np.array_equal(out, big)
+    out, f = orc.reduce_grad([np.array([0x3F80, 0x7F80], np.uint16)], fmt="bf16")
+    assert f == 1 and out[1] == 0x7F80
+    out, f = orc.reduce_grad([np.array([0x7F7F], np.uint16)] * 2, fmt="bf16")
+    assert f == 1 and out[0] == 0x7F80
 
 
 def test_bf16_swamping_is_worse_than_fp16(orc):

@@ -144,6 +144,30 @@ def test_scaled_flag_skip_and_range(orc):
             orc.adam_step_scaled(g, p, w, m, v, t=1, log2_scale=k, **HP)
 
 
+def test_scaled_flag_sees_the_unscaled_gradient(orc):
+    """The flag tests the gradient the update uses, after 2^-k.  bfloat16
+    has the fp32 exponent range, so its largest finite value (2^127 (2 -
+    2^-7)) times 2^1 (k = -1) is infinite in fp32: the flag is raised and,
+    per IEEE arithmetic, the master becomes NaN (inf / inf in the update).
+    At k = 0 the same value is finite: no flag, and since g * g overflows,
+    v is infinite and the update's denominator with it, so the master does
+    not move.  fp16's largest value times 2^100 is about 6.6e34, finite:
+    no fp16 gradient raises the flag at any |k| <= 100."""
+    big = np.ldexp(2.0 - 2.0 ** -7, 127)
+    g = _bits([big, -big, 1.0], "bf16")
+    w, m, v, p = _state(3, 9)
+    w0 = w.copy()
+    assert orc.adam_step_scaled(g, p, w, m, v, t=1, log2_scale=-1, fmt="bf16", **HP) == 1
+    assert np.isnan(w[:2]).all() and np.isfinite(w[2])
+    w, m, v, p = w0.copy(), np.zeros(3, np.float32), np.zeros(3, np.float32), p * 0
+    assert orc.adam_step_scaled(g, p, w, m, v, t=1, log2_scale=0, fmt="bf16", **HP) == 0
+    assert np.isinf(v[:2]).all() and np.array_equal(w[:2], w0[:2])
+    g16 = _bits([65504.0, -65504.0, 2.0 ** -24], "f16")
+    for k in (-100, -1, 0, 100):
+        w, m, v, p = _state(3, 9)
+        assert orc.adam_step_scaled(g16, p, w, m, v, t=1, log2_scale=k, **HP) == 0, k
+
+
 def test_loss_scale_sequence_traced_by_hand(orc):
     """interval 3, scale exponents in [0, 4], starting at 2^2."""
     flags = [0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 1, 1, 1, 1, 0, 0, 0, 0]

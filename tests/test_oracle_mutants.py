@@ -44,8 +44,8 @@ MUTANTS = {
                        "float acc = orc_widen(fmt, slices[nd - 1][i]);\n"
                        "        for (uint32_t r = nd - 1; r-- > 0;)\n"
                        "            acc = acc + orc_widen(fmt, slices[r][i]);"),
-    "flag_ignores_nan": ("if (!orc_is_finite(fmt, grad16[i]))",
-                         "if (((grad16[i] >> 10) & 0x1f) == 31 && (grad16[i] & 0x3ff) == 0)"),
+    "flag_ignores_nan": ("if (!isfinite(g))", "if (isinf(g))"),
+    "flag_before_unscale": ("if (!isfinite(g))", "if (!orc_is_finite(fmt, grad16[i]))"),
     "reduce_flag_ignores_nan": ("if (!orc_is_finite(fmt, out[i]))",
                                 "if (((out[i] >> 10) & 0x1f) == 31 && (out[i] & 0x3ff) == 0)"),
     "comm_stage3_two_passes": ("uint64_t passes = stage == 3 ? 3 : 2;", "uint64_t passes = 2;"),
