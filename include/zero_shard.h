@@ -46,6 +46,10 @@ extern "C" {
  * kernel arguments). */
 #define ZERO_MAX_SLICES 256
 
+/* Slices from which zero_reduce_adam_step runs the reduce and the Adam
+ * kernels in sequence instead of its fused kernel. */
+#define ZERO_FUSED_SPLIT_SLICES 32
+
 /* Shard of a flat buffer of psi elements split over nd ranks. */
 typedef struct zero_layout {
     uint64_t padded_total; /* psi rounded up to a multiple of nd * align */
@@ -264,8 +268,13 @@ typedef struct zero_loss_scale {
 /*
  * zero_adam_step_scaled -- zero_adam_step on gradients that carry the loss
  * scale *scale: each widened gradient is multiplied by 2^-log2_scale in fp32
- * before the update (exact for every finite fp16 value), so the step equals
- * the unscaled step on the true gradient wherever that is representable.
+ * before the update, so the step equals the unscaled step on the true
+ * gradient wherever that is representable.  The product is exact for every
+ * finite fp16 value.  bfloat16 has fp32's exponent range: there it is exact
+ * only while it stays a normal fp32 number (log2_scale > 0 can push small
+ * values into the subnormals or to zero; log2_scale < 0 can carry large
+ * ones to infinity).  The non-finite flag tests the gradient after the
+ * multiply, so such an overflow raises it.
  * log2_scale is read on the device when the step starts and clamped to
  * [-ZERO_LOG2_SCALE_MAX, ZERO_LOG2_SCALE_MAX].  Plans of either format.
  * A step skipped through skip_if_nonzero leaves everything unchanged; the
@@ -348,9 +357,9 @@ int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
  *   g16 = fp16((s_0[i] + ... + s_{nd-1}[i]) / nd)   as zero_reduce_grad_shard
  *   then the Adam element of zero_adam_step with g = fp32(g16)
  * so the results are bit-identical to the two calls in sequence (without
- * a skip input).  Below 32 slices one kernel does it all, reading the
- * slices and the fp32 state in one pass (4 bytes per element less than the
- * two calls); from 32 slices on, where that kernel's mix of state writes
+ * a skip input).  Below ZERO_FUSED_SPLIT_SLICES (32) slices one kernel
+ * does it all, reading the slices and the fp32 state in one pass (4 bytes
+ * per element less than the two calls); from there on, where its mix of state writes
  * into the slice reads costs more than it saves, the call runs the reduce
  * kernel and then the Adam kernel, with the fp16 gradient passing through
  * grad_out_f16, or without it through param_f16, which then holds the
@@ -421,7 +430,7 @@ int zero_gather_shards(const void *const *shards_f16, uint32_t nd, uint64_t shar
  * same order as zero_adam_step, so the results are bit-identical.
  * grad_f16: n fp16 (read); param_f16: n fp16 (written); master, m, v: n fp32
  * each, updated in place; all host memory, borrowed.  threads: 0 for
- * min(16, hardware threads), else the number of threads to use, at most
+ * min(16, CPUs the process may run on), else the number of threads to use, at most
  * 1024 (the calling thread is one of them).  nonfinite_flag: NULL or a host int32 that 1 is
  * OR-ed into if any gradient is infinite or NaN.  Synchronous.
  * Errors: EINVAL (NULL or misaligned arrays, written arrays overlapping,
@@ -448,16 +457,36 @@ int zero_adam_step_host_bf16(const void *grad_bf16, void *param_bf16, float *mas
  * host threads of the CPU update. */
 typedef struct zero_offload zero_offload;
 
+/* How an offload pipeline was set up (see zero_offload_describe). */
+typedef struct zero_offload_info {
+    uint32_t threads;     /* host threads of the update, the caller's included */
+    int32_t numa_node;    /* the GPU's NUMA node as the host reports it; -1: unknown */
+    uint32_t pinned_cpus; /* CPUs of that node the worker threads are pinned to;
+                             0: not pinned (node unknown, or none of its CPUs
+                             is in the process's affinity) */
+    uint32_t reserved;
+    uint64_t chunk_elems; /* elements per pipeline chunk */
+} zero_offload_info;
+
 /*
  * zero_offload_create -- set up the offload pipeline on the current device.
  * chunk_elems: elements per pipeline chunk (0: 4 Mi; else a multiple of 8,
  * at most 2^32); three chunks of fp16 gradients and three of fp16
  * parameters are staged in pinned host memory (hipHostMalloc, 12 bytes per
- * chunk element).  threads: as zero_adam_step_host.  *out belongs to the
- * caller until zero_offload_destroy.
+ * chunk element).  threads: 0 for min(16, CPUs available), else as
+ * zero_adam_step_host.  Where the host reports the GPU's NUMA node
+ * ([DSZ] "Offload trades capacity against movement": NUMA placement is one
+ * of offload's costs), the worker threads are pinned to that node's CPUs
+ * (within the process's affinity) and "CPUs available" counts those; the
+ * caller should first-touch the fp32 master, m and v from that node too.
+ * *out belongs to the caller until zero_offload_destroy.
  * Errors: EINVAL; ENOTSUP; ENOMEM; EHIP.
  */
 int zero_offload_create(uint64_t chunk_elems, uint32_t threads, zero_offload **out);
+
+/* zero_offload_describe -- the threads, NUMA placement and chunk of an
+ * offload pipeline.  Host only.  Errors: EINVAL (NULL). */
+int zero_offload_describe(const zero_offload *off, zero_offload_info *out);
 
 /* zero_offload_destroy -- wait for its copies and free everything.  NULL is
  * accepted.  Errors: EHIP. */

@@ -107,6 +107,34 @@ def test_scaled_step_matches_oracle(zs, fmt, k):
     plan.destroy()
 
 
+@pytest.mark.parametrize("k", [-1, 0])
+def test_bf16_overflow_after_unscale_raises_the_flag(zs, k):
+    """bfloat16 gradients of the largest finite magnitude, at scattered
+    positions over every access path: at k = -1 their product with 2^-k is
+    infinite in fp32, which the flag reports (and master, m, v go NaN as in
+    the oracle); at k = 0 they stay finite and the flag stays down."""
+    import torch
+    say(f"bf16 overflow after unscale k={k}")
+    plan, dev, host = _plan(zs, "bf16", 31 - k)
+    ls = zs.LossScale(log2_scale=0, min_log2=-100, device=torch.device("cuda", 0))
+    ls.state[0] = k
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    want = 0
+    for j, ((p, g, w, m, v), h) in enumerate(zip(dev, host)):
+        gb = _scaled_grads(g.numel(), 500 + j, 0, "bf16")
+        pos = np.unique(np.random.default_rng(j).integers(0, g.numel(), 3))
+        gb[pos] = np.where(pos % 2 == 0, 0x7F7F, 0xFF7F).astype(np.uint16)
+        g.copy_(_to_dev(gb, "bf16"))
+        want |= oracle.adam_step_scaled(gb, h[0], h[1], h[2], h[3], t=1, log2_scale=k,
+                                        fmt="bf16", **HP)
+    assert want == (1 if k < 0 else 0)
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, flag, loss_scale=ls)
+    torch.cuda.synchronize()
+    assert _compare(dev, host, "bf16", f"bf16 overflow k={k}") == 0
+    assert int(flag.item()) == want
+    plan.destroy()
+
+
 def test_update_matches_oracle(zs):
     """A fixed sequence of flags written from the host; after each update
     the device state equals the oracle's and the flag is 0 again."""

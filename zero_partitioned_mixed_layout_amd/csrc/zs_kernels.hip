@@ -126,11 +126,16 @@ __device__ __forceinline__ void raise_flag(int32_t *flag, int bad) {
 // ---------------------------------------------------------------------------
 
 // One element of the Adam step (Kingma and Ba, Algorithm 1, with bias
-// correction and eps outside the root).  Returns the new 16-bit parameter.
+// correction and eps outside the root).  Returns the new 16-bit parameter;
+// `bad` is raised if the gradient the update uses, after the loss scale's
+// 2^-k, is infinite or NaN.  The product is exact for every finite fp16
+// value; a finite bfloat16 value (fp32's exponent range) can underflow for
+// k > 0 and overflow to infinity for k < 0, which the flag then reports.
 template <class Fmt = FmtF16>
 __device__ __forceinline__ typename Fmt::T adam_elem(float g, float &w, float &m, float &v,
-                                                     const AdamConsts &c) {
-    g = g * c.unscale; // exact: a power of two, the product a normal fp32
+                                                     const AdamConsts &c, int &bad) {
+    g = g * c.unscale;
+    bad |= (__float_as_uint(g) & 0x7F800000u) == 0x7F800000u;
     const float m_old = c.b1 * m;
     const float m_in = c.omb1 * g;
     m = m_old + m_in;
@@ -151,11 +156,10 @@ template <class Fmt>
 __device__ __forceinline__ void adam_single(const TensorDesc &T, uint64_t i,
                                             const AdamConsts &c, int &bad) {
     const uint16_t gb = as_global(T.g)[i];
-    bad |= bits_nonfinite<Fmt>(gb);
     typename Fmt::T gh;
     memcpy(&gh, &gb, 2);
     float w = as_global(T.w)[i], m = as_global(T.m)[i], v = as_global(T.v)[i];
-    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c);
+    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c, bad);
     as_global(T.w)[i] = w;
     as_global(T.m)[i] = m;
     as_global(T.v)[i] = v;
@@ -187,11 +191,8 @@ __device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t 
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const typename Fmt::T gj = q.g[j];
-        uint16_t gb;
-        memcpy(&gb, &gj, 2);
-        bad |= bits_nonfinite<Fmt>(gb);
         float w = q.w[j], m = q.m[j], v = q.v[j];
-        p[j] = adam_elem<Fmt>((float)gj, w, m, v, c);
+        p[j] = adam_elem<Fmt>((float)gj, w, m, v, c, bad);
         q.w[j] = w;
         q.m[j] = m;
         q.v[j] = v;
@@ -284,10 +285,9 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
 #pragma unroll
         for (int k = 0; k < G; k++) {
             const uint64_t i = i0 + (uint64_t)kWave * k;
-            bad |= bits_nonfinite<Fmt>(gb[k]);
             typename Fmt::T gh;
             memcpy(&gh, &gb[k], 2);
-            const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c);
+            const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c, bad);
             as_global(T.w)[i] = w[k];
             as_global(T.m)[i] = m[k];
             as_global(T.v)[i] = v[k];
@@ -566,7 +566,7 @@ __device__ __forceinline__ void fused_single(const SliceArgs &s, uint32_t nd, ui
     if (F.gout != nullptr)
         as_global(F.gout)[i] = gb;
     float w = as_global(F.w)[i], m = as_global(F.m)[i], v = as_global(F.v)[i];
-    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c);
+    const typename Fmt::T p = adam_elem<Fmt>((float)gh, w, m, v, c, bad);
     as_global(F.w)[i] = w;
     as_global(F.m)[i] = m;
     as_global(F.v)[i] = v;
@@ -635,7 +635,7 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
             memcpy(&gb, &gj, 2);
             bad |= bits_nonfinite<Fmt>(gb);
             float ww = w[k][j], mm = m[k][j], vv = v[k][j];
-            p[j] = adam_elem<Fmt>((float)gj, ww, mm, vv, c);
+            p[j] = adam_elem<Fmt>((float)gj, ww, mm, vv, c, bad);
             w[k][j] = ww;
             m[k][j] = mm;
             v[k][j] = vv;
@@ -773,7 +773,7 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
             memcpy(&gb, &gj, 2);
             bad |= bits_nonfinite<Fmt>(gb);
             float ww = w[k][q], mm = m[k][q], vv = v[k][q];
-            p[q] = adam_elem<Fmt>((float)gj, ww, mm, vv, c);
+            p[q] = adam_elem<Fmt>((float)gj, ww, mm, vv, c, bad);
             w[k][q] = ww;
             m[k][q] = mm;
             v[k][q] = vv;
@@ -824,7 +824,7 @@ __device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t n
         bad |= bits_nonfinite<Fmt>(gb);
         if (F.gout != nullptr)
             as_global(F.gout)[i] = gb;
-        const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c);
+        const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c, bad);
         as_global(F.w)[i] = w[k];
         as_global(F.m)[i] = m[k];
         as_global(F.v)[i] = v[k];
