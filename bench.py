@@ -12,7 +12,12 @@ single rank's shard).
 Prints one JSON line: params updated per second (value), the per-kernel
 HIP-event durations measured inside the timed region on the launch stream,
 the dominant kernel's roofline against MI355X's 8 TB/s HBM peak, and the CPU
-oracle timed on a bounded sample on this host.
+oracle timed on a bounded sample on this host.  The default run also times,
+in the same process and after the headline, the Adam step of the other
+7B-scale workloads and of GPT-2-XL (`per_config`: the N_d = 8 rank-3 shard
+with its infinities, the Llama-7B list, the GPT-2-XL list, each over its
+own resident state, freed before the next) and the N_d = 64 shard's Adam
+step with the fp16 parameter view at ranks 1 and 63 (`adam_by_rank`).
 """
 from __future__ import annotations
 
@@ -144,6 +149,13 @@ def parse():
                     help="keep stepping the CPU oracle over its sample until this much "
                          "wall time has passed (at most 8 steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload (no per_config, no adam_by_rank)")
+    ap.add_argument("--per-config-steps", type=int, default=0,
+                    help="timed Adam steps per extra workload (0: max(10, --steps))")
+    ap.add_argument("--param-rank", type=int, default=None,
+                    help="flat workloads: place the fp16 parameter view of the shard at this "
+                         "rank's offset in the full buffer (the other arrays unchanged)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the step: copy a BYTES-byte device buffer into another "
                          "with torch, --steps times (the plain copy kernel that scales the "
@@ -198,7 +210,7 @@ class Step:
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
-                 slices=False, inject_inf=False, loss_scale=None):
+                 slices=False, inject_inf=False, loss_scale=None, param_rank=None):
         import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
@@ -214,6 +226,14 @@ class Step:
             self.layout = lay
             self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total,
                                                 half=half)
+            if param_rank is not None:
+                # the same shard state, its fp16 parameter view at another
+                # rank's place in the full buffer (a view off its lines for
+                # most ranks when the shard length is not a multiple of 64)
+                off = param_rank * lay.shard_len
+                if not 0 <= param_rank < wl.nd or off + lay.real_len > lay.padded_total:
+                    raise SystemExit(f"--param-rank {param_rank}: outside the layout")
+                sh.p = self.full[off:off + lay.real_len]
             self.tensors = [sh]
             if wl.reduce_slices or slices:
                 self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half)
@@ -240,7 +260,6 @@ class Step:
             self.host = [x.cpu().numpy().copy() for x in (sh.w, sh.m, sh.v)]
             self.hflag = np.zeros(1, dtype=np.int32)
             self.offload = zs.zero_offload_create(offload_chunk, offload_threads)
-            self.offload_threads_used = offload_threads or min(16, os.cpu_count() or 1)
             self.fused = False
         self.loss_scale = None
         if loss_scale is not None and self.offload is None and not self.fused:
@@ -287,7 +306,11 @@ class Step:
 
     def kernels(self):
         if self.fused:
-            ks = [("zs_fused_kernel", self.reduce_adam, (2 * self.wl.nd + 26) * self.n_params)]
+            # the entry point: one fused kernel below zs.ZERO_FUSED_SPLIT_SLICES
+            # slices, the reduce and then the Adam kernel from there on; its
+            # algorithmic bytes are the fused minimum either way
+            ks = [("zero_reduce_adam_step", self.reduce_adam,
+                   (2 * self.wl.nd + 26) * self.n_params)]
         else:
             ks = []
             if self.rows is not None:
@@ -315,7 +338,7 @@ def cpu_baseline(step, sample_n: int, min_seconds: float):
     import torch
     import oracle
 
-    T = max(1, min(16, len(os.sched_getaffinity(0))))
+    T = host_cpus()["usable"]
     sh = step.tensors[0]
     n = min(sample_n, sh.n)
     hp = dict(step.W.ADAM_HP)
@@ -354,12 +377,63 @@ def cpu_baseline(step, sample_n: int, min_seconds: float):
     n1 = bounds[0][1] - bounds[0][0]
     what = ("reduce of %d fp16 slices + Adam step" % step.wl.nd) if sl is not None else "Adam step"
     per_param = 28 + ((2 * step.wl.nd + 2) if sl is not None else 0)
+    hc = host_cpus()
     return {"value": n * steps / dt, "unit": "params/s", "cores": T, "kind": "oracle",
+            "affinity_cpus": hc["affinity"], "cgroup_cpu_quota": hc["quota"],
             "gbps": per_param * n * steps / dt / 1e9, "alg_bytes_per_param": per_param,
             "single_thread_value": n1 / dt1, "cpu_model": cpu_model(),
             "sample": f"first {n} elements of the shard: {steps} x ({what}), {T} host threads, "
                       f"{dt:.2f} s wall; then one step over the first {n1} elements on one "
                       f"thread, {dt1:.2f} s"}
+
+
+def host_cpus() -> dict:
+    """CPUs this process may use: its affinity mask, capped by the cgroup's
+    CPU quota where one is set (cpu.max), which is the share a GPU machine gives
+    one GPU's jobs."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    usable = aff if quota is None else max(1, min(aff, int(quota)))
+    return {"affinity": aff, "quota": quota, "usable": usable}
+
+
+def host_rmw_bandwidth(threads: int, nbytes: int = 4 << 30, reps: int = 4) -> dict:
+    """Host memory bandwidth of an in-place read-modify-write stream (one
+    read and one write of every byte, as the offload update does to the fp32
+    master, m and v), on `threads` threads, each touching its own part of
+    the array first.  Host only: numpy releases the interpreter lock in its
+    loops, so the threads run in parallel."""
+    import concurrent.futures as cf
+    import numpy as np
+    n = nbytes // 4
+    a = np.empty(n, np.float32)
+    parts = [(n * i // threads, n * (i + 1) // threads) for i in range(threads)]
+    one = np.float32(1.0)
+
+    def touch(r):
+        a[r[0]:r[1]] = 1.0
+
+    def work(r):
+        x = a[r[0]:r[1]]
+        for _ in range(reps):
+            np.multiply(x, one, out=x)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(touch, parts))
+        list(ex.map(work, parts))                     # warm
+        t0 = time.perf_counter()
+        list(ex.map(work, parts))
+        dt = time.perf_counter() - t0
+    del a
+    return {"gbps": 2 * nbytes * reps / dt / 1e9, "threads": threads, "bytes": nbytes,
+            "pattern": "in-place multiply of fp32 (1 read + 1 write per byte), numpy, "
+                       "first touch in the threads"}
 
 
 def cpu_model() -> str:
@@ -410,12 +484,110 @@ def pcie_copy_rates(nbytes: int = 1 << 30, reps: int = 5) -> dict:
             "both_gbps": 2 * nbytes / t_both / 1e9, "bytes": nbytes}
 
 
+def time_steps(torch, stream, ks, steps):
+    """Run `steps` steps of the launches ks = [(name, launch, alg_bytes)],
+    each launch between two HIP events on `stream`; returns (wall seconds
+    between two synchronisations, per-kernel statistics)."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ks] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for (a, b), (_, launch, _) in zip(ev[k], ks):
+            a.record(stream)
+            launch()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kstats = {}
+    for j, (name, _, alg_bytes) in enumerate(ks):
+        ms = [ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(steps)]
+        avg_s = sum(ms) / len(ms) / 1e3
+        gbps = alg_bytes / avg_s / 1e9
+        kstats[name] = {"avg_us": avg_s * 1e6, "min_us": min(ms) * 1e3,
+                        "median_us": sorted(ms)[len(ms) // 2] * 1e3,
+                        "alg_bytes_per_launch": alg_bytes, "gbps": gbps,
+                        "frac": gbps / HBM_PEAK_GBPS, "total_s": sum(ms) / 1e3}
+    return wall, kstats
+
+
+def rounded(d: dict) -> dict:
+    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items() if k != "total_s"}
+
+
+def adam_by_rank(zs, torch, stream, step, ranks, steps):
+    """The flat shard's Adam step with its fp16 parameter view placed at
+    each rank's offset in the full buffer (gradient, master, m, v the same
+    arrays): where the shard length is not a multiple of 64 elements, most
+    ranks' views start off a 128-byte line."""
+    sh = step.tensors[0]
+    lay = step.layout
+    out = {}
+    for r in ranks:
+        off = r * lay.shard_len
+        view = step.full[off:off + sh.n]
+        plan = zs.zero_plan_create([(view, sh.g, sh.w, sh.m, sh.v)])
+
+        def adam():
+            step.t += 1
+            zs.zero_adam_step(plan, step.hp, step.t)
+
+        for _ in range(3):
+            adam()
+        _, ks = time_steps(torch, stream, [("zs_adam_kernel", adam, 28 * sh.n)], steps)
+        k = ks["zs_adam_kernel"]
+        out[str(r)] = {"byte_offset_in_line": (view.data_ptr() % 128), "avg_us": round(k["avg_us"], 3),
+                       "gbps": round(k["gbps"], 3), "frac": round(k["frac"], 4)}
+        plan.destroy()
+    return out
+
+
+def per_config_leg(zs, W, torch, stream, name, warmup, steps):
+    """The Adam step of one more workload over its own resident state: warm
+    steps with finite gradients, then (the N_d = 8 shard) the workload's
+    infinities injected, then `steps` timed Adam launches.  The state is
+    freed before returning."""
+    import gc
+    print(f"[bench] per_config: setting up {name}", file=sys.stderr, flush=True)
+    st = Step(zs, W, name)
+    ks = st.kernels()
+    for _ in range(warmup):
+        for _, launch, _ in ks:
+            launch()
+    n_inf = None
+    if st.wl.inf_frac and st.layout is not None:
+        pos, sign = W.inf_positions(st.layout.real_len, st.wl.inf_frac, st.wl.seed)
+        W.device_inject_inf(st.tensors[0].g, pos, sign)
+        n_inf = int(pos.size)
+    _, kstats = time_steps(torch, stream, ks, steps)
+    k = kstats["zs_adam_kernel"]
+    entry = {"workload": name, "params": st.n_params, "kernel": "zs_adam_kernel",
+             "steps": steps, "warmup": warmup, **rounded(k),
+             "params_per_s": st.n_params / (k["avg_us"] / 1e6),
+             "traffic": measured_traffic("zs_adam_kernel", name),
+             "chunk_elems": st.plan.stats()["chunk_elems"],
+             "adam_tile_elems": st.plan.stats()["tile_elems"],
+             "tensors": len(st.wl.tensors)}
+    if n_inf is not None:
+        torch.cuda.synchronize()
+        entry["injected_inf"] = n_inf
+        entry["flag"] = int(st.flag.item())
+    if len(st.wl.tensors) > 1:
+        entry["list_layout"] = "flat"
+    st.plan.destroy()
+    del st, ks
+    gc.collect()
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the shard step "
               "has no cross-GPU exchange to time here.", file=sys.stderr)
         sys.exit(2)
+    import gc
     import torch
     from zero_partitioned_mixed_layout_amd import workloads as W
     from zero_partitioned_mixed_layout_amd import zero_shard as zs
@@ -430,7 +602,7 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
                 args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
-                args.slices, args.inject_inf, args.loss_scale)
+                args.slices, args.inject_inf, args.loss_scale, args.param_rank)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -439,34 +611,32 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warm-up done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
           flush=True)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ks] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        for (a, b), (_, launch, _) in zip(ev[k], ks):
-            a.record(stream)
-            launch()
-            b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kstats = {}
-    for j, (name, _, alg_bytes) in enumerate(ks):
-        ms = [ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(args.steps)]
-        avg_s = sum(ms) / len(ms) / 1e3
-        gbps = alg_bytes / avg_s / 1e9
-        kstats[name] = {"avg_us": avg_s * 1e6, "min_us": min(ms) * 1e3,
-                        "median_us": sorted(ms)[len(ms) // 2] * 1e3,
-                        "alg_bytes_per_launch": alg_bytes, "gbps": gbps,
-                        "frac": gbps / HBM_PEAK_GBPS, "total_s": sum(ms) / 1e3}
+    wall, kstats = time_steps(torch, stream, ks, args.steps)
     dom = max(kstats, key=lambda k: kstats[k]["total_s"])
     d = kstats[dom]
-    traffic = measured_traffic(dom, args.workload)
+    traffic = (measured_traffic(dom, args.workload)
+               if args.param_rank is None and not args.bf16 else None)
     if traffic is None:
         print(f"[bench] no HBM counters for {dom} on {args.workload} taken on the current kernel "
               f"code ({kernel_src_sha()}): traffic is null", file=sys.stderr, flush=True)
     value = step.n_params * args.steps / wall
     bytes_per_step = sum(b for _, _, b in ks)
+    # the headline configuration's other extras, while its state is resident
+    headline_plain = (not args.no_per_config and args.workload == "flat_7p5b_nd64" and
+                      not (args.fused or args.gather or args.offload or args.bf16 or
+                           args.loss_scale is not None or args.param_rank is not None))
+    pc_steps = args.per_config_steps or max(10, args.steps)
+    by_rank = None
+    if headline_plain:
+        print("[bench] Adam step by rank of the parameter view", file=sys.stderr, flush=True)
+        by_rank = {"0": {"byte_offset_in_line": step.tensors[0].p.data_ptr() % 128,
+                         "avg_us": round(kstats["zs_adam_kernel"]["avg_us"], 3),
+                         "gbps": round(kstats["zs_adam_kernel"]["gbps"], 3),
+                         "frac": round(kstats["zs_adam_kernel"]["frac"], 4)}}
+        by_rank.update(adam_by_rank(zs, torch, stream, step, (1, step.wl.nd - 1), pc_steps))
+        slow = min(by_rank, key=lambda r: by_rank[r]["frac"])
+        by_rank = {"ranks": by_rank, "slowest_rank": int(slow),
+                   "slowest_frac": by_rank[slow]["frac"], "steps": pc_steps}
     copy = plain_copy(stream)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
@@ -476,7 +646,8 @@ def main():
            (f"+loss_scale_2^{args.loss_scale}" if step.loss_scale is not None else "") +
            ("+fused" if step.fused else "") +
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
-           ("+bf16" if args.bf16 else ""),
+           ("+bf16" if args.bf16 else "") +
+           (f"+param_rank_{args.param_rank}" if args.param_rank is not None else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
@@ -487,36 +658,85 @@ def main():
            "kernels_per_step": [k for k, _, _ in ks],
            "alg_bytes_per_step": bytes_per_step,
            "step_hbm_gbps": bytes_per_step * args.steps / wall / 1e9}
+    fused_vs = None
+    if step.fused:
+        cfg["fused_route"] = ("one fused kernel" if step.wl.nd < zs.ZERO_FUSED_SPLIT_SLICES
+                              else "reduce kernel, then Adam kernel")
+        # the two separate entry points over the same buffers in the same
+        # process, each step interleaved with the fused one: placement of
+        # the buffers in physical memory differs between processes by a few
+        # percent, so only a comparison within one process is meaningful
+        print("[bench] fused against reduce + Adam, interleaved", file=sys.stderr, flush=True)
+        both = [ks[0], ("zs_reduce_kernel", step.reduce, (2 * step.wl.nd + 2) * step.n_params),
+                ("zs_adam_kernel", step.adam, 28 * step.n_params)]
+        _, kb = time_steps(torch, stream, both, args.steps)
+        sep_us = kb["zs_reduce_kernel"]["avg_us"] + kb["zs_adam_kernel"]["avg_us"]
+        fused_vs = {"steps": args.steps, "fused_us": round(kb[ks[0][0]]["avg_us"], 3),
+                    "reduce_us": round(kb["zs_reduce_kernel"]["avg_us"], 3),
+                    "adam_us": round(kb["zs_adam_kernel"]["avg_us"], 3),
+                    "separate_us": round(sep_us, 3),
+                    "fused_over_separate": round(kb[ks[0][0]]["avg_us"] / sep_us, 4)}
     roofline = {"bound": "hbm", "kernel": dom, "achieved": d["gbps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
     offload = None
     if step.offload is not None:
         rates = pcie_copy_rates()
+        info = step.offload.info()
+        host_bw = host_rmw_bandwidth(info["threads"])
         o = kstats["zero_offload_step"]
-        offload = {"avg_ms": o["avg_us"] / 1e3, "params_per_s": step.n_params / (o["avg_us"] / 1e6),
+        t_s = o["avg_us"] / 1e6
+        # host memory bytes per parameter: the CPU reads the fp16 gradient
+        # (staging) and the fp32 master, m, v and writes them and the fp16
+        # parameter (staging): 28; the copy engines write the gradient into
+        # and read the parameter out of staging: 4
+        host_bytes = 32 * step.n_params
+        offload = {"avg_ms": t_s * 1e3, "params_per_s": step.n_params / t_s,
                    "pcie_bytes_per_param": 4, "pcie_gbps": o["gbps"],
-                   "host_state_gbps": 24 * step.n_params / (o["avg_us"] / 1e6) / 1e9,
-                   "threads": step.offload_threads_used,
-                   "chunk_elems": args.offload_chunk or 4 << 20, "pinned_copy": rates}
+                   "host_bytes_per_param": 32, "host_gbps": host_bytes / t_s / 1e9,
+                   "host_rmw_probe": host_bw, "pipeline": info,
+                   "pinned_copy": rates}
         if dom == "zero_offload_step":
-            roofline = {"bound": "pcie", "kernel": dom, "achieved": o["gbps"],
-                        "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
-                        "frac": o["gbps"] / PCIE_PEAK_GBPS, "traffic": None}
+            roofline = {"bound": "host-memory", "kernel": dom,
+                        "achieved": host_bytes / t_s / 1e9, "peak": host_bw["gbps"],
+                        "unit": "GB/s", "frac": host_bytes / t_s / 1e9 / host_bw["gbps"],
+                        "traffic": None,
+                        "peak_source": "host_rmw_probe (measured in this run)"}
+    headline_params = step.n_params
+    step.plan.destroy()
+    del step, ks
+    gc.collect()
+    torch.cuda.empty_cache()
+    per_config = None
+    if headline_plain:
+        per_config = {"flat_7p5b_nd64": {
+            "workload": "flat_7p5b_nd64", "params": headline_params, "kernel": "zs_adam_kernel",
+            "steps": args.steps, "warmup": args.warmup, **rounded(kstats["zs_adam_kernel"]),
+            "params_per_s": headline_params / (kstats["zs_adam_kernel"]["avg_us"] / 1e6),
+            "traffic": measured_traffic("zs_adam_kernel", "flat_7p5b_nd64"),
+            "note": "the headline run's Adam launches"}}
+        for name in ("flat_7p5b_nd8", "llama_7b", "gpt2_xl"):
+            wl = W.WORKLOADS[name]
+            per_config[name] = per_config_leg(zs, W, torch, stream, name,
+                                              max(args.warmup, wl.warm_steps), pc_steps)
     out = {
         "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": cfg,
         "roofline": roofline,
-        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
-                        for kk, vv in s.items() if kk != "total_s"} for k, s in kstats.items()},
+        "kernels": {k: rounded(v) for k, v in kstats.items()},
         "cpu_baseline": cpu,
         "plain_copy": copy,
     }
+    if fused_vs is not None:
+        out["fused_vs_separate"] = fused_vs
+    if by_rank is not None:
+        out["adam_by_rank"] = by_rank
+    if per_config is not None:
+        out["per_config"] = per_config
     if offload is not None:
         out["offload"] = offload
     print(json.dumps(out), flush=True)
-    step.plan.destroy()
 
 
 if __name__ == "__main__":

@@ -98,3 +98,27 @@ def check16(got: np.ndarray, ref: np.ndarray, what: str, fmt: str = "f16") -> di
     assert max_ulp <= ULP16_TOL, f"{what}: {max_ulp} fp16 ulps apart"
     not_exact = int(np.count_nonzero(got[fin] != ref[fin]))
     return dict(max_ulp=max_ulp, not_bit_exact=not_exact, n=int(got.size))
+
+
+def check_whole32(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    """check32 over whole arrays of any size: the elements whose bits differ
+    (NaN payloads among them) are found first and only those go through
+    the class and relative-error rules."""
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    assert got.shape == ref.shape, what
+    diff = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    r = check32(got[diff], ref[diff], what) if diff.size else dict(max_rel=0.0, not_bit_exact=0)
+    r.update(n=int(got.size), bits_differ=int(diff.size))
+    return r
+
+
+def check_whole16(got: np.ndarray, ref: np.ndarray, what: str, fmt: str = "f16") -> dict:
+    """check16 over whole arrays of any size, as check_whole32."""
+    got = np.asarray(got).view(np.uint16)
+    ref = np.asarray(ref).view(np.uint16)
+    assert got.shape == ref.shape, what
+    diff = np.flatnonzero(got != ref)
+    r = check16(got[diff], ref[diff], what, fmt) if diff.size else dict(max_ulp=0, not_bit_exact=0)
+    r.update(n=int(got.size), bits_differ=int(diff.size))
+    return r

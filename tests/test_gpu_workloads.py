@@ -1,19 +1,27 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (same entry points, same plans).  The oracle recomputes
-sampled elements one by one from the same seeded inputs -- the initial
-master and every step's gradients gathered at the sampled indices, never a
-value the HIP path produced -- through all warm-up steps; sampled indices
-include both ends of every tensor and, for the infinity workload, every
-injected position.  Properties that hold at any size (untouched padding and
-other ranks' parameters, the non-finite positions, the ZeRO-2 ledger) are
+benchmark times (same entry points, same plans).
+
+The flat shards (117,187,500 and 937,500,160 elements) are compared with
+the oracle element by element over their whole arrays: the oracle runs
+from the same seeded inputs -- the initial master, every slice and every
+step's gradients copied to the host before the GPU uses them, never a value
+the HIP path produced -- through all warm-up steps, threaded over windows
+of the arrays on the host's CPUs.  The tensor lists (GPT-2-XL, Llama-7B)
+are compared at sampled elements (both ends of every tensor and 96 random
+ones): their whole state and the oracle's copy of it with every step's
+gradients would pass the host memory a GPU job may use (about 280 GB for
+Llama-7B).  Properties that hold at any size (untouched padding and other
+ranks' parameters, the non-finite positions, the ZeRO-2 ledger) are
 checked on the whole arrays."""
+import concurrent.futures as cf
 import gc
+import os
 
 import numpy as np
 import pytest
 
 import oracle
-from parity import check16, check32, host16, host32
+from parity import check16, check32, check_whole16, check_whole32, host16, host32
 from zero_partitioned_mixed_layout_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -60,6 +68,44 @@ def _oracle_steps(w0, grads_by_step, t0=1):
     for k, g in enumerate(grads_by_step):
         flag |= oracle.adam_step(g, p, w, m, v, t=t0 + k, **HP)
     return p, w, m, v, flag
+
+
+def _threads():
+    """Host threads for the oracle: the CPUs this process may use, capped
+    by the cgroup's CPU quota (a GPU machine's share for one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            n = min(n, max(1, int(int(q) / int(per))))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
+def _windows(n, parts):
+    return [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
+
+
+def _on_windows(fn, n):
+    """fn(lo, hi) over 8 windows per host thread; the oracle's C calls
+    release the interpreter lock.  Returns the OR of the results."""
+    T = _threads()
+    with cf.ThreadPoolExecutor(T) as ex:
+        flags = list(ex.map(lambda b: fn(*b), _windows(n, 8 * T)))
+    return int(any(flags))
+
+
+def _check_whole(got, ref, what):
+    p, w, m, v = got
+    rp, rw, rm, rv = ref
+    res = [check_whole16(p, rp, f"{what} param"), check_whole32(w, rw, f"{what} master"),
+           check_whole32(m, rm, f"{what} m"), check_whole32(v, rv, f"{what} v")]
+    inexact = sum(r["not_bit_exact"] for r in res)
+    say(f"{what}: all {res[0]['n']} elements, max rel "
+        f"{max(r.get('max_rel', 0) for r in res):.2g}, not bit-exact {inexact}, "
+        f"bit patterns differing (NaN payloads included) {[r['bits_differ'] for r in res]}")
+    return inexact
 
 
 def _check_all(got, ref, what):
@@ -125,9 +171,10 @@ def test_flat_7p5b_nd64_reduce_then_step(zs, rank):
     64 fp16 gradient slices are averaged, then Adam runs at t = 1 with the
     reduce's flag as its skip input.  Odd ranks' fp16 parameter views start
     8 bytes off a 16-byte boundary (still the vector path, whose fp16
-    accesses are 8 bytes wide).  The whole other-rank
-    part of the fp16 parameter buffer stays untouched, and the allocated
-    ZeRO-2 state equals the ledger's 16,640,625,000 bytes."""
+    accesses are 8 bytes wide).  Every element of the reduced gradient,
+    param, master, m and v is compared with the oracle.  The whole
+    other-rank part of the fp16 parameter buffer stays untouched, and the
+    allocated ZeRO-2 state equals the ledger's 16,640,625,000 bytes."""
     import torch
     wl = W.WORKLOADS["flat_7p5b_nd64"]
     lay = zs.zero_shard_layout(wl.psi, wl.nd, rank, wl.align)
@@ -148,22 +195,30 @@ def test_flat_7p5b_nd64_reduce_then_step(zs, rank):
     plan = zs.zero_plan_create([sh.arrays()])
     st = plan.stats()
     assert st["vector_elems"] >= n - 3
-    idx = W.sample_indices(n, 200_000, seed=wl.seed + rank)
-    d = torch.from_numpy(idx).cuda()
-    w0 = _gather32(sh.w, d)
-    slices = [_gather16(r, d) for r in rows]
+    # the oracle's inputs, copied before the GPU step
+    w0 = host32(sh.w)
+    slices = [host16(r) for r in rows]
     rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
     aflag = torch.zeros(1, dtype=torch.int32, device="cuda")
     zs.zero_reduce_grad_shard(rows, sh.g, rflag)
     zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, aflag, rflag)
     torch.cuda.synchronize()
-    g_ref, f_ref = oracle.reduce_grad(slices)
-    r = check16(_gather16(sh.g, d), g_ref, "reduced gradient")
-    assert r["not_bit_exact"] == 0 and int(rflag.item()) == f_ref == 0
-    rp, rw, rm, rv, fl = _oracle_steps(w0, [g_ref])
-    got = [_gather16(sh.p, d), _gather32(sh.w, d), _gather32(sh.m, d), _gather32(sh.v, d)]
-    assert _check_all(got, (rp, rw, rm, rv), f"nd64 rank {rank}") == 0
-    assert int(aflag.item()) == 0
+    got_g = host16(sh.g)
+    got = [host16(sh.p), host32(sh.w), host32(sh.m), host32(sh.v)]
+    say(f"flat_7p5b_nd64 rank={rank}: oracle over the whole shard on {_threads()} threads")
+    g_ref = np.empty(n, np.uint16)
+    rp, rw = np.zeros(n, np.uint16), w0
+    rm, rv = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    fr = _on_windows(lambda lo, hi: oracle.reduce_grad([x[lo:hi] for x in slices],
+                                                       g_ref[lo:hi])[1], n)
+    fa = _on_windows(lambda lo, hi: oracle.adam_step(g_ref[lo:hi], rp[lo:hi], rw[lo:hi],
+                                                     rm[lo:hi], rv[lo:hi], t=1, **HP), n)
+    del slices
+    r = check_whole16(got_g, g_ref, "reduced gradient")
+    say(f"reduced gradient: all {n} elements, not bit-exact {r['not_bit_exact']}")
+    assert r["not_bit_exact"] == 0 and int(rflag.item()) == fr == 0
+    assert _check_whole(got, (rp, rw, rm, rv), f"nd64 rank {rank}") == 0
+    assert int(aflag.item()) == fa == 0
     before = int(torch.count_nonzero(full[:lay.offset]).item())
     after = int(torch.count_nonzero(full[lay.offset + n:]).item())
     assert before == after == 0
@@ -174,7 +229,9 @@ def test_flat_7p5b_nd8_rank3_with_infinities(zs):
     """Psi = 7.5e9 over 8 ranks in 512-element units: rank 3's 937,500,160
     elements at 2,812,500,480.  Five warm-up steps with finite gradients,
     then step 6 with 93,750 (0.01%) gradients set to +-inf: the flag is 1,
-    and master, m, v and fp16 param are non-finite exactly there."""
+    and master, m, v and fp16 param are non-finite exactly there.  Every
+    element of param, master, m and v after step 6 is compared with the
+    oracle run through all six steps."""
     import torch
     wl = W.WORKLOADS["flat_7p5b_nd8"]
     lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
@@ -186,9 +243,7 @@ def test_flat_7p5b_nd8_rank3_with_infinities(zs):
     plan = zs.zero_plan_create([sh.arrays()])
     pos, sign = W.inf_positions(n, wl.inf_frac, wl.seed)
     assert pos.size == 93_750
-    idx = W.sample_indices(n, 200_000, seed=wl.seed, must=pos)
-    d = torch.from_numpy(idx).cuda()
-    w0 = _gather32(sh.w, d)
+    w0 = host32(sh.w)
     grads = []
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     hp = zs.AdamHParams(**HP)
@@ -199,15 +254,22 @@ def test_flat_7p5b_nd8_rank3_with_infinities(zs):
             W.device_inject_inf(sh.g, pos, sign)
             torch.cuda.synchronize()
             assert int(flag.item()) == 0          # warm-up steps were finite
-        grads.append(_gather16(sh.g, d))
+        grads.append(host16(sh.g))
         say(f"flat_7p5b_nd8: step t={t}")
         zs.zero_adam_step(plan, hp, t, flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 1
-    rp, rw, rm, rv, rflag = _oracle_steps(w0, grads)
-    assert rflag == 1
-    got = [_gather16(sh.p, d), _gather32(sh.w, d), _gather32(sh.m, d), _gather32(sh.v, d)]
-    assert _check_all(got, (rp, rw, rm, rv), "nd8 rank 3") == 0
+    got = [host16(sh.p), host32(sh.w), host32(sh.m), host32(sh.v)]
+    rp, rw = np.zeros(n, np.uint16), w0
+    rm, rv = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rflag = 0
+    for t, g in enumerate(grads, start=1):
+        say(f"flat_7p5b_nd8: oracle step t={t} over the whole shard on {_threads()} threads")
+        rflag |= _on_windows(lambda lo, hi: oracle.adam_step(g[lo:hi], rp[lo:hi], rw[lo:hi],
+                                                             rm[lo:hi], rv[lo:hi], t=t, **HP), n)
+        assert rflag == (1 if t == T else 0)
+    del grads
+    assert _check_whole(got, (rp, rw, rm, rv), "nd8 rank 3") == 0
     # whole arrays: non-finite exactly at the injected positions
     pos_dev = torch.from_numpy(pos).cuda()
     for a in (sh.w, sh.p):

@@ -125,7 +125,7 @@ inline bool fused_state_late(uint32_t nd) { return slices_in_flight(nd) < 16; }
 // is 6.9% faster at N_d = 8, 6.1% at 12, 4.2% at 16 and 3.6% at 24, and
 // 1.9% slower at 32, 6.9% at 48 and 9.8% at 64 (its mix of state writes
 // into the slice reads costs more than the 4 bytes per element it saves).
-constexpr uint32_t kFusedSplitSlices = 32;
+constexpr uint32_t kFusedSplitSlices = ZERO_FUSED_SPLIT_SLICES;
 
 // Resident one-wave workgroups per CU for the fused reduce + Adam step.
 // State first: about 70 16-byte vectors per lane in flight per CU, counting

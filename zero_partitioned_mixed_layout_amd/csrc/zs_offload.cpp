@@ -19,7 +19,10 @@
 #include <hip/hip_runtime.h>
 #include <immintrin.h>
 #include <math.h>
+#include <pthread.h>
+#include <sched.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
@@ -173,10 +176,19 @@ constexpr uint32_t kMaxHostThreads = 1024;
 // exception leaves the constructor.
 class Pool {
 public:
-    explicit Pool(uint32_t parts) : parts_(parts) {
+    // cpus: NULL, or the CPUs every worker thread (not the caller's) is
+    // pinned to when it starts.
+    explicit Pool(uint32_t parts, const cpu_set_t *cpus = nullptr) : parts_(parts) {
+        if (cpus)
+            cpus_ = *cpus;
+        const bool pin = cpus != nullptr;
         try {
             for (uint32_t k = 1; k < parts; k++)
-                threads_.emplace_back([this, k] { work(k); });
+                threads_.emplace_back([this, k, pin] {
+                    if (pin)
+                        (void)pthread_setaffinity_np(pthread_self(), sizeof(cpus_), &cpus_);
+                    work(k);
+                });
         } catch (...) {
             shutdown();
             throw;
@@ -227,6 +239,7 @@ private:
         }
     }
     uint32_t parts_;
+    cpu_set_t cpus_;
     std::vector<std::thread> threads_;
     std::mutex mu_;
     std::condition_variable cv_, done_;
@@ -257,9 +270,77 @@ int adam_parallel(Pool &pool, const uint16_t *g16, uint16_t *p16, float *w, floa
     return any;
 }
 
-uint32_t default_threads() {
+// The CPUs this process may run on.
+uint32_t affinity_count() {
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0 && CPU_COUNT(&set) > 0)
+        return (uint32_t)CPU_COUNT(&set);
     const unsigned hw = std::thread::hardware_concurrency();
-    return hw == 0 ? 1u : std::min(16u, hw);
+    return hw == 0 ? 1u : hw;
+}
+
+// Host threads of an update when the caller leaves it to the library: the
+// CPUs available (`cpus`, or the process's), at most 16.  The host update
+// is bound by host memory bandwidth, which 16 threads already drive (the
+// measurements behind this are in the build's design notes).
+uint32_t default_threads(uint32_t cpus = 0) {
+    return std::min(16u, cpus ? cpus : affinity_count());
+}
+
+// The NUMA node of device `dev` as the host's sysfs reports it (-1 if
+// unknown), and in *set the CPUs of that node this process may run on.
+// Returns how many there are (0: no placement to make).
+uint32_t gpu_node_cpus(int dev, int *node, cpu_set_t *set) {
+    *node = -1;
+    CPU_ZERO(set);
+    char bus[64] = {0};
+    if (hipDeviceGetPCIBusId(bus, (int)sizeof(bus) - 1, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    for (char *c = bus; *c; c++)
+        if (*c >= 'A' && *c <= 'F')
+            *c = (char)(*c - 'A' + 'a');
+    char path[256];
+    snprintf(path, sizeof(path), "/sys/bus/pci/devices/%s/numa_node", bus);
+    FILE *f = fopen(path, "r");
+    if (!f)
+        return 0;
+    const int got = fscanf(f, "%d", node);
+    fclose(f);
+    if (got != 1 || *node < 0) {
+        *node = -1;
+        return 0;
+    }
+    snprintf(path, sizeof(path), "/sys/devices/system/node/node%d/cpulist", *node);
+    f = fopen(path, "r");
+    if (!f)
+        return 0;
+    // "a-b,c,d-e": ranges of CPU numbers
+    cpu_set_t node_cpus;
+    CPU_ZERO(&node_cpus);
+    int lo, hi;
+    char sep;
+    while (fscanf(f, "%d", &lo) == 1) {
+        hi = lo;
+        sep = (char)fgetc(f);
+        if (sep == '-') {
+            if (fscanf(f, "%d", &hi) != 1)
+                break;
+            sep = (char)fgetc(f);
+        }
+        for (int c = lo; c <= hi && c < CPU_SETSIZE; c++)
+            if (c >= 0)
+                CPU_SET(c, &node_cpus);
+        if (sep != ',')
+            break;
+    }
+    fclose(f);
+    cpu_set_t mine;
+    if (sched_getaffinity(0, sizeof(mine), &mine) != 0)
+        return 0;
+    CPU_AND(set, &node_cpus, &mine);
+    return (uint32_t)CPU_COUNT(set);
 }
 
 // Host arrays: non-null when n > 0, aligned to their element size, the
@@ -340,6 +421,7 @@ struct zero_offload {
     int device = 0;
     uint64_t chunk = 0;
     Pool *pool = nullptr;
+    zero_offload_info info = {};
     hipStream_t d2h = nullptr, h2d = nullptr;
     hipEvent_t ready = nullptr;
     hipEvent_t d2h_done[kSlots] = {};
@@ -393,12 +475,22 @@ extern "C" int zero_offload_create(uint64_t chunk_elems, uint32_t threads, zero_
         offload_free(o);
         return ZERO_EHIP;
     }
+    // the update's threads go to the GPU's NUMA node when the host says
+    // which it is (the caller first-touches the fp32 state there)
+    int node = -1;
+    cpu_set_t node_cpus;
+    const uint32_t n_node = gpu_node_cpus(o->device, &node, &node_cpus);
+    const uint32_t nthreads = threads ? threads : default_threads(n_node);
     try {
-        o->pool = new Pool(threads ? threads : default_threads());
+        o->pool = new Pool(nthreads, n_node ? &node_cpus : nullptr);
     } catch (...) {
         offload_free(o);
         return ZERO_ENOMEM;
     }
+    o->info.threads = nthreads;
+    o->info.numa_node = node;
+    o->info.pinned_cpus = n_node;
+    o->info.chunk_elems = chunk_elems;
     bool ok = hipStreamCreateWithFlags(&o->d2h, hipStreamNonBlocking) == hipSuccess &&
               hipStreamCreateWithFlags(&o->h2d, hipStreamNonBlocking) == hipSuccess &&
               hipEventCreateWithFlags(&o->ready, hipEventDisableTiming) == hipSuccess;
@@ -419,6 +511,13 @@ extern "C" int zero_offload_create(uint64_t chunk_elems, uint32_t threads, zero_
         }
     }
     *out = o;
+    return ZERO_OK;
+}
+
+extern "C" int zero_offload_describe(const zero_offload *o, zero_offload_info *out) {
+    if (!o || !out)
+        return ZERO_EINVAL;
+    *out = o->info;
     return ZERO_OK;
 }
 

@@ -31,6 +31,7 @@ ZERO_ERANGE = -6
 ZERO_NOALLOC_SCRATCH_BYTES = 8 << 20
 ZERO_NOALLOC_MAX_TENSORS = 1024
 ZERO_MAX_SLICES = 256
+ZERO_FUSED_SPLIT_SLICES = 32
 ZERO_LOG2_SCALE_MAX = 100
 
 
@@ -60,6 +61,12 @@ class _HParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double)]
+
+
+class _OffloadInfo(ctypes.Structure):
+    _fields_ = [("threads", ctypes.c_uint32), ("numa_node", ctypes.c_int32),
+                ("pinned_cpus", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("chunk_elems", ctypes.c_uint64)]
 
 
 class _Stats(ctypes.Structure):
@@ -102,6 +109,7 @@ def _load() -> ctypes.CDLL:
                                      vp],
         "zero_offload_create": [u64, u32, ctypes.POINTER(vp)],
         "zero_offload_destroy": [vp],
+        "zero_offload_describe": [vp, ctypes.POINTER(_OffloadInfo)],
         "zero_offload_step": [vp, vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, vp, vp],
         "zero_offload_step_bf16": [vp, vp, vp, vp, vp, vp, u64, ctypes.POINTER(_HParams), u64, vp,
                                    vp],
@@ -125,7 +133,7 @@ EXPORTS = ("zero_shard_layout", "zero_state_bytes", "zero_comm_volume",
            "zero_adam_scalars", "zero_adam_step", "zero_reduce_grad_shard",
            "zero_reduce_adam_step", "zero_reduce_adam_step_bf16", "zero_adam_step_host",
            "zero_adam_step_host_bf16", "zero_offload_create", "zero_offload_step_bf16",
-           "zero_offload_destroy", "zero_offload_step", "zero_status_str",
+           "zero_offload_destroy", "zero_offload_describe", "zero_offload_step", "zero_status_str",
            "zero_adam_step_scaled", "zero_loss_scale_update", "zero_adam_step_noalloc")
 
 
@@ -533,6 +541,13 @@ class Offload:
         name = "zero_offload_step_bf16" if half == torch.bfloat16 else "zero_offload_step"
         _check(name, getattr(_lib, name)(self.handle, grad.data_ptr(), param.data_ptr(), *hs, n,
                                          ctypes.byref(h), int(t), f, _stream_handle(stream)))
+
+    def info(self) -> dict:
+        """threads, numa_node (-1: unknown), pinned_cpus (0: not pinned),
+        chunk_elems."""
+        i = _OffloadInfo()
+        _check("zero_offload_describe", _lib.zero_offload_describe(self.handle, ctypes.byref(i)))
+        return {k: getattr(i, k) for k, _ in _OffloadInfo._fields_ if k != "reserved"}
 
     def destroy(self) -> None:
         if self._h:
