@@ -44,6 +44,10 @@ LAYOUTS = {
     "mixed": ((4, 4), 0, 4, 0, 0, 0),     # 16-byte slice loads after a head of 4
     "split": ((0, 4), 0, 0, 0, 0, 0),     # slices agree only mod 8 bytes: 8-byte loads
     "odd": ((1, 1), 0, 0, 0, 0, 0),       # no common phase: single elements
+    # parameter and gradient output one element off the state: single
+    # elements in the fused kernel; from ZERO_FUSED_SPLIT_SLICES slices a
+    # single-element reduce and the one-tensor Adam kernel's single path
+    "param_off": ((0, 0), 1, 1, 0, 0, 0),
 }
 
 
@@ -83,7 +87,7 @@ def _run_case(zs, torch, n, nd, layout, with_gout, t, rng, warm=True):
     return sum(r["not_bit_exact"] for r in res)
 
 
-@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 15, 16, 17, 64, 256])
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 64, 256])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 def test_fused_matches_oracle(zs, nd, layout):
     """Sizes from 1 to 70,001 (partial tiles, heads and tails), each access

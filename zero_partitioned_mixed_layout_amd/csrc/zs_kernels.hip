@@ -336,26 +336,27 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
 // chunk of one tile (tile 0 also holds the peeled head), so the per-tile
 // code, and the results, are those of zs_adam_kernel.  Used where no table
 // exists: the second half of zero_reduce_adam_step at many slices.
+// The host gives the element counts of the first and the last tile; the
+// kernel picks a tile's count with equality tests only.  (A count taken as
+// min(n - start, TILE) on the device was miscompiled by this toolchain for
+// the single-element path: a VALU 64-bit compare feeding a scalar select
+// that read a stale SCC, so every partial tile ran as a full one.)
 template <class Fmt, uint32_t TILE>
 __global__ __launch_bounds__(kWave) void zs_adam_flat_kernel(TensorDesc T, uint64_t ntiles,
-                                                             AdamConsts c,
+                                                             uint32_t first_count,
+                                                             uint32_t last_count, AdamConsts c,
                                                              int32_t *__restrict__ flag) {
     int bad = 0;
-    const uint64_t h = T.head < T.n ? T.head : T.n;
+    const uint64_t h = T.vec == 4 && T.head < T.n ? T.head : 0;
     for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
         Chunk ch;
         ch.tensor = 0;
-        if (T.vec == 4) {
-            const uint64_t start = b == 0 ? 0 : h + b * TILE;
-            const uint64_t want = b == 0 ? h + TILE : TILE;
-            ch.start = start;
-            ch.count = (uint32_t)(T.n - start < want ? T.n - start : want);
+        ch.start = b == 0 ? 0 : h + b * TILE;
+        ch.count = b == ntiles - 1 ? last_count : (b == 0 ? first_count : TILE);
+        if (T.vec == 4)
             adam_tile_of_chunk<Fmt, TILE>(T, ch, 0, c, bad);
-        } else {
-            ch.start = b * TILE;
-            ch.count = (uint32_t)(T.n - ch.start < TILE ? T.n - ch.start : TILE);
+        else
             adam_tile_single<Fmt, TILE>(T, ch, 0, c, bad);
-        }
     }
     raise_flag(flag, bad);
 }
@@ -1305,17 +1306,20 @@ int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *
     const uintptr_t a32[3] = {(uintptr_t)w, (uintptr_t)m, (uintptr_t)v};
     zs::pick_vector_path(a16, 2, a32, 3, 4, &T.vec, &T.head);
     const uint32_t tile = T.vec == 4 ? kAdamTileFine : kTile;
-    const uint64_t h = T.head < n ? T.head : n;
-    const uint64_t ntiles = T.vec == 4 ? (n == h ? 1 : (n - h + tile - 1) / tile)
-                                       : (n + tile - 1) / tile;
+    // tiles: the first holds the peeled head (vector path) and up to `tile`
+    // elements, every later one `tile` elements, the last what is left
+    const uint64_t h = T.vec == 4 && T.head < n ? T.head : 0;
+    const uint64_t ntiles = n == h ? 1 : (n - h + tile - 1) / tile;
+    const uint64_t first = n < h + tile ? n : h + tile;
+    const uint64_t last = ntiles == 1 ? first : n - h - (ntiles - 1) * tile;
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
     const size_t lds = lds_cap_bytes(dev, zs::adam_per_cu(tile));
     if (tile == kAdamTileFine)
         hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
-                           st, T, ntiles, c, nullptr);
+                           st, T, ntiles, (uint32_t)first, (uint32_t)last, c, nullptr);
     else
         hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kTile>), dim3(grid), dim3(kWave), lds, st, T,
-                           ntiles, c, nullptr);
+                           ntiles, (uint32_t)first, (uint32_t)last, c, nullptr);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
