@@ -515,18 +515,21 @@ def rounded(d: dict) -> dict:
     return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items() if k != "total_s"}
 
 
-def adam_by_rank(zs, torch, stream, step, ranks, steps):
+def adam_by_rank(zs, torch, stream, step, ranks, steps, align=None):
     """The flat shard's Adam step with its fp16 parameter view placed at
     each rank's offset in the full buffer (gradient, master, m, v the same
     arrays): where the shard length is not a multiple of 64 elements, most
-    ranks' views start off a 128-byte line."""
+    ranks' views start off a 128-byte line.  align: the layout's unit
+    (default the workload's); a rank whose shard is shorter than this one's
+    under it updates the first elements only."""
     sh = step.tensors[0]
-    lay = step.layout
+    wl = step.wl
+    lays = {r: zs.zero_shard_layout(wl.psi, wl.nd, r, align or wl.align) for r in ranks}
     out = {}
     for r in ranks:
-        off = r * lay.shard_len
-        view = step.full[off:off + sh.n]
-        plan = zs.zero_plan_create([(view, sh.g, sh.w, sh.m, sh.v)])
+        off, n = lays[r].offset, min(sh.n, lays[r].real_len)
+        view = step.full[off:off + n]
+        plan = zs.zero_plan_create([(view, sh.g[:n], sh.w[:n], sh.m[:n], sh.v[:n])])
 
         def adam():
             step.t += 1
@@ -534,10 +537,11 @@ def adam_by_rank(zs, torch, stream, step, ranks, steps):
 
         for _ in range(3):
             adam()
-        _, ks = time_steps(torch, stream, [("zs_adam_kernel", adam, 28 * sh.n)], steps)
+        _, ks = time_steps(torch, stream, [("zs_adam_kernel", adam, 28 * n)], steps)
         k = ks["zs_adam_kernel"]
-        out[str(r)] = {"byte_offset_in_line": (view.data_ptr() % 128), "avg_us": round(k["avg_us"], 3),
-                       "gbps": round(k["gbps"], 3), "frac": round(k["frac"], 4)}
+        out[str(r)] = {"byte_offset_in_line": (view.data_ptr() % 128), "params": n,
+                       "avg_us": round(k["avg_us"], 3), "gbps": round(k["gbps"], 3),
+                       "frac": round(k["frac"], 4)}
         plan.destroy()
     return out
 
@@ -635,8 +639,13 @@ def main():
                          "frac": round(kstats["zs_adam_kernel"]["frac"], 4)}}
         by_rank.update(adam_by_rank(zs, torch, stream, step, (1, step.wl.nd - 1), pc_steps))
         slow = min(by_rank, key=lambda r: by_rank[r]["frac"])
+        # the same ranks under a layout whose unit is 64 elements: every
+        # rank's view on a 128-byte line (the workload itself has unit 1)
+        a64 = adam_by_rank(zs, torch, stream, step, (1, step.wl.nd - 1), pc_steps, align=64)
         by_rank = {"ranks": by_rank, "slowest_rank": int(slow),
-                   "slowest_frac": by_rank[slow]["frac"], "steps": pc_steps}
+                   "slowest_frac": by_rank[slow]["frac"], "steps": pc_steps,
+                   "layout_align_64": {"ranks": a64, "slowest_frac":
+                                       min(v["frac"] for v in a64.values())}}
     copy = plain_copy(stream)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))
@@ -685,22 +694,26 @@ def main():
         host_bw = host_rmw_bandwidth(info["threads"])
         o = kstats["zero_offload_step"]
         t_s = o["avg_us"] / 1e6
-        # host memory bytes per parameter: the CPU reads the fp16 gradient
-        # (staging) and the fp32 master, m, v and writes them and the fp16
-        # parameter (staging): 28; the copy engines write the gradient into
-        # and read the parameter out of staging: 4
-        host_bytes = 32 * step.n_params
+        # host memory bytes per parameter the algorithm moves: the fp32
+        # master, m and v read and written back (24).  The fp16 staging adds
+        # up to 8 more (the CPU reads the gradient and writes the parameter,
+        # the copy engines write and read them), some of it served from the
+        # host's caches, so it is reported beside the roofline, not in it
+        alg_bytes = 24 * step.n_params
         offload = {"avg_ms": t_s * 1e3, "params_per_s": step.n_params / t_s,
                    "pcie_bytes_per_param": 4, "pcie_gbps": o["gbps"],
-                   "host_bytes_per_param": 32, "host_gbps": host_bytes / t_s / 1e9,
+                   "host_state_bytes_per_param": 24,
+                   "host_state_gbps": alg_bytes / t_s / 1e9,
+                   "host_gbps_with_staging": 32 * step.n_params / t_s / 1e9,
                    "host_rmw_probe": host_bw, "pipeline": info,
                    "pinned_copy": rates}
         if dom == "zero_offload_step":
             roofline = {"bound": "host-memory", "kernel": dom,
-                        "achieved": host_bytes / t_s / 1e9, "peak": host_bw["gbps"],
-                        "unit": "GB/s", "frac": host_bytes / t_s / 1e9 / host_bw["gbps"],
+                        "achieved": alg_bytes / t_s / 1e9, "peak": host_bw["gbps"],
+                        "unit": "GB/s", "frac": alg_bytes / t_s / 1e9 / host_bw["gbps"],
                         "traffic": None,
-                        "peak_source": "host_rmw_probe (measured in this run)"}
+                        "peak_source": "host_rmw_probe, measured in this run (the host's memory "
+                                       "bandwidth varies between runs on a shared host)"}
     headline_params = step.n_params
     step.plan.destroy()
     del step, ks
