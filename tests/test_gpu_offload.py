@@ -166,3 +166,29 @@ def test_offload_bf16_matches_oracle(zs, chunk, threads):
         assert sum(r["not_bit_exact"] for r in res) == 0
         assert int(flag[0]) == rflag == (1 if n > 100 else 0)
     off.destroy()
+
+
+def test_offload_describe(zs):
+    """zero_offload_describe: the thread count asked for (or the default,
+    at most 16 and at most the CPUs available), the chunk, and a NUMA
+    placement consistent with the host's sysfs: pinned CPUs only where the
+    GPU's node is known, never more than the process may use."""
+    import os
+    say("offload describe")
+    cpus = len(os.sched_getaffinity(0))
+    off = zs.zero_offload_create(2048, 3)
+    i = off.info()
+    assert i["threads"] == 3 and i["chunk_elems"] == 2048
+    assert i["numa_node"] >= -1
+    assert 0 <= i["pinned_cpus"] <= cpus
+    if i["numa_node"] == -1:
+        assert i["pinned_cpus"] == 0
+    off.destroy()
+    off = zs.zero_offload_create()
+    d = off.info()
+    assert d["chunk_elems"] == 4 << 20
+    assert 1 <= d["threads"] <= min(16, cpus)
+    assert d["numa_node"] == i["numa_node"]
+    off.destroy()
+    with pytest.raises(ValueError):
+        off.info()
