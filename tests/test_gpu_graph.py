@@ -165,3 +165,73 @@ def test_captured_loss_scaled_step_follows_the_scale(zs):
         del scratch
     assert st[2] == 2 and st[3] == 4
     plan.destroy()
+
+
+def test_captured_noalloc_step_rebuilds_its_table(zs):
+    """zero_adam_step_noalloc captured with the reduce: the capture holds the
+    launches that write the chunk table into the library's fixed array, so
+    every replay rebuilds its own table.  Between replays an eager
+    allocation-free step over other tensors overwrites that array; the next
+    replay still matches the oracle.  Three tensors (views of one buffer
+    each: ragged sizes, the third one's parameter one element off)."""
+    import torch
+    sizes, nd, t = (70_001, 513, 4099), 4, 2
+    n = sum(sizes) + 8
+    say(f"graph capture, allocation-free step, tensors {sizes}, nd={nd}")
+    rng = np.random.default_rng(14)
+    hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
+    slices = [to_dev16(h) for h in hs]
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = torch.empty(n, dtype=torch.float16, device="cuda")
+    p = torch.zeros(n + 1, dtype=torch.float16, device="cuda")
+    w, m, v = to_dev32(w0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    views, off = [], 0
+    for k, s in enumerate(sizes):
+        po = off + (1 if k == 2 else 0)
+        views.append((p[po:po + s], g[off:off + s], w[off:off + s], m[off:off + s], v[off:off + s]))
+        off += s + 2
+    # another state whose eager steps overwrite the table between replays
+    o = [torch.zeros(5000, dtype=torch.float16, device="cuda"), to_dev16(hs[0][:5000]),
+         torch.ones(5000, device="cuda"), torch.zeros(5000, device="cuda"),
+         torch.zeros(5000, device="cuda")]
+    hp = zs.AdamHParams(**HP)
+
+    def step():
+        zs.zero_reduce_grad_shard(slices, g)
+        zs.zero_adam_step_noalloc(views, hp, t)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    w.copy_(to_dev32(w0))
+    m.zero_()
+    v.zero_()
+    p.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    assert np.array_equal(host32(w).view(np.uint32), w0.view(np.uint32))
+    g_ref, _ = oracle.reduce_grad(hs)
+    P, Wr = np.zeros(n + 1, np.uint16), w0.copy()
+    M, V = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for k in range(4):
+        say(f"graph replay {k}")
+        graph.replay()
+        torch.cuda.synchronize()
+        off = 0
+        for j, s in enumerate(sizes):
+            po = off + (1 if j == 2 else 0)
+            oracle.adam_step(g_ref[off:off + s], P[po:po + s], Wr[off:off + s], M[off:off + s],
+                             V[off:off + s], t=t, **HP)
+            off += s + 2
+        res = [check16(host16(p), P, "replay param"), check32(host32(w), Wr, "replay master"),
+               check32(host32(m), M, "replay m"), check32(host32(v), V, "replay v")]
+        assert sum(r["not_bit_exact"] for r in res) == 0, k
+        # an eager allocation-free step over other tensors rewrites the table
+        zs.zero_adam_step_noalloc([tuple(o)], hp, k + 1)
+        torch.cuda.synchronize()
