@@ -11,6 +11,9 @@ bit-exact: both sides do the same IEEE operations in the same order).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 REL_TOL = 1e-6
@@ -122,3 +125,27 @@ def check_whole16(got: np.ndarray, ref: np.ndarray, what: str, fmt: str = "f16")
     r = check16(got[diff], ref[diff], what, fmt) if diff.size else dict(max_ulp=0, not_bit_exact=0)
     r.update(n=int(got.size), bits_differ=int(diff.size))
     return r
+
+
+def host_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may use, capped
+    by the cgroup's CPU quota (a GPU machine's share for one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            n = min(n, max(1, int(int(q) / int(per))))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
+def on_windows(fn, n: int) -> int:
+    """fn(lo, hi) over 8 windows of [0, n) per host thread; the oracle's C
+    calls release the interpreter lock.  Returns the OR of the results."""
+    T = host_threads()
+    parts = 8 * T
+    wins = [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
+    with cf.ThreadPoolExecutor(T) as ex:
+        flags = list(ex.map(lambda b: fn(*b), wins))
+    return int(any(flags))

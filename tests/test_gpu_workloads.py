@@ -13,15 +13,14 @@ gradients would pass the host memory a GPU job may use (about 280 GB for
 Llama-7B).  Properties that hold at any size (untouched padding and other
 ranks' parameters, the non-finite positions, the ZeRO-2 ledger) are
 checked on the whole arrays."""
-import concurrent.futures as cf
 import gc
-import os
 
 import numpy as np
 import pytest
 
 import oracle
-from parity import check16, check32, check_whole16, check_whole32, host16, host32
+from parity import (check16, check32, check_whole16, check_whole32, host16, host32,
+                    host_threads, on_windows)
 from zero_partitioned_mixed_layout_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -68,32 +67,6 @@ def _oracle_steps(w0, grads_by_step, t0=1):
     for k, g in enumerate(grads_by_step):
         flag |= oracle.adam_step(g, p, w, m, v, t=t0 + k, **HP)
     return p, w, m, v, flag
-
-
-def _threads():
-    """Host threads for the oracle: the CPUs this process may use, capped
-    by the cgroup's CPU quota (a GPU machine's share for one GPU)."""
-    n = len(os.sched_getaffinity(0))
-    try:
-        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
-        if q != "max":
-            n = min(n, max(1, int(int(q) / int(per))))
-    except (OSError, ValueError):
-        pass
-    return max(1, n)
-
-
-def _windows(n, parts):
-    return [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
-
-
-def _on_windows(fn, n):
-    """fn(lo, hi) over 8 windows per host thread; the oracle's C calls
-    release the interpreter lock.  Returns the OR of the results."""
-    T = _threads()
-    with cf.ThreadPoolExecutor(T) as ex:
-        flags = list(ex.map(lambda b: fn(*b), _windows(n, 8 * T)))
-    return int(any(flags))
 
 
 def _check_whole(got, ref, what):
@@ -205,13 +178,13 @@ def test_flat_7p5b_nd64_reduce_then_step(zs, rank):
     torch.cuda.synchronize()
     got_g = host16(sh.g)
     got = [host16(sh.p), host32(sh.w), host32(sh.m), host32(sh.v)]
-    say(f"flat_7p5b_nd64 rank={rank}: oracle over the whole shard on {_threads()} threads")
+    say(f"flat_7p5b_nd64 rank={rank}: oracle over the whole shard on {host_threads()} threads")
     g_ref = np.empty(n, np.uint16)
     rp, rw = np.zeros(n, np.uint16), w0
     rm, rv = np.zeros(n, np.float32), np.zeros(n, np.float32)
-    fr = _on_windows(lambda lo, hi: oracle.reduce_grad([x[lo:hi] for x in slices],
+    fr = on_windows(lambda lo, hi: oracle.reduce_grad([x[lo:hi] for x in slices],
                                                        g_ref[lo:hi])[1], n)
-    fa = _on_windows(lambda lo, hi: oracle.adam_step(g_ref[lo:hi], rp[lo:hi], rw[lo:hi],
+    fa = on_windows(lambda lo, hi: oracle.adam_step(g_ref[lo:hi], rp[lo:hi], rw[lo:hi],
                                                      rm[lo:hi], rv[lo:hi], t=1, **HP), n)
     del slices
     r = check_whole16(got_g, g_ref, "reduced gradient")
@@ -264,8 +237,8 @@ def test_flat_7p5b_nd8_rank3_with_infinities(zs):
     rm, rv = np.zeros(n, np.float32), np.zeros(n, np.float32)
     rflag = 0
     for t, g in enumerate(grads, start=1):
-        say(f"flat_7p5b_nd8: oracle step t={t} over the whole shard on {_threads()} threads")
-        rflag |= _on_windows(lambda lo, hi: oracle.adam_step(g[lo:hi], rp[lo:hi], rw[lo:hi],
+        say(f"flat_7p5b_nd8: oracle step t={t} over the whole shard on {host_threads()} threads")
+        rflag |= on_windows(lambda lo, hi: oracle.adam_step(g[lo:hi], rp[lo:hi], rw[lo:hi],
                                                              rm[lo:hi], rv[lo:hi], t=t, **HP), n)
         assert rflag == (1 if t == T else 0)
     del grads
