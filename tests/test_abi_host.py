@@ -159,11 +159,17 @@ def test_plan_chunking(zs):
         for n in (1, 511, 512, 513, 5000, 100003):
             d = zs.zero_plan_describe([_fake(n)], C)
             assert d["chunk_elems"] == C and d["n_chunks"] == -(-n // C), (C, n)
-    # head of 2 rides in the first chunk
-    d = zs.zero_plan_describe([_fake(514, 0x100004, 0x200004, 0x300008, 0x400008, 0x500008)], 512)
-    assert d["n_chunks"] == 1
-    d = zs.zero_plan_describe([_fake(515, 0x100004, 0x200004, 0x300008, 0x400008, 0x500008)], 512)
-    assert d["n_chunks"] == 2
+    # fp32 arrays 8 bytes past a 1 KiB boundary: the head runs to the
+    # element where they reach the next one (254 = 2 singly, then 63 fours)
+    # and rides in the first chunk
+    two = (0x100004, 0x200004, 0x300008, 0x400008, 0x500008)
+    assert zs.zero_plan_describe([_fake(254 + 512, *two)], 512)["n_chunks"] == 1
+    assert zs.zero_plan_describe([_fake(254 + 513, *two)], 512)["n_chunks"] == 2
+    # the same vector head of 2, but v reaches its 1 KiB boundary 4
+    # elements earlier than master and m: the head stays at the vector's 2
+    off_v = (0x100004, 0x200004, 0x300008, 0x400008, 0x500018)
+    assert zs.zero_plan_describe([_fake(2 + 512, *off_v)], 512)["n_chunks"] == 1
+    assert zs.zero_plan_describe([_fake(2 + 513, *off_v)], 512)["n_chunks"] == 2
     for C in (1, 100, 511, 513, 1000, (1 << 24) + 512, 2 ** 31):
         with pytest.raises(zs.ZeroError) as e:
             zs.zero_plan_describe([_fake(10)], C)
@@ -197,7 +203,7 @@ def test_plan_chunk_choice(zs):
         ents, base = [], 1 << 40
         for n in sizes:
             n = int(n)
-            step = (n * 4 + 255) // 256 * 256
+            step = (n * 4 + 1023) // 1024 * 1024   # every array on 1 KiB: no head
             ents.append(_fake(n, base, base + step, base + 2 * step, base + 3 * step,
                               base + 4 * step))
             base += 5 * step
@@ -242,7 +248,7 @@ def test_plan_tile_choice(zs):
     for name in ("llama_7b", "gpt2_xl"):
         ents, base = [], 1 << 40
         for _, n in W.WORKLOADS[name].tensors:
-            step = (n * 4 + 255) // 256 * 256
+            step = (n * 4 + 1023) // 1024 * 1024   # every array on 1 KiB: no head
             ents.append(_fake(n, base, base + step, base + 2 * step, base + 3 * step, base + 4 * step))
             base += 5 * step
         assert tile(ents) == 256, name
@@ -255,7 +261,7 @@ def test_plan_describe_workload_lists(zs):
         wl = W.WORKLOADS[name]
         ents, base = [], 1 << 40
         for _, n in wl.tensors:
-            step = (n * 4 + 255) // 256 * 256
+            step = (n * 4 + 1023) // 1024 * 1024   # every array on 1 KiB: no head
             ents.append(_fake(n, base, base + step, base + 2 * step, base + 3 * step,
                               base + 4 * step))
             base += 5 * step
@@ -266,6 +272,31 @@ def test_plan_describe_workload_lists(zs):
         C = d["chunk_elems"]
         assert d["n_chunks"] == sum((n + C - 1) // C for _, n in wl.tensors)
         assert d["table_bytes"] == 64 * len(wl.tensors) + 16 * d["n_chunks"]
+
+
+def test_plan_heads_of_a_packed_list(zs):
+    """The GPT-2-XL list packed into five flattened buffers (each on 1 KiB):
+    a tensor at element offset o has fp32 arrays at 4·o bytes past a 1 KiB
+    boundary, so its head runs (256 - o mod 256) mod 256 elements, all by
+    fours (o is a multiple of 64), and its first chunk holds that head plus
+    up to one chunk.  Chunk counts and the vector/single split follow."""
+    wl = W.WORKLOADS["gpt2_xl"]
+    N = wl.n_params
+    bases = [1 << 40, (1 << 40) + 2 * N + 4096, 1 << 42, 1 << 43, 1 << 44]
+    bases[1] = (bases[1] + 1023) // 1024 * 1024
+    ents, o, heads = [], 0, []
+    for _, n in wl.tensors:
+        ents.append((bases[0] + 2 * o, bases[1] + 2 * o, bases[2] + 4 * o, bases[3] + 4 * o,
+                     bases[4] + 4 * o, n))
+        heads.append((256 - o % 256) % 256)
+        o += n
+    assert sum(1 for h in heads if h) > len(heads) // 2   # most tensors off 1 KiB
+    for C in (16384, 4096, 512):
+        d = zs.zero_plan_describe(ents, C)
+        want = sum(1 + -(-(n - min(n, h + C)) // C) for (_, n), h in zip(wl.tensors, heads))
+        assert d["n_chunks"] == want, C
+        assert d["scalar_elems"] == sum(n % 4 for _, n in wl.tensors)
+        assert d["vector_elems"] + d["scalar_elems"] == N
 
 
 def test_plan_describe_empty_and_zero_sized(zs):

@@ -40,15 +40,19 @@ def zs():
 
 class Arena:
     """Arrays carved out of one byte buffer, each with a guard zone before
-    and after it; `phase` shifts an array's start by that many bytes."""
+    and after it; `phase` shifts an array's start by that many bytes from a
+    multiple of `unit` bytes (256 or 1024) past the buffer's first 1 KiB
+    boundary."""
 
-    def __init__(self, specs):
+    def __init__(self, specs, unit=256):
         import torch
         self.spans, off = [], GUARD
         for nbytes, phase in specs:
             self.spans.append((off + phase, nbytes))
-            off += (phase + nbytes + 255) // 256 * 256 + GUARD
-        self.raw = torch.full((off,), FILL, dtype=torch.uint8, device="cuda")
+            off += (phase + nbytes + unit - 1) // unit * unit + GUARD
+        self.raw = torch.full((off + 1024,), FILL, dtype=torch.uint8, device="cuda")
+        base = (-self.raw.data_ptr()) % 1024
+        self.spans = [(lo + base, nbytes) for lo, nbytes in self.spans]
 
     def view(self, k, dtype):
         lo, nbytes = self.spans[k]
@@ -80,10 +84,14 @@ def _all_written(t, what):
     assert left == 0, f"{what}: {left} elements never written"
 
 
-# element offsets of (param, grad, master, m, v) in bytes: vector path, a
-# peeled head, and the parameter one element off the state (single path)
+# byte phases of (param, grad, master, m, v): vector path, a peeled head,
+# and the parameter one element off the state (single path); "kib_head":
+# every array 131 elements into a 1 KiB slot, so the fp32 arrays reach
+# their next 1 KiB boundary together and the head runs 125 elements (one
+# singly, then 31 groups of four)
 ADAM_LAYOUTS = {"aligned": (0, 0, 0, 0, 0), "head": (6, 6, 12, 12, 12),
-                "param_off": (2, 0, 0, 0, 0)}
+                "param_off": (2, 0, 0, 0, 0), "kib_head": (262, 262, 524, 524, 524)}
+UNITS = {"kib_head": 1024}
 
 
 def _adam_arena(torch, sizes, layout, fmt, seed):
@@ -91,7 +99,7 @@ def _adam_arena(torch, sizes, layout, fmt, seed):
     specs = []
     for n in sizes:
         specs += [(2 * n, po), (2 * n, go), (4 * n, wo), (4 * n, mo), (4 * n, vo)]
-    A = Arena(specs)
+    A = Arena(specs, UNITS.get(layout, 256))
     tensors = []
     for k, n in enumerate(sizes):
         p, g = A.view(5 * k, _half(fmt)), A.view(5 * k + 1, _half(fmt))
@@ -129,7 +137,7 @@ def test_adam_plan_bounds(zs, fmt, layout, chunk):
     plan.destroy()
 
 
-@pytest.mark.parametrize("layout", ["aligned", "head"])
+@pytest.mark.parametrize("layout", ["aligned", "head", "kib_head"])
 def test_adam_plan_bounds_fine_tile(zs, layout):
     """Big vector tensors (the library's 16,384-element chunk), which take
     the 256-element Adam tile."""
@@ -188,10 +196,12 @@ def test_reduce_bounds(zs, fmt, layout, nd):
         _all_written(out, f"reduce {fmt} {layout} nd={nd} n={n}")
 
 
-# byte phases of (even slices, odd slices, param, grad_out, master, m, v)
+# byte phases of (even slices, odd slices, param, grad_out, master, m, v);
+# "kib_head" in 1 KiB slots, as for the Adam step
 FUSED_LAYOUTS = {"aligned": (0, 0, 0, 0, 0, 0, 0), "phase": (4, 4, 4, 4, 8, 8, 8),
                  "split": (0, 8, 0, 0, 0, 0, 0), "odd": (2, 2, 0, 0, 0, 0, 0),
-                 "param_off": (0, 0, 2, 2, 0, 0, 0)}
+                 "param_off": (0, 0, 2, 2, 0, 0, 0),
+                 "kib_head": (262, 262, 262, 262, 524, 524, 524)}
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -208,7 +218,7 @@ def test_fused_bounds(zs, fmt, layout, nd):
         for with_gout in (False, True):
             specs = [(2 * n, se if r % 2 == 0 else so) for r in range(nd)]
             specs += [(2 * n, po), (2 * n, go), (4 * n, wo), (4 * n, mo), (4 * n, vo)]
-            A = Arena(specs)
+            A = Arena(specs, UNITS.get(layout, 256))
             sl = [A.view(r, _half(fmt)) for r in range(nd)]
             for r, s in enumerate(sl):
                 _randn16(torch, s, 500 + r)

@@ -141,6 +141,15 @@ void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n
     *head = 0;
 }
 
+uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head) {
+    uint32_t ph[3];
+    for (int i = 0; i < 3; i++)
+        ph[i] = (uint32_t)(((kTileAlignBytes - a32[i] % kTileAlignBytes) % kTileAlignBytes) / 4u);
+    if (ph[0] != ph[1] || ph[1] != ph[2] || ph[0] % 4u != vec_head)
+        return vec_head;
+    return ph[0];
+}
+
 bool writes_overlap(Range *r, size_t n) {
     std::sort(r, r + n, [](const Range &a, const Range &b) { return a.lo < b.lo; });
     // Sweep keeping the furthest end seen among written and among all ranges.
@@ -213,6 +222,8 @@ int describe_tensor(const zero_tensor &t, TensorDesc *d, Range r[5]) {
     d->n = t.n;
     const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
     pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
+    if (d->vec == 4)
+        d->head = adam_head_of(a32, d->head);
     return ZERO_OK;
 }
 
@@ -223,16 +234,17 @@ void plan_stats(const TensorDesc *tensors, size_t n_desc, uint64_t n_tensors, ui
     s->chunk_elems = C;
     for (size_t k = 0; k < n_desc; k++) {
         const TensorDesc &d = tensors[k];
-        const uint64_t head = std::min<uint64_t>(d.head, d.n);
         s->n_params += d.n;
         s->n_chunks += chunks_of(d, C);
         if (d.vec == 1) {
             s->scalar_elems += d.n;
         } else {
-            // every chunk body but the tensor's last is a whole number of
-            // tiles, so only the tensor's last fewer-than-four elements (and
-            // its head) go singly
-            const uint64_t vec = (d.n - head) / 4 * 4;
+            // the head's first head % 4 elements go singly and the rest of
+            // it by fours; every chunk body but the tensor's last is a whole
+            // number of tiles, so only the tensor's last fewer-than-four
+            // elements go singly too
+            const uint64_t singles = std::min<uint64_t>(d.head % 4u, d.n);
+            const uint64_t vec = (d.n - singles) / 4 * 4;
             s->vector_elems += vec;
             s->scalar_elems += d.n - vec;
         }

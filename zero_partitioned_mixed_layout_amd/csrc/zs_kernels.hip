@@ -242,18 +242,42 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
         quad_update_store<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k], c, bad);
 }
 
-// Tile j of a chunk on the vector path.  The tensor's peeled head (fewer
-// than four elements, so that the rest is vector-aligned) rides in its first
-// chunk and is done by tile 0; every other chunk starts vector-aligned.  The
-// chunk's last, partial tile goes four elements per lane, then the final
+// The peeled head of a tensor on the vector path: its first `count`
+// elements (count <= T.head < 256).  The first T.head % 4 go singly (they
+// precede the first aligned vector), then at most 63 groups of four, one per
+// lane; a tensor that ends inside its head does its last fewer-than-four
+// singly.
+template <class Fmt>
+__device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
+                                          const AdamConsts &c, int &bad) {
+    const uint32_t lane = threadIdx.x;
+    const uint32_t singles = min(T.head % 4u, count);
+    if (lane < singles)
+        adam_single<Fmt>(T, lane, c, bad);
+    const uint32_t nquads = (count - singles) / 4u;
+    if (lane < nquads) {
+        Quad<Fmt> x;
+        quad_load<Fmt>(T, singles + 4u * lane, x);
+        quad_update_store<Fmt>(T, singles + 4u * lane, x, c, bad);
+    }
+    const uint32_t rest = count - singles - 4u * nquads;
+    if (lane < rest)
+        adam_single<Fmt>(T, singles + 4u * nquads + lane, c, bad);
+}
+
+// Tile j of a chunk on the vector path.  The tensor's peeled head (up to
+// where its fp32 arrays reach a 1 KiB boundary, or only to the first
+// aligned vector) rides in its first chunk and is done by tile 0; every
+// other chunk starts at the head plus a whole number of tiles.  The chunk's
+// last, partial tile goes four elements per lane, then the final
 // fewer-than-four singly.
 template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
     const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
-    if (j == 0 && lane < head)
-        adam_single<Fmt>(T, lane, c, bad);
+    if (j == 0 && head != 0)
+        adam_head<Fmt>(T, head, c, bad);
     const uint64_t base = ch.start + head;
     const uint32_t body = ch.count - head;
     const uint32_t nfull = body / TILE;
@@ -1324,6 +1348,8 @@ int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *
     const uintptr_t a16[2] = {(uintptr_t)p, (uintptr_t)g};
     const uintptr_t a32[3] = {(uintptr_t)w, (uintptr_t)m, (uintptr_t)v};
     zs::pick_vector_path(a16, 2, a32, 3, 4, &T.vec, &T.head);
+    if (T.vec == 4)
+        T.head = zs::adam_head_of(a32, T.head);
     const uint32_t tile = T.vec == 4 ? kAdamTileFine : kTile;
     // tiles: the first holds the peeled head (vector path) and up to `tile`
     // elements, every later one `tile` elements, the last what is left
