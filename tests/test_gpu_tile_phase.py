@@ -8,8 +8,9 @@ singly, the rest by fours), so that the tensor's tiles start on 1 KiB of
 fp32.  With v shifted four elements against master and m the three
 disagree, and the head is only the vector's.  Offsets give head lengths
 from 1 to 255; sizes sit around the head and the tile and chunk
-boundaries after it; every element compared.  Each case prints its name
-and sizes before it touches the GPU."""
+boundaries after it; every element compared, for fp16 and bfloat16 and
+for gradients that carry a loss scale.  Each case prints its name and
+sizes before it touches the GPU."""
 import numpy as np
 import pytest
 
@@ -58,24 +59,29 @@ def _aligned(torch, elems, dtype):
 
 class Carved:
     """Five flattened buffers holding (offset, n) tensors, each in a slot of
-    its own; host mirrors of the same arrays for the oracle."""
+    its own; host mirrors of the same arrays for the oracle.  fmt: "f16" or
+    "bf16" parameters and gradients; log2_scale: gradients drawn 2^k times
+    larger, for the step that unscales them."""
 
-    def __init__(self, torch, cases, v_shift, seed):
+    def __init__(self, torch, cases, v_shift, seed, fmt="f16", log2_scale=None):
         self.starts, at = [], 0
         for o, n in cases:
             self.starts.append(at + o)
             at += (o + n + v_shift + 255) // 256 * 256 + 256
         rng = np.random.default_rng(seed)
-        self.cases, self.v_shift = cases, v_shift
-        self.g = (rng.standard_normal(at) * 1e-3).astype(np.float16).view(np.uint16)
+        self.cases, self.v_shift, self.fmt, self.k = cases, v_shift, fmt, log2_scale
+        g = rng.standard_normal(at) * 1e-3 * 2.0 ** (log2_scale or 0)
+        self.g = (g.astype(np.float16).view(np.uint16) if fmt == "f16"
+                  else oracle.f32_to_bf16(g.astype(np.float32)))
         self.w = (rng.standard_normal(at) * 0.02).astype(np.float32)
         self.m = (rng.standard_normal(at) * 1e-4).astype(np.float32)
         self.v = (rng.random(at) * 1e-6).astype(np.float32)
         self.p = np.zeros(at, np.uint16)
-        self.dp = _aligned(torch, at, torch.float16)
-        self.dg = _aligned(torch, at, torch.float16)
+        half = torch.float16 if fmt == "f16" else torch.bfloat16
+        self.dp = _aligned(torch, at, half)
+        self.dg = _aligned(torch, at, half)
         self.dw, self.dm, self.dv = (_aligned(torch, at, torch.float32) for _ in range(3))
-        self.dg.copy_(to_dev16(self.g))
+        self.dg.copy_(to_dev16(self.g).view(half))
         self.dw.copy_(to_dev32(self.w))
         self.dm.copy_(to_dev32(self.m))
         self.dv.copy_(to_dev32(self.v))
@@ -90,7 +96,12 @@ class Carved:
         for s, (_, n) in zip(self.starts, self.cases):
             p, w, m = self.p[s:s + n], self.w[s:s + n], self.m[s:s + n]
             v = self.v[s + vs:s + vs + n]
-            assert oracle.adam_step(self.g[s:s + n], p, w, m, v, t=t, **HP) == 0
+            if self.k is None:
+                flag = oracle.adam_step(self.g[s:s + n], p, w, m, v, t=t, fmt=self.fmt, **HP)
+            else:
+                flag = oracle.adam_step_scaled(self.g[s:s + n], p, w, m, v, t=t,
+                                               log2_scale=self.k, fmt=self.fmt, **HP)
+            assert flag == 0
 
     def compare(self, what):
         vs = self.v_shift
@@ -98,7 +109,7 @@ class Carved:
         gp, gw, gm, gv = host16(self.dp), host32(self.dw), host32(self.dm), host32(self.dv)
         for k, (s, (o, n)) in enumerate(zip(self.starts, self.cases)):
             tag = f"{what} tensor {k} o={o} n={n}"
-            r = [check16(gp[s:s + n], self.p[s:s + n], tag + " param"),
+            r = [check16(gp[s:s + n], self.p[s:s + n], tag + " param", fmt=self.fmt),
                  check32(gw[s:s + n], self.w[s:s + n], tag + " master"),
                  check32(gm[s:s + n], self.m[s:s + n], tag + " m"),
                  check32(gv[s + vs:s + vs + n], self.v[s + vs:s + vs + n], tag + " v")]
@@ -144,6 +155,33 @@ def test_heads_match_oracle(zs, chunk, v_shift):
         c.oracle_step(t)
         torch.cuda.synchronize()
         bad += c.compare(f"plan chunk={chunk} v_shift={v_shift} t={t}")
+    assert int(flag.item()) == 0
+    assert bad == 0, f"{bad} elements within tolerance but not bit-exact"
+    plan.destroy()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16_scaled", "bf16_scaled"])
+def test_heads_other_formats(zs, kind):
+    """bfloat16 parameters and gradients, and gradients that carry a loss
+    scale of 2^12 (the step multiplies each by 2^-12 first): the same
+    kernel template behind the same heads; the library's chunk, two steps,
+    every element."""
+    import torch
+    fmt = "bf16" if kind.startswith("bf16") else "f16"
+    k = 12 if kind.endswith("scaled") else None
+    cases = _cases(False)
+    say(f"tile phase: {kind} tensors={len(cases)}")
+    c = Carved(torch, cases, 0, seed=110 + len(kind), fmt=fmt, log2_scale=k)
+    plan = zs.zero_plan_create(c.tensors())
+    assert plan.stats()["n_chunks"] == _want_chunks(cases, 0, plan.stats()["chunk_elems"])
+    ls = zs.LossScale(log2_scale=k, device=torch.device("cuda", 0)) if k is not None else None
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad = 0
+    for t in (3, 4):
+        zs.zero_adam_step(plan, zs.AdamHParams(**HP), t, flag, loss_scale=ls)
+        c.oracle_step(t)
+        torch.cuda.synchronize()
+        bad += c.compare(f"{kind} t={t}")
     assert int(flag.item()) == 0
     assert bad == 0, f"{bad} elements within tolerance but not bit-exact"
     plan.destroy()
