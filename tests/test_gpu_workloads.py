@@ -7,12 +7,14 @@ from the same seeded inputs -- the initial master, every slice and every
 step's gradients copied to the host before the GPU uses them, never a value
 the HIP path produced -- through all warm-up steps, threaded over windows
 of the arrays on the host's CPUs.  The tensor lists (GPT-2-XL, Llama-7B)
-are compared at sampled elements (both ends of every tensor and 96 random
-ones): their whole state and the oracle's copy of it with every step's
+are compared through their six steps at sampled elements (both ends of
+every tensor and 96 random ones): their whole state with every step's
 gradients would pass the host memory a GPU job may use (about 280 GB for
-Llama-7B).  Properties that hold at any size (untouched padding and other
-ranks' parameters, the non-finite positions, the ZeRO-2 ledger) are
-checked on the whole arrays."""
+Llama-7B).  The Llama-7B list is also compared over its whole arrays for
+its first step from the seeded state (about 108 GB of host memory).
+Properties that hold at any size (untouched padding and other ranks'
+parameters, the non-finite positions, the ZeRO-2 ledger) are checked on
+the whole arrays."""
 import gc
 
 import numpy as np
@@ -252,4 +254,77 @@ def test_flat_7p5b_nd8_rank3_with_infinities(zs):
     assert torch.equal(bad_m, pos_dev)
     assert int(torch.count_nonzero(full[:lay.offset]).item()) == 0
     assert int(torch.count_nonzero(full[lay.offset + n:]).item()) == 0
+    plan.destroy()
+
+
+def _host_bytes_free() -> int:
+    """Host memory this process may still take: the kernel's MemAvailable,
+    capped by the cgroup's limit less its current use where one is set."""
+    free = 0
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemAvailable:"):
+                free = int(line.split()[1]) * 1024
+    except OSError:
+        return 0
+    try:
+        lim = open("/sys/fs/cgroup/memory.max").read().strip()
+        if lim != "max":
+            used = int(open("/sys/fs/cgroup/memory.current").read())
+            free = min(free, int(lim) - used)
+    except (OSError, ValueError):
+        pass
+    return free
+
+
+def test_llama_7b_whole_arrays_first_step(zs):
+    """The Llama-7B list (291 tensors, 6,738,415,616 parameters) in five
+    flattened buffers: step 1 from the seeded state (master N(0, 0.02),
+    m = v = 0; master and the step's gradients copied to the host before the
+    GPU uses them), every element of the parameter, master, m and v
+    compared with the oracle.  The step is elementwise with one set of
+    hyperparameters, so the oracle over the flattened arrays in windows is
+    the step of every tensor.  test_tensor_list_workload follows the
+    workload's six steps at sampled elements.  Skipped where the host
+    cannot hold the state (16 bytes per parameter, about 108 GB)."""
+    import torch
+    wl = W.WORKLOADS["llama_7b"]
+    N = wl.n_params
+    need = 16 * N + (8 << 30)
+    if _host_bytes_free() < need:
+        pytest.skip(f"needs about {need >> 30} GiB of host memory, "
+                    f"{_host_bytes_free() >> 30} GiB free")
+    say(f"llama_7b whole arrays: {len(wl.tensors)} tensors, {N} params")
+    tensors = W.device_list_state(wl, layout="flat")
+    W.device_fill_grads(wl, tensors, 1)
+    torch.cuda.synchronize()
+    bp, bg, bw, bm, bv = (getattr(tensors[0], a)._base for a in "pgwmv")
+    for b in (bp, bg, bw, bm, bv):
+        assert b is not None and b.numel() == N
+    say("llama_7b: seeded state and gradients to the host")
+    g, w, m, v = host16(bg), host32(bw), host32(bm), host32(bv)
+    assert not np.any(m) and not np.any(v)
+    p = np.zeros(N, np.uint16)
+    plan = zs.zero_plan_create([t.arrays() for t in tensors])
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_adam_step(plan, zs.AdamHParams(**HP), 1, flag)
+    torch.cuda.synchronize()
+    blocks, rflag = 24, 0
+    for b in range(blocks):
+        lo, hi = N * b // blocks, N * (b + 1) // blocks
+
+        def step(a, z, lo=lo):
+            return oracle.adam_step(g[lo + a:lo + z], p[lo + a:lo + z], w[lo + a:lo + z],
+                                    m[lo + a:lo + z], v[lo + a:lo + z], t=1, **HP)
+
+        rflag |= on_windows(step, hi - lo)
+        say(f"llama_7b: oracle block {b + 1}/{blocks}")
+    bad, win = 0, 1 << 28
+    for lo in range(0, N, win):
+        hi = min(N, lo + win)
+        got = (host16(bp[lo:hi]), host32(bw[lo:hi]), host32(bm[lo:hi]), host32(bv[lo:hi]))
+        bad += _check_whole(got, (p[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi]),
+                            f"llama_7b [{lo}, {hi})")
+    assert int(flag.item()) == rflag == 0
+    assert bad == 0, f"{bad} elements within tolerance but not bit-exact"
     plan.destroy()
