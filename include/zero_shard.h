@@ -160,7 +160,8 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * zero_plan_create -- chunk table for a list of tensors of mixed sizes.
  * tensors: host array of n_tensors descriptors (copied; the table does not
  * keep the host array).  Each tensor is cut into chunks of chunk_elems
- * elements (its last chunk may be shorter); the step runs one 64-lane wave
+ * elements after its peeled head, which rides in its first chunk (its
+ * last chunk may be shorter); the step runs one 64-lane wave
  * per tile_elems consecutive elements of a chunk: 256 when at least 7/8 of
  * the plan's elements take the vector path and chunk_elems is 16384, else
  * 512 (the faster of the two, measured, for such plans).
@@ -171,7 +172,12 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * multiple of 512 between 512 and 2^24.  Per tensor the library takes the vector
  * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree
  * in alignment after peeling at most 3 leading elements, else it moves
- * single elements.  The table is allocated on the current device
+ * single elements.  On the vector path the peeled head runs on to the
+ * element at which the tensor's master, m and v reach a 1 KiB boundary,
+ * when they reach one at the same element (at most 255 elements, done by
+ * the tensor's first tile), so that its chunks and tiles start there: a
+ * list packed at offsets that are not multiples of 256 elements streams
+ * about 3% faster so (measured).  The table is allocated on the current device
  * (hipMalloc) and filled with a synchronous copy; nothing else is
  * allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The
