@@ -389,8 +389,8 @@ def cpu_baseline(step, sample_n: int, min_seconds: float):
 
 def host_cpus() -> dict:
     """CPUs this process may use: its affinity mask, capped by the cgroup's
-    CPU quota where one is set (cpu.max), which is the share a GPU machine gives
-    one GPU's jobs."""
+    CPU quota where one is set (cpu.max), which is the share a machine
+    shared between GPUs gives the jobs of one GPU."""
     aff = len(os.sched_getaffinity(0))
     quota = None
     try:

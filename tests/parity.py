@@ -129,7 +129,7 @@ def check_whole16(got: np.ndarray, ref: np.ndarray, what: str, fmt: str = "f16")
 
 def host_threads() -> int:
     """Host threads for the oracle: the CPUs this process may use, capped
-    by the cgroup's CPU quota (a GPU machine's share for one GPU)."""
+    by the cgroup's CPU quota (a shared machine's share for one GPU)."""
     n = len(os.sched_getaffinity(0))
     try:
         q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
