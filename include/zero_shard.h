@@ -172,12 +172,12 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * multiple of 512 between 512 and 2^24.  Per tensor the library takes the vector
  * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree
  * in alignment after peeling at most 3 leading elements, else it moves
- * single elements.  On the vector path the peeled head runs on to the
- * element at which the tensor's master, m and v reach a 1 KiB boundary,
- * when they reach one at the same element (at most 255 elements, done by
- * the tensor's first tile), so that its chunks and tiles start there: a
- * list packed at offsets that are not multiples of 256 elements streams
- * about 3% faster so (measured).  The table is allocated on the current device
+ * single elements.  On the vector path, for a tensor of 1,024 elements or
+ * more, the peeled head runs on to the element at which the tensor's
+ * master, m and v reach a 1 KiB boundary, when they reach one at the same
+ * element (at most 255 elements, done by the tensor's first tile), so that
+ * its chunks and tiles start there: a list packed at offsets that are not
+ * multiples of 256 elements streams about 3% faster so (measured).  The table is allocated on the current device
  * (hipMalloc) and filled with a synchronous copy; nothing else is
  * allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The

@@ -159,17 +159,21 @@ def test_plan_chunking(zs):
         for n in (1, 511, 512, 513, 5000, 100003):
             d = zs.zero_plan_describe([_fake(n)], C)
             assert d["chunk_elems"] == C and d["n_chunks"] == -(-n // C), (C, n)
-    # fp32 arrays 8 bytes past a 1 KiB boundary: the head runs to the
-    # element where they reach the next one (254 = 2 singly, then 63 fours)
-    # and rides in the first chunk
+    # fp32 arrays 8 bytes past a 1 KiB boundary: from 1,024 elements the
+    # head runs to the element where they reach the next one (254 = 2
+    # singly, then 63 fours), riding in the first chunk: 254 + 512, then 512
     two = (0x100004, 0x200004, 0x300008, 0x400008, 0x500008)
-    assert zs.zero_plan_describe([_fake(254 + 512, *two)], 512)["n_chunks"] == 1
-    assert zs.zero_plan_describe([_fake(254 + 513, *two)], 512)["n_chunks"] == 2
+    assert zs.zero_plan_describe([_fake(254 + 1024, *two)], 512)["n_chunks"] == 2
+    assert zs.zero_plan_describe([_fake(254 + 1025, *two)], 512)["n_chunks"] == 3
+    # below 1,024 elements the head stays at the vector's 2
+    assert zs.zero_plan_describe([_fake(2 + 512, *two)], 512)["n_chunks"] == 1
+    assert zs.zero_plan_describe([_fake(2 + 513, *two)], 512)["n_chunks"] == 2
+    assert zs.zero_plan_describe([_fake(1023, *two)], 512)["n_chunks"] == 2
     # the same vector head of 2, but v reaches its 1 KiB boundary 4
     # elements earlier than master and m: the head stays at the vector's 2
     off_v = (0x100004, 0x200004, 0x300008, 0x400008, 0x500018)
-    assert zs.zero_plan_describe([_fake(2 + 512, *off_v)], 512)["n_chunks"] == 1
-    assert zs.zero_plan_describe([_fake(2 + 513, *off_v)], 512)["n_chunks"] == 2
+    assert zs.zero_plan_describe([_fake(2 + 1024, *off_v)], 512)["n_chunks"] == 2
+    assert zs.zero_plan_describe([_fake(2 + 1025, *off_v)], 512)["n_chunks"] == 3
     for C in (1, 100, 511, 513, 1000, (1 << 24) + 512, 2 ** 31):
         with pytest.raises(zs.ZeroError) as e:
             zs.zero_plan_describe([_fake(10)], C)
@@ -277,9 +281,10 @@ def test_plan_describe_workload_lists(zs):
 def test_plan_heads_of_a_packed_list(zs):
     """The GPT-2-XL list packed into five flattened buffers (each on 1 KiB):
     a tensor at element offset o has fp32 arrays at 4·o bytes past a 1 KiB
-    boundary, so its head runs (256 - o mod 256) mod 256 elements, all by
-    fours (o is a multiple of 64), and its first chunk holds that head plus
-    up to one chunk.  Chunk counts and the vector/single split follow."""
+    boundary, so a tensor of 1,024 elements or more has a head of
+    (256 - o mod 256) mod 256 elements, all by fours (o is a multiple of
+    64), and its first chunk holds that head plus up to one chunk.  Chunk
+    counts and the vector/single split follow."""
     wl = W.WORKLOADS["gpt2_xl"]
     N = wl.n_params
     bases = [1 << 40, (1 << 40) + 2 * N + 4096, 1 << 42, 1 << 43, 1 << 44]
@@ -288,7 +293,7 @@ def test_plan_heads_of_a_packed_list(zs):
     for _, n in wl.tensors:
         ents.append((bases[0] + 2 * o, bases[1] + 2 * o, bases[2] + 4 * o, bases[3] + 4 * o,
                      bases[4] + 4 * o, n))
-        heads.append((256 - o % 256) % 256)
+        heads.append((256 - o % 256) % 256 if n >= 1024 else 0)
         o += n
     assert sum(1 for h in heads if h) > len(heads) // 2   # most tensors off 1 KiB
     for C in (16384, 4096, 512):

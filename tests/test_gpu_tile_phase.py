@@ -3,10 +3,11 @@ CPU oracle.  Every array is carved out of a flattened buffer that starts on
 a 1 KiB boundary, each tensor in a slot of its own (a multiple of 256
 elements) at a chosen element offset o.  The fp32 master, m and v then
 reach their next 1 KiB boundary together, (256 - o mod 256) mod 256
-elements in, and the head runs up to there (the first (4 - o mod 4) mod 4
-singly, the rest by fours), so that the tensor's tiles start on 1 KiB of
-fp32.  With v shifted four elements against master and m the three
-disagree, and the head is only the vector's.  Offsets give head lengths
+elements in, and on a tensor of 1,024 elements or more the head runs up
+to there (the first (4 - o mod 4) mod 4 singly, the rest by fours), so
+that the tensor's tiles start on 1 KiB of fp32; a smaller tensor, or one
+whose v is shifted four elements against master and m (the three then
+disagree), keeps only the vector's head.  Offsets give head lengths
 from 1 to 255; sizes sit around the head and the tile and chunk
 boundaries after it; every element compared, for fp16 and bfloat16 and
 for gradients that carry a loss scale.  Each case prints its name and
@@ -38,14 +39,17 @@ def zs():
     return zero_shard
 
 
-def _head(o, v_shift):
+def _head(o, v_shift, n=1 << 20):
+    """The head a tensor of n elements at offset o gets: to the 1 KiB
+    boundary from 1,024 elements on when master, m and v agree, else the
+    vector head."""
     vec = (4 - o % 4) % 4
-    return vec if v_shift else (256 - o % 256) % 256
+    return vec if v_shift or n < 1024 else (256 - o % 256) % 256
 
 
 def _sizes(h):
     s = {1, 2, 3, 5, 8, h - 1, h, h + 1, h + 3, h + 4, h + 255, h + 256, h + 257,
-         h + 513, h + 16383, h + 16389, 70001}
+         h + 513, 1023, 1024, 1025, h + 1024, h + 1025, h + 16383, h + 16389, 70001}
     return sorted(x for x in s if x > 0)
 
 
@@ -128,7 +132,7 @@ def _cases(fine):
 
 
 def _want_chunks(cases, v_shift, C):
-    return sum(1 + -(-(n - min(n, _head(o, v_shift) + C)) // C) for o, n in cases)
+    return sum(1 + -(-(n - min(n, _head(o, v_shift, n) + C)) // C) for o, n in cases)
 
 
 @pytest.mark.parametrize("chunk", [0, 512, "fine"])
@@ -214,7 +218,8 @@ def test_heads_of_the_split_route(zs, o):
     h = _head(o, 0)
     rng = np.random.default_rng(400 + o)
     bad = 0
-    for n in sorted({1, 5, max(1, h - 1), max(1, h), h + 1, h + 256, h + 257, 70001}):
+    for n in sorted({1, 5, max(1, h - 1), max(1, h), h + 1, h + 256, h + 257, h + 1024,
+                     h + 1025, 70001}):
         say(f"tile phase: split route o={o} n={n} nd={nd}")
         hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16)
               for _ in range(nd)]

@@ -141,7 +141,9 @@ void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n
     *head = 0;
 }
 
-uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head) {
+uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head, uint64_t n) {
+    if (n < kTileAlignMinElems)
+        return vec_head;
     uint32_t ph[3];
     for (int i = 0; i < 3; i++)
         ph[i] = (uint32_t)(((kTileAlignBytes - a32[i] % kTileAlignBytes) % kTileAlignBytes) / 4u);
@@ -223,7 +225,7 @@ int describe_tensor(const zero_tensor &t, TensorDesc *d, Range r[5]) {
     const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
     pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
     if (d->vec == 4)
-        d->head = adam_head_of(a32, d->head);
+        d->head = adam_head_of(a32, d->head, t.n);
     return ZERO_OK;
 }
 

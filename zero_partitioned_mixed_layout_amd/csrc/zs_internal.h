@@ -98,6 +98,15 @@ constexpr uint32_t kLine = 128;
 // tiles start on where a tensor's fp32 arrays allow it (adam_head_of).
 constexpr uint32_t kTileAlignBytes = 4u * kAdamTileFine;
 
+// Smallest tensor whose head runs to that boundary.  Tile 0 finishes the
+// head before it loads its own elements, one more pass over memory, which
+// costs more than the alignment saves on small tensors.  Measured on MI355X,
+// lists at random offsets in flattened buffers, head to 1 KiB against the
+// vector head alone, one process: sizes 1-1,024 elements 0.410 against
+// 0.423 of 8 TB/s; 1,024-4,096 0.571 against 0.558; 4,096-16,384 0.613
+// against 0.562; 16,384-65,536 0.647 against 0.597.
+constexpr uint64_t kTileAlignMinElems = 1024;
+
 // Elements per chunk of the offload pipeline (8 MiB of fp16 per staging
 // buffer).
 constexpr uint64_t kOffloadChunk = 4ull << 20;
@@ -187,18 +196,19 @@ struct Range {
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,
                     HostPlan *out);
 
-// The Adam step's peeled head of a tensor on the four-element vector path,
-// given its vector head (the fewer than four elements before the first
-// vector) and its fp32 master, m and v addresses.  When the three reach a
-// 1 KiB boundary at the same element, the head runs up to that element
-// (fewer than 256, equal to the vector head mod 4), so that every full tile
-// after it starts on 1 KiB of fp32; otherwise it is the vector head.  The
-// fp32 arrays carry 24 of the step's 28 bytes per parameter.  Measured on
+// The Adam step's peeled head of a tensor of n elements on the
+// four-element vector path, given its vector head (the fewer than four
+// elements before the first vector) and its fp32 master, m and v
+// addresses.  When n >= kTileAlignMinElems and the three reach a 1 KiB
+// boundary at the same element, the head runs up to that element (fewer
+// than 256, equal to the vector head mod 4), so that every full tile after
+// it starts on 1 KiB of fp32; otherwise it is the vector head.  The fp32
+// arrays carry 24 of the step's 28 bytes per parameter.  Measured on
 // MI355X with the GPT-2-XL list packed in flattened buffers (its 1,600-
 // element tensors put the big ones at multiples of 64 elements): tiles at
 // the tensors' own offsets ran at 0.788 of 8 TB/s, tiles on 1 KiB at
 // 0.812-0.816, as fast as one flat tensor of the same size.
-uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head);
+uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head, uint64_t n);
 
 // One non-empty tensor: its descriptor (vector path and peeled head) and the
 // byte ranges of its five arrays (param, grad, master, m, v).  Errors:

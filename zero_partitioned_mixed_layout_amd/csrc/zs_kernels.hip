@@ -266,11 +266,11 @@ __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
 }
 
 // Tile j of a chunk on the vector path.  The tensor's peeled head (up to
-// where its fp32 arrays reach a 1 KiB boundary, or only to the first
-// aligned vector) rides in its first chunk and is done by tile 0; every
-// other chunk starts at the head plus a whole number of tiles.  The chunk's
-// last, partial tile goes four elements per lane, then the final
-// fewer-than-four singly.
+// where its fp32 arrays reach a 1 KiB boundary on tensors of 1,024 elements
+// or more, else only to the first aligned vector) rides in its first chunk
+// and is done by tile 0; every other chunk starts at the head plus a whole
+// number of tiles.  The chunk's last, partial tile goes four elements per
+// lane, then the final fewer-than-four singly.
 template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
@@ -1349,7 +1349,7 @@ int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *
     const uintptr_t a32[3] = {(uintptr_t)w, (uintptr_t)m, (uintptr_t)v};
     zs::pick_vector_path(a16, 2, a32, 3, 4, &T.vec, &T.head);
     if (T.vec == 4)
-        T.head = zs::adam_head_of(a32, T.head);
+        T.head = zs::adam_head_of(a32, T.head, n);
     const uint32_t tile = T.vec == 4 ? kAdamTileFine : kTile;
     // tiles: the first holds the peeled head (vector path) and up to `tile`
     // elements, every later one `tile` elements, the last what is left
