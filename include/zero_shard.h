@@ -104,6 +104,10 @@ typedef struct zero_plan_stats {
     uint64_t table_bytes;   /* device bytes of the chunk table */
     uint64_t tile_elems;    /* elements one 64-lane wave of the step updates:
                                256 or 512 (see zero_plan_create) */
+    uint64_t wg_per_cu;     /* one-wave workgroups of the step resident per CU
+                               (its occupancy cap): 12 with 256-element
+                               tiles; with 512-element tiles 7, or 14-28 for
+                               lists of small tensors (see zero_plan_create) */
 } zero_plan_stats;
 
 /*
@@ -177,7 +181,13 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * master, m and v reach a 1 KiB boundary, when they reach one at the same
  * element (at most 255 elements, done by the tensor's first tile), so that
  * its chunks and tiles start there: a list packed at offsets that are not
- * multiples of 256 elements streams about 3% faster so (measured).  The table is allocated on the current device
+ * multiples of 256 elements streams about 3% faster so (measured).  The
+ * step keeps wg_per_cu one-wave workgroups resident per CU: 12 with
+ * 256-element tiles, and with 512-element tiles 7 unless at least one
+ * tile in 20 holds a head or a tensor's partial last tile, when the cap
+ * grows as the tiles' average element count e shrinks, 7 * 512 / e + 7
+ * within 14..28 (lists of small tensors wait on memory more per element;
+ * measured up to twice as fast so).  The table is allocated on the current device
  * (hipMalloc) and filled with a synchronous copy; nothing else is
  * allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The

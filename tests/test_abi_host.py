@@ -304,6 +304,46 @@ def test_plan_heads_of_a_packed_list(zs):
         assert d["vector_elems"] + d["scalar_elems"] == N
 
 
+def _packed(zs, sizes):
+    """A would-be plan over tensors packed back to back in five flattened
+    buffers that start on 1 KiB."""
+    B = [1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44]
+    ents, o = [], 0
+    for n in sizes:
+        ents.append((B[0] + 2 * o, B[1] + 2 * o, B[2] + 4 * o, B[3] + 4 * o, B[4] + 4 * o, n))
+        o += n
+    return zs.zero_plan_describe(ents)
+
+
+def test_plan_occupancy_cap(zs):
+    """wg_per_cu: 12 with 256-element tiles; with 512-element tiles 7 while
+    fewer than one tile in 20 holds a head or a partial last tile, else
+    7 * 512 / e + 7 within 14..28 (e: elements per tile with work)."""
+    d = _packed(zs, [1 << 26])
+    assert (d["tile_elems"], d["wg_per_cu"]) == (256, 12)
+    d = _packed(zs, [n for _, n in W.WORKLOADS["gpt2_xl"].tensors])
+    assert (d["tile_elems"], d["wg_per_cu"]) == (256, 12)
+    # whole tiles only: 7
+    d = _packed(zs, [1024] * 1000)
+    assert (d["tile_elems"], d["wg_per_cu"]) == (512, 7)
+    # one partial tile per tensor of 100 elements: e = 100, 7*512/100 + 7 > 28
+    d = _packed(zs, [100] * 1000)
+    assert (d["tile_elems"], d["wg_per_cu"]) == (512, 28)
+    # e = 300: round(7*512/300 + 7) = 19
+    assert _packed(zs, [300] * 1000)["wg_per_cu"] == 19
+    # e = 400 (tensors of 800: two tiles, one partial): round(8.96 + 7) = 16
+    assert _packed(zs, [800] * 1000)["wg_per_cu"] == 16
+    # mostly whole tiles: 19 tensors of 512 and one of 100 per 20 tensors
+    # (1 irregular tile in 20: the cap moves; 1 in 21 does not)
+    assert _packed(zs, ([512] * 19 + [100]) * 50)["wg_per_cu"] == 14
+    assert _packed(zs, ([512] * 20 + [100]) * 50)["wg_per_cu"] == 7
+    # single-element tensors of whole tiles (parameter one element off)
+    one_off = [((1 << 40) + (k << 20) + 2, (1 << 41) + (k << 20), (1 << 42) + (k << 20),
+                (1 << 43) + (k << 20), (1 << 44) + (k << 20), 1024) for k in range(100)]
+    d = zs.zero_plan_describe(one_off)
+    assert d["scalar_elems"] == 102400 and d["wg_per_cu"] == 7
+
+
 def test_plan_describe_empty_and_zero_sized(zs):
     d = zs.zero_plan_describe([])
     assert d["n_params"] == 0 and d["n_chunks"] == 0

@@ -257,6 +257,22 @@ void plan_stats(const TensorDesc *tensors, size_t n_desc, uint64_t n_tensors, ui
     s->tile_elems =
         s->scalar_elems * 8 <= s->n_params && C == kDefaultChunk ? kAdamTileFine : kTile;
     s->table_bytes = n_desc * sizeof(TensorDesc) + s->n_chunks * sizeof(Chunk);
+    if (s->tile_elems == kAdamTileFine) {
+        s->wg_per_cu = adam_per_cu(kAdamTileFine);
+        return;
+    }
+    // coarse tile: count the tiles that hold elements and those that do
+    // more than stream one full tile (a head, a tensor's partial last tile)
+    uint64_t work = 0, irregular = 0;
+    for (size_t k = 0; k < n_desc; k++) {
+        const TensorDesc &d = tensors[k];
+        const uint64_t h = d.vec == 4 ? std::min<uint64_t>(d.head, d.n) : 0, body = d.n - h;
+        const uint64_t t = body == 0 ? 1 : (body + kTile - 1) / kTile;
+        const uint64_t odd = (h > 0 ? 1u : 0u) + (body % kTile != 0 ? 1u : 0u);
+        work += t;
+        irregular += t == 1 ? std::min<uint64_t>(odd, 1) : odd;
+    }
+    s->wg_per_cu = adam_per_cu_coarse(work, irregular, s->n_params);
 }
 
 int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_elems,

@@ -81,6 +81,27 @@ static_assert(kMaxGrid * kWave <= 0xFFFFFFFFull, "grid size fits 32 bits");
 // the coarse tile at 7 (over 5..8) on flat shards of 117M-6.7G elements.
 inline uint32_t adam_per_cu(uint32_t tile) { return tile == kAdamTileFine ? 12u : 7u; }
 
+// The coarse tile's cap for a plan whose `work` tiles hold elements, of
+// which `irregular` hold a tensor's head or its partial last tile.  Such
+// tiles wait on memory more than once and carry fewer bytes, so a plan of
+// many of them needs more waves in flight: with fewer than one irregular
+// tile in 20 the cap stays at 7, else it is 7 * 512 / e + 7 within 14..28,
+// where e is the average element count of a tile with work.  Measured on
+// MI355X (lists in flattened buffers at their packed offsets, caps 7..28
+// and uncapped, one process each; fraction of 8 TB/s at the best cap
+// against cap 7): 100,000 x 1,024 (no irregular tiles) best at 7; 20,000
+// of 1-8,000 elements 0.655 at 14-18 against 0.608; 50,000 of 1-2,000
+// 0.673 at 14 against 0.531; 100,000 of 1-600 0.542 at 18-22 against
+// 0.325; 100,000 x 300 0.510 at 14 against 0.376; 100,000 x 100 0.461
+// uncapped (28) against 0.229.
+inline uint32_t adam_per_cu_coarse(uint64_t work, uint64_t irregular, uint64_t n_params) {
+    if (work == 0 || irregular * 20 < work)
+        return 7u;
+    const double e = (double)n_params / (double)work;
+    const double k = 7.0 * kTile / (e > 1.0 ? e : 1.0) + 7.0;
+    return k < 14.0 ? 14u : (k > 28.0 ? 28u : (uint32_t)(k + 0.5));
+}
+
 // Elements one wave of the parameter gather moves per tile: four 16-byte
 // loads per lane in flight on the widest path.
 constexpr uint32_t kGatherTile = 2048;

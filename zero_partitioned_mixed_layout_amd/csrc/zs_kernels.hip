@@ -21,8 +21,8 @@
 // workgroup, and each launch reserves dynamic LDS that the kernel never
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
-// tiles; reduce 4 when 16 slices are in flight per lane; fused 4; gather
-// 16).  Measured on
+// tiles, up to 28 for lists of small tensors; reduce 4 when 16 slices are
+// in flight per lane; fused 4; gather 16).  Measured on
 // MI355X, HBM3E streams these many-array patterns fastest with just enough
 // bytes in flight to cover latency (about 45 KB per CU); with the 20-30
 // waves per CU that registers alone would allow, the same streams run
@@ -1061,7 +1061,7 @@ int plan_create(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_e
     plan->d_chunks = nullptr;
     plan->stats = hp.stats;
     plan->device = dev;
-    plan->lds_cap = lds_cap_bytes(dev, zs::adam_per_cu((uint32_t)hp.stats.tile_elems));
+    plan->lds_cap = lds_cap_bytes(dev, (uint32_t)hp.stats.wg_per_cu);
     plan->bf16 = bf16;
     const size_t tb = hp.tensors.size() * sizeof(zs::TensorDesc);
     const size_t cb = hp.chunks.size() * sizeof(zs::Chunk);
@@ -1707,7 +1707,7 @@ extern "C" int zero_adam_step_noalloc(const zero_tensor *tensors, uint32_t n_ten
         if (hipGetLastError() != hipSuccess)
             return ZERO_EHIP;
     }
-    const size_t lds = lds_cap_bytes(dev, zs::adam_per_cu((uint32_t)stats.tile_elems));
+    const size_t lds = lds_cap_bytes(dev, (uint32_t)stats.wg_per_cu);
     return launch_adam_table(d_tensors, d_chunks, stats, lds, false, c, nonfinite_flag,
                              skip_if_nonzero, nullptr, st);
 }

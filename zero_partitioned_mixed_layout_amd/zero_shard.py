@@ -72,7 +72,7 @@ class _OffloadInfo(ctypes.Structure):
 class _Stats(ctypes.Structure):
     _fields_ = [(k, ctypes.c_uint64) for k in (
         "n_tensors", "n_params", "n_chunks", "chunk_elems", "vector_elems",
-        "scalar_elems", "table_bytes", "tile_elems")]
+        "scalar_elems", "table_bytes", "tile_elems", "wg_per_cu")]
 
 
 def _load() -> ctypes.CDLL:
