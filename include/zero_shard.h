@@ -106,7 +106,7 @@ typedef struct zero_plan_stats {
                                256 or 512 (see zero_plan_create) */
     uint64_t wg_per_cu;     /* one-wave workgroups of the step resident per CU
                                (its occupancy cap): 12 with 256-element
-                               tiles; with 512-element tiles 7, or 14-28 for
+                               tiles; with 512-element tiles 7, or 14-27 for
                                lists of small tensors (see zero_plan_create) */
 } zero_plan_stats;
 
@@ -186,8 +186,8 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * 256-element tiles, and with 512-element tiles 7 unless at least one
  * tile in 20 holds a head or a tensor's partial last tile, when the cap
  * grows as the tiles' average element count e shrinks, 7 * 512 / e + 7
- * within 14..28 (lists of small tensors wait on memory more per element;
- * measured up to twice as fast so).  The table is allocated on the current device
+ * within 14..27, 19 and 21 taken as 20 and 22 (lists of small tensors wait
+ * on memory more per element; measured up to twice as fast so).  The table is allocated on the current device
  * (hipMalloc) and filled with a synchronous copy; nothing else is
  * allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The

@@ -318,7 +318,8 @@ def _packed(zs, sizes):
 def test_plan_occupancy_cap(zs):
     """wg_per_cu: 12 with 256-element tiles; with 512-element tiles 7 while
     fewer than one tile in 20 holds a head or a partial last tile, else
-    7 * 512 / e + 7 within 14..28 (e: elements per tile with work)."""
+    7 * 512 / e + 7 within 14..27 (e: elements per tile with work), 19 and
+    21 taken as 20 and 22."""
     d = _packed(zs, [1 << 26])
     assert (d["tile_elems"], d["wg_per_cu"]) == (256, 12)
     d = _packed(zs, [n for _, n in W.WORKLOADS["gpt2_xl"].tensors])
@@ -326,11 +327,14 @@ def test_plan_occupancy_cap(zs):
     # whole tiles only: 7
     d = _packed(zs, [1024] * 1000)
     assert (d["tile_elems"], d["wg_per_cu"]) == (512, 7)
-    # one partial tile per tensor of 100 elements: e = 100, 7*512/100 + 7 > 28
+    # one partial tile per tensor of 100 elements: e = 100, 7*512/100 + 7 > 27
     d = _packed(zs, [100] * 1000)
-    assert (d["tile_elems"], d["wg_per_cu"]) == (512, 28)
-    # e = 300: round(7*512/300 + 7) = 19
-    assert _packed(zs, [300] * 1000)["wg_per_cu"] == 19
+    assert (d["tile_elems"], d["wg_per_cu"]) == (512, 27)
+    # e = 300: round(7*512/300 + 7) = 19, taken as 20
+    assert _packed(zs, [300] * 1000)["wg_per_cu"] == 20
+    # e = 250: round(21.3) = 21, taken as 22; e = 200: 24.9 -> 25
+    assert _packed(zs, [250] * 1000)["wg_per_cu"] == 22
+    assert _packed(zs, [200] * 1000)["wg_per_cu"] == 25
     # e = 400 (tensors of 800: two tiles, one partial): round(8.96 + 7) = 16
     assert _packed(zs, [800] * 1000)["wg_per_cu"] == 16
     # mostly whole tiles: 19 tensors of 512 and one of 100 per 20 tensors

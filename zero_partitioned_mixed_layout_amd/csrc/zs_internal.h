@@ -85,7 +85,8 @@ inline uint32_t adam_per_cu(uint32_t tile) { return tile == kAdamTileFine ? 12u 
 // which `irregular` hold a tensor's head or its partial last tile.  Such
 // tiles wait on memory more than once and carry fewer bytes, so a plan of
 // many of them needs more waves in flight: with fewer than one irregular
-// tile in 20 the cap stays at 7, else it is 7 * 512 / e + 7 within 14..28,
+// tile in 20 the cap stays at 7, else it is 7 * 512 / e + 7 within 14..27
+// (19 and 21 taken as 20 and 22, the counts their LDS reservation admits),
 // where e is the average element count of a tile with work.  Measured on
 // MI355X (lists in flattened buffers at their packed offsets, caps 7..28
 // and uncapped, one process each; fraction of 8 TB/s at the best cap
@@ -93,13 +94,16 @@ inline uint32_t adam_per_cu(uint32_t tile) { return tile == kAdamTileFine ? 12u 
 // of 1-8,000 elements 0.655 at 14-18 against 0.608; 50,000 of 1-2,000
 // 0.673 at 14 against 0.531; 100,000 of 1-600 0.542 at 18-22 against
 // 0.325; 100,000 x 300 0.510 at 14 against 0.376; 100,000 x 100 0.461
-// uncapped (28) against 0.229.
+// uncapped (28, as many as the kernel's registers allow) against 0.229.
 inline uint32_t adam_per_cu_coarse(uint64_t work, uint64_t irregular, uint64_t n_params) {
     if (work == 0 || irregular * 20 < work)
         return 7u;
     const double e = (double)n_params / (double)work;
     const double k = 7.0 * kTile / (e > 1.0 ? e : 1.0) + 7.0;
-    return k < 14.0 ? 14u : (k > 28.0 ? 28u : (uint32_t)(k + 0.5));
+    const uint32_t r = k < 14.0 ? 14u : (k > 27.0 ? 27u : (uint32_t)(k + 0.5));
+    // on a 160 KiB CU the LDS reservation for 19 or 21 also admits one
+    // more workgroup (no multiple of 256 bytes separates the two): say so
+    return r == 19u || r == 21u ? r + 1u : r;
 }
 
 // Elements one wave of the parameter gather moves per tile: four 16-byte

@@ -1007,7 +1007,9 @@ __global__ __launch_bounds__(kWave) void zs_gather_kernel(GatherArgs a, uint64_t
 // Dynamic LDS to reserve per one-wave workgroup so that at most `per_cu`
 // workgroups fit on a CU: the largest multiple of 256 bytes below
 // lds_per_cu / (per_cu + 1/2), so per_cu of them fit with room to spare and
-// one more does not.  Returns 0 (no cap) if the device does not say.
+// one more does not.  (On a 160 KiB CU that holds for per_cu up to 27
+// except 19 and 21, which admit 20 and 22; the callers ask for neither.)
+// Returns 0 (no cap) if the device does not say.
 size_t lds_cap_bytes(int device, uint32_t per_cu) {
     int lds_cu = 0, lds_block = 0;
     if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
