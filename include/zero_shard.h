@@ -48,7 +48,7 @@ extern "C" {
 
 /* Slices from which zero_reduce_adam_step runs the reduce and the Adam
  * kernels in sequence instead of its fused kernel. */
-#define ZERO_FUSED_SPLIT_SLICES 32
+#define ZERO_FUSED_SPLIT_SLICES 16
 
 /* Shard of a flat buffer of psi elements split over nd ranks. */
 typedef struct zero_layout {
@@ -373,7 +373,7 @@ int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
  *   g16 = fp16((s_0[i] + ... + s_{nd-1}[i]) / nd)   as zero_reduce_grad_shard
  *   then the Adam element of zero_adam_step with g = fp32(g16)
  * so the results are bit-identical to the two calls in sequence (without
- * a skip input).  Below ZERO_FUSED_SPLIT_SLICES (32) slices one kernel
+ * a skip input).  Below ZERO_FUSED_SPLIT_SLICES (16) slices one kernel
  * does it all, reading the slices and the fp32 state in one pass (4 bytes
  * per element less than the two calls); from there on, where its mix of state writes
  * into the slice reads costs more than it saves, the call runs the reduce

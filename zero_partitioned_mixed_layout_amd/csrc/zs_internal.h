@@ -143,12 +143,25 @@ inline uint32_t slices_in_flight(uint32_t nd) {
 }
 
 // Resident one-wave workgroups per CU for the reduction over nd slices:
-// about 64 16-byte vectors per lane in flight per CU (4 workgroups at 16
-// slices in flight, 8 at 8: the measured optima at N_d = 64 and 8), between
-// 2 and 8 workgroups.
+// about 64 16-byte vectors per lane in flight per CU, at most 16
+// workgroups (16 with 1-7 slices, 8 with 8-15), and with 16 slices in
+// flight 4, raised to 5 and 6 when a lane runs only two or one batch of 16
+// (a shorter-lived wave needs more of them).  Measured on MI355X over
+// 117,187,500 elements, one process per sweep of caps 3-32, fraction of
+// 8 TB/s at the chosen cap against the former one: N_d = 1 0.532 (16)
+// against 0.310 (8); 2 0.561 against 0.318; 3 0.579 against 0.329; 4 0.881
+// against 0.662; 5 0.866 against 0.587; 6 0.835 against 0.538; 7 0.803
+// against 0.506; 8 and 12 best at 8 (0.853, 0.831); 16 0.836 (6) against
+// 0.767 (4); 24 0.825 (5) against 0.786; 32 0.827 (5) against 0.816; 48
+// and 64 best at 4 (0.839, 0.837).
 inline uint32_t reduce_per_cu(uint32_t nd) {
-    const uint32_t k = (64 + slices_in_flight(nd) - 1) / slices_in_flight(nd);
-    return k < 2 ? 2 : (k > 8 ? 8 : k);
+    const uint32_t sif = slices_in_flight(nd);
+    if (sif < 16) {
+        const uint32_t k = (64 + sif - 1) / sif;
+        return k > 16 ? 16 : k;
+    }
+    const uint32_t batches = (nd + 15) / 16;
+    return batches == 1 ? 6 : (batches == 2 ? 5 : 4);
 }
 
 // Whether the fused step's 16-byte path loads a tile's fp32 state after the
@@ -159,22 +172,28 @@ inline uint32_t reduce_per_cu(uint32_t nd) {
 inline bool fused_state_late(uint32_t nd) { return slices_in_flight(nd) < 16; }
 
 // Slices from which zero_reduce_adam_step runs the reduce and then the Adam
-// step (two kernels) instead of the fused kernel.  Measured on MI355X, one
-// process, 117,187,500 elements, against the two kernels: the fused kernel
-// is 6.9% faster at N_d = 8, 6.1% at 12, 4.2% at 16 and 3.6% at 24, and
-// 1.9% slower at 32, 6.9% at 48 and 9.8% at 64 (its mix of state writes
-// into the slice reads costs more than the 4 bytes per element it saves).
+// step (two kernels) instead of the fused kernel.  Measured on MI355X,
+// 117,187,500 elements, one process per N_d, with the caps of this file,
+// fused kernel time over the two kernels': 0.816 at N_d = 1, 0.826 at 2,
+// 0.904 at 4, 0.965 at 8, 0.967 at 12; 1.016 at 16, 0.988 at 20, 1.007 at
+// 24, 1.034 at 28, 1.124 at 31 (from 16 slices its mix of state writes
+// into the slice reads costs about what the 4 bytes per element it saves
+// gain).
 constexpr uint32_t kFusedSplitSlices = ZERO_FUSED_SPLIT_SLICES;
 
 // Resident one-wave workgroups per CU for the fused reduce + Adam step.
 // State first: about 70 16-byte vectors per lane in flight per CU, counting
 // the six fp32 state vectors issued with the first slice batch (4 workgroups
 // at N_d >= 16, 5 at N_d = 8: the measured optima), between 2 and 8.  State
-// last: 6 at 8 slices in flight and 7 at 4 (measured over 5-8), else 8.
+// last: 6 at 8 slices in flight, 8 at 4 and 12 at one.  Measured on MI355X
+// over 117,187,500 elements, caps 6-24, one process per N_d (fraction of
+// 8 TB/s at 2 N_d + 26 bytes per element): N_d = 1 0.798 at 12 against
+// 0.770 at 8; 2 0.798 at 12 against 0.711 at 8; 4 0.801 at 8 against 0.783
+// at 7; 8 and 12 best at 6; 16 and 24 best at 4.
 inline uint32_t fused_per_cu(uint32_t nd, bool state_late) {
     const uint32_t sif = slices_in_flight(nd);
     if (state_late)
-        return sif == 8 ? 6u : (sif == 4 ? 7u : 8u);
+        return sif == 8 ? 6u : (sif == 4 ? 8u : 12u);
     const uint32_t per_wave = 6 + sif;
     const uint32_t k = (70 + per_wave - 1) / per_wave;
     return k < 2 ? 2 : (k > 8 ? 8 : k);

@@ -21,8 +21,8 @@
 // workgroup, and each launch reserves dynamic LDS that the kernel never
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
-// tiles, up to 28 for lists of small tensors; reduce 4 when 16 slices are
-// in flight per lane; fused 4; gather 16).  Measured on
+// tiles, 14-27 for lists of small tensors; reduce 4-6 when 16 slices are
+// in flight per lane, 8 at 8, 16 at fewer; fused 4; gather 16).  Measured on
 // MI355X, HBM3E streams these many-array patterns fastest with just enough
 // bytes in flight to cover latency (about 45 KB per CU); with the 20-30
 // waves per CU that registers alone would allow, the same streams run
@@ -37,6 +37,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <new>
@@ -1294,13 +1295,15 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     // 16-byte path: one vector group per lane, one wave per workgroup;
     // 8-byte path: one 512-element tile per wave (two groups per lane);
     // single elements: one 512-element tile per wave, half the bytes per
-    // wave in flight, so twice as many workgroups stay resident
+    // wave in flight, so twice as many workgroups stay resident (at most
+    // 24, a count the LDS reservation admits exactly)
     const uint64_t hh = head < n ? head : n;
     const uint64_t tiles4 = (n - hh + kTile - 1) / kTile + (n == hh ? 1 : 0);
     const uint64_t want = vec == 8 ? ((n - hh) / 8 + 1 + kWave - 1) / kWave
                           : vec == 4 ? tiles4 : (n + kTile - 1) / kTile;
     const uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
-    const uint32_t per_cu = zs::reduce_per_cu(nd) * (vec == 1 ? 2u : 1u);
+    const uint32_t per_cu = vec == 1 ? std::min(2u * zs::reduce_per_cu(nd), 24u)
+                                     : zs::reduce_per_cu(nd);
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)

@@ -31,7 +31,7 @@ ZERO_ERANGE = -6
 ZERO_NOALLOC_SCRATCH_BYTES = 8 << 20
 ZERO_NOALLOC_MAX_TENSORS = 1024
 ZERO_MAX_SLICES = 256
-ZERO_FUSED_SPLIT_SLICES = 32
+ZERO_FUSED_SPLIT_SLICES = 16
 ZERO_LOG2_SCALE_MAX = 100
 
 
