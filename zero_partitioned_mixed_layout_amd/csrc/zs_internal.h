@@ -164,6 +164,29 @@ inline uint32_t reduce_per_cu(uint32_t nd) {
     return batches == 1 ? 6 : (batches == 2 ? 5 : 4);
 }
 
+// The same for the reduce's other access paths.  vec = 4 (slices sharing
+// only an 8-byte phase; two 8-byte groups per lane per slice): 24 with one
+// slice in flight and 12 with eight, else as above.  vec = 1 (no common
+// phase; eight single elements per lane per slice, half the bytes): twice
+// the above, at most 24, except 8 with eight slices in flight.  Measured
+// on MI355X, 117,187,500 elements, caps 4-24 (fraction of 8 TB/s): 8-byte
+// path N_d = 2 0.685 at 24 against 0.602 at 16, N_d = 4 best at 16
+// (0.852), N_d = 8 0.802 at 12 against 0.774 at 8; single path N_d = 2
+// best at 24 (0.655), N_d = 4 0.703-0.713 at 12-24, N_d = 8 0.713 at 8
+// against 0.658 at 16.
+inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
+    const uint32_t sif = slices_in_flight(nd);
+    if (vec == 4)
+        return sif == 1 ? 24u : (sif == 8 ? 12u : reduce_per_cu(nd));
+    if (vec == 1) {
+        if (sif == 8)
+            return 8u;
+        const uint32_t k = 2u * reduce_per_cu(nd);
+        return k > 24u ? 24u : k;
+    }
+    return reduce_per_cu(nd);
+}
+
 // Whether the fused step's 16-byte path loads a tile's fp32 state after the
 // slices (then it arrives while the reduced gradients cross the LDS) instead
 // of with the first slice batch.  Measured on MI355X, one process, 937.5M

@@ -37,7 +37,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <new>
@@ -1295,15 +1294,13 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     // 16-byte path: one vector group per lane, one wave per workgroup;
     // 8-byte path: one 512-element tile per wave (two groups per lane);
     // single elements: one 512-element tile per wave, half the bytes per
-    // wave in flight, so twice as many workgroups stay resident (at most
-    // 24, a count the LDS reservation admits exactly)
+    // wave in flight, so more workgroups stay resident (reduce_per_cu_path)
     const uint64_t hh = head < n ? head : n;
     const uint64_t tiles4 = (n - hh + kTile - 1) / kTile + (n == hh ? 1 : 0);
     const uint64_t want = vec == 8 ? ((n - hh) / 8 + 1 + kWave - 1) / kWave
                           : vec == 4 ? tiles4 : (n + kTile - 1) / kTile;
     const uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
-    const uint32_t per_cu = vec == 1 ? std::min(2u * zs::reduce_per_cu(nd), 24u)
-                                     : zs::reduce_per_cu(nd);
+    const uint32_t per_cu = zs::reduce_per_cu_path(nd, vec);
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     if (vec == 8)
