@@ -17,7 +17,8 @@ in the same process and after the headline, the Adam step of the other
 7B-scale workloads and of GPT-2-XL (`per_config`: the N_d = 8 rank-3 shard
 with its infinities, the Llama-7B list, the GPT-2-XL list, each over its
 own resident state, freed before the next) and the N_d = 64 shard's Adam
-step with the fp16 parameter view at ranks 1 and 63 (`adam_by_rank`).
+step with the fp16 parameter view at ranks 1 and 63, and one element past
+rank 0's, out of the other arrays' phase (`adam_by_rank`).
 """
 from __future__ import annotations
 
@@ -515,19 +516,23 @@ def rounded(d: dict) -> dict:
     return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items() if k != "total_s"}
 
 
-def adam_by_rank(zs, torch, stream, step, ranks, steps, align=None):
+def adam_by_rank(zs, torch, stream, step, ranks, steps, align=None, shift=0):
     """The flat shard's Adam step with its fp16 parameter view placed at
     each rank's offset in the full buffer (gradient, master, m, v the same
     arrays): where the shard length is not a multiple of 64 elements, most
     ranks' views start off a 128-byte line.  align: the layout's unit
     (default the workload's); a rank whose shard is shorter than this one's
-    under it updates the first elements only."""
+    under it updates the first elements only.  shift: elements added to the
+    view's offset (1: the parameter out of the other arrays' 8-byte phase,
+    as a rank's view is under a layout whose shard length is odd); the
+    entry is then keyed "rank+shift"."""
     sh = step.tensors[0]
     wl = step.wl
     lays = {r: zs.zero_shard_layout(wl.psi, wl.nd, r, align or wl.align) for r in ranks}
     out = {}
     for r in ranks:
-        off, n = lays[r].offset, min(sh.n, lays[r].real_len)
+        off = lays[r].offset + shift
+        n = min(sh.n, lays[r].real_len, step.full.numel() - off)
         view = step.full[off:off + n]
         plan = zs.zero_plan_create([(view, sh.g[:n], sh.w[:n], sh.m[:n], sh.v[:n])])
 
@@ -539,9 +544,10 @@ def adam_by_rank(zs, torch, stream, step, ranks, steps, align=None):
             adam()
         _, ks = time_steps(torch, stream, [("zs_adam_kernel", adam, 28 * n)], steps)
         k = ks["zs_adam_kernel"]
-        out[str(r)] = {"byte_offset_in_line": (view.data_ptr() % 128), "params": n,
-                       "avg_us": round(k["avg_us"], 3), "gbps": round(k["gbps"], 3),
-                       "frac": round(k["frac"], 4)}
+        out[f"{r}+{shift}" if shift else str(r)] = {
+            "byte_offset_in_line": (view.data_ptr() % 128), "params": n,
+            "avg_us": round(k["avg_us"], 3), "gbps": round(k["gbps"], 3),
+            "frac": round(k["frac"], 4)}
         plan.destroy()
     return out
 
@@ -639,13 +645,16 @@ def main():
                          "frac": round(kstats["zs_adam_kernel"]["frac"], 4)}}
         by_rank.update(adam_by_rank(zs, torch, stream, step, (1, step.wl.nd - 1), pc_steps))
         slow = min(by_rank, key=lambda r: by_rank[r]["frac"])
+        # rank 0's view one element further: the parameter's stores shifted
+        shifted = adam_by_rank(zs, torch, stream, step, (0,), pc_steps, shift=1)
         # the same ranks under a layout whose unit is 64 elements: every
         # rank's view on a 128-byte line (the workload itself has unit 1)
         a64 = adam_by_rank(zs, torch, stream, step, (1, step.wl.nd - 1), pc_steps, align=64)
         by_rank = {"ranks": by_rank, "slowest_rank": int(slow),
                    "slowest_frac": by_rank[slow]["frac"], "steps": pc_steps,
                    "layout_align_64": {"ranks": a64, "slowest_frac":
-                                       min(v["frac"] for v in a64.values())}}
+                                       min(v["frac"] for v in a64.values())},
+                   "param_one_element_off": shifted["0+1"]}
     copy = plain_copy(stream)
     cpu = (None if args.no_cpu_baseline
            else cpu_baseline(step, args.cpu_sample, args.cpu_seconds))

@@ -100,7 +100,9 @@ typedef struct zero_plan_stats {
     uint64_t vector_elems;  /* elements moved four at a time (8-byte fp16 and
                                16-byte fp32 vectors) */
     uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
-                               tensors whose arrays disagree in alignment) */
+                               tensors whose arrays disagree in alignment,
+                               except a parameter alone on tensors of 1,024
+                               elements or more: see zero_plan_create) */
     uint64_t table_bytes;   /* device bytes of the chunk table */
     uint64_t tile_elems;    /* elements one 64-lane wave of the step updates:
                                256 or 512 (see zero_plan_create) */
@@ -171,25 +173,29 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * 512 (the faster of the two, measured, for such plans).
  * chunk_elems: 0 lets the library choose: the largest of 16384, 8192, ...,
  * 512 whose 512-element tiles (counted over every chunk, a tensor's last
- * chunk included) exceed those with work by at most one eighth, so
- * 16384 for big tensors and smaller chunks for many small ones; otherwise a
- * multiple of 512 between 512 and 2^24.  Per tensor the library takes the vector
- * path (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree
- * in alignment after peeling at most 3 leading elements, else it moves
- * single elements.  On the vector path, for a tensor of 1,024 elements or
- * more, the peeled head runs on to the element at which the tensor's
- * master, m and v reach a 1 KiB boundary, when they reach one at the same
- * element (at most 255 elements, done by the tensor's first tile), so that
- * its chunks and tiles start there: a list packed at offsets that are not
- * multiples of 256 elements streams about 3% faster so (measured).  The
- * step keeps wg_per_cu one-wave workgroups resident per CU: 12 with
- * 256-element tiles, and with 512-element tiles 7 unless at least one
- * tile in 20 holds a head or a tensor's partial last tile, when the cap
- * grows as the tiles' average element count e shrinks, 7 * 512 / e + 7
- * within 14..27, 19 and 21 taken as 20 and 22 (lists of small tensors wait
- * on memory more per element; measured up to twice as fast so).  The table is allocated on the current device
- * (hipMalloc) and filled with a synchronous copy; nothing else is
- * allocated later.
+ * chunk included) exceed those with work by at most one eighth, so 16384 for
+ * big tensors and smaller chunks for many small ones; otherwise a multiple
+ * of 512 between 512 and 2^24.  Per tensor the library takes the vector path
+ * (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree in
+ * alignment after peeling at most 3 leading elements; when only the
+ * parameter disagrees (a view of a full buffer at an offset that is not a
+ * multiple of four elements), on a tensor of 1,024 elements or more, it
+ * keeps the vector path and stores the parameter's 8-byte vectors shifted
+ * across lanes (measured 2-30% faster than single elements there, slower on
+ * smaller tensors); otherwise it moves single elements.  On the vector path,
+ * for a tensor of 1,024 elements or more, the peeled head runs on to the
+ * element at which the tensor's master, m and v reach a 1 KiB boundary, when
+ * they reach one at the same element (at most 255 elements, done by the
+ * tensor's first tile), so that its chunks and tiles start there: a list
+ * packed at offsets that are not multiples of 256 elements streams about 3%
+ * faster so (measured).  The step keeps wg_per_cu one-wave workgroups
+ * resident per CU: 12 with 256-element tiles, and with 512-element tiles 7
+ * unless at least one tile in 20 holds a head or a tensor's partial last
+ * tile, when the cap grows as the tiles' average element count e shrinks,
+ * 7 * 512 / e + 7 within 14..27, 19 and 21 taken as 20 and 22 (lists of
+ * small tensors wait on memory more per element; measured up to twice as
+ * fast so).  The table is allocated on the current device (hipMalloc) and
+ * filled with a synchronous copy; nothing else is allocated later.
  * Ownership: *out belongs to the caller until zero_plan_destroy.  The
  * tensors' memory stays the caller's and must outlive the plan.
  * Errors: EINVAL (NULL out or tensors with n_tensors > 0, a NULL array of

@@ -140,9 +140,25 @@ def test_plan_describe_paths(zs):
     # fp16 arrays 8-byte aligned but not 16: still the vector path
     d = zs.zero_plan_describe([_fake(100, 0x100008, 0x200008)])
     assert (d["vector_elems"], d["scalar_elems"]) == (100, 0)
-    # fp16 param one element off the grad's phase: single elements
+    # fp16 param one element off the grad's phase: single elements below
+    # 1,024 elements; from 1,024 the other arrays stay on the vector path
+    # (the parameter's stores shifted), for every phase of the parameter
     d = zs.zero_plan_describe([_fake(100, 0x100002)])
     assert (d["vector_elems"], d["scalar_elems"]) == (0, 100)
+    d = zs.zero_plan_describe([_fake(1023, 0x100002)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (0, 1023)
+    for p in (0x100002, 0x100004, 0x100006, 0x100102):
+        d = zs.zero_plan_describe([_fake(1024, p)])
+        assert (d["vector_elems"], d["scalar_elems"]) == (1024, 0), hex(p)
+        d = zs.zero_plan_describe([_fake(1027, p)])
+        assert (d["vector_elems"], d["scalar_elems"]) == (1024, 3), hex(p)
+    # the state two elements past 1 KiB: a head of 254 (2 singly), the
+    # parameter off by one more element
+    d = zs.zero_plan_describe([_fake(1030, 0x100006, 0x200004, 0x300008, 0x400008, 0x500008)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (1028, 2)
+    # the gradient off instead: single elements at any size
+    d = zs.zero_plan_describe([_fake(1 << 20, 1 << 40, (1 << 41) + 2, 1 << 42, 1 << 43, 1 << 44)])
+    assert (d["vector_elems"], d["scalar_elems"]) == (0, 1 << 20)
     # fp32 master one element off: single elements
     d = zs.zero_plan_describe([_fake(100, w=0x300004)])
     assert (d["vector_elems"], d["scalar_elems"]) == (0, 100)
@@ -341,8 +357,8 @@ def test_plan_occupancy_cap(zs):
     # (1 irregular tile in 20: the cap moves; 1 in 21 does not)
     assert _packed(zs, ([512] * 19 + [100]) * 50)["wg_per_cu"] == 14
     assert _packed(zs, ([512] * 20 + [100]) * 50)["wg_per_cu"] == 7
-    # single-element tensors of whole tiles (parameter one element off)
-    one_off = [((1 << 40) + (k << 20) + 2, (1 << 41) + (k << 20), (1 << 42) + (k << 20),
+    # single-element tensors of whole tiles (gradient one element off)
+    one_off = [((1 << 40) + (k << 20), (1 << 41) + (k << 20) + 2, (1 << 42) + (k << 20),
                 (1 << 43) + (k << 20), (1 << 44) + (k << 20), 1024) for k in range(100)]
     d = zs.zero_plan_describe(one_off)
     assert d["scalar_elems"] == 102400 and d["wg_per_cu"] == 7

@@ -67,13 +67,14 @@ class Carved:
     "bf16" parameters and gradients; log2_scale: gradients drawn 2^k times
     larger, for the step that unscales them."""
 
-    def __init__(self, torch, cases, v_shift, seed, fmt="f16", log2_scale=None):
+    def __init__(self, torch, cases, v_shift, seed, fmt="f16", log2_scale=None, p_shift=0):
         self.starts, at = [], 0
         for o, n in cases:
             self.starts.append(at + o)
-            at += (o + n + v_shift + 255) // 256 * 256 + 256
+            at += (o + n + max(v_shift, p_shift) + 255) // 256 * 256 + 256
         rng = np.random.default_rng(seed)
         self.cases, self.v_shift, self.fmt, self.k = cases, v_shift, fmt, log2_scale
+        self.p_shift = p_shift
         g = rng.standard_normal(at) * 1e-3 * 2.0 ** (log2_scale or 0)
         self.g = (g.astype(np.float16).view(np.uint16) if fmt == "f16"
                   else oracle.f32_to_bf16(g.astype(np.float32)))
@@ -91,14 +92,15 @@ class Carved:
         self.dv.copy_(to_dev32(self.v))
 
     def tensors(self):
-        vs = self.v_shift
-        return [(self.dp[s:s + n], self.dg[s:s + n], self.dw[s:s + n], self.dm[s:s + n],
-                 self.dv[s + vs:s + vs + n]) for s, (_, n) in zip(self.starts, self.cases)]
+        vs, ps = self.v_shift, self.p_shift
+        return [(self.dp[s + ps:s + ps + n], self.dg[s:s + n], self.dw[s:s + n],
+                 self.dm[s:s + n], self.dv[s + vs:s + vs + n])
+                for s, (_, n) in zip(self.starts, self.cases)]
 
     def oracle_step(self, t):
-        vs = self.v_shift
+        vs, ps = self.v_shift, self.p_shift
         for s, (_, n) in zip(self.starts, self.cases):
-            p, w, m = self.p[s:s + n], self.w[s:s + n], self.m[s:s + n]
+            p, w, m = self.p[s + ps:s + ps + n], self.w[s:s + n], self.m[s:s + n]
             v = self.v[s + vs:s + vs + n]
             if self.k is None:
                 flag = oracle.adam_step(self.g[s:s + n], p, w, m, v, t=t, fmt=self.fmt, **HP)
@@ -108,12 +110,19 @@ class Carved:
             assert flag == 0
 
     def compare(self, what):
-        vs = self.v_shift
+        """Not-bit-exact elements over every tensor; the parameter buffer
+        outside the views (never written) must still be all zero."""
+        vs, ps = self.v_shift, self.p_shift
         bad = 0
         gp, gw, gm, gv = host16(self.dp), host32(self.dw), host32(self.dm), host32(self.dv)
+        outside = np.ones(gp.size, bool)
+        for s, (_, n) in zip(self.starts, self.cases):
+            outside[s + ps:s + ps + n] = False
+        assert not gp[outside].any(), f"{what}: parameter bytes written outside the views"
         for k, (s, (o, n)) in enumerate(zip(self.starts, self.cases)):
             tag = f"{what} tensor {k} o={o} n={n}"
-            r = [check16(gp[s:s + n], self.p[s:s + n], tag + " param", fmt=self.fmt),
+            r = [check16(gp[s + ps:s + ps + n], self.p[s + ps:s + ps + n], tag + " param",
+                         fmt=self.fmt),
                  check32(gw[s:s + n], self.w[s:s + n], tag + " master"),
                  check32(gm[s:s + n], self.m[s:s + n], tag + " m"),
                  check32(gv[s + vs:s + vs + n], self.v[s + vs:s + vs + n], tag + " v")]

@@ -141,6 +141,23 @@ void pick_vector_path(const uintptr_t *f16, int n16, const uintptr_t *f32, int n
     *head = 0;
 }
 
+void adam_access_path(uintptr_t p, uintptr_t g, const uintptr_t a32[3], uint64_t n,
+                      TensorDesc *d) {
+    const uintptr_t a16[2] = {p, g};
+    d->pshift = 0;
+    pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
+    if (d->vec != 4 && n >= kTileAlignMinElems) {
+        // the parameter alone out of phase: everything else by vectors, and
+        // its stores shifted (its phase then differs from 0, the head's
+        // being the one that aligns the fp32 arrays)
+        pick_vector_path(&g, 1, a32, 3, 4, &d->vec, &d->head);
+        if (d->vec == 4)
+            d->pshift = (uint32_t)((p / 2u + d->head) % 4u);
+    }
+    if (d->vec == 4)
+        d->head = adam_head_of(a32, d->head, n);
+}
+
 uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head, uint64_t n) {
     if (n < kTileAlignMinElems)
         return vec_head;
@@ -215,17 +232,15 @@ int describe_tensor(const zero_tensor &t, TensorDesc *d, Range r[5]) {
     r[2] = {w, w + b4, true};
     r[3] = {m, m + b4, true};
     r[4] = {v, v + b4, true};
-    d->unused = 0;
+    memset(d, 0, sizeof(*d));
     d->p = (uint16_t *)t.param_f16;
     d->g = (const uint16_t *)t.grad_f16;
     d->w = t.master;
     d->m = t.m;
     d->v = t.v;
     d->n = t.n;
-    const uintptr_t a16[2] = {p, g}, a32[3] = {w, m, v};
-    pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
-    if (d->vec == 4)
-        d->head = adam_head_of(a32, d->head, t.n);
+    const uintptr_t a32[3] = {w, m, v};
+    adam_access_path(p, g, a32, t.n, d);
     return ZERO_OK;
 }
 

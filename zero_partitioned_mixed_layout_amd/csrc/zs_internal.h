@@ -22,7 +22,10 @@ struct TensorDesc {
     uint32_t vec;      // 4: four-element vector path; 1: single elements
     uint32_t head;     // leading elements peeled before the first tile (vector
                        // path: head % 4 singly, then by fours; see adam_head_of)
-    uint64_t unused;   // pads the descriptor to 64 bytes
+    uint32_t pshift;   // vector path: the parameter's element phase mod 4 at
+                       // the vector-aligned elements (0: its stores are 8-byte
+                       // vectors too; 1-3: see param_shift_of)
+    uint32_t unused;   // pads the descriptor to 64 bytes
 };
 static_assert(sizeof(TensorDesc) == 64, "TensorDesc is 64 bytes");
 
@@ -276,6 +279,25 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
 // the tensors' own offsets ran at 0.788 of 8 TB/s, tiles on 1 KiB at
 // 0.812-0.816, as fast as one flat tensor of the same size.
 uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head, uint64_t n);
+
+// The Adam step's access path for a tensor of n elements (its parameter p,
+// gradient g and fp32 master, m, v at a32): sets d->vec, d->head and
+// d->pshift.  The vector path when all five arrays agree in phase after
+// peeling at most 3 elements (pshift 0); else, on a tensor of
+// kTileAlignMinElems or more whose gradient and fp32 arrays agree, the
+// vector path with the parameter, which is only written, stored shifted
+// (pshift 1-3: its element phase mod 4 at the vector-aligned elements);
+// otherwise single elements (vec 1).  A ZeRO rank's parameter is often a
+// view of the full buffer at an offset that is not a multiple of four
+// elements.  Measured on MI355X with the parameter 1-3 elements off, plans
+// over the same buffers in one process (fraction of 8 TB/s, shifted
+// against single): one tensor of 117,187,500 elements 0.747-0.764 against
+// 0.682-0.692; the GPT-2-XL list 0.738-0.751 against 0.560-0.570; random
+// sizes 1-8,192 0.637 against 0.607 and 1-100,000 0.660 against 0.643.
+// Below 1,024 elements single elements were faster (random sizes 1-1,024:
+// 0.616 with the rule against 0.551 shifted).
+void adam_access_path(uintptr_t p, uintptr_t g, const uintptr_t a32[3], uint64_t n,
+                      TensorDesc *d);
 
 // One non-empty tensor: its descriptor (vector path and peeled head) and the
 // byte ranges of its five arrays (param, grad, master, m, v).  Errors:

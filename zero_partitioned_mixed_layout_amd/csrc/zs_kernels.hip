@@ -8,8 +8,10 @@
 // parameter; reduce: 2 N_d + 2 bytes; fused: 2 N_d + 26; gather: 4), so they
 // use no matrix cores.  Every load and store instruction of a 64-lane wave
 // covers one contiguous range (Adam: 512 bytes of fp16 or 1 KiB of fp32;
-// reduce: 1 KiB of fp16), and streamed data moves with the nontemporal hint
-// (the reduce's sparse output stream writes through L2 instead: st_through).
+// reduce: 1 KiB of fp16; a parameter out of the other arrays' phase goes
+// through a cross-lane permute into aligned 8-byte vectors), and streamed
+// data moves with the nontemporal hint (the reduce's sparse output stream
+// writes through L2 instead: st_through).
 // On gfx950 nontemporal stores only stream at full rate when each
 // instruction writes whole lines, which is why a lane's four-element groups
 // of a wave tile are adjacent to its neighbours' (a 512-element tile
@@ -22,11 +24,11 @@
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
 // tiles, 14-27 for lists of small tensors; reduce 4-6 when 16 slices are
-// in flight per lane, 8 at 8, 16 at fewer; fused 4; gather 16).  Measured on
-// MI355X, HBM3E streams these many-array patterns fastest with just enough
-// bytes in flight to cover latency (about 45 KB per CU); with the 20-30
-// waves per CU that registers alone would allow, the same streams run
-// 10-15% slower.
+// in flight per lane, 8 at 8, 16 at fewer; fused 5-12, twice that on its
+// single-element path; gather 16).  Measured on MI355X, HBM3E streams these
+// many-array patterns fastest with just enough bytes in flight to cover
+// latency (about 45 KB per CU); with the 20-30 waves per CU that registers
+// alone would allow, the same streams run 10-15% slower.
 //
 // Exactness: every arithmetic step is one IEEE binary32 operation in a fixed
 // order; the library is built with -ffp-contract=off (no fused multiply-add),
@@ -203,9 +205,12 @@ __device__ __forceinline__ void quad_load(const TensorDesc &T, uint64_t i, Quad<
     q.v = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
 }
 
+// The update of four elements held in registers; stores the fp32 state and
+// returns the new parameter.
 template <class Fmt>
-__device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t i, Quad<Fmt> &q,
-                                                  const AdamConsts &c, int &bad) {
+__device__ __forceinline__ typename Fmt::V4 quad_update(const TensorDesc &T, uint64_t i,
+                                                        Quad<Fmt> &q, const AdamConsts &c,
+                                                        int &bad) {
     typename Fmt::V4 p;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -219,15 +224,100 @@ __device__ __forceinline__ void quad_update_store(const TensorDesc &T, uint64_t 
     st_nt(q.w, reinterpret_cast<f32x4 *>(T.w + i));
     st_nt(q.m, reinterpret_cast<f32x4 *>(T.m + i));
     st_nt(q.v, reinterpret_cast<f32x4 *>(T.v + i));
-    st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + i));
+    return p;
+}
+
+// Stores of a parameter that is s = T.pshift elements (1-3) out of the
+// state's phase.  Lane L holds the new values of elements 4L..4L+3 of a run
+// from the vector-aligned element `base`; the parameter's 8-byte vectors
+// start at elements 4L - s.  Lane L >= 1 joins the last s values of lane
+// L - 1 (a cross-lane permute) with its own first 4 - s and stores one
+// aligned vector; the run's first 4 - s and last s elements, whose vectors
+// the neighbouring elements share, go singly.  Every byte written belongs
+// to the run's own elements.
+
+// The vector that starts s elements before this lane's group: the last s
+// values of `src` as lane L - 1 holds it, then the first 4 - s of `own`.
+__device__ __forceinline__ uint64_t join_shifted(uint64_t own, uint64_t src, uint32_t lane,
+                                                 uint32_t s) {
+    const int from = (int)(((lane + kWave - 1u) % kWave) * 4u); // lane 0's is unused
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)(uint32_t)src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)(uint32_t)(src >> 32));
+    const uint64_t prev = ((uint64_t)hi << 32) | lo;
+    return (prev >> (16u * (4u - s))) | (own << (16u * s));
+}
+
+// The run's edges: the first 4 - s values of lane 0's group `first_vals`
+// at `first_at`, the last s of lane `last_lane`'s at `last_at`.
+__device__ __forceinline__ void store_edges(uint16_t *p, uint32_t lane, uint32_t s,
+                                            uint32_t last_lane, uint64_t vals, uint64_t at) {
+    uint16_t b[4];
+    memcpy(b, &vals, 8);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; j++)
+        if (j < 4u - s ? lane == 0 : lane == last_lane)
+            st_nt(b[j], p + at + j);
+}
+
+// nq <= 64 groups held by lanes 0..nq-1 (exactly these lanes take part):
+// a tensor's head or the groups of a partial tile.
+template <class Fmt>
+__device__ __forceinline__ void param_store_shifted(const TensorDesc &T, uint64_t base,
+                                                    uint32_t lane, uint32_t nq,
+                                                    typename Fmt::V4 p) {
+    uint64_t own;
+    memcpy(&own, &p, 8);
+    const uint64_t joined = join_shifted(own, own, lane, T.pshift);
+    if (lane != 0)
+        st_nt(joined, reinterpret_cast<uint64_t *>(T.p + base + 4u * lane - T.pshift));
+    store_edges(T.p, lane, T.pshift, nq - 1u, own, base + 4u * lane);
+}
+
+// The same for nq <= 64 groups held by lanes 0..nq-1 in the state's phase
+// (SHIFT false: one 8-byte vector per lane) or out of it.  SHIFT is
+// T.pshift != 0, decided once per tile so that the aligned path's code is
+// the same as it would be without the shifted one.
+template <class Fmt, bool SHIFT>
+__device__ __forceinline__ void param_store_quads(const TensorDesc &T, uint64_t base,
+                                                  uint32_t lane, uint32_t nq,
+                                                  typename Fmt::V4 p) {
+    if constexpr (SHIFT)
+        param_store_shifted<Fmt>(T, base, lane, nq, p);
+    else
+        st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + base + 4u * lane));
+}
+
+// A full tile of Q runs of 256 (lane L: elements 4L..4L+3 of each run from
+// `base`), out of phase: lane 0 of run k >= 1 joins the last s values of
+// run k - 1, which lane 63 hands it through the same permute, and stores a
+// whole vector, so that only the tile's first 4 - s and last s elements go
+// singly.
+template <class Fmt, int Q>
+__device__ __forceinline__ void param_store_tile(const TensorDesc &T, uint64_t base,
+                                                 uint32_t lane, const typename Fmt::V4 (&p)[Q]) {
+    const uint32_t s = T.pshift;
+    uint64_t own[Q];
+    memcpy(own, p, sizeof(own));
+#pragma unroll
+    for (int k = 0; k < Q; k++) {
+        const uint64_t src = k > 0 && lane == kWave - 1u ? own[(k + Q - 1) % Q] : own[k];
+        const uint64_t joined = join_shifted(own[k], src, lane, s);
+        if (k > 0 || lane != 0)
+            st_nt(joined, reinterpret_cast<uint64_t *>(T.p + base + 4u * kWave * k +
+                                                       4u * lane - s));
+    }
+    const bool first = lane == 0;
+    store_edges(T.p, lane, s, kWave - 1u, first ? own[0] : own[Q - 1],
+                base + (first ? 0u : 4u * kWave * (Q - 1)) + 4u * lane);
 }
 
 // A full Adam tile: TILE consecutive elements from `base` (vector-aligned),
 // TILE / 256 groups of four per lane.  Lane L takes elements 4L..4L+3 of
 // every 256, so each of the wave's load and store instructions covers one
-// contiguous 512-byte (16-bit) or 1-KiB (fp32) range.  All loads are issued
+// contiguous 512-byte (16-bit) or 1-KiB (fp32) range (a shifted
+// parameter's store: 504 bytes, plus its edges).  All loads are issued
 // before any arithmetic.
-template <class Fmt, uint32_t TILE>
+template <class Fmt, uint32_t TILE, bool SHIFT>
 __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, uint32_t lane,
                                           const AdamConsts &c, int &bad) {
     constexpr int Q = TILE / (4 * kWave);
@@ -237,9 +327,20 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
     for (int k = 0; k < Q; k++)
         quad_load<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k]);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SHIFT) {
 #pragma unroll
-    for (int k = 0; k < Q; k++)
-        quad_update_store<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k], c, bad);
+        for (int k = 0; k < Q; k++) {
+            const uint64_t i = base + 4u * lane + 4u * kWave * k;
+            st_nt(quad_update<Fmt>(T, i, a[k], c, bad),
+                  reinterpret_cast<typename Fmt::V4 *>(T.p + i));
+        }
+    } else {
+        typename Fmt::V4 p[Q];
+#pragma unroll
+        for (int k = 0; k < Q; k++)
+            p[k] = quad_update<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k], c, bad);
+        param_store_tile<Fmt, Q>(T, base, lane, p);
+    }
 }
 
 // The peeled head of a tensor on the vector path: its first `count`
@@ -247,7 +348,7 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
 // precede the first aligned vector), then at most 63 groups of four, one per
 // lane; a tensor that ends inside its head does its last fewer-than-four
 // singly.
-template <class Fmt>
+template <class Fmt, bool SHIFT>
 __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
                                           const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
@@ -257,8 +358,10 @@ __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
     const uint32_t nquads = (count - singles) / 4u;
     if (lane < nquads) {
         Quad<Fmt> x;
-        quad_load<Fmt>(T, singles + 4u * lane, x);
-        quad_update_store<Fmt>(T, singles + 4u * lane, x, c, bad);
+        const uint64_t i = singles + 4u * lane;
+        quad_load<Fmt>(T, i, x);
+        param_store_quads<Fmt, SHIFT>(T, singles, lane, nquads,
+                                      quad_update<Fmt>(T, i, x, c, bad));
     }
     const uint32_t rest = count - singles - 4u * nquads;
     if (lane < rest)
@@ -270,19 +373,20 @@ __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
 // or more, else only to the first aligned vector) rides in its first chunk
 // and is done by tile 0; every other chunk starts at the head plus a whole
 // number of tiles.  The chunk's last, partial tile goes four elements per
-// lane, then the final fewer-than-four singly.
-template <class Fmt, uint32_t TILE>
+// lane, then the final fewer-than-four singly.  SHIFT: the parameter is out
+// of the other arrays' phase (T.pshift != 0) and its stores are shifted.
+template <class Fmt, uint32_t TILE, bool SHIFT>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
     const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
     if (j == 0 && head != 0)
-        adam_head<Fmt>(T, head, c, bad);
+        adam_head<Fmt, SHIFT>(T, head, c, bad);
     const uint64_t base = ch.start + head;
     const uint32_t body = ch.count - head;
     const uint32_t nfull = body / TILE;
     if (j < nfull) {
-        adam_tile<Fmt, TILE>(T, base + (uint64_t)j * TILE, lane, c, bad);
+        adam_tile<Fmt, TILE, SHIFT>(T, base + (uint64_t)j * TILE, lane, c, bad);
         return;
     }
     if (j > nfull)
@@ -290,10 +394,24 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
     const uint64_t rbase = base + (uint64_t)nfull * TILE;
     const uint32_t rem = body - nfull * TILE; // < TILE
     const uint32_t nquads = rem / 4u;
-    for (uint32_t q = lane; q < nquads; q += kWave) {
-        Quad<Fmt> x;
-        quad_load<Fmt>(T, rbase + 4u * q, x);
-        quad_update_store<Fmt>(T, rbase + 4u * q, x, c, bad);
+    if constexpr (SHIFT) {
+        for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
+            const uint32_t nq = min(nquads - r0, kWave);
+            if (lane < nq) {
+                Quad<Fmt> x;
+                const uint64_t run = rbase + 4u * r0, i = run + 4u * lane;
+                quad_load<Fmt>(T, i, x);
+                param_store_quads<Fmt, true>(T, run, lane, nq,
+                                             quad_update<Fmt>(T, i, x, c, bad));
+            }
+        }
+    } else {
+        for (uint32_t q = lane; q < nquads; q += kWave) {
+            Quad<Fmt> x;
+            const uint64_t i = rbase + 4u * q;
+            quad_load<Fmt>(T, i, x);
+            param_store_quads<Fmt, false>(T, rbase, q, 0, quad_update<Fmt>(T, i, x, c, bad));
+        }
     }
     const uint32_t tail = rem - 4u * nquads;
     if (lane < tail)
@@ -366,10 +484,12 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
         const uint32_t j = (uint32_t)(vb - ci * tiles_per_chunk);
         const Chunk ch = chunks[ci];
         const TensorDesc T = tensors[ch.tensor];
-        if (T.vec == 4)
-            adam_tile_of_chunk<Fmt, TILE>(T, ch, j, c, bad);
-        else
+        if (T.vec != 4)
             adam_tile_single<Fmt, TILE>(T, ch, j, c, bad);
+        else if (T.pshift == 0)
+            adam_tile_of_chunk<Fmt, TILE, false>(T, ch, j, c, bad);
+        else
+            adam_tile_of_chunk<Fmt, TILE, true>(T, ch, j, c, bad);
     }
     raise_flag(flag, bad);
 }
@@ -396,10 +516,12 @@ __global__ __launch_bounds__(kWave) void zs_adam_flat_kernel(TensorDesc T, uint6
         ch.tensor = 0;
         ch.start = b == 0 ? 0 : h + b * TILE;
         ch.count = b == ntiles - 1 ? last_count : (b == 0 ? first_count : TILE);
-        if (T.vec == 4)
-            adam_tile_of_chunk<Fmt, TILE>(T, ch, 0, c, bad);
-        else
+        if (T.vec != 4)
             adam_tile_single<Fmt, TILE>(T, ch, 0, c, bad);
+        else if (T.pshift == 0)
+            adam_tile_of_chunk<Fmt, TILE, false>(T, ch, 0, c, bad);
+        else
+            adam_tile_of_chunk<Fmt, TILE, true>(T, ch, 0, c, bad);
     }
     raise_flag(flag, bad);
 }
@@ -1347,11 +1469,8 @@ int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *
     T.m = m;
     T.v = v;
     T.n = n;
-    const uintptr_t a16[2] = {(uintptr_t)p, (uintptr_t)g};
     const uintptr_t a32[3] = {(uintptr_t)w, (uintptr_t)m, (uintptr_t)v};
-    zs::pick_vector_path(a16, 2, a32, 3, 4, &T.vec, &T.head);
-    if (T.vec == 4)
-        T.head = zs::adam_head_of(a32, T.head, n);
+    zs::adam_access_path((uintptr_t)p, (uintptr_t)g, a32, n, &T);
     const uint32_t tile = T.vec == 4 ? kAdamTileFine : kTile;
     // tiles: the first holds the peeled head (vector path) and up to `tile`
     // elements, every later one `tile` elements, the last what is left
