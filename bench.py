@@ -157,6 +157,11 @@ def parse():
     ap.add_argument("--param-rank", type=int, default=None,
                     help="flat workloads: place the fp16 parameter view of the shard at this "
                          "rank's offset in the full buffer (the other arrays unchanged)")
+    ap.add_argument("--param-shift", type=int, default=0, metavar="ELEMS",
+                    help="flat workloads: move the fp16 parameter view this many elements "
+                         "further into the full buffer (1-3: out of the other arrays' 8-byte "
+                         "phase, as a rank's view is when the shard length is not a multiple "
+                         "of four)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the step: copy a BYTES-byte device buffer into another "
                          "with torch, --steps times (the plain copy kernel that scales the "
@@ -211,7 +216,8 @@ class Step:
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
-                 slices=False, inject_inf=False, loss_scale=None, param_rank=None):
+                 slices=False, inject_inf=False, loss_scale=None, param_rank=None,
+                 param_shift=0):
         import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
@@ -227,13 +233,16 @@ class Step:
             self.layout = lay
             self.full, sh = W.device_flat_state(wl, lay.offset, lay.real_len, lay.padded_total,
                                                 half=half)
-            if param_rank is not None:
+            if param_rank is not None or param_shift:
                 # the same shard state, its fp16 parameter view at another
                 # rank's place in the full buffer (a view off its lines for
-                # most ranks when the shard length is not a multiple of 64)
-                off = param_rank * lay.shard_len
-                if not 0 <= param_rank < wl.nd or off + lay.real_len > lay.padded_total:
-                    raise SystemExit(f"--param-rank {param_rank}: outside the layout")
+                # most ranks when the shard length is not a multiple of 64),
+                # param_shift elements further
+                r = wl.rank if param_rank is None else param_rank
+                off = r * lay.shard_len + param_shift
+                if not 0 <= r < wl.nd or off < 0 or off + lay.real_len > lay.padded_total:
+                    raise SystemExit(f"--param-rank {param_rank} --param-shift {param_shift}: "
+                                     "outside the layout")
                 sh.p = self.full[off:off + lay.real_len]
             self.tensors = [sh]
             if wl.reduce_slices or slices:
@@ -612,7 +621,8 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
                 args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
-                args.slices, args.inject_inf, args.loss_scale, args.param_rank)
+                args.slices, args.inject_inf, args.loss_scale, args.param_rank,
+                args.param_shift)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -625,7 +635,7 @@ def main():
     dom = max(kstats, key=lambda k: kstats[k]["total_s"])
     d = kstats[dom]
     traffic = (measured_traffic(dom, args.workload)
-               if args.param_rank is None and not args.bf16 else None)
+               if args.param_rank is None and not args.param_shift and not args.bf16 else None)
     if traffic is None:
         print(f"[bench] no HBM counters for {dom} on {args.workload} taken on the current kernel "
               f"code ({kernel_src_sha()}): traffic is null", file=sys.stderr, flush=True)
@@ -634,7 +644,8 @@ def main():
     # the headline configuration's other extras, while its state is resident
     headline_plain = (not args.no_per_config and args.workload == "flat_7p5b_nd64" and
                       not (args.fused or args.gather or args.offload or args.bf16 or
-                           args.loss_scale is not None or args.param_rank is not None))
+                           args.loss_scale is not None or args.param_rank is not None or
+                           args.param_shift))
     pc_steps = args.per_config_steps or max(10, args.steps)
     by_rank = None
     if headline_plain:
@@ -665,7 +676,8 @@ def main():
            ("+fused" if step.fused else "") +
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
            ("+bf16" if args.bf16 else "") +
-           (f"+param_rank_{args.param_rank}" if args.param_rank is not None else ""),
+           (f"+param_rank_{args.param_rank}" if args.param_rank is not None else "") +
+           (f"+param_shift_{args.param_shift}" if args.param_shift else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),

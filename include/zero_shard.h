@@ -101,8 +101,8 @@ typedef struct zero_plan_stats {
                                16-byte fp32 vectors) */
     uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
                                tensors whose arrays disagree in alignment,
-                               except a parameter alone on tensors of 1,024
-                               elements or more: see zero_plan_create) */
+                               except the 16-bit arrays alone on tensors of
+                               1,024 elements or more: see zero_plan_create) */
     uint64_t table_bytes;   /* device bytes of the chunk table */
     uint64_t tile_elems;    /* elements one 64-lane wave of the step updates:
                                256 or 512 (see zero_plan_create) */
@@ -178,11 +178,12 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * of 512 between 512 and 2^24.  Per tensor the library takes the vector path
  * (8-byte fp16 and 16-byte fp32 accesses) when all five arrays agree in
  * alignment after peeling at most 3 leading elements; when only the
- * parameter disagrees (a view of a full buffer at an offset that is not a
+ * 16-bit arrays disagree (views of full buffers at an offset that is not a
  * multiple of four elements), on a tensor of 1,024 elements or more, it
- * keeps the vector path and stores the parameter's 8-byte vectors shifted
- * across lanes (measured 2-30% faster than single elements there, slower on
- * smaller tensors); otherwise it moves single elements.  On the vector path,
+ * keeps the vector path, stores the parameter's 8-byte vectors shifted
+ * across lanes and reads the gradient's four values per lane from two
+ * whole aligned 8-byte words (measured 2-30% faster than single elements
+ * there, slower on smaller tensors); otherwise it moves single elements.  On the vector path,
  * for a tensor of 1,024 elements or more, the peeled head runs on to the
  * element at which the tensor's master, m and v reach a 1 KiB boundary, when
  * they reach one at the same element (at most 255 elements, done by the
@@ -348,9 +349,12 @@ int zero_loss_scale_update(zero_loss_scale *scale, int32_t *nonfinite_flag,
  * nonfinite_flag: NULL or a device int32; 1 is OR-ed into it if any output
  *   is infinite or NaN.
  * Asynchronous; allocates nothing.  n = 0 launches nothing.
- * Fastest with every slice 16-byte aligned at the same phase as out; slices
- * spaced an exact power of two apart (256 MiB, say) read about a fifth
- * slower than with a few KiB more between them.
+ * Fastest with every slice 16-byte aligned at the same phase as out; with
+ * out alone 1-3 elements out of the slices' phase (and n >= 1,024), the
+ * slices keep their vector loads and out is stored shifted across lanes
+ * (measured 0.77-0.78 of 8 TB/s against 0.64-0.66 element by element).
+ * Slices spaced an exact power of two apart (256 MiB, say) read about a
+ * fifth slower than with a few KiB more between them.
  * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not
  * 2-byte aligned, out overlapping a slice); EHIP.
  */
@@ -386,6 +390,10 @@ int zero_reduce_grad_shard_bf16(const void *const *slices_bf16, uint32_t nd,
  * kernel and then the Adam kernel, with the fp16 gradient passing through
  * grad_out_f16, or without it through param_f16, which then holds the
  * gradient until the Adam kernel overwrites it with the new parameter.
+ * The 16-bit outputs may be out of phase with the slices and the state (a
+ * parameter view at an offset that is not a multiple of four elements):
+ * from 1,024 elements both routes keep their vector loads and store them
+ * shifted, and the Adam kernel reads a gradient held in param_f16 shifted.
  * slices_f16: host array of nd device pointers to n fp16 each (read only).
  * param_f16: n fp16, written.  master, m, v: n fp32 each, updated in place.
  * grad_out_f16: NULL, or n fp16 that receive g16.

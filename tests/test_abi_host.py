@@ -156,8 +156,16 @@ def test_plan_describe_paths(zs):
     # parameter off by one more element
     d = zs.zero_plan_describe([_fake(1030, 0x100006, 0x200004, 0x300008, 0x400008, 0x500008)])
     assert (d["vector_elems"], d["scalar_elems"]) == (1028, 2)
-    # the gradient off instead: single elements at any size
-    d = zs.zero_plan_describe([_fake(1 << 20, 1 << 40, (1 << 41) + 2, 1 << 42, 1 << 43, 1 << 44)])
+    # the gradient off instead, or both 16-bit arrays: the vector path from
+    # 1,024 elements (the gradient's loads shifted too), single below
+    for g, p in (((1 << 41) + 2, 1 << 40), ((1 << 41) + 6, (1 << 40) + 2)):
+        d = zs.zero_plan_describe([_fake(1 << 20, p, g, 1 << 42, 1 << 43, 1 << 44)])
+        assert (d["vector_elems"], d["scalar_elems"]) == (1 << 20, 0)
+        d = zs.zero_plan_describe([_fake(1000, p, g, 1 << 42, 1 << 43, 1 << 44)])
+        assert (d["vector_elems"], d["scalar_elems"]) == (0, 1000)
+    # the fp32 arrays disagreeing: single elements at any size
+    d = zs.zero_plan_describe([_fake(1 << 20, 1 << 40, 1 << 41, 1 << 42, (1 << 43) + 4,
+                                     1 << 44)])
     assert (d["vector_elems"], d["scalar_elems"]) == (0, 1 << 20)
     # fp32 master one element off: single elements
     d = zs.zero_plan_describe([_fake(100, w=0x300004)])
@@ -357,9 +365,9 @@ def test_plan_occupancy_cap(zs):
     # (1 irregular tile in 20: the cap moves; 1 in 21 does not)
     assert _packed(zs, ([512] * 19 + [100]) * 50)["wg_per_cu"] == 14
     assert _packed(zs, ([512] * 20 + [100]) * 50)["wg_per_cu"] == 7
-    # single-element tensors of whole tiles (gradient one element off)
-    one_off = [((1 << 40) + (k << 20), (1 << 41) + (k << 20) + 2, (1 << 42) + (k << 20),
-                (1 << 43) + (k << 20), (1 << 44) + (k << 20), 1024) for k in range(100)]
+    # single-element tensors of whole tiles (m one element off)
+    one_off = [((1 << 40) + (k << 20), (1 << 41) + (k << 20), (1 << 42) + (k << 20),
+                (1 << 43) + (k << 20) + 4, (1 << 44) + (k << 20), 1024) for k in range(100)]
     d = zs.zero_plan_describe(one_off)
     assert d["scalar_elems"] == 102400 and d["wg_per_cu"] == 7
 

@@ -44,9 +44,11 @@ LAYOUTS = {
     "mixed": ((4, 4), 0, 4, 0, 0, 0),     # 16-byte slice loads after a head of 4
     "split": ((0, 4), 0, 0, 0, 0, 0),     # slices agree only mod 8 bytes: 8-byte loads
     "odd": ((1, 1), 0, 0, 0, 0, 0),       # no common phase: single elements
-    # parameter and gradient output one element off the state: single
-    # elements in the fused kernel; from ZERO_FUSED_SPLIT_SLICES slices a
-    # single-element reduce and the one-tensor Adam kernel's single path
+    # parameter and gradient output one element off the state: the fused
+    # kernel stores both shifted across lanes from 1,024 elements (single
+    # elements below); from ZERO_FUSED_SPLIT_SLICES slices a single-element
+    # reduce and the one-tensor Adam kernel's single path (its gradient,
+    # the reduce's output, is off too)
     "param_off": ((0, 0), 1, 1, 0, 0, 0),
 }
 

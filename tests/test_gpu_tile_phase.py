@@ -67,14 +67,15 @@ class Carved:
     "bf16" parameters and gradients; log2_scale: gradients drawn 2^k times
     larger, for the step that unscales them."""
 
-    def __init__(self, torch, cases, v_shift, seed, fmt="f16", log2_scale=None, p_shift=0):
+    def __init__(self, torch, cases, v_shift, seed, fmt="f16", log2_scale=None, p_shift=0,
+                 g_shift=0):
         self.starts, at = [], 0
         for o, n in cases:
             self.starts.append(at + o)
-            at += (o + n + max(v_shift, p_shift) + 255) // 256 * 256 + 256
+            at += (o + n + max(v_shift, p_shift, g_shift) + 255) // 256 * 256 + 256
         rng = np.random.default_rng(seed)
         self.cases, self.v_shift, self.fmt, self.k = cases, v_shift, fmt, log2_scale
-        self.p_shift = p_shift
+        self.p_shift, self.g_shift = p_shift, g_shift
         g = rng.standard_normal(at) * 1e-3 * 2.0 ** (log2_scale or 0)
         self.g = (g.astype(np.float16).view(np.uint16) if fmt == "f16"
                   else oracle.f32_to_bf16(g.astype(np.float32)))
@@ -92,21 +93,21 @@ class Carved:
         self.dv.copy_(to_dev32(self.v))
 
     def tensors(self):
-        vs, ps = self.v_shift, self.p_shift
-        return [(self.dp[s + ps:s + ps + n], self.dg[s:s + n], self.dw[s:s + n],
+        vs, ps, gs = self.v_shift, self.p_shift, self.g_shift
+        return [(self.dp[s + ps:s + ps + n], self.dg[s + gs:s + gs + n], self.dw[s:s + n],
                  self.dm[s:s + n], self.dv[s + vs:s + vs + n])
                 for s, (_, n) in zip(self.starts, self.cases)]
 
     def oracle_step(self, t):
-        vs, ps = self.v_shift, self.p_shift
+        vs, ps, gs = self.v_shift, self.p_shift, self.g_shift
         for s, (_, n) in zip(self.starts, self.cases):
             p, w, m = self.p[s + ps:s + ps + n], self.w[s:s + n], self.m[s:s + n]
-            v = self.v[s + vs:s + vs + n]
+            v, g = self.v[s + vs:s + vs + n], self.g[s + gs:s + gs + n]
             if self.k is None:
-                flag = oracle.adam_step(self.g[s:s + n], p, w, m, v, t=t, fmt=self.fmt, **HP)
+                flag = oracle.adam_step(g, p, w, m, v, t=t, fmt=self.fmt, **HP)
             else:
-                flag = oracle.adam_step_scaled(self.g[s:s + n], p, w, m, v, t=t,
-                                               log2_scale=self.k, fmt=self.fmt, **HP)
+                flag = oracle.adam_step_scaled(g, p, w, m, v, t=t, log2_scale=self.k,
+                                               fmt=self.fmt, **HP)
             assert flag == 0
 
     def compare(self, what):

@@ -145,14 +145,17 @@ void adam_access_path(uintptr_t p, uintptr_t g, const uintptr_t a32[3], uint64_t
                       TensorDesc *d) {
     const uintptr_t a16[2] = {p, g};
     d->pshift = 0;
+    d->gshift = 0;
     pick_vector_path(a16, 2, a32, 3, 4, &d->vec, &d->head);
     if (d->vec != 4 && n >= kTileAlignMinElems) {
-        // the parameter alone out of phase: everything else by vectors, and
-        // its stores shifted (its phase then differs from 0, the head's
-        // being the one that aligns the fp32 arrays)
-        pick_vector_path(&g, 1, a32, 3, 4, &d->vec, &d->head);
-        if (d->vec == 4)
+        // a 16-bit array out of phase: the fp32 arrays by vectors at their
+        // head, the parameter's stores and the gradient's loads shifted by
+        // their own phase there (one of the two is then not 0)
+        pick_vector_path(nullptr, 0, a32, 3, 4, &d->vec, &d->head);
+        if (d->vec == 4) {
             d->pshift = (uint32_t)((p / 2u + d->head) % 4u);
+            d->gshift = (uint32_t)((g / 2u + d->head) % 4u);
+        }
     }
     if (d->vec == 4)
         d->head = adam_head_of(a32, d->head, n);

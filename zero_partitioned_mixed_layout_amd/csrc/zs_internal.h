@@ -24,8 +24,8 @@ struct TensorDesc {
                        // path: head % 4 singly, then by fours; see adam_head_of)
     uint32_t pshift;   // vector path: the parameter's element phase mod 4 at
                        // the vector-aligned elements (0: its stores are 8-byte
-                       // vectors too; 1-3: see param_shift_of)
-    uint32_t unused;   // pads the descriptor to 64 bytes
+                       // vectors too; 1-3: shifted, see adam_access_path)
+    uint32_t gshift;   // the same for the gradient (1-3: shifted loads)
 };
 static_assert(sizeof(TensorDesc) == 64, "TensorDesc is 64 bytes");
 
@@ -281,23 +281,37 @@ int build_host_plan(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chu
 uint32_t adam_head_of(const uintptr_t a32[3], uint32_t vec_head, uint64_t n);
 
 // The Adam step's access path for a tensor of n elements (its parameter p,
-// gradient g and fp32 master, m, v at a32): sets d->vec, d->head and
-// d->pshift.  The vector path when all five arrays agree in phase after
-// peeling at most 3 elements (pshift 0); else, on a tensor of
-// kTileAlignMinElems or more whose gradient and fp32 arrays agree, the
-// vector path with the parameter, which is only written, stored shifted
-// (pshift 1-3: its element phase mod 4 at the vector-aligned elements);
-// otherwise single elements (vec 1).  A ZeRO rank's parameter is often a
-// view of the full buffer at an offset that is not a multiple of four
-// elements.  Measured on MI355X with the parameter 1-3 elements off, plans
-// over the same buffers in one process (fraction of 8 TB/s, shifted
-// against single): one tensor of 117,187,500 elements 0.747-0.764 against
-// 0.682-0.692; the GPT-2-XL list 0.738-0.751 against 0.560-0.570; random
-// sizes 1-8,192 0.637 against 0.607 and 1-100,000 0.660 against 0.643.
-// Below 1,024 elements single elements were faster (random sizes 1-1,024:
-// 0.616 with the rule against 0.551 shifted).
+// gradient g and fp32 master, m, v at a32): sets d->vec, d->head, d->pshift
+// and d->gshift.  The vector path when all five arrays agree in phase after
+// peeling at most 3 elements (both shifts 0); else, on a tensor of
+// kTileAlignMinElems or more whose fp32 arrays agree, the vector path with
+// the parameter stored shifted (pshift 1-3: its element phase mod 4 at the
+// vector-aligned elements) and the gradient loaded shifted (gshift 1-3)
+// where either is out of phase; otherwise single elements (vec 1).  A ZeRO
+// rank's 16-bit arrays are often views of full buffers at an offset that
+// is not a multiple of four elements.  Measured on MI355X, plans over the
+// same buffers in one process (fraction of 8 TB/s, shifted against
+// single): the parameter 1-3 elements off, one tensor of 117,187,500
+// elements 0.747-0.764 against 0.682-0.692, the GPT-2-XL list 0.738-0.751
+// against 0.560-0.570, random sizes 1-8,192 0.637 against 0.607 and
+// 1-100,000 0.660 against 0.643; the gradient off too, 0.739-0.745 against
+// 0.681-0.682 (117M) and 0.731-0.734 against 0.629-0.631 (GPT-2-XL); the
+// gradient alone off, 0.774-0.788 against 0.707-0.708.  Below 1,024
+// elements single elements were faster (random sizes 1-1,024: 0.616 with
+// the rule against 0.551 shifted).
 void adam_access_path(uintptr_t p, uintptr_t g, const uintptr_t a32[3], uint64_t n,
                       TensorDesc *d);
+
+// Whether any of the descriptors is on the vector path with a 16-bit array
+// out of phase: the Adam kernels are built twice, with the shifted modes
+// and without them (so that in-phase plans run the in-phase tile code
+// alone: measured 0.3% faster than with the modes compiled in).
+inline bool any_shift(const TensorDesc *d, size_t n) {
+    for (size_t k = 0; k < n; k++)
+        if (d[k].vec == 4 && (d[k].pshift | d[k].gshift) != 0)
+            return true;
+    return false;
+}
 
 // One non-empty tensor: its descriptor (vector path and peeled head) and the
 // byte ranges of its five arrays (param, grad, master, m, v).  Errors:

@@ -227,9 +227,10 @@ __device__ __forceinline__ typename Fmt::V4 quad_update(const TensorDesc &T, uin
     return p;
 }
 
-// Stores of a parameter that is s = T.pshift elements (1-3) out of the
-// state's phase.  Lane L holds the new values of elements 4L..4L+3 of a run
-// from the vector-aligned element `base`; the parameter's 8-byte vectors
+// Stores of a 16-bit output (the parameter; the fused step's gradient
+// output too) that is s elements (1-3) out of the phase of the arrays its
+// values come from.  Lane L holds the new values of elements 4L..4L+3 of a
+// run from the vector-aligned element `base`; the output's 8-byte vectors
 // start at elements 4L - s.  Lane L >= 1 joins the last s values of lane
 // L - 1 (a cross-lane permute) with its own first 4 - s and stores one
 // aligned vector; the run's first 4 - s and last s elements, whose vectors
@@ -247,55 +248,42 @@ __device__ __forceinline__ uint64_t join_shifted(uint64_t own, uint64_t src, uin
     return (prev >> (16u * (4u - s))) | (own << (16u * s));
 }
 
-// The run's edges: the first 4 - s values of lane 0's group `first_vals`
-// at `first_at`, the last s of lane `last_lane`'s at `last_at`.
-__device__ __forceinline__ void store_edges(uint16_t *p, uint32_t lane, uint32_t s,
+// The run's edges: the first 4 - s values of lane 0's group and the last s
+// of lane `last_lane`'s (`vals`: this lane's group, at element `at`).
+__device__ __forceinline__ void store_edges(uint16_t *dst, uint32_t lane, uint32_t s,
                                             uint32_t last_lane, uint64_t vals, uint64_t at) {
     uint16_t b[4];
     memcpy(b, &vals, 8);
 #pragma unroll
     for (uint32_t j = 0; j < 4; j++)
         if (j < 4u - s ? lane == 0 : lane == last_lane)
-            st_nt(b[j], p + at + j);
+            st_nt(b[j], dst + at + j);
 }
 
-// nq <= 64 groups held by lanes 0..nq-1 (exactly these lanes take part):
-// a tensor's head or the groups of a partial tile.
-template <class Fmt>
-__device__ __forceinline__ void param_store_shifted(const TensorDesc &T, uint64_t base,
-                                                    uint32_t lane, uint32_t nq,
-                                                    typename Fmt::V4 p) {
+// nq <= 64 groups held by lanes 0..nq-1 (exactly these lanes take part): a
+// tensor's head or the groups of a partial tile.  V: the 8-byte vector of
+// four 16-bit values.
+template <typename V>
+__device__ __forceinline__ void shifted_store_groups(uint16_t *dst, uint32_t s, uint64_t base,
+                                                     uint32_t lane, uint32_t nq, V p) {
+    static_assert(sizeof(V) == 8, "four 16-bit values");
     uint64_t own;
     memcpy(&own, &p, 8);
-    const uint64_t joined = join_shifted(own, own, lane, T.pshift);
+    const uint64_t joined = join_shifted(own, own, lane, s);
     if (lane != 0)
-        st_nt(joined, reinterpret_cast<uint64_t *>(T.p + base + 4u * lane - T.pshift));
-    store_edges(T.p, lane, T.pshift, nq - 1u, own, base + 4u * lane);
-}
-
-// The same for nq <= 64 groups held by lanes 0..nq-1 in the state's phase
-// (SHIFT false: one 8-byte vector per lane) or out of it.  SHIFT is
-// T.pshift != 0, decided once per tile so that the aligned path's code is
-// the same as it would be without the shifted one.
-template <class Fmt, bool SHIFT>
-__device__ __forceinline__ void param_store_quads(const TensorDesc &T, uint64_t base,
-                                                  uint32_t lane, uint32_t nq,
-                                                  typename Fmt::V4 p) {
-    if constexpr (SHIFT)
-        param_store_shifted<Fmt>(T, base, lane, nq, p);
-    else
-        st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + base + 4u * lane));
+        st_nt(joined, reinterpret_cast<uint64_t *>(dst + base + 4u * lane - s));
+    store_edges(dst, lane, s, nq - 1u, own, base + 4u * lane);
 }
 
 // A full tile of Q runs of 256 (lane L: elements 4L..4L+3 of each run from
-// `base`), out of phase: lane 0 of run k >= 1 joins the last s values of
-// run k - 1, which lane 63 hands it through the same permute, and stores a
-// whole vector, so that only the tile's first 4 - s and last s elements go
+// `base`): lane 0 of run k >= 1 joins the last s values of run k - 1,
+// which lane 63 hands it through the same permute, and stores a whole
+// vector, so that only the tile's first 4 - s and last s elements go
 // singly.
-template <class Fmt, int Q>
-__device__ __forceinline__ void param_store_tile(const TensorDesc &T, uint64_t base,
-                                                 uint32_t lane, const typename Fmt::V4 (&p)[Q]) {
-    const uint32_t s = T.pshift;
+template <typename V, int Q>
+__device__ __forceinline__ void shifted_store_tile(uint16_t *dst, uint32_t s, uint64_t base,
+                                                   uint32_t lane, const V (&p)[Q]) {
+    static_assert(sizeof(V) == 8, "four 16-bit values");
     uint64_t own[Q];
     memcpy(own, p, sizeof(own));
 #pragma unroll
@@ -303,21 +291,70 @@ __device__ __forceinline__ void param_store_tile(const TensorDesc &T, uint64_t b
         const uint64_t src = k > 0 && lane == kWave - 1u ? own[(k + Q - 1) % Q] : own[k];
         const uint64_t joined = join_shifted(own[k], src, lane, s);
         if (k > 0 || lane != 0)
-            st_nt(joined, reinterpret_cast<uint64_t *>(T.p + base + 4u * kWave * k +
+            st_nt(joined, reinterpret_cast<uint64_t *>(dst + base + 4u * kWave * k +
                                                        4u * lane - s));
     }
     const bool first = lane == 0;
-    store_edges(T.p, lane, s, kWave - 1u, first ? own[0] : own[Q - 1],
+    store_edges(dst, lane, s, kWave - 1u, first ? own[0] : own[Q - 1],
                 base + (first ? 0u : 4u * kWave * (Q - 1)) + 4u * lane);
+}
+
+// The four values of a 16-bit input that is s elements (1-3) out of phase
+// at element i (vector-aligned for the other arrays): they lie in the two
+// aligned 8-byte words from element i - s, which every lane loads whole and
+// joins in registers, with no cross-lane step and no lane conditions.  The
+// words also hold s elements before i and 4 - s after i + 3, which are
+// discarded; an aligned word holding an element of the array lies in a
+// page that holds the array's own bytes, so reading it cannot fault, and
+// a neighbouring tile that writes those elements meanwhile (the gradient
+// read from the parameter's place) changes only discarded values.
+__device__ __forceinline__ uint64_t load_shifted(const uint16_t *src, uint32_t s, uint64_t i) {
+    const uint64_t *word = reinterpret_cast<const uint64_t *>(src + i - s);
+    const uint64_t lo = ld_nt(word), hi = ld_nt(word + 1);
+    return (lo >> (16u * s)) | (hi << (16u * (4u - s)));
+}
+
+// The Adam step's access modes on the vector path, decided once per tile
+// so that each mode's code is what it would be without the others:
+// kInPhase, every array in phase; kParamShift, the parameter s = T.pshift
+// out of phase (shifted stores); kGradShift, the gradient T.gshift out of
+// phase (shifted loads) and the parameter in phase or out by T.pshift.
+enum { kInPhase = 0, kParamShift = 1, kGradShift = 2 };
+
+// The parameter stores of nq <= 64 groups held by lanes 0..nq-1 (only
+// these lanes take part).
+template <class Fmt, int MODE>
+__device__ __forceinline__ void param_store_quads(const TensorDesc &T, uint64_t base,
+                                                  uint32_t lane, uint32_t nq,
+                                                  typename Fmt::V4 p) {
+    if (MODE == kInPhase || (MODE == kGradShift && T.pshift == 0))
+        st_nt(p, reinterpret_cast<typename Fmt::V4 *>(T.p + base + 4u * lane));
+    else
+        shifted_store_groups(T.p, T.pshift, base, lane, nq, p);
+}
+
+// The four elements from i into q: the fp32 state, and the gradient
+// shifted or not.
+template <class Fmt, int MODE>
+__device__ __forceinline__ void quad_load_mode(const TensorDesc &T, uint64_t i, Quad<Fmt> &q) {
+    if constexpr (MODE == kGradShift) {
+        q.w = ld_nt(reinterpret_cast<const f32x4 *>(T.w + i));
+        q.m = ld_nt(reinterpret_cast<const f32x4 *>(T.m + i));
+        q.v = ld_nt(reinterpret_cast<const f32x4 *>(T.v + i));
+        const uint64_t g = load_shifted(T.g, T.gshift, i);
+        memcpy(&q.g, &g, 8);
+    } else {
+        quad_load<Fmt>(T, i, q);
+    }
 }
 
 // A full Adam tile: TILE consecutive elements from `base` (vector-aligned),
 // TILE / 256 groups of four per lane.  Lane L takes elements 4L..4L+3 of
 // every 256, so each of the wave's load and store instructions covers one
-// contiguous 512-byte (16-bit) or 1-KiB (fp32) range (a shifted
-// parameter's store: 504 bytes, plus its edges).  All loads are issued
-// before any arithmetic.
-template <class Fmt, uint32_t TILE, bool SHIFT>
+// contiguous 512-byte (16-bit) or 1-KiB (fp32) range (a shifted 16-bit
+// array's: 504 or 512 bytes, plus a shifted store's edges).  All loads are
+// issued before any arithmetic.
+template <class Fmt, uint32_t TILE, int MODE>
 __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, uint32_t lane,
                                           const AdamConsts &c, int &bad) {
     constexpr int Q = TILE / (4 * kWave);
@@ -325,9 +362,9 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
     Quad<Fmt> a[Q];
 #pragma unroll
     for (int k = 0; k < Q; k++)
-        quad_load<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k]);
+        quad_load_mode<Fmt, MODE>(T, base + 4u * lane + 4u * kWave * k, a[k]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!SHIFT) {
+    if constexpr (MODE == kInPhase) {
 #pragma unroll
         for (int k = 0; k < Q; k++) {
             const uint64_t i = base + 4u * lane + 4u * kWave * k;
@@ -339,8 +376,26 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
 #pragma unroll
         for (int k = 0; k < Q; k++)
             p[k] = quad_update<Fmt>(T, base + 4u * lane + 4u * kWave * k, a[k], c, bad);
-        param_store_tile<Fmt, Q>(T, base, lane, p);
+        if (MODE == kGradShift && T.pshift == 0) {
+#pragma unroll
+            for (int k = 0; k < Q; k++)
+                st_nt(p[k], reinterpret_cast<typename Fmt::V4 *>(T.p + base + 4u * lane +
+                                                                  4u * kWave * k));
+        } else {
+            shifted_store_tile(T.p, T.pshift, base, lane, p);
+        }
     }
+}
+
+// nq <= 64 groups of four from the vector-aligned element `base`, held by
+// lanes 0..nq-1 (only these lanes take part): a head's or a partial tile's.
+template <class Fmt, int MODE>
+__device__ __forceinline__ void adam_quads(const TensorDesc &T, uint64_t base, uint32_t lane,
+                                           uint32_t nq, const AdamConsts &c, int &bad) {
+    Quad<Fmt> x;
+    quad_load_mode<Fmt, MODE>(T, base + 4u * lane, x);
+    param_store_quads<Fmt, MODE>(T, base, lane, nq, quad_update<Fmt>(T, base + 4u * lane, x, c,
+                                                                       bad));
 }
 
 // The peeled head of a tensor on the vector path: its first `count`
@@ -348,7 +403,7 @@ __device__ __forceinline__ void adam_tile(const TensorDesc &T, uint64_t base, ui
 // precede the first aligned vector), then at most 63 groups of four, one per
 // lane; a tensor that ends inside its head does its last fewer-than-four
 // singly.
-template <class Fmt, bool SHIFT>
+template <class Fmt, int MODE>
 __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
                                           const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
@@ -356,13 +411,8 @@ __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
     if (lane < singles)
         adam_single<Fmt>(T, lane, c, bad);
     const uint32_t nquads = (count - singles) / 4u;
-    if (lane < nquads) {
-        Quad<Fmt> x;
-        const uint64_t i = singles + 4u * lane;
-        quad_load<Fmt>(T, i, x);
-        param_store_quads<Fmt, SHIFT>(T, singles, lane, nquads,
-                                      quad_update<Fmt>(T, i, x, c, bad));
-    }
+    if (lane < nquads)
+        adam_quads<Fmt, MODE>(T, singles, lane, nquads, c, bad);
     const uint32_t rest = count - singles - 4u * nquads;
     if (lane < rest)
         adam_single<Fmt>(T, singles + 4u * nquads + lane, c, bad);
@@ -373,20 +423,20 @@ __device__ __forceinline__ void adam_head(const TensorDesc &T, uint32_t count,
 // or more, else only to the first aligned vector) rides in its first chunk
 // and is done by tile 0; every other chunk starts at the head plus a whole
 // number of tiles.  The chunk's last, partial tile goes four elements per
-// lane, then the final fewer-than-four singly.  SHIFT: the parameter is out
-// of the other arrays' phase (T.pshift != 0) and its stores are shifted.
-template <class Fmt, uint32_t TILE, bool SHIFT>
+// lane, then the final fewer-than-four singly.  MODE: which 16-bit array
+// is out of phase (kInPhase, kParamShift, kGradShift).
+template <class Fmt, uint32_t TILE, int MODE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
     const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
     if (j == 0 && head != 0)
-        adam_head<Fmt, SHIFT>(T, head, c, bad);
+        adam_head<Fmt, MODE>(T, head, c, bad);
     const uint64_t base = ch.start + head;
     const uint32_t body = ch.count - head;
     const uint32_t nfull = body / TILE;
     if (j < nfull) {
-        adam_tile<Fmt, TILE, SHIFT>(T, base + (uint64_t)j * TILE, lane, c, bad);
+        adam_tile<Fmt, TILE, MODE>(T, base + (uint64_t)j * TILE, lane, c, bad);
         return;
     }
     if (j > nfull)
@@ -394,28 +444,35 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
     const uint64_t rbase = base + (uint64_t)nfull * TILE;
     const uint32_t rem = body - nfull * TILE; // < TILE
     const uint32_t nquads = rem / 4u;
-    if constexpr (SHIFT) {
+    if constexpr (MODE != kInPhase) {
         for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
             const uint32_t nq = min(nquads - r0, kWave);
-            if (lane < nq) {
-                Quad<Fmt> x;
-                const uint64_t run = rbase + 4u * r0, i = run + 4u * lane;
-                quad_load<Fmt>(T, i, x);
-                param_store_quads<Fmt, true>(T, run, lane, nq,
-                                             quad_update<Fmt>(T, i, x, c, bad));
-            }
+            if (lane < nq)
+                adam_quads<Fmt, MODE>(T, rbase + 4u * r0, lane, nq, c, bad);
         }
     } else {
         for (uint32_t q = lane; q < nquads; q += kWave) {
             Quad<Fmt> x;
             const uint64_t i = rbase + 4u * q;
             quad_load<Fmt>(T, i, x);
-            param_store_quads<Fmt, false>(T, rbase, q, 0, quad_update<Fmt>(T, i, x, c, bad));
+            st_nt(quad_update<Fmt>(T, i, x, c, bad), reinterpret_cast<typename Fmt::V4 *>(T.p + i));
         }
     }
     const uint32_t tail = rem - 4u * nquads;
     if (lane < tail)
         adam_single<Fmt>(T, rbase + 4u * nquads + lane, c, bad);
+}
+
+// Tile j of a chunk on the vector path in the tensor's mode.
+template <class Fmt, uint32_t TILE>
+__device__ __forceinline__ void adam_tile_vec(const TensorDesc &T, const Chunk &ch, uint32_t j,
+                                              const AdamConsts &c, int &bad) {
+    if ((T.pshift | T.gshift) == 0)
+        adam_tile_of_chunk<Fmt, TILE, kInPhase>(T, ch, j, c, bad);
+    else if (T.gshift == 0)
+        adam_tile_of_chunk<Fmt, TILE, kParamShift>(T, ch, j, c, bad);
+    else
+        adam_tile_of_chunk<Fmt, TILE, kGradShift>(T, ch, j, c, bad);
 }
 
 // Tile j of a chunk of a tensor whose arrays disagree in alignment: single
@@ -467,7 +524,7 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
 // b / tiles_per_chunk.  Launches with fewer workgroups than virtual ones
 // stride over them.  Fmt: the 16-bit format of parameters and gradients;
 // TILE: the plan's Adam tile (kAdamTileFine or kTile elements).
-template <class Fmt, uint32_t TILE>
+template <class Fmt, uint32_t TILE, bool SHIFTS>
 __global__ __launch_bounds__(kWave) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
     uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
@@ -484,12 +541,14 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
         const uint32_t j = (uint32_t)(vb - ci * tiles_per_chunk);
         const Chunk ch = chunks[ci];
         const TensorDesc T = tensors[ch.tensor];
-        if (T.vec != 4)
+        if (T.vec == 4) {
+            if constexpr (SHIFTS)
+                adam_tile_vec<Fmt, TILE>(T, ch, j, c, bad);
+            else
+                adam_tile_of_chunk<Fmt, TILE, kInPhase>(T, ch, j, c, bad);
+        } else {
             adam_tile_single<Fmt, TILE>(T, ch, j, c, bad);
-        else if (T.pshift == 0)
-            adam_tile_of_chunk<Fmt, TILE, false>(T, ch, j, c, bad);
-        else
-            adam_tile_of_chunk<Fmt, TILE, true>(T, ch, j, c, bad);
+        }
     }
     raise_flag(flag, bad);
 }
@@ -504,7 +563,7 @@ __global__ __launch_bounds__(kWave) void zs_adam_kernel(
 // min(n - start, TILE) on the device was miscompiled by this toolchain for
 // the single-element path: a VALU 64-bit compare feeding a scalar select
 // that read a stale SCC, so every partial tile ran as a full one.)
-template <class Fmt, uint32_t TILE>
+template <class Fmt, uint32_t TILE, bool SHIFTS>
 __global__ __launch_bounds__(kWave) void zs_adam_flat_kernel(TensorDesc T, uint64_t ntiles,
                                                              uint32_t first_count,
                                                              uint32_t last_count, AdamConsts c,
@@ -516,12 +575,14 @@ __global__ __launch_bounds__(kWave) void zs_adam_flat_kernel(TensorDesc T, uint6
         ch.tensor = 0;
         ch.start = b == 0 ? 0 : h + b * TILE;
         ch.count = b == ntiles - 1 ? last_count : (b == 0 ? first_count : TILE);
-        if (T.vec != 4)
+        if (T.vec == 4) {
+            if constexpr (SHIFTS)
+                adam_tile_vec<Fmt, TILE>(T, ch, 0, c, bad);
+            else
+                adam_tile_of_chunk<Fmt, TILE, kInPhase>(T, ch, 0, c, bad);
+        } else {
             adam_tile_single<Fmt, TILE>(T, ch, 0, c, bad);
-        else if (T.pshift == 0)
-            adam_tile_of_chunk<Fmt, TILE, false>(T, ch, 0, c, bad);
-        else
-            adam_tile_of_chunk<Fmt, TILE, true>(T, ch, 0, c, bad);
+        }
     }
     raise_flag(flag, bad);
 }
@@ -581,8 +642,9 @@ __device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, ui
 // in rank order, in batches of 16, 8, 4 and 1 slices in flight per lane,
 // then one division by nd.
 template <class Fmt, int VEC>
-__device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, uint64_t i,
-                                             float count, uint16_t *out, int &bad) {
+__device__ __forceinline__ typename HVec<Fmt, VEC>::T reduce_group_value(const SliceArgs &s,
+                                                                        uint32_t nd, uint64_t i,
+                                                                        float count, int &bad) {
     typedef typename HVec<Fmt, VEC>::T hv;
     float acc[VEC];
     uint32_t r = 0;
@@ -603,7 +665,44 @@ __device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, ui
         memcpy(&b, &oj, 2);
         bad |= bits_nonfinite<Fmt>(b);
     }
-    st_through(o, reinterpret_cast<hv *>(out + i));
+    return o;
+}
+
+// The same, stored at out + i.
+template <class Fmt, int VEC>
+__device__ __forceinline__ void reduce_group(const SliceArgs &s, uint32_t nd, uint64_t i,
+                                             float count, uint16_t *out, int &bad) {
+    typedef typename HVec<Fmt, VEC>::T hv;
+    st_through(reduce_group_value<Fmt, VEC>(s, nd, i, count, bad), reinterpret_cast<hv *>(out + i));
+}
+
+// The reduce's output of nq <= 64 groups of eight held by lanes 0..nq-1
+// (lane L: elements 8L..8L+7 from `base`, exactly these lanes take part)
+// when the output is s elements (1-3) out of the slices' phase: lane L
+// stores the aligned vector of its elements 4 - s..7 - s whole, and the
+// one before it joined with the last s values of lane L - 1 (a cross-lane
+// permute); the first 4 - s and the last s elements go singly.
+template <typename V8>
+__device__ __forceinline__ void reduce_store_shifted8(uint16_t *out, uint32_t s, uint64_t base,
+                                                      uint32_t lane, uint32_t nq, V8 o) {
+    static_assert(sizeof(V8) == 16, "eight 16-bit values");
+    uint64_t h[2];
+    memcpy(h, &o, 16);
+    const uint64_t at = base + 8u * lane;
+    st_through((h[0] >> (16u * (4u - s))) | (h[1] << (16u * s)),
+               reinterpret_cast<uint64_t *>(out + at + 4u - s));
+    const uint64_t joined = join_shifted(h[0], h[1], lane, s);
+    if (lane != 0)
+        st_through(joined, reinterpret_cast<uint64_t *>(out + at - s));
+    uint16_t b[8];
+    memcpy(b, &o, 16);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; j++) {
+        if (lane == 0 && j < 4u - s)
+            as_global(out)[at + j] = b[j];
+        if (lane == nq - 1u && j >= 4u - s)
+            as_global(out)[at + 4u + j] = b[4 + j];
+    }
 }
 
 template <class Fmt>
@@ -619,11 +718,14 @@ __device__ __forceinline__ void reduce_one(const SliceArgs &s, uint32_t nd, uint
 // Each lane reduces one vector group of VEC elements (grid-striding when the
 // launch is smaller than the work); the unaligned head (fewer than VEC
 // leading elements) and the tail past the last whole group go one element
-// per lane.  VEC = 1: every element singly.
-template <class Fmt, int VEC>
+// per lane.  VEC = 1: every element singly.  SHIFT (VEC = 8): the output
+// is oshift elements out of the slices' phase and each wave's 64 groups
+// are stored shifted.
+template <class Fmt, int VEC, bool SHIFT = false>
 __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t nd, uint64_t n,
                                                           uint32_t head, uint16_t *__restrict__ out,
-                                                          int32_t *__restrict__ flag) {
+                                                          int32_t *__restrict__ flag,
+                                                          uint32_t oshift) {
     const float count = (float)nd;
     const uint64_t gtid = (uint64_t)blockIdx.x * kWave + threadIdx.x;
     const uint64_t gstride = (uint64_t)gridDim.x * kWave;
@@ -635,9 +737,20 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
         reduce_one<Fmt>(s, nd, gtid, count, out, bad);
     for (uint64_t i = body_end + gtid; i < n; i += gstride)
         reduce_one<Fmt>(s, nd, i, count, out, bad);
-    if (VEC > 1)
+    if constexpr (SHIFT) {
+        static_assert(VEC == 8, "shifted output on the 16-byte path");
+        const uint32_t lane = threadIdx.x;
+        for (uint64_t k0 = (uint64_t)blockIdx.x * kWave; k0 < ngroups; k0 += gstride) {
+            const uint32_t nq = (uint32_t)min(ngroups - k0, (uint64_t)kWave);
+            if (lane < nq)
+                reduce_store_shifted8(out, oshift, h + k0 * 8u, lane, nq,
+                                      reduce_group_value<Fmt, 8>(s, nd, h + (k0 + lane) * 8u,
+                                                                 count, bad));
+        }
+    } else if (VEC > 1) {
         for (uint64_t k = gtid; k < ngroups; k += gstride)
             reduce_group<Fmt, VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
+    }
     raise_flag(flag, bad);
 }
 
@@ -719,7 +832,24 @@ struct FlatState {
     uint16_t *p;    // 16-bit parameter (written)
     float *w, *m, *v;
     uint16_t *gout; // 16-bit reduced gradient (written), or null
+    uint32_t pshift, gshift; // the two outputs' element phase mod 4 at the
+                             // vector-aligned elements (the kernels' SHIFT)
 };
+
+// One 16-bit output of a full fused tile (lane L: elements 4L..4L+3 of
+// each run of 256 from `base`): 8-byte vectors when it is in phase (s 0),
+// else shifted.
+template <typename V, int Q>
+__device__ __forceinline__ void out16_store_tile(uint16_t *dst, uint32_t s, uint64_t base,
+                                                 uint32_t lane, const V (&x)[Q]) {
+    if (s == 0) {
+#pragma unroll
+        for (int k = 0; k < Q; k++)
+            st_nt(x[k], reinterpret_cast<V *>(dst + base + 4u * kWave * k + 4u * lane));
+    } else {
+        shifted_store_tile(dst, s, base, lane, x);
+    }
+}
 
 template <class Fmt>
 __device__ __forceinline__ void fused_single(const SliceArgs &s, uint32_t nd, uint64_t i,
@@ -766,12 +896,14 @@ __device__ __forceinline__ void fused_batch(const SliceArgs &s, uint32_t r0, con
 
 // Q four-element groups at i[0..Q-1] (vector-aligned): the fp32 state is
 // loaded first, then the slices in batches of 16, 8, 4 and 1; then the
-// reduced gradient,
-// the update and the stores.
-template <class Fmt, int Q>
+// reduced gradient, the update and the stores.  SHIFT: the 16-bit outputs
+// may be out of phase; they are then stored after the state, Q = 2 as a
+// full tile from `base`, Q = 1 as groups of the nq lanes from `base`.
+template <class Fmt, int Q, bool SHIFT = false>
 __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
                                              const uint64_t (&i)[Q], float count,
-                                             const FlatState &F, const AdamConsts &c, int &bad) {
+                                             const FlatState &F, const AdamConsts &c, int &bad,
+                                             uint64_t base = 0, uint32_t nq = 0) {
     f32x4 w[Q], m[Q], v[Q];
 #pragma unroll
     for (int k = 0; k < Q; k++) {
@@ -790,6 +922,7 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
         fused_batch<Fmt, 4, Q>(s, r, i, r == 0, acc);
     for (; r < nd; r++)
         fused_batch<Fmt, 1, Q>(s, r, i, r == 0, acc);
+    typename Fmt::V4 gs[Q], ps[Q];
 #pragma unroll
     for (int k = 0; k < Q; k++) {
         typename Fmt::V4 g, p;
@@ -806,12 +939,31 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
             m[k][j] = mm;
             v[k][j] = vv;
         }
-        if (F.gout != nullptr)
+        if (!SHIFT && F.gout != nullptr)
             st_nt(g, reinterpret_cast<typename Fmt::V4 *>(F.gout + i[k]));
         st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
         st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
         st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
-        st_nt(p, reinterpret_cast<typename Fmt::V4 *>(F.p + i[k]));
+        if (!SHIFT)
+            st_nt(p, reinterpret_cast<typename Fmt::V4 *>(F.p + i[k]));
+        gs[k] = g;
+        ps[k] = p;
+    }
+    if constexpr (SHIFT) {
+        if constexpr (Q == 1) {
+            if (F.pshift == 0)
+                st_nt(ps[0], reinterpret_cast<typename Fmt::V4 *>(F.p + i[0]));
+            else
+                shifted_store_groups(F.p, F.pshift, base, threadIdx.x, nq, ps[0]);
+            if (F.gout != nullptr && F.gshift == 0)
+                st_nt(gs[0], reinterpret_cast<typename Fmt::V4 *>(F.gout + i[0]));
+            else if (F.gout != nullptr)
+                shifted_store_groups(F.gout, F.gshift, base, threadIdx.x, nq, gs[0]);
+        } else {
+            out16_store_tile(F.p, F.pshift, base, threadIdx.x, ps);
+            if (F.gout != nullptr)
+                out16_store_tile(F.gout, F.gshift, base, threadIdx.x, gs);
+        }
     }
 }
 
@@ -821,12 +973,13 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
 // lane keeps as many bytes per slice in flight as on the 16-byte path; the
 // rank-order sum and the division of reduce_single.  The last, partial tile
 // goes by groups of four, then singly; tile 0 also does the head.
-template <class Fmt>
+template <class Fmt, bool SHIFT = false>
 __global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint32_t nd,
                                                                uint64_t n, uint32_t head,
                                                                uint64_t ntiles,
                                                                uint16_t *__restrict__ out,
-                                                               int32_t *__restrict__ flag) {
+                                                               int32_t *__restrict__ flag,
+                                                               uint32_t oshift) {
     const float count = (float)nd;
     const uint32_t lane = threadIdx.x;
     const uint64_t h = head < n ? head : n;
@@ -848,6 +1001,7 @@ __global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint
                 fused_batch<Fmt, 4, 2>(s, r, i, r == 0, acc);
             for (; r < nd; r++)
                 fused_batch<Fmt, 1, 2>(s, r, i, r == 0, acc);
+            typename Fmt::V4 os[2];
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 typename Fmt::V4 o;
@@ -859,13 +1013,29 @@ __global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint
                     memcpy(&ob, &oj, 2);
                     bad |= bits_nonfinite<Fmt>(ob);
                 }
-                st_through(o, reinterpret_cast<typename Fmt::V4 *>(out + i[k]));
+                if (!SHIFT)
+                    st_through(o, reinterpret_cast<typename Fmt::V4 *>(out + i[k]));
+                os[k] = o;
             }
+            if (SHIFT)
+                shifted_store_tile(out, oshift, lo, lane, os);
             continue;
         }
         const uint32_t nquads = (uint32_t)(hi - lo) / 4u;
-        for (uint32_t q = lane; q < nquads; q += kWave)
-            reduce_group<Fmt, 4>(s, nd, lo + 4u * q, count, out, bad);
+        if constexpr (SHIFT) {
+            for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
+                const uint32_t nq = min(nquads - r0, kWave);
+                if (lane < nq) {
+                    const uint64_t run = lo + 4u * r0;
+                    shifted_store_groups(out, oshift, run, lane, nq,
+                                         reduce_group_value<Fmt, 4>(s, nd, run + 4u * lane,
+                                                                    count, bad));
+                }
+            }
+        } else {
+            for (uint32_t q = lane; q < nquads; q += kWave)
+                reduce_group<Fmt, 4>(s, nd, lo + 4u * q, count, out, bad);
+        }
         const uint64_t t0 = lo + 4u * (uint64_t)nquads;
         if (t0 + lane < hi)
             reduce_one<Fmt>(s, nd, t0 + lane, count, out, bad);
@@ -883,7 +1053,7 @@ extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
 // the Adam tile's mapping (lane L: 4L..4L+3 and kTile/2+4L..), and the
 // update runs there.  The fp32 state loads are issued before the slices, or
 // with LATE after them (before the LDS exchange).
-template <class Fmt, bool LATE>
+template <class Fmt, bool LATE, bool SHIFT>
 __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uint64_t lo,
                                             uint32_t lane, float count, const FlatState &F,
                                             const AdamConsts &c, int &bad) {
@@ -929,6 +1099,7 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
     g[0] = reinterpret_cast<const hv4 *>(zs_lds)[lane];
     g[1] = reinterpret_cast<const hv4 *>(zs_lds)[kWave + lane];
     __syncthreads(); // the next tile of this workgroup rewrites the buffer
+    hv4 ps[2];
 #pragma unroll
     for (int k = 0; k < 2; k++) {
         hv4 p;
@@ -944,12 +1115,19 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
             m[k][q] = mm;
             v[k][q] = vv;
         }
-        if (F.gout != nullptr)
+        if (!SHIFT && F.gout != nullptr)
             st_nt(g[k], reinterpret_cast<hv4 *>(F.gout + i[k]));
         st_nt(w[k], reinterpret_cast<f32x4 *>(F.w + i[k]));
         st_nt(m[k], reinterpret_cast<f32x4 *>(F.m + i[k]));
         st_nt(v[k], reinterpret_cast<f32x4 *>(F.v + i[k]));
-        st_nt(p, reinterpret_cast<hv4 *>(F.p + i[k]));
+        if (!SHIFT)
+            st_nt(p, reinterpret_cast<hv4 *>(F.p + i[k]));
+        ps[k] = p;
+    }
+    if constexpr (SHIFT) {
+        out16_store_tile(F.p, F.pshift, lo, lane, ps);
+        if (F.gout != nullptr)
+            out16_store_tile(F.gout, F.gshift, lo, lane, g);
     }
 }
 
@@ -1006,8 +1184,9 @@ __device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t n
 // of four (slices 8-byte aligned).  Both: the last partial tile four per
 // lane, then singly.  VEC = 1: the tile's elements one at a time.  Tiles
 // beyond the grid stride.  LATE: fused_tile8 loads the state after the
-// slices.
-template <class Fmt, int VEC, bool LATE = false>
+// slices.  SHIFT: the parameter or the gradient output is out of the
+// others' phase (F.pshift, F.gshift) and is stored shifted.
+template <class Fmt, int VEC, bool LATE = false, bool SHIFT = false>
 __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t nd, uint64_t n,
                                                          uint32_t head, uint64_t ntiles,
                                                          FlatState F, AdamConsts c,
@@ -1023,15 +1202,26 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
         const uint64_t hi = min(n, lo + kTile);
         if (VEC > 1) {
             if (hi - lo == kTile && VEC == 8) {
-                fused_tile8<Fmt, LATE>(s, nd, lo, lane, count, F, c, bad);
+                fused_tile8<Fmt, LATE, SHIFT>(s, nd, lo, lane, count, F, c, bad);
             } else if (hi - lo == kTile) {
                 const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
-                fused_groups<Fmt, 2>(s, nd, i, count, F, c, bad);
+                fused_groups<Fmt, 2, SHIFT>(s, nd, i, count, F, c, bad, lo, kWave);
             } else {
                 const uint32_t nquads = (uint32_t)(hi - lo) / 4u;
-                for (uint32_t q = lane; q < nquads; q += kWave) {
-                    const uint64_t i[1] = {lo + 4u * q};
-                    fused_groups<Fmt, 1>(s, nd, i, count, F, c, bad);
+                if constexpr (SHIFT) {
+                    for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
+                        const uint32_t nq = min(nquads - r0, kWave);
+                        if (lane < nq) {
+                            const uint64_t run = lo + 4u * r0;
+                            const uint64_t i[1] = {run + 4u * lane};
+                            fused_groups<Fmt, 1, true>(s, nd, i, count, F, c, bad, run, nq);
+                        }
+                    }
+                } else {
+                    for (uint32_t q = lane; q < nquads; q += kWave) {
+                        const uint64_t i[1] = {lo + 4u * q};
+                        fused_groups<Fmt, 1>(s, nd, i, count, F, c, bad);
+                    }
                 }
                 const uint64_t t0 = lo + 4u * (uint64_t)nquads;
                 if (t0 + lane < hi)
@@ -1160,6 +1350,7 @@ struct zero_plan {
     int device;
     size_t lds_cap; // dynamic LDS per Adam workgroup (the occupancy cap)
     bool bf16;      // parameters and gradients are bfloat16 (else fp16)
+    bool shifts;    // some tensor has a 16-bit array out of phase
 };
 
 namespace {
@@ -1187,6 +1378,7 @@ int plan_create(const zero_tensor *tensors, uint32_t n_tensors, uint32_t chunk_e
     plan->device = dev;
     plan->lds_cap = lds_cap_bytes(dev, (uint32_t)hp.stats.wg_per_cu);
     plan->bf16 = bf16;
+    plan->shifts = zs::any_shift(hp.tensors.data(), hp.tensors.size());
     const size_t tb = hp.tensors.size() * sizeof(zs::TensorDesc);
     const size_t cb = hp.chunks.size() * sizeof(zs::Chunk);
     if (tb + cb > 0) {
@@ -1246,26 +1438,42 @@ namespace {
 // given statistics: one one-wave workgroup per Adam tile, dispatched in
 // order and balanced over the CUs by the hardware; only tables beyond
 // kMaxGrid tiles stride.
+template <class Fmt, uint32_t TILE>
+void launch_adam_kernel(bool shifts, uint32_t grid, size_t lds, hipStream_t st,
+                        const TensorDesc *d_tensors, const Chunk *d_chunks, uint64_t n_virtual,
+                        uint32_t tpc, const AdamConsts &c, int32_t *flag, const int32_t *skip,
+                        const int32_t *log2_scale) {
+    if (shifts)
+        hipLaunchKernelGGL((zs_adam_kernel<Fmt, TILE, true>), dim3(grid), dim3(kWave), lds, st,
+                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+    else
+        hipLaunchKernelGGL((zs_adam_kernel<Fmt, TILE, false>), dim3(grid), dim3(kWave), lds, st,
+                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+}
+
+// shifts: some tensor of the table has a 16-bit array out of phase (the
+// kernel variant with the shifted modes; without, the in-phase tile code
+// is compiled alone).
 int launch_adam_table(const TensorDesc *d_tensors, const Chunk *d_chunks,
-                      const zero_plan_stats &stats, size_t lds, bool bf16, const AdamConsts &c,
-                      int32_t *flag, const int32_t *skip, const int32_t *log2_scale,
-                      hipStream_t st) {
+                      const zero_plan_stats &stats, size_t lds, bool bf16, bool shifts,
+                      const AdamConsts &c, int32_t *flag, const int32_t *skip,
+                      const int32_t *log2_scale, hipStream_t st) {
     const uint32_t tile = (uint32_t)stats.tile_elems;
     const uint32_t tpc = (uint32_t)(stats.chunk_elems / tile);
     const uint64_t n_virtual = stats.n_chunks * tpc;
     const uint32_t grid = (uint32_t)(n_virtual < zs::kMaxGrid ? n_virtual : zs::kMaxGrid);
     if (bf16 && tile == kAdamTileFine)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
-                           st, d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+        launch_adam_kernel<FmtBF16, kAdamTileFine>(shifts, grid, lds, st, d_tensors, d_chunks,
+                                                   n_virtual, tpc, c, flag, skip, log2_scale);
     else if (bf16)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtBF16, kTile>), dim3(grid), dim3(kWave), lds, st,
-                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+        launch_adam_kernel<FmtBF16, kTile>(shifts, grid, lds, st, d_tensors, d_chunks, n_virtual,
+                                           tpc, c, flag, skip, log2_scale);
     else if (tile == kAdamTileFine)
-        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
-                           st, d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+        launch_adam_kernel<FmtF16, kAdamTileFine>(shifts, grid, lds, st, d_tensors, d_chunks,
+                                                  n_virtual, tpc, c, flag, skip, log2_scale);
     else
-        hipLaunchKernelGGL((zs_adam_kernel<FmtF16, kTile>), dim3(grid), dim3(kWave), lds, st,
-                           d_tensors, d_chunks, n_virtual, tpc, c, flag, skip, log2_scale);
+        launch_adam_kernel<FmtF16, kTile>(shifts, grid, lds, st, d_tensors, d_chunks, n_virtual,
+                                          tpc, c, flag, skip, log2_scale);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -1310,8 +1518,8 @@ static int adam_step_launch(const zero_plan *plan, const zero_adam_hparams *hp, 
     if (dev != plan->device)
         return ZERO_EINVAL;
     return launch_adam_table(plan->d_tensors, plan->d_chunks, plan->stats, plan->lds_cap,
-                             plan->bf16, c, nonfinite_flag, skip_if_nonzero, log2_scale,
-                             (hipStream_t)stream);
+                             plan->bf16, plan->shifts, c, nonfinite_flag, skip_if_nonzero,
+                             log2_scale, (hipStream_t)stream);
 }
 
 extern "C" int zero_adam_step(const zero_plan *plan, const zero_adam_hparams *hp, uint64_t t,
@@ -1413,6 +1621,21 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     addr[nd] = o;
     uint32_t vec, head;
     zs::pick_vector_path(addr, (int)nd + 1, nullptr, 0, 8, &vec, &head);
+    // the output alone out of the slices' phase (a parameter view at an
+    // offset that is not a multiple of four elements, which the fused
+    // route reduces into): the slices' path, the output stored shifted,
+    // on outputs of kTileAlignMinElems or more, as the Adam step does
+    uint32_t oshift = 0;
+    if (vec == 1 && n >= zs::kTileAlignMinElems) {
+        uint32_t vs, hs;
+        zs::pick_vector_path(addr, (int)nd, nullptr, 0, 8, &vs, &hs);
+        const uint32_t sh = (uint32_t)((o / 2u + hs) % 4u);
+        if (vs > 1 && sh != 0) {
+            vec = vs;
+            head = hs;
+            oshift = sh;
+        }
+    }
     // 16-byte path: one vector group per lane, one wave per workgroup;
     // 8-byte path: one 512-element tile per wave (two groups per lane);
     // single elements: one 512-element tile per wave, half the bytes per
@@ -1425,15 +1648,22 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     const uint32_t per_cu = zs::reduce_per_cu_path(nd, vec);
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
-    if (vec == 8)
+    uint16_t *out = (uint16_t *)out_f16;
+    if (vec == 8 && oshift != 0)
+        hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 8, true>), dim3(grid), dim3(kWave), lds, st,
+                           args, nd, n, head, out, nonfinite_flag, oshift);
+    else if (vec == 8)
         hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
-                           n, head, (uint16_t *)out_f16, nonfinite_flag);
+                           n, head, out, nonfinite_flag, 0u);
+    else if (vec == 4 && oshift != 0)
+        hipLaunchKernelGGL((zs_reduce_vec4_kernel<Fmt, true>), dim3(grid), dim3(kWave), lds, st,
+                           args, nd, n, head, tiles4, out, nonfinite_flag, oshift);
     else if (vec == 4)
         hipLaunchKernelGGL((zs_reduce_vec4_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
-                           nd, n, head, tiles4, (uint16_t *)out_f16, nonfinite_flag);
+                           nd, n, head, tiles4, out, nonfinite_flag, 0u);
     else
         hipLaunchKernelGGL((zs_reduce_single_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
-                           nd, n, (uint16_t *)out_f16, nonfinite_flag);
+                           nd, n, out, nonfinite_flag);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -1480,12 +1710,21 @@ int adam_flat_launch(uint16_t *p, const uint16_t *g, float *w, float *m, float *
     const uint64_t last = ntiles == 1 ? first : n - h - (ntiles - 1) * tile;
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
     const size_t lds = lds_cap_bytes(dev, zs::adam_per_cu(tile));
-    if (tile == kAdamTileFine)
-        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kAdamTileFine>), dim3(grid), dim3(kWave), lds,
+    const bool shifts = zs::any_shift(&T, 1);
+    if (tile == kAdamTileFine && shifts)
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kAdamTileFine, true>), dim3(grid),
+                           dim3(kWave), lds, st, T, ntiles, (uint32_t)first, (uint32_t)last, c,
+                           nullptr);
+    else if (tile == kAdamTileFine)
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kAdamTileFine, false>), dim3(grid),
+                           dim3(kWave), lds, st, T, ntiles, (uint32_t)first, (uint32_t)last, c,
+                           nullptr);
+    else if (shifts)
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kTile, true>), dim3(grid), dim3(kWave), lds,
                            st, T, ntiles, (uint32_t)first, (uint32_t)last, c, nullptr);
     else
-        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kTile>), dim3(grid), dim3(kWave), lds, st, T,
-                           ntiles, (uint32_t)first, (uint32_t)last, c, nullptr);
+        hipLaunchKernelGGL((zs_adam_flat_kernel<Fmt, kTile, false>), dim3(grid), dim3(kWave), lds,
+                           st, T, ntiles, (uint32_t)first, (uint32_t)last, c, nullptr);
     if (hipGetLastError() != hipSuccess)
         return ZERO_EHIP;
     return ZERO_OK;
@@ -1577,6 +1816,33 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
         if (vec != 1)
             break;
     }
+    // Only the outputs out of phase (a parameter view at an offset that is
+    // not a multiple of four elements): the same paths with the outputs'
+    // stores shifted, on shards of kTileAlignMinElems or more, as the Adam
+    // plan does.
+    bool shift = false;
+    uint32_t pshift = 0, gshift = 0;
+    if (vec == 1 && n >= zs::kTileAlignMinElems) {
+        for (uint32_t want : {8u, 4u}) {
+            for (uint32_t h = 0; h < want && vec == 1; h++) {
+                bool ok = (w + 4u * h) % 16 == 0 && (mm + 4u * h) % 16 == 0 &&
+                          (vv + 4u * h) % 16 == 0;
+                for (uint32_t r = 0; r < nd && ok; r++)
+                    ok = (a16[r] + 2u * h) % (2u * want) == 0;
+                if (ok) {
+                    vec = want;
+                    head = h;
+                }
+            }
+            if (vec != 1)
+                break;
+        }
+        if (vec != 1) {
+            shift = true;
+            pshift = (uint32_t)((p / 2u + head) % 4u);
+            gshift = go ? (uint32_t)((go / 2u + head) % 4u) : 0u;
+        }
+    }
     const uint64_t h = head < n ? head : n;
     const uint64_t ntiles = (n - h + kTile - 1) / kTile + (n == h ? 1 : 0);
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
@@ -1587,14 +1853,24 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late) * (vec == 1 ? 2u : 1u));
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
-    const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16};
+    const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16, pshift,
+                         gshift};
     hipStream_t st = (hipStream_t)stream;
-    if (vec == 8 && late)
+    if (vec == 8 && late && shift)
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8, true, true>), dim3(grid), dim3(kWave), lds,
+                           st, args, nd, n, head, ntiles, F, c, nonfinite_flag);
+    else if (vec == 8 && late)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8, true>), dim3(grid), dim3(kWave), lds, st, args,
                            nd, n, head, ntiles, F, c, nonfinite_flag);
+    else if (vec == 8 && shift)
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8, false, true>), dim3(grid), dim3(kWave), lds,
+                           st, args, nd, n, head, ntiles, F, c, nonfinite_flag);
     else if (vec == 8)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 8>), dim3(grid), dim3(kWave), lds, st, args, nd,
                            n, head, ntiles, F, c, nonfinite_flag);
+    else if (vec == 4 && shift)
+        hipLaunchKernelGGL((zs_fused_kernel<Fmt, 4, false, true>), dim3(grid), dim3(kWave), lds,
+                           st, args, nd, n, head, ntiles, F, c, nonfinite_flag);
     else if (vec == 4)
         hipLaunchKernelGGL((zs_fused_kernel<Fmt, 4>), dim3(grid), dim3(kWave), lds, st, args, nd,
                            n, head, ntiles, F, c, nonfinite_flag);
@@ -1829,6 +2105,6 @@ extern "C" int zero_adam_step_noalloc(const zero_tensor *tensors, uint32_t n_ten
             return ZERO_EHIP;
     }
     const size_t lds = lds_cap_bytes(dev, (uint32_t)stats.wg_per_cu);
-    return launch_adam_table(d_tensors, d_chunks, stats, lds, false, c, nonfinite_flag,
-                             skip_if_nonzero, nullptr, st);
+    return launch_adam_table(d_tensors, d_chunks, stats, lds, false, zs::any_shift(d, nd), c,
+                             nonfinite_flag, skip_if_nonzero, nullptr, st);
 }
