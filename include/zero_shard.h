@@ -441,7 +441,10 @@ int zero_reduce_adam_step_bf16(const void *const *slices_bf16, uint32_t nd, uint
  * shards_f16: host array of nd device pointers (read only; they may
  *   overlap each other; a shard not already in place must not overlap any
  *   part of full).  Fastest when full sits on a 128-byte line and
- *   shard_len is a multiple of 64 (every destination on a line).
+ *   shard_len is a multiple of 64 (every destination on a line); from
+ *   1,024 elements a source out of its destination's 4-element phase is
+ *   read as whole aligned 8-byte words (which may reach up to 3 elements
+ *   past either end of the shard; those values are not used).
  * full_f16: device pointer to nd * shard_len fp16, written.
  * Asynchronous; allocates nothing.  shard_len = 0 launches nothing.
  * Errors: EINVAL (NULL arrays, nd = 0 or > ZERO_MAX_SLICES, a pointer not

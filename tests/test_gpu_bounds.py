@@ -242,11 +242,12 @@ def test_fused_bounds(zs, fmt, layout, nd):
 @pytest.mark.parametrize("layout", ["aligned", "dst_off", "src_off"])
 def test_gather_bounds(zs, layout):
     """zero_gather_shards into a full buffer (destination on a line, or one
-    element off it; sources at other phases), every shard moved except the
-    one already in place."""
+    element off it; sources at other phases, read shifted from 1,024
+    elements, whole aligned words that may reach past a shard's ends), every
+    shard moved except the one already in place."""
     import torch
     say(f"bounds: gather layout={layout}")
-    for S in (1, 63, 64, 65, 2047, 2048, 2049, 5000):
+    for S in (1, 63, 64, 65, 1026, 2047, 2048, 2049, 4099, 5000):
         nd = 5
         fo = 2 if layout == "dst_off" else 0
         specs = [(2 * S * nd, fo)] + [(2 * S, 2 * (r % 3) if layout == "src_off" else 0)

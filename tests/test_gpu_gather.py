@@ -36,11 +36,13 @@ def zs():
 
 @pytest.mark.parametrize("nd", [1, 2, 3, 8, 64, 256])
 def test_gather_matches_oracle(zs, nd):
-    """Shards at every source phase (so each takes its own access width),
-    ragged lengths, and one shard already in place in the full buffer."""
+    """Shards at every source phase (so each takes its own access width;
+    from 1,024 elements a source out of its destination's 4-element phase
+    is read shifted), ragged lengths of every residue mod 4, and one shard
+    already in place in the full buffer."""
     import torch
     rng = np.random.default_rng(nd)
-    for S in (1, 7, 511, 512, 513, 4099, 70001):
+    for S in (1, 7, 511, 512, 513, 1023, 1024, 4098, 4099, 65540, 70001):
         say(f"gather nd={nd} S={S}")
         hs = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(nd)]
         full = torch.zeros(nd * S, dtype=torch.float16, device="cuda")

@@ -1242,8 +1242,11 @@ __global__ __launch_bounds__(kWave) void zs_fused_kernel(SliceArgs s, uint32_t n
 // ---------------------------------------------------------------------------
 struct GatherArgs {
     const uint16_t *src[ZERO_MAX_SLICES];
-    uint8_t vec[ZERO_MAX_SLICES];  // 8, 4, 2 or 1 elements per access; 0: in place, skip
-    uint8_t head[ZERO_MAX_SLICES]; // leading elements copied singly
+    uint8_t vec[ZERO_MAX_SLICES];   // 8, 4, 2 or 1 elements per access; 3: four, the
+                                    // source read shifted; 0: in place, skip
+    uint8_t head[ZERO_MAX_SLICES];  // leading elements copied singly
+    uint8_t shift[ZERO_MAX_SLICES]; // vec 3: the source's element phase mod 4 at
+                                    // the destination's vector-aligned elements
 };
 
 template <typename V>
@@ -1288,6 +1291,40 @@ __device__ __forceinline__ void gather_tile(const uint16_t *src, uint16_t *dst, 
         as_global(dst)[i] = as_global(src)[i];
 }
 
+// Tile j of shard r when the source is s elements (1-3) out of the
+// destination's phase: the tiles of gather_tile's four-element path, each
+// lane reading its groups as two whole aligned words of the source
+// (load_shifted) and storing them as aligned 8-byte vectors on the
+// destination's lines.
+__device__ __forceinline__ void gather_tile_shifted(const uint16_t *src, uint16_t *dst,
+                                                    uint64_t S, uint32_t head, uint64_t j,
+                                                    uint32_t s) {
+    const uint32_t lane = threadIdx.x;
+    const uint64_t h = head < S ? head : S;
+    if (j == 0 && lane < h)
+        as_global(dst)[lane] = as_global(src)[lane];
+    const uint64_t lo = h + j * zs::kGatherTile;
+    if (lo >= S)
+        return;
+    const uint64_t hi = min(S, lo + zs::kGatherTile);
+    if (hi - lo == zs::kGatherTile) {
+        constexpr int G = zs::kGatherTile / (kWave * 4);
+        uint64_t x[G];
+#pragma unroll
+        for (int k = 0; k < G; k++)
+            x[k] = load_shifted(src, s, lo + (lane + kWave * k) * 4u);
+#pragma unroll
+        for (int k = 0; k < G; k++)
+            st_nt(x[k], reinterpret_cast<uint64_t *>(dst + lo + (lane + kWave * k) * 4u));
+        return;
+    }
+    const uint64_t ngroups = (hi - lo) / 4u;
+    for (uint64_t q = lane; q < ngroups; q += kWave)
+        st_nt(load_shifted(src, s, lo + q * 4u), reinterpret_cast<uint64_t *>(dst + lo + q * 4u));
+    for (uint64_t i = lo + ngroups * 4u + lane; i < hi; i += kWave)
+        as_global(dst)[i] = as_global(src)[i];
+}
+
 // Grid: x over a shard's tiles (striding when a shard has more than the
 // launch's x extent), y over the shards, so consecutive workgroups take
 // consecutive tiles of one shard and no workgroup divides to find its
@@ -1306,6 +1343,7 @@ __global__ __launch_bounds__(kWave) void zs_gather_kernel(GatherArgs a, uint64_t
         switch (vec) {
         case 8: gather_tile<8, f16x8>(src, dst, S, head, j); break;
         case 4: gather_tile<4, f16x4>(src, dst, S, head, j); break;
+        case 3: gather_tile_shifted(src, dst, S, head, j, a.shift[r]); break;
         case 2: gather_tile<2, u16x2>(src, dst, S, head, j); break;
         default: gather_tile<1, uint16_t>(src, dst, S, head, j); break;
         }
@@ -1921,6 +1959,7 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
         const uintptr_t d = f + (uintptr_t)r * sb;
         args.src[r] = (const uint16_t *)shards_f16[r];
         args.head[r] = 0;
+        args.shift[r] = 0;
         if (s == d) {
             args.vec[r] = 0; // already in place
             continue;
@@ -1940,6 +1979,11 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
             }
         }
         const uint32_t head = (uint32_t)(((zs::kLine - d % zs::kLine) % zs::kLine) / 2u);
+        if (vec < 4 && shard_len >= zs::kTileAlignMinElems) {
+            // out of 4-element phase: four at a time, the source read shifted
+            vec = 3;
+            args.shift[r] = (uint8_t)((s / 2u + head) % 4u);
+        }
         args.vec[r] = (uint8_t)vec;
         args.head[r] = (uint8_t)head;
         moving++;
@@ -1948,6 +1992,7 @@ extern "C" int zero_gather_shards(const void *const *shards_f16, uint32_t nd, ui
         args.src[r] = nullptr;
         args.vec[r] = 0;
         args.head[r] = 0;
+        args.shift[r] = 0;
     }
     if (shard_len == 0 || moving == 0)
         return ZERO_OK;
