@@ -97,8 +97,12 @@ typedef struct zero_plan_stats {
     uint64_t n_chunks;      /* work items; one workgroup handles one at a time */
     uint64_t chunk_elems;   /* elements per chunk (a tensor's first chunk also
                                holds its peeled head; its last may be short) */
-    uint64_t vector_elems;  /* elements moved four at a time (8-byte fp16 and
-                               16-byte fp32 vectors) */
+    uint64_t vector_elems;  /* elements of tensors on the vector path (8-byte
+                               fp16 and 16-byte fp32 vectors) outside their
+                               single heads and tails; a partial last tile
+                               or small chunk of more than 64 elements is
+                               still updated element by element, in one
+                               pass over memory */
     uint64_t scalar_elems;  /* elements done one at a time (heads, tails,
                                tensors whose arrays disagree in alignment,
                                except the 16-bit arrays alone on tensors of

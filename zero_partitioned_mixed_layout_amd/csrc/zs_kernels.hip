@@ -28,7 +28,9 @@
 // single-element path; gather 16).  Measured on MI355X, HBM3E streams these
 // many-array patterns fastest with just enough bytes in flight to cover
 // latency (about 45 KB per CU); with the 20-30 waves per CU that registers
-// alone would allow, the same streams run 10-15% slower.
+// alone would allow, the same streams run 10-15% slower.  The Adam kernels
+// are built for 7 waves per SIMD so that registers never cap below the 27
+// workgroups per CU that plans of small tensors take.
 //
 // Exactness: every arithmetic step is one IEEE binary32 operation in a fixed
 // order; the library is built with -ffp-contract=off (no fused multiply-add),
@@ -348,6 +350,52 @@ __device__ __forceinline__ void quad_load_mode(const TensorDesc &T, uint64_t i, 
     }
 }
 
+// count (65..64 G) consecutive elements from `lo` in one pass over memory,
+// whatever the arrays' phases: lane L takes elements L + 64k, k < G, every
+// lane loading all G of its elements first (an index past the end clamped
+// to the last element, so that no load waits on a lane condition and the
+// wave waits on memory once), then updating and storing those in range.
+// It takes a tensor's partial last tile, or a whole small chunk, of more
+// than 64 elements, which the head / groups / singles sequence covered in
+// two or three passes.  Measured on MI355X against that sequence (one
+// process, identical outputs, fraction of 8 TB/s): lists of 300- and
+// 1,000-element tensors 0.56 and 0.75 against 0.48 and 0.60, random sizes
+// 1-1,024 0.70 against 0.57 and 1-8,192 0.70 against 0.65; at 64
+// elements or fewer, where the sequence is one pass, the span's seven
+// extra loads per lane and array lost (0.36 against 0.38-0.44), so those
+// keep it.
+template <class Fmt, int G>
+__device__ __forceinline__ void adam_span_g(const TensorDesc &T, uint64_t lo, uint32_t count,
+                                            const AdamConsts &c, int &bad) {
+    const uint32_t lane = threadIdx.x;
+    uint16_t gb[G];
+    float w[G], m[G], v[G];
+#pragma unroll
+    for (int k = 0; k < G; k++) {
+        const uint64_t i = lo + min(lane + kWave * k, count - 1u);
+        gb[k] = as_global(T.g)[i];
+        w[k] = as_global(T.w)[i];
+        m[k] = as_global(T.m)[i];
+        v[k] = as_global(T.v)[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < G; k++) {
+        if (lane + kWave * k >= count)
+            continue;
+        const uint64_t i = lo + lane + kWave * k;
+        typename Fmt::T gh;
+        memcpy(&gh, &gb[k], 2);
+        const typename Fmt::T p = adam_elem<Fmt>((float)gh, w[k], m[k], v[k], c, bad);
+        as_global(T.w)[i] = w[k];
+        as_global(T.m)[i] = m[k];
+        as_global(T.v)[i] = v[k];
+        uint16_t pb;
+        memcpy(&pb, &p, 2);
+        as_global(T.p)[i] = pb;
+    }
+}
+
 // A full Adam tile: TILE consecutive elements from `base` (vector-aligned),
 // TILE / 256 groups of four per lane.  Lane L takes elements 4L..4L+3 of
 // every 256, so each of the wave's load and store instructions covers one
@@ -429,6 +477,22 @@ template <class Fmt, uint32_t TILE, int MODE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
+    if (ch.count < TILE && ch.count > kWave) {
+        // the whole chunk (a small tensor, its head included) in one pass:
+        // whole groups of four, one per lane, when it is just that (in
+        // phase, from a vector-aligned start, at most 64 groups), else
+        // element by element
+        if (j != 0)
+            return;
+        const uint32_t head = ch.start == 0 ? T.head : 0u;
+        if (MODE == kInPhase && head == 0 && ch.count % 4u == 0 && ch.count <= 4u * kWave) {
+            if (lane < ch.count / 4u)
+                adam_quads<Fmt, kInPhase>(T, ch.start, lane, ch.count / 4u, c, bad);
+        } else {
+            adam_span_g<Fmt, TILE / kWave>(T, ch.start, ch.count, c, bad);
+        }
+        return;
+    }
     const uint32_t head = ch.start == 0 ? min(T.head, ch.count) : 0u;
     if (j == 0 && head != 0)
         adam_head<Fmt, MODE>(T, head, c, bad);
@@ -443,21 +507,14 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
         return; // past the end of a short chunk
     const uint64_t rbase = base + (uint64_t)nfull * TILE;
     const uint32_t rem = body - nfull * TILE; // < TILE
-    const uint32_t nquads = rem / 4u;
-    if constexpr (MODE != kInPhase) {
-        for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
-            const uint32_t nq = min(nquads - r0, kWave);
-            if (lane < nq)
-                adam_quads<Fmt, MODE>(T, rbase + 4u * r0, lane, nq, c, bad);
-        }
-    } else {
-        for (uint32_t q = lane; q < nquads; q += kWave) {
-            Quad<Fmt> x;
-            const uint64_t i = rbase + 4u * q;
-            quad_load<Fmt>(T, i, x);
-            st_nt(quad_update<Fmt>(T, i, x, c, bad), reinterpret_cast<typename Fmt::V4 *>(T.p + i));
-        }
+    if (rem > kWave) {
+        adam_span_g<Fmt, TILE / kWave>(T, rbase, rem, c, bad);
+        return;
     }
+    // at most 64 elements: at most 16 groups of four, then singly
+    const uint32_t nquads = rem / 4u;
+    if (lane < nquads)
+        adam_quads<Fmt, MODE>(T, rbase, lane, nquads, c, bad);
     const uint32_t tail = rem - 4u * nquads;
     if (lane < tail)
         adam_single<Fmt>(T, rbase + 4u * nquads + lane, c, bad);
@@ -485,6 +542,8 @@ template <class Fmt, uint32_t TILE>
 __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chunk &ch,
                                                  uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lo = j * TILE;
+    if (lo >= ch.count)
+        return; // past the end of a short chunk
     const uint32_t hi = min(ch.count, lo + TILE);
     if (hi - lo == TILE) {
         constexpr int G = TILE / kWave;
@@ -515,8 +574,12 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
         }
         return;
     }
-    for (uint32_t k = lo + threadIdx.x; k < hi; k += kWave)
-        adam_single<Fmt>(T, ch.start + k, c, bad);
+    if (hi - lo > kWave) {
+        adam_span_g<Fmt, TILE / kWave>(T, ch.start + lo, hi - lo, c, bad);
+        return;
+    }
+    if (threadIdx.x < hi - lo)
+        adam_single<Fmt>(T, ch.start + lo + threadIdx.x, c, bad);
 }
 
 // The fused step over a plan.  Each workgroup is one wave and takes one Adam
@@ -525,7 +588,7 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
 // stride over them.  Fmt: the 16-bit format of parameters and gradients;
 // TILE: the plan's Adam tile (kAdamTileFine or kTile elements).
 template <class Fmt, uint32_t TILE, bool SHIFTS>
-__global__ __launch_bounds__(kWave) void zs_adam_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(7))) void zs_adam_kernel(
     const TensorDesc *__restrict__ tensors, const Chunk *__restrict__ chunks,
     uint64_t n_virtual, uint32_t tiles_per_chunk, AdamConsts c, int32_t *__restrict__ flag,
     const int32_t *__restrict__ skip, const int32_t *__restrict__ log2_scale) {
