@@ -195,7 +195,7 @@ int zero_comm_volume(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t align,
  * packed at offsets that are not multiples of 256 elements streams about 3%
  * faster so (measured).  The step keeps wg_per_cu one-wave workgroups
  * resident per CU: 12 with 256-element tiles, and with 512-element tiles 7
- * unless at least one tile in 20 holds a head or a tensor's partial last
+ * unless at least one tile in 200 holds a head or a tensor's partial last
  * tile, when the cap grows as the tiles' average element count e shrinks,
  * 7 * 512 / e + 7 within 14..27, 19 and 21 taken as 20 and 22 (lists of
  * small tensors wait on memory more per element; measured up to twice as

@@ -341,7 +341,7 @@ def _packed(zs, sizes):
 
 def test_plan_occupancy_cap(zs):
     """wg_per_cu: 12 with 256-element tiles; with 512-element tiles 7 while
-    fewer than one tile in 20 holds a head or a partial last tile, else
+    fewer than one tile in 200 holds a head or a partial last tile, else
     7 * 512 / e + 7 within 14..27 (e: elements per tile with work), 19 and
     21 taken as 20 and 22."""
     d = _packed(zs, [1 << 26])
@@ -361,10 +361,10 @@ def test_plan_occupancy_cap(zs):
     assert _packed(zs, [200] * 1000)["wg_per_cu"] == 25
     # e = 400 (tensors of 800: two tiles, one partial): round(8.96 + 7) = 16
     assert _packed(zs, [800] * 1000)["wg_per_cu"] == 16
-    # mostly whole tiles: 19 tensors of 512 and one of 100 per 20 tensors
-    # (1 irregular tile in 20: the cap moves; 1 in 21 does not)
-    assert _packed(zs, ([512] * 19 + [100]) * 50)["wg_per_cu"] == 14
-    assert _packed(zs, ([512] * 20 + [100]) * 50)["wg_per_cu"] == 7
+    # mostly whole tiles: 199 tensors of 512 and one of 100 per 200 tensors
+    # (1 irregular tile in 200: the cap moves; 1 in 201 does not)
+    assert _packed(zs, ([512] * 199 + [100]) * 5)["wg_per_cu"] == 14
+    assert _packed(zs, ([512] * 200 + [100]) * 5)["wg_per_cu"] == 7
     # single-element tensors of whole tiles (m one element off)
     one_off = [((1 << 40) + (k << 20), (1 << 41) + (k << 20), (1 << 42) + (k << 20),
                 (1 << 43) + (k << 20) + 4, (1 << 44) + (k << 20), 1024) for k in range(100)]

@@ -86,20 +86,25 @@ inline uint32_t adam_per_cu(uint32_t tile) { return tile == kAdamTileFine ? 12u 
 
 // The coarse tile's cap for a plan whose `work` tiles hold elements, of
 // which `irregular` hold a tensor's head or its partial last tile.  Such
-// tiles wait on memory more than once and carry fewer bytes, so a plan of
-// many of them needs more waves in flight: with fewer than one irregular
-// tile in 20 the cap stays at 7, else it is 7 * 512 / e + 7 within 14..27
-// (19 and 21 taken as 20 and 22, the counts their LDS reservation admits),
-// where e is the average element count of a tile with work.  Measured on
-// MI355X (lists in flattened buffers at their packed offsets, caps 7..28
-// and uncapped, one process each; fraction of 8 TB/s at the best cap
-// against cap 7): 100,000 x 1,024 (no irregular tiles) best at 7; 20,000
-// of 1-8,000 elements 0.655 at 14-18 against 0.608; 50,000 of 1-2,000
-// 0.673 at 14 against 0.531; 100,000 of 1-600 0.542 at 18-22 against
-// 0.325; 100,000 x 300 0.510 at 14 against 0.376; 100,000 x 100 0.461
-// uncapped (28, as many as the kernel's registers allow) against 0.229.
+// tiles carry fewer bytes and a partial one also more loads per lane, so a
+// plan of many of them needs more waves in flight: with fewer than one
+// irregular tile in 200 the cap stays at 7, else it is 7 * 512 / e + 7
+// within 14..27 (19 and 21 taken as 20 and 22, the counts their LDS
+// reservation admits), where e is the average element count of a tile with
+// work.  Measured on MI355X (lists in flattened buffers at their packed
+// offsets, caps 7..28 and uncapped, one process each; fraction of 8 TB/s
+// at the best cap against cap 7): 100,000 x 1,024 (no irregular tiles)
+// best at 7; 20,000 of 1-8,000 elements 0.655 at 14-18 against 0.608;
+// 50,000 of 1-2,000 0.673 at 14 against 0.531; 100,000 of 1-600 0.542 at
+// 18-22 against 0.325; 100,000 x 300 0.510 at 14 against 0.376; 100,000 x
+// 100 0.461 uncapped (28, as many as the kernel's registers allow) against
+// 0.229.  With partial tiles updated in one pass (adam_span_g), caps 7-24
+// in one process: one tensor of 117M and the GPT-2-XL list on 512-element
+// tiles (0.04% irregular tiles) best at 7-8; 1,000 tensors of 1-100,000
+// (2%) 0.714-0.717 at 10-12 and 0.709 at 14 against 0.690 at 7, hence the
+// threshold of one in 200 (it was one in 20).
 inline uint32_t adam_per_cu_coarse(uint64_t work, uint64_t irregular, uint64_t n_params) {
-    if (work == 0 || irregular * 20 < work)
+    if (work == 0 || irregular * 200 < work)
         return 7u;
     const double e = (double)n_params / (double)work;
     const double k = 7.0 * kTile / (e > 1.0 ? e : 1.0) + 7.0;

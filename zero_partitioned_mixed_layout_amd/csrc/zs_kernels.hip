@@ -355,9 +355,9 @@ __device__ __forceinline__ void quad_load_mode(const TensorDesc &T, uint64_t i, 
 // lane loading all G of its elements first (an index past the end clamped
 // to the last element, so that no load waits on a lane condition and the
 // wave waits on memory once), then updating and storing those in range.
-// It takes a tensor's partial last tile, or a whole small chunk, of more
-// than 64 elements, which the head / groups / singles sequence covered in
-// two or three passes.  Measured on MI355X against that sequence (one
+// In the 512-element kernel it takes a tensor's partial last tile, or a
+// whole small chunk, of more than 64 elements, which the head / groups /
+// singles sequence covered in two or three passes.  Measured on MI355X against that sequence (one
 // process, identical outputs, fraction of 8 TB/s): lists of 300- and
 // 1,000-element tensors 0.56 and 0.75 against 0.48 and 0.60, random sizes
 // 1-1,024 0.70 against 0.57 and 1-8,192 0.70 against 0.65; at 64
@@ -477,7 +477,12 @@ template <class Fmt, uint32_t TILE, int MODE>
 __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Chunk &ch,
                                                    uint32_t j, const AdamConsts &c, int &bad) {
     const uint32_t lane = threadIdx.x;
-    if (ch.count < TILE && ch.count > kWave) {
+    // one-pass spans in the 512-element kernel, which plans of small
+    // tensors take; the 256-element kernel (big tensors, one partial tile
+    // each) keeps the former sequence (with the spans compiled in, big
+    // plans ran 0.2% slower)
+    constexpr bool kSpans = TILE == kTile;
+    if (kSpans && ch.count < TILE && ch.count > kWave) {
         // the whole chunk (a small tensor, its head included) in one pass:
         // whole groups of four, one per lane, when it is just that (in
         // phase, from a vector-aligned start, at most 64 groups), else
@@ -507,14 +512,26 @@ __device__ __forceinline__ void adam_tile_of_chunk(const TensorDesc &T, const Ch
         return; // past the end of a short chunk
     const uint64_t rbase = base + (uint64_t)nfull * TILE;
     const uint32_t rem = body - nfull * TILE; // < TILE
-    if (rem > kWave) {
+    if (kSpans && rem > kWave) {
         adam_span_g<Fmt, TILE / kWave>(T, rbase, rem, c, bad);
         return;
     }
-    // at most 64 elements: at most 16 groups of four, then singly
+    // groups of four, one per lane (in rounds of 64), then singly
     const uint32_t nquads = rem / 4u;
-    if (lane < nquads)
-        adam_quads<Fmt, MODE>(T, rbase, lane, nquads, c, bad);
+    if constexpr (MODE != kInPhase) {
+        for (uint32_t r0 = 0; r0 < nquads; r0 += kWave) {
+            const uint32_t nq = min(nquads - r0, kWave);
+            if (lane < nq)
+                adam_quads<Fmt, MODE>(T, rbase + 4u * r0, lane, nq, c, bad);
+        }
+    } else {
+        for (uint32_t q = lane; q < nquads; q += kWave) {
+            Quad<Fmt> x;
+            const uint64_t i = rbase + 4u * q;
+            quad_load<Fmt>(T, i, x);
+            st_nt(quad_update<Fmt>(T, i, x, c, bad), reinterpret_cast<typename Fmt::V4 *>(T.p + i));
+        }
+    }
     const uint32_t tail = rem - 4u * nquads;
     if (lane < tail)
         adam_single<Fmt>(T, rbase + 4u * nquads + lane, c, bad);
@@ -574,12 +591,12 @@ __device__ __forceinline__ void adam_tile_single(const TensorDesc &T, const Chun
         }
         return;
     }
-    if (hi - lo > kWave) {
+    if (TILE == kTile && hi - lo > kWave) {
         adam_span_g<Fmt, TILE / kWave>(T, ch.start + lo, hi - lo, c, bad);
         return;
     }
-    if (threadIdx.x < hi - lo)
-        adam_single<Fmt>(T, ch.start + lo + threadIdx.x, c, bad);
+    for (uint32_t k = lo + threadIdx.x; k < hi; k += kWave)
+        adam_single<Fmt>(T, ch.start + k, c, bad);
 }
 
 // The fused step over a plan.  Each workgroup is one wave and takes one Adam
