@@ -405,3 +405,67 @@ def test_shifted_outputs_fused_route(zs, nd, slices, outs):
         bad += sum(x["not_bit_exact"] for x in r)
         assert int(flag.item()) == (rflag | aflag)
     assert bad == 0, f"{bad} elements within tolerance but not bit-exact"
+
+
+@pytest.mark.parametrize("route", ["fused_nd8_p1_g3", "split_nd32_in_place_p2", "reduce_nd16_o1",
+                                   "reduce_nd4_v8_o3"])
+def test_shifted_bfloat16_routes(zs, route):
+    """The bfloat16 instantiations of the shifted stores and loads: the
+    fused kernel (8 slices, parameter and gradient output out of phase), the
+    split route in place (32 slices, no gradient output) and the reduce into
+    a shifted output (16-byte and 8-byte paths); bit-exact against the
+    oracle in bfloat16, the bytes around each written view untouched."""
+    import torch
+    kind, nd = route.split("_")[0], int(route.split("_")[1][2:])
+    rng = np.random.default_rng(800 + len(route))
+    for n in (1029, 4096 + 259, 70001):
+        say(f"param shift: bf16 {route} n={n}")
+        hs = [oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+              for _ in range(nd)]
+        so = 4 if route.endswith("v8_o3") else 0
+        ds = []
+        for r in range(nd):
+            b = _aligned(torch, n + so, torch.bfloat16)[so:]
+            b.copy_(to_dev16(hs[r]).view(torch.bfloat16))
+            ds.append(b)
+        g_ref, rflag = oracle.reduce_grad(hs, fmt="bf16")
+        what = f"bf16 {route} n={n}"
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if kind == "reduce":
+            os_ = int(route[-1])
+            obuf = _aligned(torch, n + 8, torch.bfloat16)
+            zs.zero_reduce_grad_shard(ds, obuf[os_:os_ + n], nonfinite_flag=flag)
+            torch.cuda.synchronize()
+            got = host16(obuf)
+            assert not got[:os_].any() and not got[os_ + n:].any(), what + ": guard"
+            assert np.array_equal(got[os_:os_ + n], g_ref), what
+            assert int(flag.item()) == rflag
+            continue
+        ps = 1 if kind == "fused" else 2
+        gs = 3 if kind == "fused" else None
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v0 = (rng.random(n) * 1e-6).astype(np.float32)
+        pbuf = _aligned(torch, n + 8, torch.bfloat16)
+        gbuf = _aligned(torch, n + 8, torch.bfloat16) if gs is not None else None
+        w, m, v = (_aligned(torch, n, torch.float32) for _ in range(3))
+        w.copy_(to_dev32(w0))
+        m.copy_(to_dev32(m0))
+        v.copy_(to_dev32(v0))
+        zs.zero_reduce_adam_step(ds, pbuf[ps:ps + n], w, m, v, zs.AdamHParams(**HP), 3,
+                                 grad_out=gbuf[gs:gs + n] if gs is not None else None,
+                                 nonfinite_flag=flag)
+        p_ref = np.zeros(n, np.uint16)
+        aflag = oracle.adam_step(g_ref, p_ref, w0, m0, v0, t=3, fmt="bf16", **HP)
+        torch.cuda.synchronize()
+        hp_all = host16(pbuf)
+        assert not hp_all[:ps].any() and not hp_all[ps + n:].any(), what + ": param guard"
+        r = [check16(hp_all[ps:ps + n], p_ref, what + " param", fmt="bf16"),
+             check32(host32(w), w0, what + " master"), check32(host32(m), m0, what + " m"),
+             check32(host32(v), v0, what + " v")]
+        if gs is not None:
+            hg = host16(gbuf)
+            assert not hg[:gs].any() and not hg[gs + n:].any(), what + ": grad guard"
+            r.append(check16(hg[gs:gs + n], g_ref, what + " grad", fmt="bf16"))
+        assert sum(x["not_bit_exact"] for x in r) == 0, what
+        assert int(flag.item()) == (rflag | aflag)
