@@ -195,6 +195,17 @@ inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
     return reduce_per_cu(nd);
 }
 
+// The same for zs_reduce_few_kernel (1-3 slices, four groups per lane, 4 N_d
+// 16-byte loads per lane in flight): about 100 such loads per lane per CU.
+// Measured on MI355X over 117,187,500 elements, caps 8-28 in one process
+// (fraction of 8 TB/s at 2 N_d + 2 bytes per element, against 0.521 /
+// 0.554 / 0.577 with one group per lane): N_d = 1 0.861-0.868 at 24-28
+// (0.845 at 16), N_d = 2 0.867-0.868 at 16-20, N_d = 3 0.853 at 8 (0.844 at
+// 12, 0.828 at 16).
+inline uint32_t reduce_per_cu_few(uint32_t nd) {
+    return nd == 1 ? 27u : (nd == 2 ? 16u : 8u);
+}
+
 // Whether the fused step's 16-byte path loads a tile's fp32 state after the
 // slices (then it arrives while the reduced gradients cross the LDS) instead
 // of with the first slice batch.  Measured on MI355X, one process, 937.5M

@@ -24,7 +24,8 @@
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
 // tiles, 14-27 for lists of small tensors; reduce 4-6 when 16 slices are
-// in flight per lane, 8 at 8, 16 at fewer; fused 5-12, twice that on its
+// in flight per lane, 8 at 8, 16 at 4-7, 27 / 16 / 8 at 1 / 2 / 3 slices
+// (four groups per lane there); fused 5-12, twice that on its
 // single-element path; gather 16).  Measured on MI355X, HBM3E streams these
 // many-array patterns fastest with just enough bytes in flight to cover
 // latency (about 45 KB per CU); with the 20-30 waves per CU that registers
@@ -830,6 +831,68 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
     } else if (VEC > 1) {
         for (uint64_t k = gtid; k < ngroups; k += gstride)
             reduce_group<Fmt, VEC == 8 ? 8 : 4>(s, nd, h + k * VEC, count, out, bad);
+    }
+    raise_flag(flag, bad);
+}
+
+// The reduction over ND = 1-3 slices on the 16-byte path: each lane takes
+// four groups of eight (groups lane + 64q of the wave's 256) and issues all
+// 4 ND of its 16-byte loads before the first add (indices past the last
+// group clamped to it, so no load waits on a lane condition); then the
+// rank-order sum and the division of reduce_group per group, the stores of
+// those in range.  With one group per lane and batches of one slice, a wave
+// moved 2-6 KiB in 1-3 dependent round trips: 0.53-0.58 of 8 TB/s.  The
+// unaligned head and the tail past the last whole group go one element per
+// lane, as in zs_reduce_kernel.
+template <class Fmt, int ND>
+__global__ __launch_bounds__(kWave) void zs_reduce_few_kernel(SliceArgs s, uint64_t n,
+                                                              uint32_t head,
+                                                              uint16_t *__restrict__ out,
+                                                              int32_t *__restrict__ flag) {
+    constexpr int Q = 4;
+    typedef typename Fmt::V8 hv;
+    const float count = (float)ND;
+    const uint32_t lane = threadIdx.x;
+    const uint64_t gtid = (uint64_t)blockIdx.x * kWave + lane;
+    const uint64_t gstride = (uint64_t)gridDim.x * kWave;
+    int bad = 0;
+    const uint64_t h = head < n ? head : n;
+    const uint64_t ngroups = (n - h) / 8u;
+    const uint64_t body_end = h + ngroups * 8u;
+    if (gtid < h)
+        reduce_one<Fmt>(s, ND, gtid, count, out, bad);
+    for (uint64_t i = body_end + gtid; i < n; i += gstride)
+        reduce_one<Fmt>(s, ND, i, count, out, bad);
+    for (uint64_t k0 = (uint64_t)blockIdx.x * kWave * Q; k0 < ngroups; k0 += gstride * Q) {
+        hv x[Q][ND];
+#pragma unroll
+        for (int q = 0; q < Q; q++) {
+            const uint64_t g = min(k0 + lane + (uint64_t)kWave * q, ngroups - 1u);
+#pragma unroll
+            for (int r = 0; r < ND; r++)
+                x[q][r] = ld_nt(reinterpret_cast<const hv *>(s.p[r] + h + g * 8u));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < Q; q++) {
+            const uint64_t g = k0 + lane + (uint64_t)kWave * q;
+            if (g >= ngroups)
+                continue;
+            hv o;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                float acc = (float)x[q][0][j];
+#pragma unroll
+                for (int r = 1; r < ND; r++)
+                    acc = acc + (float)x[q][r][j];
+                o[j] = (typename Fmt::T)(acc / count);
+                const typename Fmt::T oj = o[j];
+                uint16_t b;
+                memcpy(&b, &oj, 2);
+                bad |= bits_nonfinite<Fmt>(b);
+            }
+            st_through(o, reinterpret_cast<hv *>(out + h + g * 8u));
+        }
     }
     raise_flag(flag, bad);
 }
@@ -1767,6 +1830,26 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     uint16_t *out = (uint16_t *)out_f16;
+    if (vec == 8 && oshift == 0 && nd <= 3) {
+        // 1-3 slices: four groups per lane, all loads in flight at once
+        const uint64_t groups = (n - hh) / 8;
+        const uint64_t w4 = (groups + 4 * kWave - 1) / (4 * kWave);
+        const uint64_t wf = w4 > 0 ? w4 : 1;
+        const uint32_t gf = (uint32_t)(wf < zs::kMaxGrid ? wf : zs::kMaxGrid);
+        const size_t lf = lds_cap_bytes(dev, zs::reduce_per_cu_few(nd));
+        if (nd == 1)
+            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 1>), dim3(gf), dim3(kWave), lf, st,
+                               args, n, head, out, nonfinite_flag);
+        else if (nd == 2)
+            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 2>), dim3(gf), dim3(kWave), lf, st,
+                               args, n, head, out, nonfinite_flag);
+        else
+            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 3>), dim3(gf), dim3(kWave), lf, st,
+                               args, n, head, out, nonfinite_flag);
+        if (hipGetLastError() != hipSuccess)
+            return ZERO_EHIP;
+        return ZERO_OK;
+    }
     if (vec == 8 && oshift != 0)
         hipLaunchKernelGGL((zs_reduce_kernel<Fmt, 8, true>), dim3(grid), dim3(kWave), lds, st,
                            args, nd, n, head, out, nonfinite_flag, oshift);
