@@ -178,7 +178,7 @@ REDUCE_LAYOUTS = {"v16": (0, 0, 0), "v8": (0, 8, 0), "single": (0, 0, 2)}
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("layout", list(REDUCE_LAYOUTS))
-@pytest.mark.parametrize("nd", [1, 2, 3, 4, 17, 64])
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 7, 15, 17, 19, 64])
 def test_reduce_bounds(zs, fmt, layout, nd):
     import torch
     say(f"bounds: reduce fmt={fmt} layout={layout} nd={nd}")

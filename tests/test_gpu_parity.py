@@ -322,6 +322,38 @@ def test_reduce_matches_oracle(zs, torch_mod, nd, layout):
         assert int(flag.item()) == rflag == 0
 
 
+@pytest.mark.parametrize("nd", [4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 23, 31, 47])
+@pytest.mark.parametrize("oshift", [0, 3])
+def test_reduce_every_batch_size(zs, torch_mod, nd, oshift):
+    """The 16-byte path loads batches of 16 slices and then the rest in one
+    batch: every rest of 1-15 slices (after zero, one and two batches of
+    16), with the output in the slices' phase and three elements off it,
+    against the oracle bit for bit; a non-finite value in the last slice of
+    the rest raises the flag."""
+    torch = torch_mod
+    rng = np.random.default_rng(5000 + nd)
+    n = 9 * 512 + 13
+    say(f"reduce batches nd={nd} oshift={oshift} n={n}")
+    hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
+    ds = [to_dev16(h) for h in hs]
+    obuf = torch.zeros(n + 8, dtype=torch.float16, device="cuda")
+    out = obuf[oshift:oshift + n]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_reduce_grad_shard(ds, out, flag)
+    ref, rflag = oracle.reduce_grad(hs)
+    torch.cuda.synchronize()
+    assert check16(host16(out), ref, f"reduce nd={nd}")["not_bit_exact"] == 0
+    assert int(flag.item()) == rflag == 0
+    assert not host16(obuf[:oshift]).any() and not host16(obuf[oshift + n:]).any()
+    hs[-1][n // 2] = 0x7C00
+    ds[-1].copy_(to_dev16(hs[-1]))
+    zs.zero_reduce_grad_shard(ds, out, flag)
+    ref, rflag = oracle.reduce_grad(hs)
+    torch.cuda.synchronize()
+    assert check16(host16(out), ref, f"reduce nd={nd} inf")["not_bit_exact"] == 0
+    assert int(flag.item()) == rflag == 1
+
+
 def test_reduce_special_values(zs, torch_mod):
     """N_d = 1 copies all 65,536 patterns; +inf with -inf gives NaN and the
     flag; the fp32 sum does not overflow where the fp16 mean fits."""

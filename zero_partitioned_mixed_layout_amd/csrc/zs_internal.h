@@ -145,13 +145,16 @@ constexpr uint64_t kTileAlignMinElems = 1024;
 constexpr uint64_t kOffloadChunk = 4ull << 20;
 
 // Slices whose fp16 vectors one lane keeps in flight at once when reducing
-// nd slices (the kernels load batches of 16, 8, 4, then 1).
+// nd slices in batches of 16, 8, 4, then 1 (the fused kernel and the
+// reduce's 8-byte and single-element paths).
 inline uint32_t slices_in_flight(uint32_t nd) {
     return nd >= 16 ? 16 : (nd >= 8 ? 8 : (nd >= 4 ? 4 : 1));
 }
 
-// Resident one-wave workgroups per CU for the reduction over nd slices:
-// about 64 16-byte vectors per lane in flight per CU, at most 16
+// Resident one-wave workgroups per CU for the reduction over nd slices in
+// batches of 16, 8, 4 and 1 (the 16-byte path before it took the rest
+// after the batches of 16 in one batch; the other paths derive their caps
+// from this): about 64 16-byte vectors per lane in flight per CU, at most 16
 // workgroups (16 with 1-7 slices, 8 with 8-15), and with 16 slices in
 // flight 4, raised to 5 and 6 when a lane runs only two or one batch of 16
 // (a shorter-lived wave needs more of them).  Measured on MI355X over
@@ -170,6 +173,36 @@ inline uint32_t reduce_per_cu(uint32_t nd) {
     }
     const uint32_t batches = (nd + 15) / 16;
     return batches == 1 ? 6 : (batches == 2 ? 5 : 4);
+}
+
+// The same for the reduce's 16-byte path (zs_reduce_kernel, one group of
+// eight per lane), which loads batches of 16 slices and then the rest in
+// one batch, every load of a batch in flight before its first add.
+// Measured on MI355X over 117,187,500 elements, caps 4-16 in one process
+// (fraction of 8 TB/s at 2 N_d + 2 bytes per element, best cap, against
+// batches of 16, 8, 4 and 1 at their caps): N_d = 5 0.880 at 12 (0.846),
+// 6 0.863 at 10 (0.813), 7 0.843 at 10 (0.785), 9-11 0.820-0.840 at 8
+// (0.656-0.758), 13 0.808 at 8 (0.770), 14-15 0.817-0.821 at 6
+// (0.694-0.726), 17 0.812 at 8 (0.734), 19-23 0.804-0.813 at 6
+// (0.626-0.784), 28 0.814 at 5 (0.807), 31 0.796 at 5 (0.701); at 4, 8,
+// 12, 16, 24, 32 and 64 (the same batches as before, or 12 at once
+// against 8 then 4) within 1.1% of the former code.
+inline uint32_t reduce_per_cu_vec8(uint32_t nd) {
+    if (nd <= 4)
+        return 16;
+    if (nd == 5)
+        return 12;
+    if (nd <= 7)
+        return 10;
+    if (nd <= 13)
+        return 8;
+    if (nd <= 16)
+        return 6;
+    if (nd == 17)
+        return 8;
+    if (nd <= 23)
+        return 6;
+    return nd <= 32 ? 5 : 4;
 }
 
 // The same for the reduce's other access paths.  vec = 4 (slices sharing
@@ -192,7 +225,7 @@ inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
         const uint32_t k = 2u * reduce_per_cu(nd);
         return k > 24u ? 24u : k;
     }
-    return reduce_per_cu(nd);
+    return reduce_per_cu_vec8(nd);
 }
 
 // The same for zs_reduce_few_kernel (1-3 slices, four groups per lane, 4 N_d

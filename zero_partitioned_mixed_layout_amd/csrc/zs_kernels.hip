@@ -23,9 +23,9 @@
 // workgroup, and each launch reserves dynamic LDS that the kernel never
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
-// tiles, 14-27 for lists of small tensors; reduce 4-6 when 16 slices are
-// in flight per lane, 8 at 8, 16 at 4-7, 27 / 16 / 8 at 1 / 2 / 3 slices
-// (four groups per lane there); fused 5-12, twice that on its
+// tiles, 14-27 for lists of small tensors; reduce 4-16 on its 16-byte
+// path by slice count, 27 / 16 / 8 at 1 / 2 / 3 slices (four groups per
+// lane there); fused 5-12, twice that on its
 // single-element path; gather 16).  Measured on MI355X, HBM3E streams these
 // many-array patterns fastest with just enough bytes in flight to cover
 // latency (about 45 KB per CU); with the 20-30 waves per CU that registers
@@ -719,9 +719,29 @@ __device__ __forceinline__ void reduce_batch(const SliceArgs &s, uint32_t r0, ui
             acc[j] = (first && q == 0) ? (float)x[0][j] : acc[j] + (float)x[q][j];
 }
 
+// Slices r0 .. r0+rest-1 (rest = 1-15) as one batch: every load in flight
+// before the first add.
+template <int VEC, class Fmt>
+__device__ __forceinline__ void reduce_rest(const SliceArgs &s, uint32_t r0, uint32_t rest,
+                                            uint64_t i, float (&acc)[VEC]) {
+    const bool first = r0 == 0;
+    switch (rest) {
+#define ZS_REST(R)                                                                                 \
+    case R:                                                                                        \
+        reduce_batch<VEC, R, Fmt>(s, r0, i, first, acc);                                          \
+        break;
+        ZS_REST(1) ZS_REST(2) ZS_REST(3) ZS_REST(4) ZS_REST(5) ZS_REST(6) ZS_REST(7) ZS_REST(8)
+        ZS_REST(9) ZS_REST(10) ZS_REST(11) ZS_REST(12) ZS_REST(13) ZS_REST(14) ZS_REST(15)
+#undef ZS_REST
+    default:
+        break;
+    }
+}
+
 // One vector group of VEC outputs at element i: the sum over the nd slices
-// in rank order, in batches of 16, 8, 4 and 1 slices in flight per lane,
-// then one division by nd.
+// in rank order, then one division by nd.  VEC = 8: batches of 16 slices in
+// flight per lane, then the rest in one batch; VEC = 4: batches of 16, 8, 4
+// and 1.
 template <class Fmt, int VEC>
 __device__ __forceinline__ typename HVec<Fmt, VEC>::T reduce_group_value(const SliceArgs &s,
                                                                         uint32_t nd, uint64_t i,
@@ -731,12 +751,17 @@ __device__ __forceinline__ typename HVec<Fmt, VEC>::T reduce_group_value(const S
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
         reduce_batch<VEC, 16, Fmt>(s, r, i, r == 0, acc);
-    for (; r + 8 <= nd; r += 8)
-        reduce_batch<VEC, 8, Fmt>(s, r, i, r == 0, acc);
-    for (; r + 4 <= nd; r += 4)
-        reduce_batch<VEC, 4, Fmt>(s, r, i, r == 0, acc);
-    for (; r < nd; r++)
-        reduce_batch<VEC, 1, Fmt>(s, r, i, r == 0, acc);
+    if constexpr (VEC == 8) {
+        if (r < nd)
+            reduce_rest<VEC, Fmt>(s, r, nd - r, i, acc);
+    } else {
+        for (; r + 8 <= nd; r += 8)
+            reduce_batch<VEC, 8, Fmt>(s, r, i, r == 0, acc);
+        for (; r + 4 <= nd; r += 4)
+            reduce_batch<VEC, 4, Fmt>(s, r, i, r == 0, acc);
+        for (; r < nd; r++)
+            reduce_batch<VEC, 1, Fmt>(s, r, i, r == 0, acc);
+    }
     hv o;
 #pragma unroll
     for (int j = 0; j < VEC; j++) {
