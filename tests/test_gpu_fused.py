@@ -89,7 +89,7 @@ def _run_case(zs, torch, n, nd, layout, with_gout, t, rng, warm=True):
     return sum(r["not_bit_exact"] for r in res)
 
 
-@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 64, 256])
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 31, 32, 33, 64, 256])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 def test_fused_matches_oracle(zs, nd, layout):
     """Sizes from 1 to 70,001 (partial tiles, heads and tails), each access

@@ -257,18 +257,23 @@ inline bool fused_state_late(uint32_t nd) { return slices_in_flight(nd) < 16; }
 constexpr uint32_t kFusedSplitSlices = ZERO_FUSED_SPLIT_SLICES;
 
 // Resident one-wave workgroups per CU for the fused reduce + Adam step.
-// State first: about 70 16-byte vectors per lane in flight per CU, counting
-// the six fp32 state vectors issued with the first slice batch (4 workgroups
-// at N_d >= 16, 5 at N_d = 8: the measured optima), between 2 and 8.  State
-// last: 6 at 8 slices in flight, 8 at 4 and 12 at one.  Measured on MI355X
-// over 117,187,500 elements, caps 6-24, one process per N_d (fraction of
-// 8 TB/s at 2 N_d + 26 bytes per element): N_d = 1 0.798 at 12 against
-// 0.770 at 8; 2 0.798 at 12 against 0.711 at 8; 4 0.801 at 8 against 0.783
-// at 7; 8 and 12 best at 6; 16 and 24 best at 4.
+// State first (the 8-byte and single-element paths, and the 16-byte path
+// from 16 slices): about 70 16-byte vectors per lane in flight per CU,
+// counting the six fp32 state vectors issued with the first slice batch (4
+// workgroups at N_d >= 16, 5 at N_d = 8: the measured optima), between 2
+// and 8.  State last (the 16-byte path below 16 slices, which loads all of
+// its 1-15 slices as one batch): 12 at one slice, 8 at 2-6, 6 at 7-10 and
+// 5 at 11-15.  Measured on MI355X over 117,187,500 elements, caps 4-20, one
+// process (fraction of 8 TB/s at 2 N_d + 26 bytes per element, against the
+// former batches of 8, 4 and 1 at their caps): N_d = 1 0.792 at 12 (0.789),
+// 2 0.783 at 8 (0.785), 3 0.795 at 8 (0.772), 5 0.804 at 8 (0.782), 6
+// 0.753-0.781 at 8 (0.741-0.747), 7 0.772 at 6 (0.707), 9-10 0.784-0.788
+// at 6 (0.711-0.755), 11 0.761-0.763 at 5 (0.670-0.671), 13-15 0.772-0.778
+// at 5 (0.690-0.765); 4, 8 and 12 within 0.4% of the former code.
 inline uint32_t fused_per_cu(uint32_t nd, bool state_late) {
     const uint32_t sif = slices_in_flight(nd);
     if (state_late)
-        return sif == 8 ? 6u : (sif == 4 ? 8u : 12u);
+        return nd == 1 ? 12u : (nd <= 6 ? 8u : (nd <= 10 ? 6u : 5u));
     const uint32_t per_wave = 6 + sif;
     const uint32_t k = (70 + per_wave - 1) / per_wave;
     return k < 2 ? 2 : (k > 8 ? 8 : k);

@@ -1217,7 +1217,8 @@ extern __shared__ __attribute__((aligned(16))) unsigned char zs_lds[];
 
 // A full tile with the slices 16-byte aligned: lane L reduces the 8
 // consecutive elements 8L..8L+7 (16-byte loads, 1 KiB per wave
-// instruction, as zs_reduce_kernel), the fp16 gradients go through LDS to
+// instruction, batches of 16 slices and then the rest in one batch, as
+// zs_reduce_kernel), the fp16 gradients go through LDS to
 // the Adam tile's mapping (lane L: 4L..4L+3 and kTile/2+4L..), and the
 // update runs there.  The fp32 state loads are issued before the slices, or
 // with LATE after them (before the LDS exchange).
@@ -1241,12 +1242,8 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
         reduce_batch<8, 16, Fmt>(s, r, j, r == 0, acc);
-    for (; r + 8 <= nd; r += 8)
-        reduce_batch<8, 8, Fmt>(s, r, j, r == 0, acc);
-    for (; r + 4 <= nd; r += 4)
-        reduce_batch<8, 4, Fmt>(s, r, j, r == 0, acc);
-    for (; r < nd; r++)
-        reduce_batch<8, 1, Fmt>(s, r, j, r == 0, acc);
+    if (r < nd)
+        reduce_rest<8, Fmt>(s, r, nd - r, j, acc);
     typedef typename Fmt::V8 hv8;
     typedef typename Fmt::V4 hv4;
     hv8 g8;
