@@ -324,18 +324,25 @@ def test_reduce_matches_oracle(zs, torch_mod, nd, layout):
 
 @pytest.mark.parametrize("nd", [4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 23, 31, 47])
 @pytest.mark.parametrize("oshift", [0, 3])
-def test_reduce_every_batch_size(zs, torch_mod, nd, oshift):
-    """The 16-byte path loads batches of 16 slices and then the rest in one
-    batch: every rest of 1-15 slices (after zero, one and two batches of
-    16), with the output in the slices' phase and three elements off it,
-    against the oracle bit for bit; a non-finite value in the last slice of
-    the rest raises the flag."""
+@pytest.mark.parametrize("phase", ["aligned", "mixed4"])
+def test_reduce_every_batch_size(zs, torch_mod, nd, oshift, phase):
+    """The 16- and 8-byte paths load batches of 16 slices and then the rest
+    in one batch: every rest of 1-15 slices (after zero, one and two batches
+    of 16), slices 16-byte aligned or every other one 8 bytes off, the
+    output in the slices' phase and three elements off it, against the
+    oracle bit for bit; a non-finite value in the last slice of the rest
+    raises the flag."""
     torch = torch_mod
     rng = np.random.default_rng(5000 + nd)
     n = 9 * 512 + 13
-    say(f"reduce batches nd={nd} oshift={oshift} n={n}")
+    say(f"reduce batches nd={nd} oshift={oshift} phase={phase} n={n}")
     hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
-    ds = [to_dev16(h) for h in hs]
+    ds = []
+    for r, h in enumerate(hs):
+        o = 4 * (r % 2) if phase == "mixed4" else 0
+        b = torch.zeros(n + 8, dtype=torch.float16, device="cuda")[o:o + n]
+        b.copy_(to_dev16(h))
+        ds.append(b)
     obuf = torch.zeros(n + 8, dtype=torch.float16, device="cuda")
     out = obuf[oshift:oshift + n]
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -206,19 +206,27 @@ inline uint32_t reduce_per_cu_vec8(uint32_t nd) {
 }
 
 // The same for the reduce's other access paths.  vec = 4 (slices sharing
-// only an 8-byte phase; two 8-byte groups per lane per slice): 24 with one
-// slice in flight and 12 with eight, else as above.  vec = 1 (no common
-// phase; eight single elements per lane per slice, half the bytes): twice
-// the above, at most 24, except 8 with eight slices in flight.  Measured
-// on MI355X, 117,187,500 elements, caps 4-24 (fraction of 8 TB/s): 8-byte
-// path N_d = 2 0.685 at 24 against 0.602 at 16, N_d = 4 best at 16
-// (0.852), N_d = 8 0.802 at 12 against 0.774 at 8; single path N_d = 2
-// best at 24 (0.655), N_d = 4 0.703-0.713 at 12-24, N_d = 8 0.713 at 8
-// against 0.658 at 16.
+// only an 8-byte phase; two 8-byte groups per lane per slice, the same
+// batches as the 16-byte path): 24 at 1-2 slices, 12 at 8 (0.754-0.760
+// at 10-12 against 0.751 at 8), else the 16-byte path's.
+// Measured on MI355X, 117,187,500 elements, slices back to back in one
+// buffer (every other one 8 bytes off), caps 4-24 in one process (fraction
+// of 8 TB/s, best cap, against batches of 8, 4 and 1 at their former
+// caps): N_d = 7 0.772 at 10 (0.739), 12 0.749 at 8 (0.738), 16 0.738 at 6
+// (0.718), 17 0.730 at 8 (0.644), 24 0.731 at 6 (0.717), 32 0.724 at 5
+// (0.714), 64 0.732 at 4 (0.713); 2, 4 and 8 equal; the table's cap within
+// 1.2% of the best at every N_d measured (with batches of 8, 4 and 1 the
+// path had 24 with one slice in flight, 0.685 against 0.602 at 16 for
+// N_d = 2, and 12 with eight).  vec = 1 (no common phase; eight single
+// elements per lane per slice in batches of 16, 8, 4 and 1, half the
+// bytes): twice reduce_per_cu's cap, at most 24, except 8 with eight
+// slices in flight.  Measured on MI355X, 117,187,500 elements, caps 4-24
+// (fraction of 8 TB/s): N_d = 2 best at 24 (0.655), N_d = 4 0.703-0.713 at
+// 12-24, N_d = 8 0.713 at 8 against 0.658 at 16.
 inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
     const uint32_t sif = slices_in_flight(nd);
     if (vec == 4)
-        return sif == 1 ? 24u : (sif == 8 ? 12u : reduce_per_cu(nd));
+        return nd <= 2 ? 24u : (nd == 8 ? 12u : reduce_per_cu_vec8(nd));
     if (vec == 1) {
         if (sif == 8)
             return 8u;

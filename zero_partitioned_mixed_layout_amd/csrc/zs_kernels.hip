@@ -1062,6 +1062,24 @@ __device__ __forceinline__ void fused_batch(const SliceArgs &s, uint32_t r0, con
                 acc[k][j] = (first && q == 0) ? (float)x[0][k][j] : acc[k][j] + (float)x[q][k][j];
 }
 
+// Slices r0 .. r0+rest-1 (rest = 1-15) at the Q groups as one batch.
+template <class Fmt, int Q>
+__device__ __forceinline__ void fused_rest(const SliceArgs &s, uint32_t r0, uint32_t rest,
+                                           const uint64_t (&i)[Q], f32x4 (&acc)[Q]) {
+    const bool first = r0 == 0;
+    switch (rest) {
+#define ZS_REST(R)                                                                                 \
+    case R:                                                                                        \
+        fused_batch<Fmt, R, Q>(s, r0, i, first, acc);                                             \
+        break;
+        ZS_REST(1) ZS_REST(2) ZS_REST(3) ZS_REST(4) ZS_REST(5) ZS_REST(6) ZS_REST(7) ZS_REST(8)
+        ZS_REST(9) ZS_REST(10) ZS_REST(11) ZS_REST(12) ZS_REST(13) ZS_REST(14) ZS_REST(15)
+#undef ZS_REST
+    default:
+        break;
+    }
+}
+
 // Q four-element groups at i[0..Q-1] (vector-aligned): the fp32 state is
 // loaded first, then the slices in batches of 16, 8, 4 and 1; then the
 // reduced gradient, the update and the stores.  SHIFT: the 16-bit outputs
@@ -1138,7 +1156,8 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
 // The reduction when the slices and the output share an 8-byte phase but
 // not a 16-byte one: one wave per kTile elements after the head, each lane
 // reducing two groups of four (elements 4L..4L+3 and kTile/2+4L..), so a
-// lane keeps as many bytes per slice in flight as on the 16-byte path; the
+// lane keeps as many bytes per slice in flight as on the 16-byte path
+// (batches of 16 slices, then the rest in one batch); the
 // rank-order sum and the division of reduce_single.  The last, partial tile
 // goes by groups of four, then singly; tile 0 also does the head.
 template <class Fmt, bool SHIFT = false>
@@ -1163,12 +1182,10 @@ __global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint
             const uint64_t i[2] = {lo + 4u * lane, lo + 4u * lane + kTile / 2};
             f32x4 acc[2];
             uint32_t r = 0;
-            for (; r + 8 <= nd; r += 8)
-                fused_batch<Fmt, 8, 2>(s, r, i, r == 0, acc);
-            for (; r + 4 <= nd; r += 4)
-                fused_batch<Fmt, 4, 2>(s, r, i, r == 0, acc);
-            for (; r < nd; r++)
-                fused_batch<Fmt, 1, 2>(s, r, i, r == 0, acc);
+            for (; r + 16 <= nd; r += 16)
+                fused_batch<Fmt, 16, 2>(s, r, i, r == 0, acc);
+            if (r < nd)
+                fused_rest<Fmt, 2>(s, r, nd - r, i, acc);
             typename Fmt::V4 os[2];
 #pragma unroll
             for (int k = 0; k < 2; k++) {
