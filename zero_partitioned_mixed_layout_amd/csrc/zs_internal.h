@@ -205,6 +205,22 @@ inline uint32_t reduce_per_cu_vec8(uint32_t nd) {
     return nd <= 32 ? 5 : 4;
 }
 
+// Tiles per run of one XCD on the reduce's 8-byte path (zs_reduce_vec4_kernel;
+// 0: tiles in launch order).  Its slices sit 8 bytes off their 128-byte
+// lines, so neighbouring tiles share a line of each; in launch order they run
+// on different XCDs and each XCD's L2 reads it (1.117 times the algorithmic
+// bytes from HBM over 64 slices of 117,187,500 elements back to back in one
+// buffer).  Measured on MI355X there, one process, runs of 2-12 tiles
+// (fraction of 8 TB/s against launch order): runs of 4 at N_d = 8 0.800
+// (0.761), 12 0.809 (0.747), 16 0.798 (0.737), 24 0.783 (0.734), 32 0.774
+// (0.732), 48 0.756 (0.725), 64 0.757 (0.733); 4 equal (0.828 against
+// 0.824); 2 lower at every run (0.644-0.659 against 0.686); runs of 3, 6
+// and 12 below those of 2, 4 and 8.  One run per XCD (8 far-apart streams
+// per slice) cut the reads to 1.040 times but ran 5% slower at N_d = 64;
+// on 16-byte-aligned slices, where no line is shared, runs of 2-8 lost up
+// to 9%.
+inline uint32_t reduce_vec4_run(uint32_t nd) { return nd >= 4 ? 4u : 0u; }
+
 // The same for the reduce's other access paths.  vec = 4 (slices sharing
 // only an 8-byte phase; two 8-byte groups per lane per slice, the same
 // batches as the 16-byte path): 24 at 1-2 slices, 12 at 8 (0.754-0.760

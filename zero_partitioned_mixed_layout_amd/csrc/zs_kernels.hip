@@ -1159,19 +1159,30 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
 // lane keeps as many bytes per slice in flight as on the 16-byte path
 // (batches of 16 slices, then the rest in one batch); the
 // rank-order sum and the division of reduce_single.  The last, partial tile
-// goes by groups of four, then singly; tile 0 also does the head.
+// goes by groups of four, then singly; tile 0 also does the head.  With
+// xrun != 0 (the grid a multiple of 8 xrun), workgroup b takes, within each
+// window of 8 xrun tiles, tile (b mod 8) xrun + (b mod 8 xrun) / 8: the
+// workgroups of one XCD (the hardware deals them out in turn, b mod 8) walk
+// runs of xrun neighbouring tiles, so the line that two neighbouring tiles
+// of a slice off its 128-byte lines share is mostly read once into that
+// XCD's L2 instead of once into each of two.
 template <class Fmt, bool SHIFT = false>
 __global__ __launch_bounds__(kWave) void zs_reduce_vec4_kernel(SliceArgs s, uint32_t nd,
                                                                uint64_t n, uint32_t head,
                                                                uint64_t ntiles,
                                                                uint16_t *__restrict__ out,
                                                                int32_t *__restrict__ flag,
-                                                               uint32_t oshift) {
+                                                               uint32_t oshift, uint32_t xrun) {
     const float count = (float)nd;
     const uint32_t lane = threadIdx.x;
     const uint64_t h = head < n ? head : n;
     int bad = 0;
-    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+    uint64_t b0 = blockIdx.x;
+    if (xrun != 0) {
+        const uint32_t w = 8u * xrun, within = blockIdx.x % w;
+        b0 = (uint64_t)(blockIdx.x / w) * w + (within % 8u) * xrun + within / 8u;
+    }
+    for (uint64_t b = b0; b < ntiles; b += gridDim.x) {
         if (b == 0 && lane < h)
             reduce_one<Fmt>(s, nd, lane, count, out, bad);
         const uint64_t lo = h + b * kTile;
@@ -1864,8 +1875,12 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     const uint64_t tiles4 = (n - hh + kTile - 1) / kTile + (n == hh ? 1 : 0);
     const uint64_t want = vec == 8 ? ((n - hh) / 8 + 1 + kWave - 1) / kWave
                           : vec == 4 ? tiles4 : (n + kTile - 1) / kTile;
-    const uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
+    uint32_t grid = (uint32_t)(want < zs::kMaxGrid ? want : zs::kMaxGrid);
     const uint32_t per_cu = zs::reduce_per_cu_path(nd, vec);
+    // the 8-byte path's tiles in runs per XCD: a grid of whole windows
+    const uint32_t xrun = vec == 4 ? zs::reduce_vec4_run(nd) : 0u;
+    if (xrun != 0)
+        grid = (grid + 8u * xrun - 1u) / (8u * xrun) * (8u * xrun);
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     uint16_t *out = (uint16_t *)out_f16;
@@ -1897,10 +1912,10 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
                            n, head, out, nonfinite_flag, 0u);
     else if (vec == 4 && oshift != 0)
         hipLaunchKernelGGL((zs_reduce_vec4_kernel<Fmt, true>), dim3(grid), dim3(kWave), lds, st,
-                           args, nd, n, head, tiles4, out, nonfinite_flag, oshift);
+                           args, nd, n, head, tiles4, out, nonfinite_flag, oshift, xrun);
     else if (vec == 4)
         hipLaunchKernelGGL((zs_reduce_vec4_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
-                           nd, n, head, tiles4, out, nonfinite_flag, 0u);
+                           nd, n, head, tiles4, out, nonfinite_flag, 0u, xrun);
     else
         hipLaunchKernelGGL((zs_reduce_single_kernel<Fmt>), dim3(grid), dim3(kWave), lds, st, args,
                            nd, n, out, nonfinite_flag);
