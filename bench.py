@@ -162,6 +162,11 @@ def parse():
                          "further into the full buffer (1-3: out of the other arrays' 8-byte "
                          "phase, as a rank's view is when the shard length is not a multiple "
                          "of four)")
+    ap.add_argument("--slices-back-to-back", action="store_true",
+                    help="workloads with gradient slices: lay the N_d slices back to back in "
+                         "one buffer (slice r at r times the shard length) instead of rows of a "
+                         "128-byte-aligned pitch; with a shard length of 4 mod 8 every other "
+                         "slice sits 8 bytes off and the reduce takes its 8-byte path")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the step: copy a BYTES-byte device buffer into another "
                          "with torch, --steps times (the plain copy kernel that scales the "
@@ -211,13 +216,28 @@ def plain_copy(stream, nbytes: int = 4 << 30, reps: int = 10) -> dict:
             "avg_us": s * 1e6, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
 
 
+def reduce_kernel_name(rows, out):
+    """The name of the reduce kernel zero_reduce_grad_shard launches over
+    these slices and output, to label its timed launch: zs_reduce_kernel
+    when all share a 16-byte phase (zs_reduce_few_kernel at 1-3 slices),
+    zs_reduce_vec4_kernel when they share an 8-byte one, else
+    zs_reduce_single_kernel (outputs alone out of phase are not told
+    apart: the bench's outputs are aligned)."""
+    ptrs = [r.data_ptr() for r in rows] + [out.data_ptr()]
+    if len({p % 16 for p in ptrs}) == 1:
+        return "zs_reduce_kernel" if len(rows) > 3 else "zs_reduce_few_kernel"
+    if len({p % 8 for p in ptrs}) == 1:
+        return "zs_reduce_vec4_kernel"
+    return "zs_reduce_single_kernel"
+
+
 class Step:
     """Device state and the launches of one step for a workload."""
 
     def __init__(self, zs, W, name, chunk_elems=0, fused=False, gather=False, offload=False,
                  offload_threads=0, bf16=False, list_layout="flat", offload_chunk=0,
                  slices=False, inject_inf=False, loss_scale=None, param_rank=None,
-                 param_shift=0):
+                 param_shift=0, slices_back_to_back=False):
         import numpy as np
         import torch
         self.zs, self.W, self.torch = zs, W, torch
@@ -228,6 +248,7 @@ class Step:
         self.flag = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.rflag = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.rows = None
+        self.reduce_name = "zs_reduce_kernel"
         if len(wl.tensors) == 1:
             lay = zs.zero_shard_layout(wl.psi, wl.nd, wl.rank, wl.align)
             self.layout = lay
@@ -246,7 +267,9 @@ class Step:
                 sh.p = self.full[off:off + lay.real_len]
             self.tensors = [sh]
             if wl.reduce_slices or slices:
-                self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half)
+                self.slice_buf, self.rows = W.device_slices(wl, lay.real_len, half=half,
+                                                            back_to_back=slices_back_to_back)
+                self.reduce_name = reduce_kernel_name(self.rows, sh.g)
             else:
                 W.device_fill_grads(wl, self.tensors, 1)
                 if inject_inf:
@@ -324,7 +347,7 @@ class Step:
         else:
             ks = []
             if self.rows is not None:
-                ks.append(("zs_reduce_kernel", self.reduce, (2 * self.wl.nd + 2) * self.n_params))
+                ks.append((self.reduce_name, self.reduce, (2 * self.wl.nd + 2) * self.n_params))
             if self.offload is not None:
                 ks.append(("zero_offload_step", self.offload_step, 4 * self.n_params))
             else:
@@ -622,7 +645,7 @@ def main():
     step = Step(zs, W, args.workload, args.chunk_elems, args.fused, args.gather, args.offload,
                 args.offload_threads, args.bf16, args.list_layout, args.offload_chunk,
                 args.slices, args.inject_inf, args.loss_scale, args.param_rank,
-                args.param_shift)
+                args.param_shift, args.slices_back_to_back)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -645,7 +668,7 @@ def main():
     headline_plain = (not args.no_per_config and args.workload == "flat_7p5b_nd64" and
                       not (args.fused or args.gather or args.offload or args.bf16 or
                            args.loss_scale is not None or args.param_rank is not None or
-                           args.param_shift))
+                           args.param_shift or args.slices_back_to_back))
     pc_steps = args.per_config_steps or max(10, args.steps)
     by_rank = None
     if headline_plain:
@@ -677,7 +700,8 @@ def main():
            ("+gather" if step.gather else "") + ("+offload" if step.offload else "") +
            ("+bf16" if args.bf16 else "") +
            (f"+param_rank_{args.param_rank}" if args.param_rank is not None else "") +
-           (f"+param_shift_{args.param_shift}" if args.param_shift else ""),
+           (f"+param_shift_{args.param_shift}" if args.param_shift else "") +
+           ("+slices_back_to_back" if args.slices_back_to_back and step.rows is not None else ""),
            "psi": step.wl.psi, "nd": step.wl.nd,
            "rank": step.wl.rank, "align": step.wl.align, "shard_params": step.n_params,
            "tensors": len(step.wl.tensors),
@@ -697,12 +721,13 @@ def main():
         # the buffers in physical memory differs between processes by a few
         # percent, so only a comparison within one process is meaningful
         print("[bench] fused against reduce + Adam, interleaved", file=sys.stderr, flush=True)
-        both = [ks[0], ("zs_reduce_kernel", step.reduce, (2 * step.wl.nd + 2) * step.n_params),
+        rn = step.reduce_name
+        both = [ks[0], (rn, step.reduce, (2 * step.wl.nd + 2) * step.n_params),
                 ("zs_adam_kernel", step.adam, 28 * step.n_params)]
         _, kb = time_steps(torch, stream, both, args.steps)
-        sep_us = kb["zs_reduce_kernel"]["avg_us"] + kb["zs_adam_kernel"]["avg_us"]
+        sep_us = kb[rn]["avg_us"] + kb["zs_adam_kernel"]["avg_us"]
         fused_vs = {"steps": args.steps, "fused_us": round(kb[ks[0][0]]["avg_us"], 3),
-                    "reduce_us": round(kb["zs_reduce_kernel"]["avg_us"], 3),
+                    "reduce_us": round(kb[rn]["avg_us"], 3),
                     "adam_us": round(kb["zs_adam_kernel"]["avg_us"], 3),
                     "separate_us": round(sep_us, 3),
                     "fused_over_separate": round(kb[ks[0][0]]["avg_us"] / sep_us, 4)}

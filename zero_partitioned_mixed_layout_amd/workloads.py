@@ -315,13 +315,14 @@ def device_inject_inf(grad, positions: np.ndarray, signs: np.ndarray) -> None:
     grad.index_copy_(0, pos, val.to(grad.dtype))
 
 
-def device_slices(wl: Workload, length: int, device="cuda", half=None):
+def device_slices(wl: Workload, length: int, device="cuda", half=None, back_to_back=False):
     """N_d fp16 gradient slices of this rank's partition, ~ N(0, 1e-3), as
     rows of one buffer whose row pitch is rounded up to 64 elements (so every
     row starts 128-byte aligned, as separately allocated receive buffers
-    would).  Returns (buffer, [row views])."""
+    would), or with back_to_back at r * length in one buffer (a receive
+    buffer of N_d shards).  Returns (buffer, [row views])."""
     import torch
-    pitch = (length + 63) // 64 * 64
+    pitch = length if back_to_back else (length + 63) // 64 * 64
     buf = torch.zeros(wl.nd, pitch, dtype=half or torch.float16, device=device)
     rows = [buf[r, :length] for r in range(wl.nd)]
     for r in range(wl.nd):
