@@ -259,7 +259,14 @@ inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
 // 0.554 / 0.577 with one group per lane): N_d = 1 0.861-0.868 at 24-28
 // (0.845 at 16), N_d = 2 0.867-0.868 at 16-20, N_d = 3 0.853 at 8 (0.844 at
 // 12, 0.828 at 16).
-inline uint32_t reduce_per_cu_few(uint32_t nd) {
+// With eight groups of four per lane (vec = 4, slices that share only an
+// 8-byte phase, the same 32 elements per lane), over 117,187,500 elements,
+// caps 8-28 in one process, against one 512-element tile per wave with
+// batches of one slice: N_d = 1 0.854 at 28 (0.495), 2 0.854 at 16 (0.680),
+// 3 0.848 at 12 (0.801).
+inline uint32_t reduce_per_cu_few(uint32_t nd, uint32_t vec) {
+    if (vec == 4)
+        return nd == 1 ? 28u : (nd == 2 ? 16u : 12u);
     return nd == 1 ? 27u : (nd == 2 ? 16u : 8u);
 }
 

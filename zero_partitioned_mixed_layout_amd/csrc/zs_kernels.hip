@@ -860,30 +860,32 @@ __global__ __launch_bounds__(kWave) void zs_reduce_kernel(SliceArgs s, uint32_t 
     raise_flag(flag, bad);
 }
 
-// The reduction over ND = 1-3 slices on the 16-byte path: each lane takes
-// four groups of eight (groups lane + 64q of the wave's 256) and issues all
-// 4 ND of its 16-byte loads before the first add (indices past the last
-// group clamped to it, so no load waits on a lane condition); then the
-// rank-order sum and the division of reduce_group per group, the stores of
-// those in range.  With one group per lane and batches of one slice, a wave
-// moved 2-6 KiB in 1-3 dependent round trips: 0.53-0.58 of 8 TB/s.  The
-// unaligned head and the tail past the last whole group go one element per
-// lane, as in zs_reduce_kernel.
-template <class Fmt, int ND>
+// The reduction over ND = 1-3 slices: each lane takes Q = 32 / VEC groups
+// of VEC (VEC = 8: four groups of eight, the 16-byte path; VEC = 4: eight
+// groups of four, slices that share only an 8-byte phase), groups lane +
+// 64q of the wave's 64 Q, and issues all Q ND of its loads before the first
+// add (indices past the last group clamped to it, so no load waits on a
+// lane condition); then the rank-order sum and the division of
+// reduce_group per group, the stores of those in range.  With one group of
+// eight per lane and batches of one slice, a wave moved 2-6 KiB in 1-3
+// dependent round trips: 0.53-0.58 of 8 TB/s.  The unaligned head and the
+// tail past the last whole group go one element per lane, as in
+// zs_reduce_kernel.
+template <class Fmt, int ND, int VEC = 8>
 __global__ __launch_bounds__(kWave) void zs_reduce_few_kernel(SliceArgs s, uint64_t n,
                                                               uint32_t head,
                                                               uint16_t *__restrict__ out,
                                                               int32_t *__restrict__ flag) {
-    constexpr int Q = 4;
-    typedef typename Fmt::V8 hv;
+    constexpr int Q = 32 / VEC;
+    typedef typename HVec<Fmt, VEC>::T hv;
     const float count = (float)ND;
     const uint32_t lane = threadIdx.x;
     const uint64_t gtid = (uint64_t)blockIdx.x * kWave + lane;
     const uint64_t gstride = (uint64_t)gridDim.x * kWave;
     int bad = 0;
     const uint64_t h = head < n ? head : n;
-    const uint64_t ngroups = (n - h) / 8u;
-    const uint64_t body_end = h + ngroups * 8u;
+    const uint64_t ngroups = (n - h) / VEC;
+    const uint64_t body_end = h + ngroups * VEC;
     if (gtid < h)
         reduce_one<Fmt>(s, ND, gtid, count, out, bad);
     for (uint64_t i = body_end + gtid; i < n; i += gstride)
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(kWave) void zs_reduce_few_kernel(SliceArgs s, uint6
             const uint64_t g = min(k0 + lane + (uint64_t)kWave * q, ngroups - 1u);
 #pragma unroll
             for (int r = 0; r < ND; r++)
-                x[q][r] = ld_nt(reinterpret_cast<const hv *>(s.p[r] + h + g * 8u));
+                x[q][r] = ld_nt(reinterpret_cast<const hv *>(s.p[r] + h + g * VEC));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -905,7 +907,7 @@ __global__ __launch_bounds__(kWave) void zs_reduce_few_kernel(SliceArgs s, uint6
                 continue;
             hv o;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
+            for (int j = 0; j < VEC; j++) {
                 float acc = (float)x[q][0][j];
 #pragma unroll
                 for (int r = 1; r < ND; r++)
@@ -916,7 +918,7 @@ __global__ __launch_bounds__(kWave) void zs_reduce_few_kernel(SliceArgs s, uint6
                 memcpy(&b, &oj, 2);
                 bad |= bits_nonfinite<Fmt>(b);
             }
-            st_through(o, reinterpret_cast<hv *>(out + h + g * 8u));
+            st_through(o, reinterpret_cast<hv *>(out + h + g * VEC));
         }
     }
     raise_flag(flag, bad);
@@ -1884,22 +1886,33 @@ int reduce_grad_shard(const void *const *slices_f16, uint32_t nd, uint64_t n, vo
     const size_t lds = lds_cap_bytes(dev, per_cu);
     hipStream_t st = (hipStream_t)stream;
     uint16_t *out = (uint16_t *)out_f16;
-    if (vec == 8 && oshift == 0 && nd <= 3) {
-        // 1-3 slices: four groups per lane, all loads in flight at once
-        const uint64_t groups = (n - hh) / 8;
-        const uint64_t w4 = (groups + 4 * kWave - 1) / (4 * kWave);
+    if ((vec == 8 || vec == 4) && oshift == 0 && nd <= 3) {
+        // 1-3 slices: 32 elements per lane, all loads in flight at once
+        const uint64_t groups = (n - hh) / vec;
+        const uint64_t per_wave = (uint64_t)(32u / vec) * kWave;
+        const uint64_t w4 = (groups + per_wave - 1) / per_wave;
         const uint64_t wf = w4 > 0 ? w4 : 1;
         const uint32_t gf = (uint32_t)(wf < zs::kMaxGrid ? wf : zs::kMaxGrid);
-        const size_t lf = lds_cap_bytes(dev, zs::reduce_per_cu_few(nd));
-        if (nd == 1)
-            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 1>), dim3(gf), dim3(kWave), lf, st,
-                               args, n, head, out, nonfinite_flag);
-        else if (nd == 2)
-            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 2>), dim3(gf), dim3(kWave), lf, st,
-                               args, n, head, out, nonfinite_flag);
-        else
-            hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, 3>), dim3(gf), dim3(kWave), lf, st,
-                               args, n, head, out, nonfinite_flag);
+        const size_t lf = lds_cap_bytes(dev, zs::reduce_per_cu_few(nd, vec));
+#define ZS_FEW(ND, V)                                                                              \
+    hipLaunchKernelGGL((zs_reduce_few_kernel<Fmt, ND, V>), dim3(gf), dim3(kWave), lf, st, args, n, \
+                       head, out, nonfinite_flag)
+        if (vec == 8) {
+            if (nd == 1)
+                ZS_FEW(1, 8);
+            else if (nd == 2)
+                ZS_FEW(2, 8);
+            else
+                ZS_FEW(3, 8);
+        } else {
+            if (nd == 1)
+                ZS_FEW(1, 4);
+            else if (nd == 2)
+                ZS_FEW(2, 4);
+            else
+                ZS_FEW(3, 4);
+        }
+#undef ZS_FEW
         if (hipGetLastError() != hipSuccess)
             return ZERO_EHIP;
         return ZERO_OK;
