@@ -23,9 +23,9 @@
 // workgroup, and each launch reserves dynamic LDS that the kernel never
 // touches (the fused kernel uses 1 KiB of it), so that only a few workgroups
 // are resident per CU (Adam 12 with 256-element tiles, 7 with 512-element
-// tiles, 14-27 for lists of small tensors; reduce 4-16 on its 16-byte
-// path by slice count, 27 / 16 / 8 at 1 / 2 / 3 slices (four groups per
-// lane there); fused 5-12, twice that on its
+// tiles, 14-27 for lists of small tensors; reduce 4-16 on its 16- and
+// 8-byte paths by slice count, 27 / 16 / 8 (28 / 16 / 12 on 8-byte groups)
+// at 1 / 2 / 3 slices (32 elements per lane there); fused 5-12, twice that on its
 // single-element path; gather 16).  Measured on MI355X, HBM3E streams these
 // many-array patterns fastest with just enough bytes in flight to cover
 // latency (about 45 KB per CU); with the 20-30 waves per CU that registers
