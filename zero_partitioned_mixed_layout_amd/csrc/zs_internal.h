@@ -301,12 +301,23 @@ constexpr uint32_t kFusedSplitSlices = ZERO_FUSED_SPLIT_SLICES;
 // 0.753-0.781 at 8 (0.741-0.747), 7 0.772 at 6 (0.707), 9-10 0.784-0.788
 // at 6 (0.711-0.755), 11 0.761-0.763 at 5 (0.670-0.671), 13-15 0.772-0.778
 // at 5 (0.690-0.765); 4, 8 and 12 within 0.4% of the former code.
-inline uint32_t fused_per_cu(uint32_t nd, bool state_late) {
+// The 8-byte path (vec = 4, state first, its 1-15 slices below 16 as one
+// batch) takes about 75 vectors with all of those slices counted: 8 at 1-4
+// slices, 7 at 5-6, 6 at 7-8, 5 at 9-12, 4 from 13.  Measured
+// over 117,187,500 elements, slices back to back in one buffer (every other
+// one 8 bytes off), caps 3-10 in one process (fraction of 8 TB/s against
+// batches of 8, 4 and 1 at the former caps): N_d = 2 0.783 at 8 (0.757), 3
+// 0.769 at 8 (0.714), 5 0.743 at 8 (0.721), 7 0.747 at 6 (0.654), 9 0.759
+// at 6 (0.728), 11 0.751 at 5 (0.647), 15 0.726 at 4 (0.639); 4, 8 and 12
+// equal; the rule within 1% of the best cap at every N_d measured.
+inline uint32_t fused_per_cu(uint32_t nd, bool state_late, uint32_t vec = 8) {
     const uint32_t sif = slices_in_flight(nd);
     if (state_late)
         return nd == 1 ? 12u : (nd <= 6 ? 8u : (nd <= 10 ? 6u : 5u));
-    const uint32_t per_wave = 6 + sif;
-    const uint32_t k = (70 + per_wave - 1) / per_wave;
+    const uint32_t in_flight = vec == 4 ? (nd < 16 ? nd : 16u) : sif;
+    const uint32_t target = vec == 4 ? 75u : 70u;
+    const uint32_t per_wave = 6 + in_flight;
+    const uint32_t k = (target + per_wave - 1) / per_wave;
     return k < 2 ? 2 : (k > 8 ? 8 : k);
 }
 

@@ -1083,7 +1083,7 @@ __device__ __forceinline__ void fused_rest(const SliceArgs &s, uint32_t r0, uint
 }
 
 // Q four-element groups at i[0..Q-1] (vector-aligned): the fp32 state is
-// loaded first, then the slices in batches of 16, 8, 4 and 1; then the
+// loaded first, then the slices in batches of 16 and the rest in one; then the
 // reduced gradient, the update and the stores.  SHIFT: the 16-bit outputs
 // may be out of phase; they are then stored after the state, Q = 2 as a
 // full tile from `base`, Q = 1 as groups of the nq lanes from `base`.
@@ -1104,12 +1104,8 @@ __device__ __forceinline__ void fused_groups(const SliceArgs &s, uint32_t nd,
     uint32_t r = 0;
     for (; r + 16 <= nd; r += 16)
         fused_batch<Fmt, 16, Q>(s, r, i, r == 0, acc);
-    for (; r + 8 <= nd; r += 8)
-        fused_batch<Fmt, 8, Q>(s, r, i, r == 0, acc);
-    for (; r + 4 <= nd; r += 4)
-        fused_batch<Fmt, 4, Q>(s, r, i, r == 0, acc);
-    for (; r < nd; r++)
-        fused_batch<Fmt, 1, Q>(s, r, i, r == 0, acc);
+    if (r < nd)
+        fused_rest<Fmt, Q>(s, r, nd - r, i, acc);
     typename Fmt::V4 gs[Q], ps[Q];
 #pragma unroll
     for (int k = 0; k < Q; k++) {
@@ -2118,7 +2114,7 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     // resident workgroups; the 16-byte path loads the state after the slices
     // when fewer than 16 are in flight per batch
     const bool late = vec == 8 && zs::fused_state_late(nd);
-    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late) * (vec == 1 ? 2u : 1u));
+    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late, vec) * (vec == 1 ? 2u : 1u));
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16, pshift,
