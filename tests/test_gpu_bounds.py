@@ -171,9 +171,10 @@ def test_adam_noalloc_bounds(zs, layout):
     A.check(f"noalloc {layout}, second call")
 
 
-# byte phases of (even slices, odd slices, output): 16-byte, 8-byte and
+# byte phases of (even slices, odd slices, output): 16-byte, 8-byte (every
+# other slice or every slice 8 bytes off the output's 16-byte phase) and
 # 2-byte common phases (the reduce's three paths)
-REDUCE_LAYOUTS = {"v16": (0, 0, 0), "v8": (0, 8, 0), "single": (0, 0, 2)}
+REDUCE_LAYOUTS = {"v16": (0, 0, 0), "v8": (0, 8, 0), "v8_all": (8, 8, 0), "single": (0, 0, 2)}
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
