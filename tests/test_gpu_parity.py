@@ -324,14 +324,15 @@ def test_reduce_matches_oracle(zs, torch_mod, nd, layout):
 
 @pytest.mark.parametrize("nd", [4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 23, 31, 47])
 @pytest.mark.parametrize("oshift", [0, 3])
-@pytest.mark.parametrize("phase", ["aligned", "mixed4"])
+@pytest.mark.parametrize("phase", ["aligned", "mixed4", "odd"])
 def test_reduce_every_batch_size(zs, torch_mod, nd, oshift, phase):
     """The 16- and 8-byte paths load batches of 16 slices and then the rest
-    in one batch: every rest of 1-15 slices (after zero, one and two batches
-    of 16), slices 16-byte aligned or every other one 8 bytes off, the
-    output in the slices' phase and three elements off it, against the
-    oracle bit for bit; a non-finite value in the last slice of the rest
-    raises the flag."""
+    in one batch, the single-element path batches of 8 and then the rest:
+    every rest of 1-15 slices (after zero, one and two batches of 16),
+    slices 16-byte aligned, every other one 8 bytes off, or at r mod 3
+    elements (no common phase), the output in the slices' phase and three
+    elements off it, against the oracle bit for bit; a non-finite value in
+    the last slice of the rest raises the flag."""
     torch = torch_mod
     rng = np.random.default_rng(5000 + nd)
     n = 9 * 512 + 13
@@ -339,7 +340,7 @@ def test_reduce_every_batch_size(zs, torch_mod, nd, oshift, phase):
     hs = [(rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(nd)]
     ds = []
     for r, h in enumerate(hs):
-        o = 4 * (r % 2) if phase == "mixed4" else 0
+        o = 4 * (r % 2) if phase == "mixed4" else (r % 3 if phase == "odd" else 0)
         b = torch.zeros(n + 8, dtype=torch.float16, device="cuda")[o:o + n]
         b.copy_(to_dev16(h))
         ds.append(b)

@@ -234,21 +234,20 @@ inline uint32_t reduce_vec4_run(uint32_t nd) { return nd >= 4 ? 4u : 0u; }
 // 1.2% of the best at every N_d measured (with batches of 8, 4 and 1 the
 // path had 24 with one slice in flight, 0.685 against 0.602 at 16 for
 // N_d = 2, and 12 with eight).  vec = 1 (no common phase; eight single
-// elements per lane per slice in batches of 16, 8, 4 and 1, half the
-// bytes): twice reduce_per_cu's cap, at most 24, except 8 with eight
-// slices in flight.  Measured on MI355X, 117,187,500 elements, caps 4-24
-// (fraction of 8 TB/s): N_d = 2 best at 24 (0.655), N_d = 4 0.703-0.713 at
-// 12-24, N_d = 8 0.713 at 8 against 0.658 at 16.
+// elements per lane per slice, batches of 8 slices and then the rest in
+// one, half the bytes): 24 at 1-2 slices, 16 at 3, 12 at 4-5, 8 at 6-23, 6
+// from 24.  Measured on MI355X, 117,187,501 elements, slices back to back
+// in one buffer (every 2-byte phase), caps 4-24 in one process (fraction
+// of 8 TB/s against batches of 8, 4 and 1 at twice reduce_per_cu's cap, at
+// most 24, 8 with eight slices in flight): N_d = 2 0.724 at 24 (0.664), 3
+// 0.728 at 16 (0.691), 4-5 0.706-0.712 at 12 (0.672-0.680), 6-7
+// 0.687-0.707 at 8 (0.655-0.659), 8 0.697 (0.698), 11-16 0.681-0.691 at 8
+// (0.623-0.659), 24-64 0.662-0.668 at 6 (0.651-0.660).
 inline uint32_t reduce_per_cu_path(uint32_t nd, uint32_t vec) {
-    const uint32_t sif = slices_in_flight(nd);
     if (vec == 4)
         return nd <= 2 ? 24u : (nd == 8 ? 12u : reduce_per_cu_vec8(nd));
-    if (vec == 1) {
-        if (sif == 8)
-            return 8u;
-        const uint32_t k = 2u * reduce_per_cu(nd);
-        return k > 24u ? 24u : k;
-    }
+    if (vec == 1)
+        return nd <= 2 ? 24u : (nd == 3 ? 16u : (nd <= 5 ? 12u : (nd < 24 ? 8u : 6u)));
     return reduce_per_cu_vec8(nd);
 }
 

@@ -949,8 +949,8 @@ __device__ __forceinline__ void reduce_batch_single(const SliceArgs &s, uint32_t
 // The reduction when the slices and the output share no common phase: one
 // wave per kTile elements, lane L taking elements L + 64k (k < 8), so every
 // two-byte load and store instruction of the wave is one contiguous
-// 128-byte range; slices in batches of 8, 4 and 1, each batch's loads all
-// in flight before its adds; the sum in rank order and one division, as
+// 128-byte range; slices in batches of 8 and then the rest (1-7) in one,
+// each batch's loads all in flight before its adds; the sum in rank order and one division, as
 // reduce_single.  A partial last tile goes element by element.
 template <class Fmt>
 __global__ __launch_bounds__(kWave) void zs_reduce_single_kernel(SliceArgs s, uint32_t nd,
@@ -973,10 +973,16 @@ __global__ __launch_bounds__(kWave) void zs_reduce_single_kernel(SliceArgs s, ui
         uint32_t r = 0;
         for (; r + 8 <= nd; r += 8)
             reduce_batch_single<8, Fmt>(s, r, i0, r == 0, acc);
-        for (; r + 4 <= nd; r += 4)
-            reduce_batch_single<4, Fmt>(s, r, i0, r == 0, acc);
-        for (; r < nd; r++)
-            reduce_batch_single<1, Fmt>(s, r, i0, r == 0, acc);
+        switch (nd - r) {
+#define ZS_REST(R)                                                                                 \
+    case R:                                                                                        \
+        reduce_batch_single<R, Fmt>(s, r, i0, r == 0, acc);                                       \
+        break;
+            ZS_REST(1) ZS_REST(2) ZS_REST(3) ZS_REST(4) ZS_REST(5) ZS_REST(6) ZS_REST(7)
+#undef ZS_REST
+        default:
+            break;
+        }
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const typename Fmt::T o = (typename Fmt::T)(acc[k] / count);
