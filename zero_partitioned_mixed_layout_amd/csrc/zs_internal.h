@@ -309,8 +309,18 @@ constexpr uint32_t kFusedSplitSlices = ZERO_FUSED_SPLIT_SLICES;
 // 0.769 at 8 (0.714), 5 0.743 at 8 (0.721), 7 0.747 at 6 (0.654), 9 0.759
 // at 6 (0.728), 11 0.751 at 5 (0.647), 15 0.726 at 4 (0.639); 4, 8 and 12
 // equal; the rule within 1% of the best cap at every N_d measured.
+// The single-element path (vec = 1, no common phase; batches of 8 slices
+// and then the rest in one, half the bytes per wave) takes 8 at 1-5 slices
+// and 6 from 6: over 117,187,501 elements, slices back to back in one
+// buffer (every 2-byte phase), caps 4-16 in one process, against twice the
+// state-first rule above (10-16): N_d = 2 0.726 (0.704), 3 0.707 (0.685), 5
+// 0.694 (0.677), 7 0.673 (0.662), 8 0.685 (0.663), 11 0.695 (0.666), 15
+// 0.671 (0.650); a second process: 2 0.709 (0.716), 8 0.720 (0.719), 11
+// 0.690 (0.667).
 inline uint32_t fused_per_cu(uint32_t nd, bool state_late, uint32_t vec = 8) {
     const uint32_t sif = slices_in_flight(nd);
+    if (vec == 1)
+        return nd <= 5 ? 8u : 6u;
     if (state_late)
         return nd == 1 ? 12u : (nd <= 6 ? 8u : (nd <= 10 ? 6u : 5u));
     const uint32_t in_flight = vec == 4 ? (nd < 16 ? nd : 16u) : sif;

@@ -946,6 +946,23 @@ __device__ __forceinline__ void reduce_batch_single(const SliceArgs &s, uint32_t
         }
 }
 
+// Slices r0 .. r0+rest-1 (rest = 0-7) at a lane's eight single elements as
+// one batch.
+template <class Fmt>
+__device__ __forceinline__ void reduce_rest_single(const SliceArgs &s, uint32_t r0, uint32_t rest,
+                                                   uint64_t i0, float (&acc)[8]) {
+    switch (rest) {
+#define ZS_REST(R)                                                                                 \
+    case R:                                                                                        \
+        reduce_batch_single<R, Fmt>(s, r0, i0, r0 == 0, acc);                                     \
+        break;
+        ZS_REST(1) ZS_REST(2) ZS_REST(3) ZS_REST(4) ZS_REST(5) ZS_REST(6) ZS_REST(7)
+#undef ZS_REST
+    default:
+        break;
+    }
+}
+
 // The reduction when the slices and the output share no common phase: one
 // wave per kTile elements, lane L taking elements L + 64k (k < 8), so every
 // two-byte load and store instruction of the wave is one contiguous
@@ -973,16 +990,7 @@ __global__ __launch_bounds__(kWave) void zs_reduce_single_kernel(SliceArgs s, ui
         uint32_t r = 0;
         for (; r + 8 <= nd; r += 8)
             reduce_batch_single<8, Fmt>(s, r, i0, r == 0, acc);
-        switch (nd - r) {
-#define ZS_REST(R)                                                                                 \
-    case R:                                                                                        \
-        reduce_batch_single<R, Fmt>(s, r, i0, r == 0, acc);                                       \
-        break;
-            ZS_REST(1) ZS_REST(2) ZS_REST(3) ZS_REST(4) ZS_REST(5) ZS_REST(6) ZS_REST(7)
-#undef ZS_REST
-        default:
-            break;
-        }
+        reduce_rest_single<Fmt>(s, r, nd - r, i0, acc);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const typename Fmt::T o = (typename Fmt::T)(acc[k] / count);
@@ -1331,7 +1339,8 @@ __device__ __forceinline__ void fused_tile8(const SliceArgs &s, uint32_t nd, uin
 // A full tile of the fused step when the slices, parameter and state share
 // no common phase: lane L takes elements L + 64k (k < 8), every access
 // instruction of the wave contiguous; the fp32 state is loaded first, the
-// slices in batches of 8, 4 and 1 (loads in flight before the adds), then
+// slices in batches of 8 and then the rest in one (loads in flight before
+// the adds), then
 // the same per-element reduction, narrowing and update as fused_single.
 template <class Fmt>
 __device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t nd, uint64_t lo,
@@ -1352,10 +1361,7 @@ __device__ __forceinline__ void fused_tile_single(const SliceArgs &s, uint32_t n
     uint32_t r = 0;
     for (; r + 8 <= nd; r += 8)
         reduce_batch_single<8, Fmt>(s, r, i0, r == 0, acc);
-    for (; r + 4 <= nd; r += 4)
-        reduce_batch_single<4, Fmt>(s, r, i0, r == 0, acc);
-    for (; r < nd; r++)
-        reduce_batch_single<1, Fmt>(s, r, i0, r == 0, acc);
+    reduce_rest_single<Fmt>(s, r, nd - r, i0, acc);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         const uint64_t i = i0 + (uint64_t)kWave * k;
@@ -2116,11 +2122,10 @@ int reduce_adam_step(const void *const *slices_f16, uint32_t nd, uint64_t n, voi
     const uint64_t h = head < n ? head : n;
     const uint64_t ntiles = (n - h + kTile - 1) / kTile + (n == h ? 1 : 0);
     const uint32_t grid = (uint32_t)(ntiles < zs::kMaxGrid ? ntiles : zs::kMaxGrid);
-    // the single-element path keeps fewer bytes per wave in flight: twice the
-    // resident workgroups; the 16-byte path loads the state after the slices
-    // when fewer than 16 are in flight per batch
+    // the 16-byte path loads the state after the slices when fewer than 16
+    // are in flight per batch
     const bool late = vec == 8 && zs::fused_state_late(nd);
-    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late, vec) * (vec == 1 ? 2u : 1u));
+    size_t lds = lds_cap_bytes(dev, zs::fused_per_cu(nd, late, vec));
     if (lds < 2u * kTile)
         lds = 2u * kTile; // the fp16 exchange buffer of fused_tile8
     const FlatState F = {(uint16_t *)param_f16, master, m, v, (uint16_t *)grad_out_f16, pshift,
